@@ -1,0 +1,19 @@
+"""Exact grouped-query decode attention over a KV cache, HIP on MI355X (gfx950).
+
+The compute lives in ``libgqa_decode.so`` (hand-written HIP kernels behind a
+C ABI, declared in ``include/gqa_decode.h``).  ``kv_append``,
+``attend_decode`` and ``softmax_state_merge`` here are thin ctypes bindings:
+they marshal torch tensors and the current HIP stream into the C calls.  The
+library is loaded on first use and a missing build raises at once.
+"""
+
+__all__ = ["kv_append", "attend_decode", "softmax_state_merge",
+           "attend_partition", "attend_combine", "attend_plan",
+           "workspace_bytes", "Carry", "empty_carry", "GqaError", "library"]
+
+
+def __getattr__(name):
+    if name in __all__:
+        from . import binding
+        return getattr(binding, name)
+    raise AttributeError(name)

@@ -1,0 +1,13 @@
+"""CPU oracle for exact GQA decode attention (test infrastructure only).
+
+Only ``tests/``, the smoke check in ``__graft_entry__`` and the CPU-baseline leg
+of ``bench.py`` may import this package.  It shares no code with the HIP path.
+"""
+
+from .attention import (Carry, attend, empty_carry, finalize, group_logits,
+                        kv_append, kv_head_of, live_length, merge,
+                        resolve_scale, softmax_state)
+
+__all__ = ["Carry", "attend", "empty_carry", "finalize", "group_logits",
+           "kv_append", "kv_head_of", "live_length", "merge", "resolve_scale",
+           "softmax_state"]

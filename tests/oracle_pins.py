@@ -1,0 +1,345 @@
+"""Pins for the CPU oracle: checks against what the pages and the mathematics fix.
+
+Each ``pin_*`` takes an oracle module (``oracle.attention`` or a copy of it with
+a planted mistake) and raises ``AssertionError`` when the oracle breaks the
+property.  None of them re-types the oracle's two-pass formula: they use
+closed forms (equal keys give the plain mean; a dominant key returns its own
+value row), a library routine (torch's fp64 ``scaled_dot_product_attention`` on
+repeat-copied heads), exact 50-digit evaluation of the softmax definition
+without a max shift, the carry algebra (any split merged equals one pass), the
+page's own recovery-trial reference, and special cases.
+"""
+
+from __future__ import annotations
+
+import itertools
+import json
+import math
+from decimal import Decimal, localcontext
+from pathlib import Path
+
+import numpy as np
+import torch
+
+GOLDEN = Path(__file__).parent / "golden"
+
+
+def _problem(seed, B, Hq, Hkv, dk, dv, T, lens=None, poison=True,
+             dyadic=False):
+    """Random problem; padding slots past each length are NaN-poisoned."""
+    rng = np.random.default_rng(seed)
+    if dyadic:
+        q = rng.integers(-16, 17, (B, Hq, dk)) / 16.0
+        k = rng.integers(-16, 17, (B, T, Hkv, dk)) / 16.0
+        v = rng.integers(-16, 17, (B, T, Hkv, dv)) / 16.0
+    else:
+        q = rng.uniform(-1, 1, (B, Hq, dk))
+        k = rng.uniform(-1, 1, (B, T, Hkv, dk))
+        v = rng.uniform(-1, 1, (B, T, Hkv, dv))
+    lens = np.full(B, T) if lens is None else np.asarray(lens)
+    if poison:
+        for b in range(B):
+            n = int(min(max(lens[b], 0), T))
+            k[b, n:] = np.nan
+            v[b, n:] = np.nan
+    return q, k, v, lens
+
+
+def _close(a, b, tol, what):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    assert np.all(np.isfinite(a) == np.isfinite(b)), f"{what}: finiteness"
+    fin = np.isfinite(b)
+    assert np.array_equal(a[~fin], b[~fin]), f"{what}: non-finite entries"
+    err = np.max(np.abs(a[fin] - b[fin])) if fin.any() else 0.0
+    assert err <= tol, f"{what}: max err {err:.3e} > {tol:.3e}"
+
+
+# --- closed forms ---------------------------------------------------------
+
+def pin_equal_keys(orc):
+    """All live keys of a group equal (or q = 0): every weight is 1/n, so the
+    output is the plain mean of the group's live value rows (math.fsum)."""
+    B, Hq, Hkv, dk, dv, T = 3, 8, 4, 16, 8, 37
+    q, k, v, lens = _problem(1, B, Hq, Hkv, dk, dv, T, lens=[37, 20, 1])
+    for b in range(B):
+        n = int(lens[b])
+        k[b, :n] = k[b, :1]
+    q[1] = 0.0                       # q = 0: any keys give the mean too
+    rng = np.random.default_rng(2)
+    k[1, :20] = rng.uniform(-1, 1, (20, Hkv, dk))
+    out, c = orc.attend(q, k, v, lens, scale=0.3)
+    hpk = Hq // Hkv
+    for b in range(B):
+        n = int(lens[b])
+        for h in range(Hq):
+            g = h // hpk             # needle-core: kv_hi = hi / kv_repeat
+            want = [math.fsum(v[b, :n, g, c_]) / n for c_ in range(dv)]
+            _close(out[b, h], want, 1e-14, f"mean b={b} h={h}")
+            _close(c.l[b * Hq + h], float(n), 1e-12, "partition of equal keys")
+
+
+def pin_dominant_key(orc):
+    """One key per group leads every other logit by > 800: its weight is 1 to
+    far below fp64 rounding, so the output is that key's value row, and the
+    running max is its logit.  Logits near 1000 also overflow exp() unless the
+    maximum is taken out first."""
+    B, Hq, Hkv, dk, dv, T = 2, 4, 2, 8, 5, 50
+    q, k, v, lens = _problem(3, B, Hq, Hkv, dk, dv, T, lens=[50, 33])
+    q[:, :, 0] = 1.0
+    pos = {(0, 0): 7, (0, 1): 49, (1, 0): 0, (1, 1): 32}
+    for (b, g), p in pos.items():
+        k[b, p, g, 0] = 1000.0
+    out, c = orc.attend(q, k, v, lens, scale=1.0)
+    hpk = Hq // Hkv
+    for b in range(B):
+        for h in range(Hq):
+            g = h // hpk
+            p = pos[(b, g)]
+            _close(out[b, h], v[b, p, g], 1e-13, f"dominant b={b} h={h}")
+            s_p = math.fsum(q[b, h, c_] * k[b, p, g, c_] for c_ in range(dk))
+            _close(c.m[b * Hq + h], s_p, 1e-9, "max logit")
+            _close(c.l[b * Hq + h], 1.0, 1e-14, "partition of dominant key")
+
+
+def pin_recovery_trial(orc):
+    """The recovery trial of the cortiq-engine page: the exact answer's
+    channel 0 is the planted key's softmax weight; the page's reference
+    computes it from f32 logits and f64 exponentials.  An exact method gives
+    got[0] / want0 = 1."""
+    spec = json.loads((GOLDEN / "recovery_trial.json").read_text())
+    fixed, ours = spec["what_the_page_fixes"], spec["our_choices"]
+    d, dv, w, m = fixed["d"], fixed["dv"], ours["w"], ours["m"]
+    tol = ours["ratio_tolerance"]
+    for case in ours["cases"]:
+        amp, depth = case["amp"], case["depth"]
+        rng = np.random.default_rng(case["seed"])
+        unif = lambda n: rng.uniform(-1.0, 1.0, n).astype(np.float32)
+        t = 8 * m + w + depth
+
+        def unit():
+            u = unif(d)
+            return u / np.float32(np.sqrt(np.sum(u * u, dtype=np.float32)))
+
+        q_hat = unit()
+        rd = np.float32(np.sqrt(np.float32(d)))
+        q = q_hat * rd
+        ks = unif(t * d).reshape(t, d) * np.float32(1.732)
+        vs = unif(t * dv).reshape(t, dv)
+        vs[:, 0] = 0.0
+        p = t - depth
+        ks[p] += np.float32(amp) * q_hat
+        vs[p, 0] = 1.0
+        k_new = unif(d) * np.float32(1.732)
+        v_new = unif(dv)
+        v_new[0] = 0.0
+        # the page's exact reference: f32 logits, their max, f64 exp sums
+        keys = np.vstack([ks, k_new[None]])
+        vals = np.vstack([vs, v_new[None]])
+        logits = [np.float32(np.sum(q * keys[j], dtype=np.float32)) / rd
+                  for j in range(t + 1)]
+        mx = max(logits)
+        den = num0 = 0.0
+        for j, lg in enumerate(logits):
+            e = math.exp(float(np.float32(lg - mx)))
+            den += e
+            num0 += e * float(vals[j, 0])
+        want0 = num0 / den
+        assert abs(want0) >= 1e-4, "trial case too weak to measure"
+        out, _ = orc.attend(q[None, None].astype(np.float64),
+                            keys[None, :, None].astype(np.float64),
+                            vals[None, :, None].astype(np.float64),
+                            [t + 1], scale=1.0 / math.sqrt(d))
+        ratio = out[0, 0, 0] / want0
+        assert abs(ratio - 1.0) <= tol, f"recovery ratio {ratio} ({case})"
+
+
+# --- library routine ------------------------------------------------------
+
+def pin_gqa_is_repeated_mha(orc):
+    """GQA broadcasts each KV head to its group (needle-core module doc:
+    broadcast, not repeat-copy).  It must equal plain multi-head attention on
+    K/V repeat-copied per query head, which torch's fp64 CPU
+    scaled_dot_product_attention computes independently.  scale = 0 must give
+    torch's default 1/sqrt(key width) (dk != dv here)."""
+    B, Hq, Hkv, dk, dv, T = 2, 12, 3, 24, 40, 29
+    q, k, v, lens = _problem(4, B, Hq, Hkv, dk, dv, T, lens=[29, 11])
+    hpk = Hq // Hkv
+    out, _ = orc.attend(q, k, v, lens, scale=0.0)
+    out_mha, _ = orc.attend(q, np.repeat(k, hpk, axis=2),
+                            np.repeat(v, hpk, axis=2), lens, scale=0.0)
+    _close(out, out_mha, 1e-14, "gqa vs repeated mha (oracle)")
+    for b in range(B):
+        n = int(lens[b])
+        qt = torch.from_numpy(q[b]).reshape(1, Hq, 1, dk)
+        kt = torch.from_numpy(np.ascontiguousarray(k[b, :n])).permute(1, 0, 2)
+        vt = torch.from_numpy(np.ascontiguousarray(v[b, :n])).permute(1, 0, 2)
+        kt = kt.repeat_interleave(hpk, dim=0).unsqueeze(0).contiguous()
+        vt = vt.repeat_interleave(hpk, dim=0).unsqueeze(0).contiguous()
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt)
+        _close(out[b], ref[0, :, 0].numpy(), 1e-13, f"vs torch sdpa b={b}")
+
+
+# --- exact evaluation of the definition -----------------------------------
+
+def pin_brute_force(orc):
+    """Tiny dyadic inputs (exact in binary) evaluated at 50 digits straight
+    from the softmax definition w_j = exp(s_j) / sum_i exp(s_i), with no max
+    shift; m is the largest logit and l the sum of exp(s_j - m)."""
+    B, Hq, Hkv, dk, dv, T = 2, 4, 2, 3, 3, 6
+    q, k, v, lens = _problem(5, B, Hq, Hkv, dk, dv, T, lens=[6, 4],
+                             dyadic=True)
+    scale = 0.75
+    out, c = orc.attend(q, k, v, lens, scale=scale)
+    hpk = Hq // Hkv
+    with localcontext() as ctx:
+        ctx.prec = 50
+        for b in range(B):
+            n = int(lens[b])
+            for h in range(Hq):
+                g = h // hpk
+                s = [Decimal(scale) * sum(Decimal(float(q[b, h, i])) *
+                                          Decimal(float(k[b, j, g, i]))
+                                          for i in range(dk))
+                     for j in range(n)]
+                ex = [x.exp() for x in s]
+                z = sum(ex)
+                for ch in range(dv):
+                    want = sum(e * Decimal(float(v[b, j, g, ch]))
+                               for j, e in enumerate(ex)) / z
+                    got = Decimal(float(out[b, h, ch]))
+                    assert abs(got - want) <= Decimal("1e-14"), \
+                        f"brute force out b={b} h={h} c={ch}: {got} vs {want}"
+                mx = max(s)
+                lw = sum((x - mx).exp() for x in s)
+                r = b * Hq + h
+                assert abs(Decimal(float(c.m[r])) - mx) <= Decimal("1e-14"), \
+                    "brute force m"
+                assert abs(Decimal(float(c.l[r])) - lw) <= Decimal("1e-13"), \
+                    "brute force l"
+                for ch in range(dv):
+                    wa = sum((x - mx).exp() * Decimal(float(v[b, j, g, ch]))
+                             for j, x in enumerate(s))
+                    assert abs(Decimal(float(c.acc[r, ch])) - wa) <= \
+                        Decimal("1e-13"), "brute force acc"
+
+
+# --- carry algebra --------------------------------------------------------
+
+def pin_split_merge(orc):
+    """Folding the carries of any split of the keys equals one pass over all
+    of them (usearch carry: partial-softmax rescaling).  Checked for every
+    split point, through merge() and through carry_in, and for every order of
+    a three-way merge; the empty state is the identity."""
+    B, Hq, Hkv, dk, dv, T = 2, 4, 2, 8, 6, 23
+    q, k, v, lens = _problem(6, B, Hq, Hkv, dk, dv, T, lens=[23, 9])
+    scale = 0.5
+    out_all, c_all = orc.attend(q, k, v, lens, scale=scale)
+
+    def part(lo, hi):
+        ln = [max(0, min(int(x), hi) - lo) for x in lens]
+        return orc.attend(q, k[:, lo:hi], v[:, lo:hi], ln, scale=scale)
+
+    def same(c, what):
+        _close(c.m, c_all.m, 1e-13, what + " m")
+        _close(c.l, c_all.l, 1e-12, what + " l")
+        _close(c.acc, c_all.acc, 1e-12, what + " acc")
+        _close(orc.finalize(c).reshape(out_all.shape), out_all, 1e-13,
+               what + " out")
+
+    for s in range(T + 1):
+        a, b_ = part(0, s)[1], part(s, T)[1]
+        same(orc.merge(a, b_), f"split {s}")
+        same(orc.merge(b_, a), f"split {s} swapped")
+        ln = [max(0, int(x) - s) for x in lens]
+        out2, c2 = orc.attend(q, k[:, s:], v[:, s:], ln, scale=scale,
+                              carry_in=a)
+        same(c2, f"carry_in split {s}")
+    pieces = [part(0, 5)[1], part(5, 14)[1], part(14, T)[1]]
+    for p in itertools.permutations(range(3)):
+        x, y, z = (pieces[i] for i in p)
+        same(orc.merge(orc.merge(x, y), z), f"three-way {p} left")
+        same(orc.merge(x, orc.merge(y, z)), f"three-way {p} right")
+    rows = B * Hq
+    same(orc.merge(orc.empty_carry(rows, dv), c_all), "empty left")
+    same(orc.merge(c_all, orc.empty_carry(rows, dv)), "empty right")
+    zero_default = orc.Carry(np.zeros(rows), np.zeros(rows),
+                             np.zeros((rows, dv)))
+    same(orc.merge(zero_default, c_all), "default (0, 0) state is empty")
+
+
+# --- special cases --------------------------------------------------------
+
+def pin_special_cases(orc):
+    """n = 1 returns its value row with l = 1; a vanishing scale gives the
+    mean; permuting the live (K, V) rows changes nothing; the output is linear
+    in V; an empty key set gives 0 and an empty carry, never NaN (DSA
+    pool_states guard); lengths clamp into [0, max_len]."""
+    B, Hq, Hkv, dk, dv, T = 2, 6, 3, 10, 7, 19
+    q, k, v, lens = _problem(7, B, Hq, Hkv, dk, dv, T, lens=[1, 19])
+    out, c = orc.attend(q, k, v, lens, scale=0.9)
+    hpk = Hq // Hkv
+    for h in range(Hq):
+        g = h // hpk
+        _close(out[0, h], v[0, 0, g], 0.0, "n = 1 output")
+        _close(c.l[h], 1.0, 0.0, "n = 1 partition")
+        s0 = 0.9 * math.fsum(q[0, h, i] * k[0, 0, g, i] for i in range(dk))
+        _close(c.m[h], s0, 1e-14, "n = 1 max")
+
+    out_tiny, _ = orc.attend(q, k, v, lens, scale=1e-30)
+    for h in range(Hq):
+        g = h // hpk
+        want = [math.fsum(v[1, :19, g, ch]) / 19 for ch in range(dv)]
+        _close(out_tiny[1, h], want, 1e-14, "vanishing scale mean")
+
+    perm = np.random.default_rng(8).permutation(19)
+    kp, vp = k.copy(), v.copy()
+    kp[1, :19], vp[1, :19] = k[1, perm], v[1, perm]
+    outp, cp = orc.attend(q, kp, vp, lens, scale=0.9)
+    _close(outp, out, 1e-14, "permutation invariance")
+    _close(cp.m, c.m, 0.0, "permutation invariance of m")
+
+    rng = np.random.default_rng(9)
+    v2 = rng.uniform(-1, 1, v.shape)
+    out2, _ = orc.attend(q, k, v2, lens, scale=0.9)
+    out3, _ = orc.attend(q, k, 2.0 * v - 3.0 * v2, lens, scale=0.9)
+    _close(out3, 2.0 * out - 3.0 * out2, 1e-13, "linearity in V")
+
+    oute, ce = orc.attend(q, k, v, [0, -5], scale=0.9)
+    assert np.all(oute == 0.0), "empty key set must give 0"
+    assert np.all(ce.l == 0.0) and np.all(ce.acc == 0.0), "empty carry"
+    assert np.all(np.isneginf(ce.m)), "empty carry max is -inf"
+
+    outc, _ = orc.attend(q, k, v, [1, 10 ** 6], scale=0.9)
+    _close(outc, out, 0.0, "length clamps to max_len")
+
+
+def pin_kv_append(orc):
+    """needle-core KvCache::push_kv: a full cache is left untouched (the page
+    warns and returns); otherwise slot `len` receives the token's rows for
+    every KV head and the length grows by one.  Bit copy on uint16 words."""
+    B, T, Hkv, dk, dv = 5, 4, 3, 6, 2
+    rng = np.random.default_rng(10)
+    k = rng.integers(0, 65536, (B, T, Hkv, dk), dtype=np.uint16)
+    v = rng.integers(0, 65536, (B, T, Hkv, dv), dtype=np.uint16)
+    kn = rng.integers(0, 65536, (B, Hkv, dk), dtype=np.uint16)
+    vn = rng.integers(0, 65536, (B, Hkv, dv), dtype=np.uint16)
+    lens = np.array([0, 2, 4, 3, 7], dtype=np.int32)
+    k2, v2, lens2, dropped = orc.kv_append(k, v, kn, vn, lens)
+    assert list(lens2) == [1, 3, 4, 4, 7], f"lens after append {lens2}"
+    assert dropped == 2, f"dropped {dropped}"
+    for b, slot in [(0, 0), (1, 2), (3, 3)]:
+        assert np.array_equal(k2[b, slot], kn[b]) and \
+            np.array_equal(v2[b, slot], vn[b]), f"written row b={b}"
+        keep = [s for s in range(T) if s != slot]
+        assert np.array_equal(k2[b, keep], k[b, keep]), "other slots kept"
+        assert np.array_equal(v2[b, keep], v[b, keep]), "other slots kept"
+    for b in (2, 4):
+        assert np.array_equal(k2[b], k[b]) and np.array_equal(v2[b], v[b]), \
+            "full cache untouched"
+
+
+ALL_PINS = [pin_equal_keys, pin_dominant_key, pin_recovery_trial,
+            pin_gqa_is_repeated_mha, pin_brute_force, pin_split_merge,
+            pin_special_cases, pin_kv_append]
