@@ -1,0 +1,340 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of exact GQA decode attention on one MI355X.
+
+One step is the whole hot path on one batch: kv_append of the new token, then
+attend_decode (split-K partition + log-sum-exp combine) over the cache
+including it; the long-context workload also folds its recent window in
+through the carry.  Prints ONE JSON line on stdout; diagnostics go to stderr.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+The timed region replays a HIP graph of K steps with all inputs resident in
+HBM.  Successive steps rotate over R copies of the cache (R * cache >= 1 GiB
+where memory allows) so that each step streams from HBM rather than from the
+256 MB last-level cache.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+if str(ROOT) not in sys.path:
+    sys.path.insert(0, str(ROOT))
+
+METRIC = ("KV-cache GB/s streamed (and % HBM peak) in GQA decode; "
+          "µs per decode step")
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published figure
+ROTATE_TARGET_BYTES = 1 << 30
+PARTITION_SOURCE = ROOT / "gqa_kv_cache_decode_amd" / "csrc" / "partition_bf16.hip"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=60)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="batched",
+                   choices=["tiny", "batched", "ragged", "long", "spike"])
+    p.add_argument("--rotate", type=int, default=0,
+                   help="cache copies to rotate over (0 = enough for 1 GiB)")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="budget of the oracle's CPU-baseline timing")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-ceiling", action="store_true")
+    return p.parse_args()
+
+
+def workload_by_name(name):
+    from gqa_kv_cache_decode_amd import workloads as wl
+    return {"tiny": wl.TINY_F32, "batched": wl.BATCHED_BF16,
+            "ragged": wl.RAGGED_BF16, "long": wl.LONG_WINDOW_BF16,
+            "spike": wl.WIDE_SPIKE_BF16}[name]
+
+
+def kv_bytes(w, lens_total, hkv=None):
+    return lens_total * (hkv or w.num_kv_heads) * (w.dk + w.dv) * w.esz
+
+
+class Branch:
+    """One attend branch: R cache copies, lens before/after the append."""
+
+    def __init__(self, g, torch, w, k, v, lens_after, copies, append):
+        self.w = w
+        self.k = [k] + [k.clone() for _ in range(copies - 1)]
+        self.v = [v] + [v.clone() for _ in range(copies - 1)]
+        self.append = append
+        self.lens_after = lens_after
+        self.lens_before = (lens_after - 1).clamp_(min=0) if append else None
+        self.lens_cur = [lens_after.clone() for _ in range(copies)]
+        self.plan = g.attend_plan(self.k[0], self.v[0], w.num_q_heads)
+        self.ws = torch.empty(self.plan.workspace_bytes, dtype=torch.uint8,
+                              device="cuda")
+        self.n_tot = int(lens_after.clamp(0, k.shape[1]).sum().item())
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not "
+              "supported (the decode path needs no collectives).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gqa_kv_cache_decode_amd as g
+    from gqa_kv_cache_decode_amd import workloads as wl
+
+    w = workload_by_name(args.workload)
+    t_gen = time.time()
+    x = wl.make_inputs(w)
+    log(f"[bench] workload {w.name}: inputs drawn in {time.time() - t_gen:.1f}s")
+    dev = torch.device("cuda")
+    B, Hq, Hkv = w.batch, w.num_q_heads, w.num_kv_heads
+
+    main_bytes = (x["k"].numel() + x["v"].numel()) * w.esz
+    copies = args.rotate or max(1, min(8, math.ceil(ROTATE_TARGET_BYTES /
+                                                    main_bytes)))
+    q = x["q"].to(dev)
+    gen = torch.Generator().manual_seed(w.seed + 1000)
+    k_new = torch.randn(B, Hkv, w.dk, generator=gen).to(w.torch_dtype).to(dev)
+    v_new = torch.randn(B, Hkv, w.dv, generator=gen).to(w.torch_dtype).to(dev)
+    out = torch.empty(B, Hq, w.dv, dtype=torch.float32, device=dev)
+
+    branches = []
+    if w.window:
+        # the long cache is attended as is; the new token enters the window
+        branches.append(Branch(g, torch, w, x["k"].to(dev), x["v"].to(dev),
+                               x["lens"].to(dev), copies, append=False))
+        branches.append(Branch(g, torch, w, x["wk"].to(dev), x["wv"].to(dev),
+                               x["wlens"].to(dev), copies, append=True))
+        carry = g.empty_carry(B * Hq, w.dv)
+    else:
+        branches.append(Branch(g, torch, w, x["k"].to(dev), x["v"].to(dev),
+                               x["lens"].to(dev), copies, append=True))
+        carry = None
+    del x
+    torch.cuda.synchronize()
+    log(f"[bench] {copies} rotating cache copies, "
+        f"{main_bytes * copies / 2**30:.2f} GiB of K/V resident")
+
+    def step(r):
+        for i, br in enumerate(branches):
+            lens = br.lens_cur[r]
+            if br.append:
+                g.kv_append(br.k[r], br.v[r], k_new, v_new, br.lens_before,
+                            lens_out=lens)
+            g.attend_partition(q, br.k[r], br.v[r], lens, br.plan, br.ws,
+                               w.scale)
+            last = i == len(branches) - 1
+            g.attend_combine(Hq, br.k[r], br.v[r], lens, br.plan, br.ws,
+                             carry_in=carry if i > 0 else None,
+                             carry_out=None if last else carry,
+                             out=out if last else None)
+
+    dom = branches[0]
+
+    def partition_only(r):
+        g.attend_partition(q, dom.k[r], dom.v[r], dom.lens_cur[r], dom.plan,
+                           dom.ws, w.scale)
+
+    # warm up eagerly (also fixes lens_cur to the post-append lengths)
+    for i in range(args.warmup):
+        step(i % copies)
+    torch.cuda.synchronize()
+
+    def graph_of(fn, n):
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn(0)  # one eager call on the capture stream first
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for i in range(n):
+                fn(i % copies)
+        torch.cuda.synchronize()
+        return gr
+
+    def time_graph(gr, n, reps=3):
+        times = []
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            gr.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) / n)
+        return statistics.median(times)
+
+    K = args.steps
+    g_step = graph_of(step, K)
+    g_step.replay()  # warm the graph
+    torch.cuda.synchronize()
+    ms_step = time_graph(g_step, K)
+
+    g_part = graph_of(partition_only, K)
+    g_part.replay()
+    torch.cuda.synchronize()
+    ms_part = time_graph(g_part, K)
+
+    # eager reference timing of one step (diagnostic)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(i % copies)
+    torch.cuda.synchronize()
+    ms_eager = (time.perf_counter() - t0) * 1e3 / K
+
+    # bytes
+    q_bytes = B * Hq * w.dk * w.esz
+    out_bytes = B * Hq * w.dv * 4
+    carry_bytes = B * Hq * (w.dv + 2) * 4
+    step_bytes = 0
+    for i, br in enumerate(branches):
+        step_bytes += kv_bytes(w, br.n_tot) + q_bytes
+        if br.append:
+            step_bytes += 2 * B * Hkv * (w.dk + w.dv) * w.esz + 2 * B * 4
+    step_bytes += out_bytes + (2 * carry_bytes if len(branches) > 1 else 0)
+    part_bytes = kv_bytes(w, dom.n_tot) + q_bytes
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    achieved = part_bytes / (ms_part * 1e-3) / 1e9
+    log(f"[bench] step {ms_step * 1e3:.2f} us (graph), eager {ms_eager * 1e3:.1f}"
+        f" us; partition {ms_part * 1e3:.2f} us; step bytes {step_bytes}; "
+        f"{value:.1f} GB/s per step, partition {achieved:.1f} GB/s")
+
+    ceiling = None
+    if not args.no_ceiling:
+        ceiling = read_ceiling(torch)
+        log(f"[bench] pure-read stream ceiling: {ceiling:.1f} GB/s")
+
+    traffic = measured_traffic(args.workload)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic,
+                "kernel": "partition_bf16_kernel" if w.dtype == "bf16"
+                else "partition_f32_kernel",
+                "algorithmic_bytes_per_launch": part_bytes,
+                "avg_launch_us": round(ms_part * 1e3, 3)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        del branches, dom, g_step, g_part
+        torch.cuda.empty_cache()
+        cpu = cpu_baseline(w, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded; shapes and distributions of the workload)",
+        "config": {"workload": w.name, "batch": B, "num_q_heads": Hq,
+                   "num_kv_heads": Hkv, "dk": w.dk, "dv": w.dv,
+                   "seq_len": w.max_len, "window": w.window,
+                   "kv_dtype": w.dtype, "rotating_cache_copies": copies,
+                   "timing": "HIP graph of K steps"},
+        "us_per_step": round(ms_step * 1e3, 2),
+        "hbm_frac_per_step": round(value / HBM_PEAK_GBS, 4),
+        "eager_us_per_step": round(ms_eager * 1e3, 2),
+        "read_ceiling_gbs": None if ceiling is None else round(ceiling, 1),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def read_ceiling(torch, nbytes=4 << 30, reps=5):
+    """A plain 16-byte-vector read of 4 GiB: the HBM read rate reachable here."""
+    from gqa_kv_cache_decode_amd.build import BENCH_LIB
+    lib = ctypes.CDLL(str(BENCH_LIB))
+    lib.gqa_bench_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_size_t,
+                                          ctypes.c_void_p, ctypes.c_int,
+                                          ctypes.c_void_p]
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    blocks = 256 * 16
+    sink = torch.zeros(blocks, dtype=torch.int32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    best = 0.0
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        rc = lib.gqa_bench_read_stream(buf.data_ptr(), nbytes, sink.data_ptr(),
+                                       blocks, stream)
+        e1.record()
+        torch.cuda.synchronize()
+        assert rc == 0
+        best = max(best, nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del buf
+    return best
+
+
+def measured_traffic(workload):
+    """HBM bytes per partition launch from committed counter readings, if they
+    were taken on the current kernel source (else None)."""
+    path = ROOT / "profiles" / f"traffic_{workload}.json"
+    if not path.exists():
+        return None
+    rec = json.loads(path.read_text())
+    src_hash = hashlib.sha256(PARTITION_SOURCE.read_bytes()).hexdigest()[:16]
+    if rec.get("partition_source_sha256_16") != src_hash:
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s):
+    """The oracle as it stands, on the host, one BLAS thread, over (b, g)
+    units of the same workload until the budget is spent."""
+    import numpy as np
+    import oracle
+    from gqa_kv_cache_decode_amd import workloads as wl
+    from threadpoolctl import threadpool_limits
+    x = wl.make_inputs(w)
+    hpk = w.hpk
+    units = [(b, gg) for b in range(w.batch) for gg in range(w.num_kv_heads)]
+    order = np.random.default_rng(0).permutation(len(units))
+    done_bytes = 0
+    done = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        for idx in order:
+            b, gg = units[idx]
+            n = int(min(max(int(x["lens"][b]), 0), w.max_len))
+            q = x["q"][b:b + 1, gg * hpk:(gg + 1) * hpk].float().numpy()
+            k = x["k"][b:b + 1, :n, gg:gg + 1].float().numpy()
+            v = x["v"][b:b + 1, :n, gg:gg + 1].float().numpy()
+            oracle.attend(q, k, v, [n], w.scale)
+            done_bytes += (n * (w.dk + w.dv) * w.esz +
+                           hpk * (w.dk * w.esz + w.dv * 4))
+            done += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        el = time.perf_counter() - t0
+    return {"value": round(done_bytes / el / 1e9, 4), "unit": "GB/s",
+            "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {len(units)} (sequence, KV group) units of "
+                      f"{w.name}, fp64 numpy oracle, 1 thread, "
+                      f"{el:.1f} s wall"}
+
+
+if __name__ == "__main__":
+    main()

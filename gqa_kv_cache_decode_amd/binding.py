@@ -1,0 +1,286 @@
+"""ctypes binding of libgqa_decode.so (include/gqa_decode.h).
+
+Argument marshalling only: torch tensors become device pointers and sizes, and
+every call is enqueued on torch's current HIP stream.  All compute happens in
+the library's HIP kernels.  A missing library raises ``GqaError`` at the first
+call; there is no other path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import math
+from pathlib import Path
+from typing import Optional
+
+import torch
+
+LIB_PATH = Path(__file__).resolve().with_name("libgqa_decode.so")
+
+DTYPE_CODES = {torch.float32: 0, torch.bfloat16: 1}
+
+
+class GqaError(RuntimeError):
+    """A failed library call (the status name is in the message)."""
+
+
+class _Cache(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("batch", ctypes.c_int32), ("max_len", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("dk", ctypes.c_int32),
+                ("dv", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class _Carry(ctypes.Structure):
+    _fields_ = [("m", ctypes.c_void_p), ("l", ctypes.c_void_p),
+                ("acc", ctypes.c_void_p)]
+
+
+class Plan(ctypes.Structure):
+    """gqa_plan: split-K chunking and workspace layout of one attend call."""
+
+    _fields_ = [("chunk_tokens", ctypes.c_int32), ("num_chunks", ctypes.c_int32),
+                ("off_l", ctypes.c_size_t), ("off_acc", ctypes.c_size_t),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
+_lib = None
+_AUTO = object()   # default of ``out``: allocate one (None means "no output")
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_CACHE_P = ctypes.POINTER(_Cache)
+_CARRY_P = ctypes.POINTER(_Carry)
+_PLAN_P = ctypes.POINTER(Plan)
+
+_SIGNATURES = {
+    "gqa_abi_version": (_I32, []),
+    "gqa_status_string": (ctypes.c_char_p, [_I32]),
+    "gqa_kv_append": (_I32, [_CACHE_P, _P, _P, _P, _P, _P, _P]),
+    "gqa_attend_plan": (_I32, [_CACHE_P, _I32, _I32, _PLAN_P]),
+    "gqa_attend_workspace_bytes": (ctypes.c_size_t, [_CACHE_P, _I32]),
+    "gqa_attend_decode": (_I32, [_P, _I32, _CACHE_P, _P, ctypes.c_float,
+                                 _CARRY_P, _CARRY_P, _P, _P, ctypes.c_size_t,
+                                 _P]),
+    "gqa_attend_partition": (_I32, [_P, _I32, _CACHE_P, _P, ctypes.c_float,
+                                    _PLAN_P, _P, ctypes.c_size_t, _P]),
+    "gqa_attend_combine": (_I32, [_I32, _CACHE_P, _P, _PLAN_P, _P,
+                                  ctypes.c_size_t, _CARRY_P, _CARRY_P, _P, _P]),
+    "gqa_softmax_state_merge": (_I32, [_CARRY_P, _CARRY_P, _CARRY_P,
+                                       ctypes.c_int64, _I32, _P, _P]),
+}
+
+
+def library() -> ctypes.CDLL:
+    """Load libgqa_decode.so (once) and declare its signatures."""
+    global _lib
+    if _lib is None:
+        if not LIB_PATH.exists():
+            raise GqaError(
+                f"{LIB_PATH} is not built: run "
+                "`python -m gqa_kv_cache_decode_amd.build` (needs hipcc)")
+        lib = ctypes.CDLL(str(LIB_PATH))
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        name = library().gqa_status_string(status).decode()
+        raise GqaError(f"{what}: {name}")
+
+
+def _stream(t: torch.Tensor) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise GqaError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise GqaError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise GqaError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise GqaError(f"{name} must have shape {tuple(shape)}, got "
+                       f"{tuple(t.shape)}")
+
+
+def _cache(k: torch.Tensor, v: torch.Tensor) -> _Cache:
+    _need(k, "k_cache")
+    _need(v, "v_cache", dtype=k.dtype)
+    if k.dtype not in DTYPE_CODES:
+        raise GqaError(f"cache dtype {k.dtype} is not supported")
+    if k.dim() != 4 or v.dim() != 4 or k.shape[:3] != v.shape[:3]:
+        raise GqaError("caches must be [batch, max_len, num_kv_heads, d] with "
+                       "matching batch, max_len and heads")
+    B, T, H, dk = k.shape
+    return _Cache(k.data_ptr(), v.data_ptr(), B, T, H, dk, v.shape[3],
+                  DTYPE_CODES[k.dtype])
+
+
+@dataclasses.dataclass
+class Carry:
+    """Online-softmax carry: m [rows], l [rows], acc [rows, dv] (fp32)."""
+
+    m: torch.Tensor
+    l: torch.Tensor
+    acc: torch.Tensor
+
+    def _struct(self, rows: int, dv: int, name: str) -> _Carry:
+        _need(self.m, name + ".m", torch.float32, (rows,))
+        _need(self.l, name + ".l", torch.float32, (rows,))
+        _need(self.acc, name + ".acc", torch.float32, (rows, dv))
+        return _Carry(self.m.data_ptr(), self.l.data_ptr(), self.acc.data_ptr())
+
+
+def empty_carry(rows: int, dv: int, device="cuda") -> Carry:
+    return Carry(torch.full((rows,), -math.inf, device=device),
+                 torch.zeros(rows, device=device),
+                 torch.zeros(rows, dv, device=device))
+
+
+def kv_append(k_cache, v_cache, k_new, v_new, lens, lens_out=None,
+              dropped=None):
+    """Append one token per sequence (needle-core KvCache::push_kv).
+
+    k_new [B, Hkv, dk], v_new [B, Hkv, dv] in the cache dtype; lens [B] int32.
+    Writes lens_out (default: lens itself, updated in place); a full cache is
+    left untouched and counted in ``dropped`` (int32 [1]) if given."""
+    c = _cache(k_cache, v_cache)
+    _need(k_new, "k_new", k_cache.dtype, (c.batch, c.num_kv_heads, c.dk))
+    _need(v_new, "v_new", k_cache.dtype, (c.batch, c.num_kv_heads, c.dv))
+    _need(lens, "lens", torch.int32, (c.batch,))
+    if lens_out is None:
+        lens_out = lens
+    _need(lens_out, "lens_out", torch.int32, (c.batch,))
+    if dropped is not None:
+        _need(dropped, "dropped", torch.int32, (1,))
+    _check(library().gqa_kv_append(ctypes.byref(c), _ptr(k_new), _ptr(v_new),
+                                   _ptr(lens), _ptr(lens_out), _ptr(dropped),
+                                   _stream(k_cache)), "kv_append")
+    return lens_out
+
+
+def attend_plan(k_cache, v_cache, num_q_heads: int, chunk_tokens: int = 0) -> Plan:
+    c = _cache(k_cache, v_cache)
+    p = Plan()
+    _check(library().gqa_attend_plan(ctypes.byref(c), num_q_heads, chunk_tokens,
+                                     ctypes.byref(p)), "attend_plan")
+    return p
+
+
+def workspace_bytes(k_cache, v_cache, num_q_heads: int) -> int:
+    c = _cache(k_cache, v_cache)
+    return int(library().gqa_attend_workspace_bytes(ctypes.byref(c),
+                                                    num_q_heads))
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
+def _attend_args(q, k_cache, v_cache, lens):
+    c = _cache(k_cache, v_cache)
+    _need(q, "q", k_cache.dtype)
+    if q.dim() != 3 or q.shape[0] != c.batch or q.shape[2] != c.dk:
+        raise GqaError(f"q must be [batch={c.batch}, num_q_heads, dk={c.dk}]")
+    _need(lens, "lens", torch.int32, (c.batch,))
+    return c, q.shape[1]
+
+
+def _carries(c, hq, carry_in, carry_out, out):
+    rows = c.batch * hq
+    cin = None if carry_in is None else carry_in._struct(rows, c.dv, "carry_in")
+    cout = None if carry_out is None else carry_out._struct(rows, c.dv,
+                                                            "carry_out")
+    if out is not None:
+        _need(out, "out", torch.float32, (c.batch, hq, c.dv))
+    return (None if cin is None else ctypes.byref(cin),
+            None if cout is None else ctypes.byref(cout))
+
+
+def attend_decode(q, k_cache, v_cache, lens, scale: float = 0.0,
+                  carry_in: Optional[Carry] = None,
+                  carry_out: Optional[Carry] = None,
+                  out=_AUTO,
+                  workspace: Optional[torch.Tensor] = None):
+    """Exact GQA decode attention: q [B, Hq, dk] over the caches.
+
+    Returns ``out`` [B, Hq, dv] fp32: allocated unless given; pass
+    ``out=None`` together with ``carry_out`` to get the carry only."""
+    c, hq = _attend_args(q, k_cache, v_cache, lens)
+    if out is _AUTO:
+        out = torch.empty(c.batch, hq, c.dv, dtype=torch.float32,
+                          device=q.device)
+    cin, cout = _carries(c, hq, carry_in, carry_out, out)
+    need = library().gqa_attend_workspace_bytes(ctypes.byref(c), hq)
+    if workspace is None:
+        workspace = _workspace(need, q.device)
+    _need(workspace, "workspace")
+    _check(library().gqa_attend_decode(
+        _ptr(q), hq, ctypes.byref(c), _ptr(lens), float(scale), cin, cout,
+        _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(q)), "attend_decode")
+    return out
+
+
+def attend_partition(q, k_cache, v_cache, lens, plan: Plan,
+                     workspace: torch.Tensor, scale: float = 0.0) -> None:
+    """Split-K partials of every live (query row, chunk) into ``workspace``."""
+    c, hq = _attend_args(q, k_cache, v_cache, lens)
+    _need(workspace, "workspace")
+    _check(library().gqa_attend_partition(
+        _ptr(q), hq, ctypes.byref(c), _ptr(lens), float(scale),
+        ctypes.byref(plan), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(q)),
+        "attend_partition")
+
+
+def attend_combine(num_q_heads: int, k_cache, v_cache, lens, plan: Plan,
+                   workspace: torch.Tensor, carry_in: Optional[Carry] = None,
+                   carry_out: Optional[Carry] = None,
+                   out=_AUTO):
+    """Fold the partials (and carry_in) into ``out`` and/or ``carry_out``;
+    ``out`` is allocated unless given (None: carry only)."""
+    c = _cache(k_cache, v_cache)
+    _need(lens, "lens", torch.int32, (c.batch,))
+    _need(workspace, "workspace")
+    if out is _AUTO:
+        out = torch.empty(c.batch, num_q_heads, c.dv, dtype=torch.float32,
+                          device=lens.device)
+    cin, cout = _carries(c, num_q_heads, carry_in, carry_out, out)
+    _check(library().gqa_attend_combine(
+        num_q_heads, ctypes.byref(c), _ptr(lens), ctypes.byref(plan),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), cin,
+        cout, _ptr(out), _stream(lens)), "attend_combine")
+    return out
+
+
+def softmax_state_merge(a: Carry, b: Carry, dst: Optional[Carry] = None,
+                        out: Optional[torch.Tensor] = None) -> Carry:
+    """dst = merge(a, b) row by row; ``out`` (optional) gets acc / l."""
+    rows, dv = a.acc.shape
+    if dst is None:
+        dst = Carry(torch.empty_like(a.m), torch.empty_like(a.l),
+                    torch.empty_like(a.acc))
+    sa, sb, sd = (x._struct(rows, dv, n) for x, n in
+                  ((a, "a"), (b, "b"), (dst, "dst")))
+    if out is not None:
+        _need(out, "out", torch.float32)
+        if out.numel() != rows * dv:
+            raise GqaError("out must hold rows * dv elements")
+    _check(library().gqa_softmax_state_merge(
+        ctypes.byref(sa), ctypes.byref(sb), ctypes.byref(sd), rows, dv,
+        _ptr(out), _stream(a.m)), "softmax_state_merge")
+    return dst

@@ -1,0 +1,338 @@
+// Host side of the C ABI declared in include/gqa_decode.h: argument checks,
+// the split-K plan and kernel dispatch.  Nothing here allocates, frees or
+// synchronises, and no HIP call happens before the checks pass.
+#include "gqa_decode.h"
+
+#include <cmath>
+#include <cstdint>
+#include <limits>
+
+#include "launch.h"
+
+namespace {
+
+using gqa::AppendArgs;
+using gqa::CombineArgs;
+using gqa::MergeArgs;
+using gqa::PartitionArgs;
+
+constexpr size_t kAlign = 256;
+constexpr int kChunkQuantum = 64;
+constexpr int kMaxCombineDv = 256;
+// Work-groups a partition launch should offer: four per compute unit of an
+// MI355X (256 CUs), so that the tail of a launch stays short.
+constexpr int64_t kTargetGroups = 1024;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void *p) {
+  return (reinterpret_cast<uintptr_t>(p) & 15) == 0;
+}
+
+int esize(int32_t dtype) { return dtype == GQA_DTYPE_F32 ? 4 : 2; }
+
+gqa_status check_cache_dims(const gqa_cache *c) {
+  if (!c) return GQA_ERR_INVALID_ARGUMENT;
+  if (c->batch <= 0 || c->max_len <= 0 || c->num_kv_heads <= 0 || c->dk <= 0 ||
+      c->dv <= 0)
+    return GQA_ERR_INVALID_ARGUMENT;
+  if (c->dtype != GQA_DTYPE_F32 && c->dtype != GQA_DTYPE_BF16)
+    return GQA_ERR_INVALID_ARGUMENT;
+  return GQA_OK;
+}
+
+gqa_status check_cache_data(const gqa_cache *c) {
+  if (!c->k || !c->v) return GQA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(c->k) || !aligned16(c->v)) return GQA_ERR_INVALID_ARGUMENT;
+  return GQA_OK;
+}
+
+gqa_status check_heads(const gqa_cache *c, int32_t hq) {
+  if (hq <= 0) return GQA_ERR_INVALID_ARGUMENT;
+  if (hq % c->num_kv_heads != 0) return GQA_ERR_SHAPE_MISMATCH;
+  const int hpk = hq / c->num_kv_heads;
+  if (c->dv > kMaxCombineDv) return GQA_ERR_UNSUPPORTED;
+  const bool ok = c->dtype == GQA_DTYPE_BF16
+                      ? gqa::partition_bf16_supported(c->dk, c->dv, hpk)
+                      : gqa::partition_f32_supported(c->dk, c->dv, hpk);
+  return ok ? GQA_OK : GQA_ERR_UNSUPPORTED;
+}
+
+gqa_status check_carry(const gqa_carry *x) {
+  if (!x) return GQA_OK;
+  return (x->m && x->l && x->acc) ? GQA_OK : GQA_ERR_INVALID_ARGUMENT;
+}
+
+// Chunk length: the largest power of two in [min_chunk, 2048] that still gives
+// the launch kTargetGroups work-groups, and no longer than the cache needs.
+int32_t auto_chunk(const gqa_cache *c) {
+  const int64_t units = (int64_t)c->batch * c->num_kv_heads;
+  const int32_t min_chunk = c->dtype == GQA_DTYPE_BF16 ? 256 : kChunkQuantum;
+  int32_t chunk = 2048;
+  while (chunk > min_chunk &&
+         units * ((c->max_len + chunk - 1) / chunk) < kTargetGroups)
+    chunk /= 2;
+  while (chunk > kChunkQuantum && chunk / 2 >= c->max_len) chunk /= 2;
+  return chunk;
+}
+
+gqa_status make_plan(const gqa_cache *c, int32_t hq, int32_t chunk_tokens,
+                     gqa_plan *p) {
+  gqa_status st = check_cache_dims(c);
+  if (st != GQA_OK) return st;
+  if ((st = check_heads(c, hq)) != GQA_OK) return st;
+  if (chunk_tokens < 0 || chunk_tokens % kChunkQuantum != 0)
+    return GQA_ERR_INVALID_ARGUMENT;
+  const int32_t chunk = chunk_tokens ? chunk_tokens : auto_chunk(c);
+  const int64_t nchunk = ((int64_t)c->max_len + chunk - 1) / chunk;
+  const int64_t groups = (int64_t)c->batch * c->num_kv_heads * nchunk;
+  const int64_t rows = (int64_t)c->batch * hq;
+  if (groups > std::numeric_limits<int32_t>::max() ||
+      rows > std::numeric_limits<int32_t>::max())
+    return GQA_ERR_UNSUPPORTED;
+  const size_t ml = (size_t)rows * nchunk * sizeof(float);
+  p->chunk_tokens = chunk;
+  p->num_chunks = (int32_t)nchunk;
+  p->off_l = align_up(ml);
+  p->off_acc = p->off_l + align_up(ml);
+  p->workspace_bytes = p->off_acc + align_up(ml * c->dv);
+  return GQA_OK;
+}
+
+// A caller's plan must be the one make_plan gives for its chunk length.
+gqa_status check_plan(const gqa_cache *c, int32_t hq, const gqa_plan *plan,
+                      size_t ws_bytes, const void *ws) {
+  if (!plan) return GQA_ERR_INVALID_ARGUMENT;
+  gqa_plan want;
+  gqa_status st = make_plan(c, hq, plan->chunk_tokens, &want);
+  if (st != GQA_OK) return st;
+  if (plan->chunk_tokens == 0 || want.num_chunks != plan->num_chunks ||
+      want.off_l != plan->off_l || want.off_acc != plan->off_acc ||
+      want.workspace_bytes != plan->workspace_bytes)
+    return GQA_ERR_SHAPE_MISMATCH;
+  if (!ws) return GQA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(ws)) return GQA_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < plan->workspace_bytes) return GQA_ERR_WORKSPACE_TOO_SMALL;
+  return GQA_OK;
+}
+
+gqa_status device_status(hipError_t e) {
+  return e == hipSuccess ? GQA_OK : GQA_ERR_DEVICE;
+}
+
+gqa_status partition_checked(const void *q, int32_t hq, const gqa_cache *c,
+                             const int32_t *lens, float scale,
+                             const gqa_plan *plan, void *ws, hipStream_t s) {
+  const int hpk = hq / c->num_kv_heads;
+  const double sc = scale != 0.0f ? (double)scale : 1.0 / std::sqrt((double)c->dk);
+  PartitionArgs a;
+  a.q = q;
+  a.k = c->k;
+  a.v = c->v;
+  a.lens = lens;
+  a.batch = c->batch;
+  a.max_len = c->max_len;
+  a.num_kv_heads = c->num_kv_heads;
+  a.hpk = hpk;
+  a.dk = c->dk;
+  a.dv = c->dv;
+  a.chunk_tokens = plan->chunk_tokens;
+  a.num_chunks = plan->num_chunks;
+  a.scale_log2 = (float)(sc * 1.4426950408889634);
+  char *base = static_cast<char *>(ws);
+  a.part_m = reinterpret_cast<float *>(base);
+  a.part_l = reinterpret_cast<float *>(base + plan->off_l);
+  a.part_acc = reinterpret_cast<float *>(base + plan->off_acc);
+  return device_status(c->dtype == GQA_DTYPE_BF16
+                           ? gqa::launch_partition_bf16(a, s)
+                           : gqa::launch_partition_f32(a, s));
+}
+
+gqa_status combine_checked(int32_t hq, const gqa_cache *c, const int32_t *lens,
+                           const gqa_plan *plan, const void *ws,
+                           const gqa_carry *cin, const gqa_carry *cout,
+                           float *out, hipStream_t s) {
+  CombineArgs a;
+  a.lens = lens;
+  a.batch = c->batch;
+  a.num_q_heads = hq;
+  a.max_len = c->max_len;
+  a.dv = c->dv;
+  a.chunk_tokens = plan->chunk_tokens;
+  a.num_chunks = plan->num_chunks;
+  const char *base = static_cast<const char *>(ws);
+  a.part_m = reinterpret_cast<const float *>(base);
+  a.part_l = reinterpret_cast<const float *>(base + plan->off_l);
+  a.part_acc = reinterpret_cast<const float *>(base + plan->off_acc);
+  a.in_m = cin ? cin->m : nullptr;
+  a.in_l = cin ? cin->l : nullptr;
+  a.in_acc = cin ? cin->acc : nullptr;
+  a.out_m = cout ? cout->m : nullptr;
+  a.out_l = cout ? cout->l : nullptr;
+  a.out_acc = cout ? cout->acc : nullptr;
+  a.out = out;
+  return device_status(gqa::launch_combine(a, s));
+}
+
+gqa_status check_attend_args(const void *q, int32_t hq, const gqa_cache *c,
+                             const int32_t *lens, float scale) {
+  gqa_status st = check_cache_dims(c);
+  if (st != GQA_OK) return st;
+  if ((st = check_cache_data(c)) != GQA_OK) return st;
+  if ((st = check_heads(c, hq)) != GQA_OK) return st;
+  if (!q || !lens) return GQA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q)) return GQA_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(scale)) return GQA_ERR_INVALID_ARGUMENT;
+  return GQA_OK;
+}
+
+gqa_status check_combine_args(int32_t hq, const gqa_cache *c,
+                              const int32_t *lens, const gqa_carry *cin,
+                              const gqa_carry *cout, const float *out) {
+  gqa_status st = check_cache_dims(c);
+  if (st != GQA_OK) return st;
+  if ((st = check_heads(c, hq)) != GQA_OK) return st;
+  if (!lens) return GQA_ERR_INVALID_ARGUMENT;
+  if ((st = check_carry(cin)) != GQA_OK) return st;
+  if ((st = check_carry(cout)) != GQA_OK) return st;
+  if (!out && !cout) return GQA_ERR_INVALID_ARGUMENT;
+  return GQA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t gqa_abi_version(void) { return GQA_ABI_VERSION; }
+
+const char *gqa_status_string(int32_t status) {
+  switch (status) {
+    case GQA_OK: return "GQA_OK";
+    case GQA_ERR_INVALID_ARGUMENT: return "GQA_ERR_INVALID_ARGUMENT";
+    case GQA_ERR_SHAPE_MISMATCH: return "GQA_ERR_SHAPE_MISMATCH";
+    case GQA_ERR_UNSUPPORTED: return "GQA_ERR_UNSUPPORTED";
+    case GQA_ERR_WORKSPACE_TOO_SMALL: return "GQA_ERR_WORKSPACE_TOO_SMALL";
+    case GQA_ERR_DEVICE: return "GQA_ERR_DEVICE";
+    default: return "GQA_ERR_UNKNOWN";
+  }
+}
+
+gqa_status gqa_kv_append(const gqa_cache *cache, const void *k_new,
+                         const void *v_new, const int32_t *lens_in,
+                         int32_t *lens_out, int32_t *dropped,
+                         hipStream_t stream) {
+  gqa_status st = check_cache_dims(cache);
+  if (st != GQA_OK) return st;
+  if ((st = check_cache_data(cache)) != GQA_OK) return st;
+  if (!k_new || !v_new || !lens_in || !lens_out) return GQA_ERR_INVALID_ARGUMENT;
+  const int64_t rk = (int64_t)cache->num_kv_heads * cache->dk * esize(cache->dtype);
+  const int64_t rv = (int64_t)cache->num_kv_heads * cache->dv * esize(cache->dtype);
+  if (rk > std::numeric_limits<int32_t>::max() ||
+      rv > std::numeric_limits<int32_t>::max())
+    return GQA_ERR_UNSUPPORTED;
+  AppendArgs a;
+  a.k = cache->k;
+  a.v = cache->v;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.lens_in = lens_in;
+  a.lens_out = lens_out;
+  a.dropped = dropped;
+  a.batch = cache->batch;
+  a.max_len = cache->max_len;
+  a.row_bytes_k = (int)rk;
+  a.row_bytes_v = (int)rv;
+  return device_status(gqa::launch_append(a, stream));
+}
+
+gqa_status gqa_attend_plan(const gqa_cache *cache, int32_t num_q_heads,
+                           int32_t chunk_tokens, gqa_plan *plan) {
+  if (!plan) return GQA_ERR_INVALID_ARGUMENT;
+  return make_plan(cache, num_q_heads, chunk_tokens, plan);
+}
+
+size_t gqa_attend_workspace_bytes(const gqa_cache *cache, int32_t num_q_heads) {
+  gqa_plan p;
+  return make_plan(cache, num_q_heads, 0, &p) == GQA_OK ? p.workspace_bytes : 0;
+}
+
+gqa_status gqa_attend_partition(const void *q, int32_t num_q_heads,
+                                const gqa_cache *cache, const int32_t *lens,
+                                float scale, const gqa_plan *plan,
+                                void *workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+  gqa_status st = check_attend_args(q, num_q_heads, cache, lens, scale);
+  if (st != GQA_OK) return st;
+  if ((st = check_plan(cache, num_q_heads, plan, workspace_bytes, workspace)) !=
+      GQA_OK)
+    return st;
+  return partition_checked(q, num_q_heads, cache, lens, scale, plan, workspace,
+                           stream);
+}
+
+gqa_status gqa_attend_combine(int32_t num_q_heads, const gqa_cache *cache,
+                              const int32_t *lens, const gqa_plan *plan,
+                              const void *workspace, size_t workspace_bytes,
+                              const gqa_carry *carry_in,
+                              const gqa_carry *carry_out, float *out,
+                              hipStream_t stream) {
+  gqa_status st =
+      check_combine_args(num_q_heads, cache, lens, carry_in, carry_out, out);
+  if (st != GQA_OK) return st;
+  if ((st = check_plan(cache, num_q_heads, plan, workspace_bytes, workspace)) !=
+      GQA_OK)
+    return st;
+  return combine_checked(num_q_heads, cache, lens, plan, workspace, carry_in,
+                         carry_out, out, stream);
+}
+
+gqa_status gqa_attend_decode(const void *q, int32_t num_q_heads,
+                             const gqa_cache *cache, const int32_t *lens,
+                             float scale, const gqa_carry *carry_in,
+                             const gqa_carry *carry_out, float *out,
+                             void *workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  gqa_status st = check_attend_args(q, num_q_heads, cache, lens, scale);
+  if (st != GQA_OK) return st;
+  if ((st = check_combine_args(num_q_heads, cache, lens, carry_in, carry_out,
+                               out)) != GQA_OK)
+    return st;
+  gqa_plan plan;
+  if ((st = make_plan(cache, num_q_heads, 0, &plan)) != GQA_OK) return st;
+  if ((st = check_plan(cache, num_q_heads, &plan, workspace_bytes, workspace)) !=
+      GQA_OK)
+    return st;
+  st = partition_checked(q, num_q_heads, cache, lens, scale, &plan, workspace,
+                         stream);
+  if (st != GQA_OK) return st;
+  return combine_checked(num_q_heads, cache, lens, &plan, workspace, carry_in,
+                         carry_out, out, stream);
+}
+
+gqa_status gqa_softmax_state_merge(const gqa_carry *a, const gqa_carry *b,
+                                   const gqa_carry *dst, int64_t rows,
+                                   int32_t dv, float *out, hipStream_t stream) {
+  if (!a || !b || !dst) return GQA_ERR_INVALID_ARGUMENT;
+  gqa_status st;
+  if ((st = check_carry(a)) != GQA_OK || (st = check_carry(b)) != GQA_OK ||
+      (st = check_carry(dst)) != GQA_OK)
+    return st;
+  if (rows <= 0 || dv <= 0) return GQA_ERR_INVALID_ARGUMENT;
+  if (rows > std::numeric_limits<int32_t>::max()) return GQA_ERR_UNSUPPORTED;
+  MergeArgs m;
+  m.a_m = a->m;
+  m.a_l = a->l;
+  m.a_acc = a->acc;
+  m.b_m = b->m;
+  m.b_l = b->l;
+  m.b_acc = b->acc;
+  m.d_m = dst->m;
+  m.d_l = dst->l;
+  m.d_acc = dst->acc;
+  m.out = out;
+  m.rows = rows;
+  m.dv = dv;
+  return device_status(gqa::launch_merge(m, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,58 @@
+// Device-side helpers shared by the decode kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gqa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
+
+// 2^x on the hardware exp unit (v_exp_f32): exact 0 for -inf.
+__device__ __forceinline__ float fast_exp2(float x) {
+  return __builtin_amdgcn_exp2f(x);
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Butterfly reductions across the 64 lanes of a wavefront.
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+// Makes this wavefront's own LDS writes visible to its other lanes and keeps
+// the compiler from moving LDS accesses across the point.  Only valid for LDS
+// regions private to one wavefront.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ int clamp_len(int n, int max_len) {
+  return n < 0 ? 0 : (n > max_len ? max_len : n);
+}
+
+// Spreads consecutive work items over the same XCD: hardware hands block i to
+// XCD i % 8, so item w = (i % 8) * (N / 8) + i / 8 gives each XCD a contiguous
+// run of items (the N % 8 tail keeps the identity map).
+__device__ __forceinline__ int xcd_local_item(int i, int n) {
+  const int per = n >> 3;
+  return (i < (per << 3)) ? (i & 7) * per + (i >> 3) : i;
+}
+
+}  // namespace gqa

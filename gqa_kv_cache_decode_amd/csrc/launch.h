@@ -1,0 +1,61 @@
+// Internal interface between the host ABI (abi.cpp) and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gqa {
+
+struct PartitionArgs {
+  const void *q;        // [B][Hkv*hpk][dk]
+  const void *k;        // [B][max_len][Hkv][dk]
+  const void *v;        // [B][max_len][Hkv][dv]
+  const int32_t *lens;  // [B]
+  int batch, max_len, num_kv_heads, hpk, dk, dv;
+  int chunk_tokens, num_chunks;
+  float scale_log2;     // logit scale times log2(e)
+  float *part_m;        // [rows][num_chunks]  (natural-log units)
+  float *part_l;        // [rows][num_chunks]
+  float *part_acc;      // [rows][num_chunks][dv]
+};
+
+struct CombineArgs {
+  const int32_t *lens;
+  int batch, num_q_heads, max_len, dv, chunk_tokens, num_chunks;
+  const float *part_m, *part_l, *part_acc;
+  const float *in_m, *in_l, *in_acc;   // carry_in, all NULL if absent
+  float *out_m, *out_l, *out_acc;      // carry_out, all NULL if absent
+  float *out;                          // [rows][dv] or NULL
+};
+
+struct MergeArgs {
+  const float *a_m, *a_l, *a_acc;
+  const float *b_m, *b_l, *b_acc;
+  float *d_m, *d_l, *d_acc;
+  float *out;  // or NULL
+  int64_t rows;
+  int dv;
+};
+
+struct AppendArgs {
+  void *k, *v;
+  const void *k_new, *v_new;
+  const int32_t *lens_in;
+  int32_t *lens_out;
+  int32_t *dropped;
+  int batch, max_len, row_bytes_k, row_bytes_v;  // bytes of one token's K/V row
+};
+
+// Kernel families compiled into the library.
+bool partition_bf16_supported(int dk, int dv, int hpk);
+bool partition_f32_supported(int dk, int dv, int hpk);
+size_t partition_f32_lds_bytes(int dk, int dv, int hpk);
+
+hipError_t launch_partition_bf16(const PartitionArgs &a, hipStream_t s);
+hipError_t launch_partition_f32(const PartitionArgs &a, hipStream_t s);
+hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
+hipError_t launch_merge(const MergeArgs &a, hipStream_t s);
+hipError_t launch_append(const AppendArgs &a, hipStream_t s);
+
+}  // namespace gqa

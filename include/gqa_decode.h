@@ -1,0 +1,217 @@
+/*
+ * gqa_decode.h — exact grouped-query decode attention over a KV cache,
+ * hand-written HIP for AMD Instinct MI355X (gfx950).
+ *
+ * One decode step appends the new token's K/V rows to each sequence's cache
+ * and then lets every query head attend over all cached keys of its KV group:
+ *
+ *   s_j  = scale * <q[b,h,:], K[b,j,g,:]>          j < n_b,  g = h / (Hq/Hkv)
+ *   out  = sum_j exp(s_j - m) V[b,j,g,:] / sum_j exp(s_j - m),  m = max_j s_j
+ *
+ * (needle-core attn.rs, self_attn_incremental: push_kv then attend over the
+ * cache; query head hi reads KV head hi / kv_repeat; scores are
+ * dot(q_head, k_head) * head_dim^-0.5, softmaxed, and the value rows summed.)
+ * The result can also be handed out as a mergeable online-softmax carry
+ * (m, l, acc) so that two branches over the same queries — for example a long
+ * main cache and a recent window — fold into one (usearch
+ * "linear-algebra", section Attention and struct DenseSoftmaxState).
+ *
+ * Conventions for every entry point:
+ *  - Every data pointer is a DEVICE pointer, owned by the caller.  The library
+ *    never allocates, frees or synchronises; every call only enqueues kernels
+ *    on `stream` (NULL = the default stream) and returns.
+ *  - Arguments are checked on the host before anything is enqueued; a failed
+ *    check returns an error code and enqueues nothing.  No HIP call is made
+ *    before the checks pass.  GQA_ERR_DEVICE reports a failed launch.
+ *  - All sizes are element counts unless named *_bytes.
+ *  - q, cache->k, cache->v and the workspace must be 16-byte aligned.
+ *  - Shapes with a kernel: bf16 caches with (dk, dv) in {(64, 64), (128, 128),
+ *    (192, 128), (256, 256)} and 1..16 query heads per KV head (matrix-core
+ *    path); fp32 caches with dk, dv multiples of 4 up to 256, 1..16 query
+ *    heads per KV head and a 64-token tile that fits 64 KiB of LDS (vector
+ *    ALU path).
+ *  - Errors: GQA_ERR_INVALID_ARGUMENT (a required pointer is NULL, a size is
+ *    non-positive, a scale is not finite), GQA_ERR_SHAPE_MISMATCH (the query
+ *    heads are not a multiple of the KV heads — usearch head_count "must
+ *    divide the rows" — or the sizes of two arguments disagree),
+ *    GQA_ERR_UNSUPPORTED (no kernel for this dtype / head widths / group
+ *    size), GQA_ERR_WORKSPACE_TOO_SMALL, GQA_ERR_DEVICE.
+ */
+#ifndef GQA_DECODE_H
+#define GQA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GQA_ABI_VERSION 1
+
+/* Only the entry points below are exported from the shared library. */
+#define GQA_API __attribute__((visibility("default")))
+
+typedef enum gqa_status {
+  GQA_OK = 0,
+  GQA_ERR_INVALID_ARGUMENT = 1,
+  GQA_ERR_SHAPE_MISMATCH = 2,
+  GQA_ERR_UNSUPPORTED = 3,
+  GQA_ERR_WORKSPACE_TOO_SMALL = 4,
+  GQA_ERR_DEVICE = 5
+} gqa_status;
+
+/* Storage type of q, K and V.  Outputs and carries are always fp32. */
+typedef enum gqa_dtype { GQA_DTYPE_F32 = 0, GQA_DTYPE_BF16 = 1 } gqa_dtype;
+
+/*
+ * A batch of KV caches (needle-core struct KvCache: keys and values stored
+ * [max_len, num_kv_heads, head_dim]; here with a leading batch dimension and
+ * separate key and value widths):
+ *   k: [batch][max_len][num_kv_heads][dk]   contiguous, `dtype` elements
+ *   v: [batch][max_len][num_kv_heads][dv]   contiguous, `dtype` elements
+ * The per-sequence fill level lives in a separate device int32 array `lens`.
+ * Slots at or past lens[b] are never read by attend.
+ */
+typedef struct gqa_cache {
+  void *k;
+  void *v;
+  int32_t batch;
+  int32_t max_len;
+  int32_t num_kv_heads;
+  int32_t dk;
+  int32_t dv;
+  int32_t dtype; /* gqa_dtype */
+} gqa_cache;
+
+/*
+ * Online-softmax carry, one row per query row r = b * num_q_heads + h
+ * (usearch DenseSoftmaxState, "lent by you", extended with the accumulator):
+ *   m   [rows]      largest scaled logit seen, natural-log units
+ *   l   [rows]      sum of exp(s - m) over the keys seen
+ *   acc [rows][dv]  sum of exp(s - m) * v, NOT divided by l
+ * A row with l == 0 is empty whatever its m (a zero-initialised carry is the
+ * empty state).  Empty rows are written as (-inf, 0, 0).
+ */
+typedef struct gqa_carry {
+  float *m;
+  float *l;
+  float *acc;
+} gqa_carry;
+
+/*
+ * Split-K plan of one attend call.  The key axis of every sequence is cut into
+ * chunks of `chunk_tokens`; one partial carry per (query row, chunk) goes to
+ * the workspace, laid out as three fp32 arrays at 256-byte aligned offsets:
+ *   part_m   [rows][num_chunks]       at byte 0
+ *   part_l   [rows][num_chunks]       at off_l
+ *   part_acc [rows][num_chunks][dv]   at off_acc
+ * Only chunks c < ceil(min(lens[b], max_len) / chunk_tokens) are written.
+ */
+typedef struct gqa_plan {
+  int32_t chunk_tokens;
+  int32_t num_chunks;
+  size_t off_l;
+  size_t off_acc;
+  size_t workspace_bytes;
+} gqa_plan;
+
+/* Version of this ABI (GQA_ABI_VERSION). */
+GQA_API int32_t gqa_abi_version(void);
+
+/* Static, NUL-terminated name of a status code. */
+GQA_API const char *gqa_status_string(int32_t status);
+
+/*
+ * kv_append — needle-core KvCache::push_kv, batched.
+ * For every sequence b with n = lens_in[b]:
+ *   0 <= n < max_len: K[b][n][:][:] = k_new[b][:][:], V[b][n][:][:] =
+ *     v_new[b][:][:] (bit copies), lens_out[b] = n + 1;
+ *   otherwise (a full cache, or a negative length): nothing is written,
+ *     lens_out[b] = n, and *dropped is incremented (if dropped != NULL).
+ *     The page warns and returns without writing; here the drop is counted.
+ * k_new [batch][num_kv_heads][dk], v_new [batch][num_kv_heads][dv], in the
+ * cache dtype.  lens_out may alias lens_in.  dropped is a device int32.
+ */
+GQA_API gqa_status gqa_kv_append(const gqa_cache *cache, const void *k_new,
+                         const void *v_new, const int32_t *lens_in,
+                         int32_t *lens_out, int32_t *dropped,
+                         hipStream_t stream);
+
+/*
+ * Plan the split-K decomposition for `cache` and `num_q_heads` query heads.
+ * chunk_tokens = 0 picks the library's choice; otherwise it must be a
+ * positive multiple of 64.  Pure host computation (no HIP calls).
+ */
+GQA_API gqa_status gqa_attend_plan(const gqa_cache *cache, int32_t num_q_heads,
+                           int32_t chunk_tokens, gqa_plan *plan);
+
+/* Workspace bytes gqa_attend_decode needs (its own plan); 0 if invalid. */
+GQA_API size_t gqa_attend_workspace_bytes(const gqa_cache *cache, int32_t num_q_heads);
+
+/*
+ * attend_decode — one query token per sequence attends over its cache.
+ *   q     [batch][num_q_heads][dk], cache dtype.
+ *   lens  [batch] device int32; keys attended are [0, clamp(lens[b], 0,
+ *         max_len)).
+ *   scale logit scale; 0 means 1/sqrt(dk) (usearch score_scale: zero derives
+ *         it; conventionally the inverse square root of the head width).
+ *         Must be finite.
+ *   carry_in   NULL, or a carry over the same query rows folded into this
+ *              branch (usearch carry: folds this branch into another over the
+ *              same queries, such as a recent window).
+ *   carry_out  NULL, or receives the merged carry; may alias carry_in.
+ *   out   NULL, or [batch][num_q_heads][dv] fp32: the merged value mix already
+ *         divided by the partition; rows with no keys at all get 0.
+ *   At least one of out / carry_out must be given.
+ *   workspace  device buffer of at least gqa_attend_workspace_bytes().
+ * Enqueues the split-K partition kernel and the log-sum-exp combine kernel.
+ */
+GQA_API gqa_status gqa_attend_decode(const void *q, int32_t num_q_heads,
+                             const gqa_cache *cache, const int32_t *lens,
+                             float scale, const gqa_carry *carry_in,
+                             const gqa_carry *carry_out, float *out,
+                             void *workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
+/*
+ * First half of attend_decode with an explicit plan: writes the partial
+ * carries of every live (query row, chunk) into the workspace (layout in
+ * gqa_plan).  Arguments as in gqa_attend_decode.
+ */
+GQA_API gqa_status gqa_attend_partition(const void *q, int32_t num_q_heads,
+                                const gqa_cache *cache, const int32_t *lens,
+                                float scale, const gqa_plan *plan,
+                                void *workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
+/*
+ * Second half of attend_decode: folds the live partials of each query row
+ * (and carry_in) by log-sum-exp merge, writes out and/or carry_out.  `cache`
+ * supplies the sizes only (its k/v pointers are not read).
+ */
+GQA_API gqa_status gqa_attend_combine(int32_t num_q_heads, const gqa_cache *cache,
+                              const int32_t *lens, const gqa_plan *plan,
+                              const void *workspace, size_t workspace_bytes,
+                              const gqa_carry *carry_in,
+                              const gqa_carry *carry_out, float *out,
+                              hipStream_t stream);
+
+/*
+ * softmax_state_merge — dst = merge(a, b) row by row (usearch carry,
+ * "partial-softmax rescaling"): m = max(m_a, m_b), l = e^(m_a-m) l_a +
+ * e^(m_b-m) l_b, acc = e^(m_a-m) acc_a + e^(m_b-m) acc_b; an empty row
+ * (l == 0) is the identity.  dst may alias a or b.  out, if not NULL,
+ * receives acc / l ([rows][dv] fp32, 0 for empty rows).
+ */
+GQA_API gqa_status gqa_softmax_state_merge(const gqa_carry *a, const gqa_carry *b,
+                                   const gqa_carry *dst, int64_t rows,
+                                   int32_t dv, float *out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_DECODE_H */

@@ -1,0 +1,168 @@
+"""The C ABI on the CPU: the library loads, exports every entry point the
+header declares, and rejects bad arguments before any HIP call (every call
+here fails validation, so nothing is launched)."""
+
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+from gqa_kv_cache_decode_amd import binding as bd
+
+ROOT = Path(__file__).resolve().parents[1]
+HEADER = ROOT / "include" / "gqa_decode.h"
+
+OK, INVALID, SHAPE, UNSUPPORTED, WORKSPACE, DEVICE = range(6)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not bd.LIB_PATH.exists():
+        pytest.fail("libgqa_decode.so is not built (run the build first)")
+    return bd.library()
+
+
+def _declared():
+    text = HEADER.read_text()
+    return re.findall(r"GQA_API\s+[\w\s\*]+?\b(gqa_\w+)\s*\(", text)
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert len(names) == 9, names
+    for n in names:
+        assert hasattr(lib, n), f"missing export {n}"
+    assert set(names) == set(bd._SIGNATURES), "binding covers the header"
+
+
+def test_version_and_status_strings(lib):
+    assert lib.gqa_abi_version() == 1
+    names = [lib.gqa_status_string(i).decode() for i in range(7)]
+    assert names == ["GQA_OK", "GQA_ERR_INVALID_ARGUMENT",
+                     "GQA_ERR_SHAPE_MISMATCH", "GQA_ERR_UNSUPPORTED",
+                     "GQA_ERR_WORKSPACE_TOO_SMALL", "GQA_ERR_DEVICE",
+                     "GQA_ERR_UNKNOWN"]
+
+
+def _cache(B=16, T=4096, H=8, dk=128, dv=128, dtype=1, k=0x10000, v=0x20000):
+    return bd._Cache(k, v, B, T, H, dk, dv, dtype)
+
+
+def _plan(lib, c, hq, chunk=0):
+    p = bd.Plan()
+    st = lib.gqa_attend_plan(ctypes.byref(c), hq, chunk, ctypes.byref(p))
+    return st, p
+
+
+def test_plan_layout(lib):
+    c = _cache()
+    st, p = _plan(lib, c, 32)
+    assert st == OK
+    assert p.chunk_tokens % 64 == 0 and p.chunk_tokens > 0
+    assert p.num_chunks == -(-4096 // p.chunk_tokens)
+    rows = 16 * 32
+    ml = rows * p.num_chunks * 4
+    up = lambda x: (x + 255) // 256 * 256
+    assert p.off_l == up(ml) and p.off_acc == 2 * up(ml)
+    assert p.workspace_bytes == 2 * up(ml) + up(ml * 128)
+    assert lib.gqa_attend_workspace_bytes(ctypes.byref(c), 32) == \
+        p.workspace_bytes
+    st, p = _plan(lib, c, 32, chunk=320)
+    assert st == OK and p.chunk_tokens == 320 and p.num_chunks == 13
+
+
+@pytest.mark.parametrize("kw,hq,chunk,want", [
+    (dict(), 30, 0, SHAPE),                 # Hq not a multiple of Hkv
+    (dict(), 0, 0, INVALID),
+    (dict(), 32, 100, INVALID),             # chunk not a multiple of 64
+    (dict(), 32, -64, INVALID),
+    (dict(B=0), 32, 0, INVALID),
+    (dict(dtype=7), 32, 0, INVALID),
+    (dict(dk=96, dv=96), 32, 0, UNSUPPORTED),  # no bf16 kernel for 96
+    (dict(), 8 * 17, 0, UNSUPPORTED),       # 17 heads per KV head
+    (dict(dtype=0, dk=512, dv=64), 32, 0, UNSUPPORTED),  # dk > 256
+    (dict(dtype=0, dk=256, dv=256), 32, 0, OK),
+    (dict(dtype=0, dk=96, dv=32), 32, 0, OK),
+    (dict(dk=192, dv=128, H=4), 64, 0, OK),
+])
+def test_plan_validation(lib, kw, hq, chunk, want):
+    st, _ = _plan(lib, _cache(**kw), hq, chunk)
+    assert st == want
+
+
+def test_attend_rejects_before_launch(lib):
+    c = _cache()
+    hq = 32
+    _, p = _plan(lib, c, hq)
+    q, lens, ws, out = (ctypes.c_void_p(x) for x in
+                        (0x30000, 0x40000, 0x50000, 0x60000))
+    nbytes = p.workspace_bytes
+    f = lib.gqa_attend_decode
+    carry = bd._Carry(0x70000, 0x80000, 0x90000)
+    # null q, null lens
+    assert f(None, hq, ctypes.byref(c), lens, 0.0, None, None, out, ws, nbytes,
+             None) == INVALID
+    assert f(q, hq, ctypes.byref(c), None, 0.0, None, None, out, ws, nbytes,
+             None) == INVALID
+    # neither out nor carry_out
+    assert f(q, hq, ctypes.byref(c), lens, 0.0, None, None, None, ws, nbytes,
+             None) == INVALID
+    # non-finite scale
+    for s in (float("nan"), float("inf")):
+        assert f(q, hq, ctypes.byref(c), lens, s, None, None, out, ws, nbytes,
+                 None) == INVALID
+    # misaligned q
+    assert f(ctypes.c_void_p(0x30002), hq, ctypes.byref(c), lens, 0.0, None,
+             None, out, ws, nbytes, None) == INVALID
+    # workspace too small
+    assert f(q, hq, ctypes.byref(c), lens, 0.0, None, None, out, ws,
+             nbytes - 1, None) == WORKSPACE
+    # a carry with a null member
+    bad = bd._Carry(0x70000, None, 0x90000)
+    assert f(q, hq, ctypes.byref(c), lens, 0.0, ctypes.byref(bad), None, out,
+             ws, nbytes, None) == INVALID
+    assert f(q, 30, ctypes.byref(c), lens, 0.0, ctypes.byref(carry), None,
+             out, ws, nbytes, None) == SHAPE
+    # null cache data
+    c0 = _cache(k=0)
+    assert f(q, hq, ctypes.byref(c0), lens, 0.0, None, None, out, ws, nbytes,
+             None) == INVALID
+
+
+def test_partition_combine_plan_checks(lib):
+    c = _cache()
+    _, p = _plan(lib, c, 32)
+    q, lens, ws = (ctypes.c_void_p(x) for x in (0x30000, 0x40000, 0x50000))
+    bad = bd.Plan(p.chunk_tokens, p.num_chunks + 1, p.off_l, p.off_acc,
+                  p.workspace_bytes)
+    assert lib.gqa_attend_partition(q, 32, ctypes.byref(c), lens, 0.0,
+                                    ctypes.byref(bad), ws, p.workspace_bytes,
+                                    None) == SHAPE
+    assert lib.gqa_attend_partition(q, 32, ctypes.byref(c), lens, 0.0, None,
+                                    ws, p.workspace_bytes, None) == INVALID
+    assert lib.gqa_attend_combine(32, ctypes.byref(c), lens, ctypes.byref(p),
+                                  ws, p.workspace_bytes, None, None, None,
+                                  None) == INVALID
+    assert lib.gqa_attend_combine(32, ctypes.byref(c), lens, ctypes.byref(p),
+                                  None, p.workspace_bytes, None, None,
+                                  ctypes.c_void_p(0x60000), None) == INVALID
+
+
+def test_append_and_merge_reject(lib):
+    c = _cache()
+    p = ctypes.c_void_p(0x30000)
+    assert lib.gqa_kv_append(ctypes.byref(c), None, p, p, p, None, None) == \
+        INVALID
+    assert lib.gqa_kv_append(None, p, p, p, p, None, None) == INVALID
+    assert lib.gqa_kv_append(ctypes.byref(_cache(T=0)), p, p, p, p, None,
+                             None) == INVALID
+    a = bd._Carry(0x10000, 0x20000, 0x30000)
+    assert lib.gqa_softmax_state_merge(ctypes.byref(a), None, ctypes.byref(a),
+                                       4, 8, None, None) == INVALID
+    assert lib.gqa_softmax_state_merge(ctypes.byref(a), ctypes.byref(a),
+                                       ctypes.byref(a), 0, 8, None, None) == \
+        INVALID
+    assert lib.gqa_softmax_state_merge(ctypes.byref(a), ctypes.byref(a),
+                                       ctypes.byref(a), 4, 0, None, None) == \
+        INVALID
