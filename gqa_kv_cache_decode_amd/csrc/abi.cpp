@@ -19,9 +19,9 @@ using gqa::PartitionArgs;
 constexpr size_t kAlign = 256;
 constexpr int kChunkQuantum = 64;
 constexpr int kMaxCombineDv = 256;
-// Work-groups a partition launch should offer: four per compute unit of an
-// MI355X (256 CUs), so that the tail of a launch stays short.
-constexpr int64_t kTargetGroups = 1024;
+// Wavefronts a partition launch should hold: about four per compute unit of an
+// MI355X (256 CUs), each streaming a long run of tiles.
+constexpr int64_t kTargetWaves = 1024;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -63,15 +63,18 @@ gqa_status check_carry(const gqa_carry *x) {
   return (x->m && x->l && x->acc) ? GQA_OK : GQA_ERR_INVALID_ARGUMENT;
 }
 
-// Chunk length: the largest power of two in [min_chunk, 2048] that still gives
-// the launch kTargetGroups work-groups, and no longer than the cache needs.
+// Chunk length: the power of two that spreads the cache over kTargetWaves
+// wavefronts, clamped to [min_chunk, 4096] (longer chunks leave ragged
+// batches unbalanced) and to what the cache needs.
 int32_t auto_chunk(const gqa_cache *c) {
   const int64_t units = (int64_t)c->batch * c->num_kv_heads;
-  const int32_t min_chunk = c->dtype == GQA_DTYPE_BF16 ? 256 : kChunkQuantum;
-  int32_t chunk = 2048;
-  while (chunk > min_chunk &&
-         units * ((c->max_len + chunk - 1) / chunk) < kTargetGroups)
-    chunk /= 2;
+  const bool bf16 = c->dtype == GQA_DTYPE_BF16;
+  const bool mfma = bf16 || gqa::partition_f32_uses_mfma(c->dk, c->dv);
+  const int64_t waves_per_group = mfma ? gqa::kPartitionWaves : 1;
+  const int32_t min_chunk = bf16 ? 256 : kChunkQuantum;
+  const int64_t want = units * c->max_len * waves_per_group / kTargetWaves;
+  int32_t chunk = min_chunk;
+  while (chunk < 4096 && chunk < want) chunk *= 2;
   while (chunk > kChunkQuantum && chunk / 2 >= c->max_len) chunk /= 2;
   return chunk;
 }

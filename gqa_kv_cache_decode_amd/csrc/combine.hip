@@ -15,76 +15,78 @@
 namespace gqa {
 namespace {
 
-template <int THREADS>
-__device__ __forceinline__ float block_max(float x, float *red) {
-  x = wave_max(x);
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  if (lane == 0) red[w] = x;
-  __syncthreads();
-  float r = red[0];
-#pragma unroll
-  for (int i = 1; i < THREADS / 64; ++i) r = fmaxf(r, red[i]);
-  return r;
-}
-
 // One work-group per query row; threads are (slice, column) pairs: column
-// threads cover dv, slices split the chunk list.
+// threads cover dv, slices split the chunk list.  Each thread folds its chunks
+// online (so every partial load can be in flight at once), then the slices
+// fold through LDS.
 template <int THREADS>
 __global__ __launch_bounds__(THREADS) void combine_kernel(CombineArgs a) {
-  __shared__ float red[THREADS / 64];
-  __shared__ float sacc[THREADS];
+  __shared__ float sm[THREADS];
   __shared__ float sl[THREADS];
+  __shared__ float sacc[THREADS];
 
   const int row = blockIdx.x;
   const int b = row / a.num_q_heads;
+  const int tps = min(THREADS, ((a.dv + 63) / 64) * 64);  // threads per slice
+  const int nslice = THREADS / tps;
+  const int slice = threadIdx.x / tps;
+  const int col = threadIdx.x % tps;
+  const bool worker = slice < nslice && col < a.dv;
+
+  const float in_l = a.in_l ? a.in_l[row] : 0.0f;
+  const bool has_in = in_l > 0.0f;
+  const float in_m = has_in ? a.in_m[row] : -INFINITY;
+  const float in_acc =
+      (has_in && worker) ? a.in_acc[(size_t)row * a.dv + col] : 0.0f;
+
   const int n = clamp_len(a.lens[b], a.max_len);
   const int nc = (n + a.chunk_tokens - 1) / a.chunk_tokens;
   const float *pm = a.part_m + (size_t)row * a.num_chunks;
   const float *pl = a.part_l + (size_t)row * a.num_chunks;
   const float *pa = a.part_acc + (size_t)row * a.num_chunks * a.dv;
 
-  const float in_l = a.in_l ? a.in_l[row] : 0.0f;
-  const bool has_in = in_l > 0.0f;
-  const float in_m = has_in ? a.in_m[row] : -INFINITY;
-
-  float mx = -INFINITY;
-  for (int i = threadIdx.x; i < nc; i += THREADS) mx = fmaxf(mx, pm[i]);
-  mx = fmaxf(block_max<THREADS>(mx, red), in_m);
-
-  const int tps = min(THREADS, ((a.dv + 63) / 64) * 64);  // threads per slice
-  const int nslice = THREADS / tps;
-  const int slice = threadIdx.x / tps;
-  const int col = threadIdx.x % tps;
-
-  float acc = 0.0f, L = 0.0f;
-  if (slice < nslice && col < a.dv) {
-    int i = slice;
+  float m = -INFINITY, L = 0.0f, acc = 0.0f;  // base-2 running state
+  if (worker) {
 #pragma unroll 4
-    for (; i < nc; i += nslice) {
-      const float f = fast_exp2((pm[i] - mx) * kLog2e);
-      acc += f * pa[(size_t)i * a.dv + col];
-      L += f * pl[i];
+    for (int i = slice; i < nc; i += nslice) {
+      const float mi = pm[i] * kLog2e;
+      const float li = pl[i];
+      const float ai = pa[(size_t)i * a.dv + col];
+      const float mn = fmaxf(m, mi);
+      const float fo = fast_exp2(m - mn), fi = fast_exp2(mi - mn);
+      acc = acc * fo + ai * fi;
+      L = L * fo + li * fi;
+      m = mn;
     }
   }
-  sacc[threadIdx.x] = acc;
+  sm[threadIdx.x] = m;
   sl[threadIdx.x] = L;
+  sacc[threadIdx.x] = acc;
   __syncthreads();
-  if (slice != 0 || col >= a.dv) return;
-  for (int s = 1; s < nslice; ++s) {
-    acc += sacc[s * tps + col];
-    L += sl[s * tps + col];
-  }
-  if (has_in) {
-    const float f = fast_exp2((in_m - mx) * kLog2e);
-    acc += f * a.in_acc[(size_t)row * a.dv + col];
-    L += f * in_l;
+  if (slice != 0 || !worker) return;
+
+  float M = has_in ? in_m * kLog2e : -INFINITY;
+  for (int s = 0; s < nslice; ++s) M = fmaxf(M, sm[s * tps + col]);
+  acc = 0.0f;
+  L = 0.0f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < nslice; ++s) {
+      const float f = fast_exp2(sm[s * tps + col] - M);
+      acc += f * sacc[s * tps + col];
+      L += f * sl[s * tps + col];
+    }
+    if (has_in) {
+      const float f = fast_exp2(in_m * kLog2e - M);
+      acc += f * in_acc;
+      L += f * in_l;
+    }
   }
   const bool live = L > 0.0f;
   if (a.out) a.out[(size_t)row * a.dv + col] = live ? acc / L : 0.0f;
   if (a.out_acc) {
     a.out_acc[(size_t)row * a.dv + col] = live ? acc : 0.0f;
     if (col == 0) {
-      a.out_m[row] = live ? mx : -INFINITY;
+      a.out_m[row] = live ? M * kLn2 : -INFINITY;
       a.out_l[row] = live ? L : 0.0f;
     }
   }

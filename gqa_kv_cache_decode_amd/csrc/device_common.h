@@ -8,6 +8,7 @@ namespace gqa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
@@ -15,6 +16,11 @@ constexpr float kLog2e = 1.44269504088896340736f;
 // 2^x on the hardware exp unit (v_exp_f32): exact 0 for -inf.
 __device__ __forceinline__ float fast_exp2(float x) {
   return __builtin_amdgcn_exp2f(x);
+}
+
+// 16-byte load marked nontemporal (data read once per call).
+__device__ __forceinline__ u32x4 stream_load16(const void *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
 }
 
 __device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {

@@ -7,6 +7,9 @@
 
 namespace gqa {
 
+// Wavefronts per work-group of the bf16 partition kernel.
+constexpr int kPartitionWaves = 2;
+
 struct PartitionArgs {
   const void *q;        // [B][Hkv*hpk][dk]
   const void *k;        // [B][max_len][Hkv][dk]
@@ -50,6 +53,7 @@ struct AppendArgs {
 // Kernel families compiled into the library.
 bool partition_bf16_supported(int dk, int dv, int hpk);
 bool partition_f32_supported(int dk, int dv, int hpk);
+bool partition_f32_uses_mfma(int dk, int dv);
 size_t partition_f32_lds_bytes(int dk, int dv, int hpk);
 
 hipError_t launch_partition_bf16(const PartitionArgs &a, hipStream_t s);

@@ -104,7 +104,9 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
   const uint16_t *Kg = K + ((size_t)b * max_len * Hkv + g) * DK;
   const uint16_t *Vg = V + ((size_t)b * max_len * Hkv + g) * DV;
 
-  uint4 kr[G::kLoads], vr[G::vLoads];
+  // K/V are read exactly once per call, so the loads are nontemporal: they
+  // stream through without displacing cached lines.
+  u32x4 kr[G::kLoads], vr[G::vLoads];
   auto issue = [&](int tile) {
     const int tb = t0 + tile * kTileTokens;
 #pragma unroll
@@ -112,16 +114,14 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
       const int idx = i * 64 + lane;
       const int t = tb + idx / G::kPieces;
       const int pc = idx % G::kPieces;
-      kr[i] = (t < t1) ? *reinterpret_cast<const uint4 *>(Kg + t * kTok + pc * 8)
-                       : make_uint4(0, 0, 0, 0);
+      kr[i] = (t < t1) ? stream_load16(Kg + t * kTok + pc * 8) : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int i = 0; i < G::vLoads; ++i) {
       const int idx = i * 64 + lane;
       const int t = tb + idx / G::vPieces;
       const int pc = idx % G::vPieces;
-      vr[i] = (t < t1) ? *reinterpret_cast<const uint4 *>(Vg + t * vTok + pc * 8)
-                       : make_uint4(0, 0, 0, 0);
+      vr[i] = (t < t1) ? stream_load16(Vg + t * vTok + pc * 8) : u32x4{0, 0, 0, 0};
     }
   };
 
@@ -138,13 +138,13 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < G::kLoads; ++i) {
       const int idx = i * 64 + lane;
-      *reinterpret_cast<uint4 *>(Ks + (idx / G::kPieces) * G::kStride +
+      *reinterpret_cast<u32x4 *>(Ks + (idx / G::kPieces) * G::kStride +
                                  (idx % G::kPieces) * 8) = kr[i];
     }
 #pragma unroll
     for (int i = 0; i < G::vLoads; ++i) {
       const int idx = i * 64 + lane;
-      *reinterpret_cast<uint4 *>(Vs + (idx / G::vPieces) * G::vStride +
+      *reinterpret_cast<u32x4 *>(Vs + (idx / G::vPieces) * G::vStride +
                                  (idx % G::vPieces) * 8) = vr[i];
     }
     if (tile + NW < ntiles) issue(tile + NW);  // next tile in flight meanwhile
@@ -276,11 +276,14 @@ bool partition_bf16_supported(int dk, int dv, int hpk) {
          (dk == 192 && dv == 128) || (dk == 256 && dv == 256);
 }
 
+// Two wavefronts per work-group: the split-K plan sizes chunks so that the
+// launch holds about a thousand wavefronts, each streaming a long run of
+// tiles, which measured best across the workload shapes on MI355X.
 hipError_t launch_partition_bf16(const PartitionArgs &a, hipStream_t s) {
-  if (a.dk == 64 && a.dv == 64) return launch_one<64, 64, 4>(a, s);
-  if (a.dk == 128 && a.dv == 128) return launch_one<128, 128, 4>(a, s);
-  if (a.dk == 192 && a.dv == 128) return launch_one<192, 128, 4>(a, s);
-  if (a.dk == 256 && a.dv == 256) return launch_one<256, 256, 4>(a, s);
+  if (a.dk == 64 && a.dv == 64) return launch_one<64, 64, kPartitionWaves>(a, s);
+  if (a.dk == 128 && a.dv == 128) return launch_one<128, 128, kPartitionWaves>(a, s);
+  if (a.dk == 192 && a.dv == 128) return launch_one<192, 128, kPartitionWaves>(a, s);
+  if (a.dk == 256 && a.dv == 256) return launch_one<256, 256, kPartitionWaves>(a, s);
   return hipErrorInvalidValue;
 }
 

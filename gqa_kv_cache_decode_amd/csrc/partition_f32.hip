@@ -1,23 +1,277 @@
-// Split-K partition kernel for fp32 caches (VALU, any dk/dv up to 256).
+// Split-K partition kernels for fp32 caches.
 //
-// fp32 keeps full-precision products, so this family runs on the vector ALUs
-// rather than on bf16 matrix cores.  One wavefront per work-group handles one
-// (sequence b, KV group g, chunk c) for all heads_per_kv query heads: each
-// 64-token tile of K and V is read once with coalesced loads into LDS and
-// shared by the group's heads (needle-core attn.rs: each KV head serves its
-// query heads by broadcast).  Lane t scores token t against every head,
-// the wavefront folds the tile into each head's running maximum, partition and
-// weighted value sum (usearch attend), and lane t then owns value columns
-// t, t+64, ... of every head for the P.V sum.
+// Matrix-core family (head widths 64/64, 128/128, 192/128, 256/256): the same
+// structure as the bf16 kernel, on the exact-fp32 MFMA 16x16x4.  A wavefront
+// takes 16-token tiles (the bytes of a 32-token bf16 tile), stages K and V once
+// per KV group in its own LDS slice, forms S^T[token][head] = K . q^T for all
+// heads of the group at once, folds the tile into each head's running maximum,
+// partition and weighted value sum (usearch attend), and accumulates
+// acc^T[dv][head] += V^T . P^T with P straight from the S^T registers.
+//
+// Vector-ALU family (any other head widths that are multiples of 4, up to
+// 256): one wavefront per work-group, lane t scores token t of a 64-token tile
+// against every head, then owns value columns t, t+64, ... for the P.V sum.
+// Both read each K/V row of a KV group once and share it among the group's
+// query heads (needle-core attn.rs: each KV head serves its query heads by
+// broadcast).
 #include "device_common.h"
 #include "launch.h"
 
 namespace gqa {
 namespace {
 
+// ---- matrix-core family ---------------------------------------------------
+
+constexpr int kF32Tile = 16;  // tokens per wavefront tile
+
+template <int DK, int DV>
+struct F32Geom {
+  static_assert(DK % 16 == 0 && DV % 16 == 0, "head widths");
+  static constexpr int kPieces = DK / 4;  // 16-byte pieces per K row
+  static constexpr int vPieces = DV / 4;
+  static constexpr int kLoads = kF32Tile * kPieces / 64;  // per lane
+  static constexpr int vLoads = kF32Tile * vPieces / 64;
+  static_assert(kF32Tile * kPieces % 64 == 0, "K tile split");
+  static_assert(kF32Tile * vPieces % 64 == 0, "V tile split");
+  static constexpr int kStride = DK + 4;  // LDS row stride in floats
+  static constexpr int vStride = DV + 4;
+  static constexpr int waveLdsFloats = kF32Tile * (kStride + vStride);
+};
+
+template <int DK, int DV, int NW>
+__global__ __launch_bounds__(NW * 64) void partition_f32_mfma_kernel(
+    const float *__restrict__ q, const float *__restrict__ K,
+    const float *__restrict__ V, const int32_t *__restrict__ lens, int batch,
+    int max_len, int Hkv, int hpk, int chunk, int nchunk, float scale_log2,
+    float *__restrict__ part_m, float *__restrict__ part_l,
+    float *__restrict__ part_acc) {
+  using G = F32Geom<DK, DV>;
+  constexpr int kMergeFloats = NW * 16 * (DV + 2);
+  constexpr int kTileFloats = NW * G::waveLdsFloats;
+  constexpr int kLdsFloats = kTileFloats > kMergeFloats ? kTileFloats : kMergeFloats;
+  __shared__ __attribute__((aligned(16))) float lds[kLdsFloats];
+
+  const int nwork = batch * Hkv * nchunk;
+  const int item = xcd_local_item(blockIdx.x, nwork);
+  const int c = item % nchunk;
+  const int bg = item / nchunk;
+  const int g = bg % Hkv;
+  const int b = bg / Hkv;
+  const int n = clamp_len(lens[b], max_len);
+  const int t0 = c * chunk;
+  if (t0 >= n) return;
+  const int t1 = min(t0 + chunk, n);
+  const int ntiles = (t1 - t0 + kF32Tile - 1) / kF32Tile;
+
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int hl = lane & 15;
+  const int kg = lane >> 4;
+  const int Hq = Hkv * hpk;
+
+  // q as the B operand: for dim block blk and step j the lane holds
+  // q[head hl][blk*16 + kg*4 + j]; K's A operand uses the same dims.
+  f32x4 qf[DK / 16];
+  {
+    const float *qrow = q + ((size_t)b * Hq + (size_t)g * hpk + hl) * DK;
+#pragma unroll
+    for (int blk = 0; blk < DK / 16; ++blk)
+      qf[blk] = hl < hpk ? *reinterpret_cast<const f32x4 *>(qrow + blk * 16 + kg * 4)
+                         : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  float *Ks = lds + w * G::waveLdsFloats;
+  float *Vs = Ks + kF32Tile * G::kStride;
+  const size_t kTok = (size_t)Hkv * DK, vTok = (size_t)Hkv * DV;
+  const float *Kg = K + ((size_t)b * max_len * Hkv + g) * DK;
+  const float *Vg = V + ((size_t)b * max_len * Hkv + g) * DV;
+
+  u32x4 kr[G::kLoads], vr[G::vLoads];
+  auto issue = [&](int tile) {
+    const int tb = t0 + tile * kF32Tile;
+#pragma unroll
+    for (int i = 0; i < G::kLoads; ++i) {
+      const int idx = i * 64 + lane;
+      const int t = tb + idx / G::kPieces;
+      kr[i] = (t < t1) ? stream_load16(Kg + t * kTok + (idx % G::kPieces) * 4)
+                       : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < G::vLoads; ++i) {
+      const int idx = i * 64 + lane;
+      const int t = tb + idx / G::vPieces;
+      vr[i] = (t < t1) ? stream_load16(Vg + t * vTok + (idx % G::vPieces) * 4)
+                       : u32x4{0, 0, 0, 0};
+    }
+  };
+
+  float m_run = -INFINITY, l_run = 0.0f;
+  f32x4 o[DV / 16];
+#pragma unroll
+  for (int blk = 0; blk < DV / 16; ++blk) o[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  int tile = w;
+  if (tile < ntiles) issue(tile);
+  for (; tile < ntiles; tile += NW) {
+    wave_lds_sync();
+#pragma unroll
+    for (int i = 0; i < G::kLoads; ++i) {
+      const int idx = i * 64 + lane;
+      *reinterpret_cast<u32x4 *>(Ks + (idx / G::kPieces) * G::kStride +
+                                 (idx % G::kPieces) * 4) = kr[i];
+    }
+#pragma unroll
+    for (int i = 0; i < G::vLoads; ++i) {
+      const int idx = i * 64 + lane;
+      *reinterpret_cast<u32x4 *>(Vs + (idx / G::vPieces) * G::vStride +
+                                 (idx % G::vPieces) * 4) = vr[i];
+    }
+    if (tile + NW < ntiles) issue(tile + NW);
+    wave_lds_sync();
+
+    // S^T[token kg*4 + i][head hl]
+    f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int blk = 0; blk < DK / 16; ++blk) {
+      const f32x4 a =
+          *reinterpret_cast<const f32x4 *>(Ks + hl * G::kStride + blk * 16 + kg * 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], qf[blk][j], sacc, 0, 0, 0);
+    }
+
+    const int tb = t0 + tile * kF32Tile;
+    float x[4];
+    float mt = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] = (tb + kg * 4 + i < t1) ? sacc[i] * scale_log2 : -INFINITY;
+      mt = fmaxf(mt, x[i]);
+    }
+    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    const float m_new = fmaxf(m_run, mt);
+    const float alpha = fast_exp2(m_run - m_new);
+    m_run = m_new;
+    float p[4], psum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p[i] = fast_exp2(x[i] - m_new);
+      psum += p[i];
+    }
+    l_run = l_run * alpha + psum;
+
+    // acc^T += V^T P^T, one token per MFMA step: A = V[kg*4 + i][blk*16 + hl]
+#pragma unroll
+    for (int blk = 0; blk < DV / 16; ++blk) {
+      o[blk] *= alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        o[blk] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+            Vs[(kg * 4 + i) * G::vStride + blk * 16 + hl], p[i], o[blk], 0, 0, 0);
+    }
+  }
+
+  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
+  l_tot += __shfl_xor(l_tot, 32, 64);
+
+  __syncthreads();
+  float *wm = lds;
+  float *wl = wm + NW * 16;
+  float *wacc = wl + NW * 16;
+  if (lane < 16) {
+    wm[w * 16 + lane] = m_run;
+    wl[w * 16 + lane] = l_tot;
+  }
+#pragma unroll
+  for (int blk = 0; blk < DV / 16; ++blk)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      wacc[(w * 16 + hl) * DV + blk * 16 + kg * 4 + i] = o[blk][i];
+  __syncthreads();
+
+  for (int e = threadIdx.x; e < hpk * DV; e += NW * 64) {
+    const int h = e / DV, d = e % DV;
+    float M = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, wm[ww * 16 + h]);
+    float acc = 0.0f, L = 0.0f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      const float f = fast_exp2(wm[ww * 16 + h] - M);
+      acc += f * wacc[(ww * 16 + h) * DV + d];
+      L += f * wl[ww * 16 + h];
+    }
+    const size_t row = (size_t)b * Hq + (size_t)g * hpk + h;
+    part_acc[(row * nchunk + c) * DV + d] = acc;
+    if (d == 0) {
+      part_m[row * nchunk + c] = M * kLn2;
+      part_l[row * nchunk + c] = L;
+    }
+  }
+}
+
+template <int DK, int DV>
+hipError_t launch_mfma(const PartitionArgs &a, hipStream_t s) {
+  const int nwork = a.batch * a.num_kv_heads * a.num_chunks;
+  hipLaunchKernelGGL((partition_f32_mfma_kernel<DK, DV, kPartitionWaves>),
+                     dim3(nwork), dim3(kPartitionWaves * 64), 0, s,
+                     static_cast<const float *>(a.q),
+                     static_cast<const float *>(a.k),
+                     static_cast<const float *>(a.v), a.lens, a.batch,
+                     a.max_len, a.num_kv_heads, a.hpk, a.chunk_tokens,
+                     a.num_chunks, a.scale_log2, a.part_m, a.part_l,
+                     a.part_acc);
+  return hipGetLastError();
+}
+
+bool mfma_shape(int dk, int dv) {
+  return (dk == 64 && dv == 64) || (dk == 128 && dv == 128) ||
+         (dk == 192 && dv == 128) || (dk == 256 && dv == 256);
+}
+
+// ---- vector-ALU family ----------------------------------------------------
+
 constexpr int kTok = 64;       // tokens per tile (one per lane)
 constexpr int kMaxHeads = 16;  // heads per KV group
 constexpr int kMaxCols = 4;    // value columns per lane (dv <= 256)
+
+constexpr int kBatch = 16;     // 16-byte loads in flight per lane
+
+// Stages tokens [tb, tb + kTok) of one group (row stride `gstride` floats,
+// width d) into LDS rows of `lstride` floats; tokens at or past t1 read as 0.
+// Loads are issued kBatch at a time before any of them is stored.
+__device__ __forceinline__ void load_tile(const float *src, size_t gstride,
+                                          int d, int tb, int t1, int lane,
+                                          float *dst, int lstride,
+                                          bool vec_store) {
+  const int d4 = d >> 2;
+  const int total = kTok * d4;
+  for (int e0 = 0; e0 < total; e0 += kBatch * 64) {
+    float4 x[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int e = e0 + j * 64 + lane;
+      const int tok = e / d4, col = (e % d4) * 4;
+      x[j] = (e < total && tb + tok < t1)
+                 ? *reinterpret_cast<const float4 *>(src + (tb + tok) * gstride + col)
+                 : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const int e = e0 + j * 64 + lane;
+      if (e < total) {
+        const int tok = e / d4, col = (e % d4) * 4;
+        float *p = dst + tok * lstride + col;
+        if (vec_store) {
+          *reinterpret_cast<float4 *>(p) = x[j];
+        } else {
+          p[0] = x[j].x; p[1] = x[j].y; p[2] = x[j].z; p[3] = x[j].w;
+        }
+      }
+    }
+  }
+}
 
 __global__ __launch_bounds__(64) void partition_f32_kernel(
     const float *__restrict__ q, const float *__restrict__ K,
@@ -63,22 +317,8 @@ __global__ __launch_bounds__(64) void partition_f32_kernel(
 
   for (int tb = t0; tb < t1; tb += kTok) {
     wave_lds_sync();
-    const int d4 = dk >> 2, v4 = dv >> 2;
-    for (int e = lane; e < kTok * d4; e += 64) {
-      const int tok = e / d4, col = (e % d4) * 4;
-      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (tb + tok < t1)
-        x = *reinterpret_cast<const float4 *>(Kg + (tb + tok) * kT + col);
-      float *dst = Ks + tok * ks + col;
-      dst[0] = x.x; dst[1] = x.y; dst[2] = x.z; dst[3] = x.w;
-    }
-    for (int e = lane; e < kTok * v4; e += 64) {
-      const int tok = e / v4, col = (e % v4) * 4;
-      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (tb + tok < t1)
-        x = *reinterpret_cast<const float4 *>(Vg + (tb + tok) * vT + col);
-      *reinterpret_cast<float4 *>(Vs + tok * dv + col) = x;
-    }
+    load_tile(Kg, kT, dk, tb, t1, lane, Ks, ks, false);
+    load_tile(Vg, vT, dv, tb, t1, lane, Vs, dv, true);
     wave_lds_sync();
 
     float s[kMaxHeads];
@@ -148,14 +388,23 @@ size_t partition_f32_lds_bytes(int dk, int dv, int hpk) {
 // LDS of one gfx950 work-group.
 constexpr size_t kMaxLds = 160 * 1024;
 
-// Shapes whose tile fits the LDS of a work-group.
+// Shapes with a kernel: the matrix-core shapes (1..16 heads per KV head),
+// or a vector-ALU tile that fits the LDS of a work-group.
 bool partition_f32_supported(int dk, int dv, int hpk) {
-  return hpk >= 1 && hpk <= kMaxHeads && dk >= 4 && dk <= 256 &&
-         dk % 4 == 0 && dv >= 4 && dv <= 64 * kMaxCols && dv % 4 == 0 &&
+  if (hpk < 1 || hpk > kMaxHeads) return false;
+  if (mfma_shape(dk, dv)) return true;
+  return dk >= 4 && dk <= 256 && dk % 4 == 0 && dv >= 4 &&
+         dv <= 64 * kMaxCols && dv % 4 == 0 &&
          partition_f32_lds_bytes(dk, dv, hpk) <= kMaxLds;
 }
 
+bool partition_f32_uses_mfma(int dk, int dv) { return mfma_shape(dk, dv); }
+
 hipError_t launch_partition_f32(const PartitionArgs &a, hipStream_t s) {
+  if (a.dk == 64 && a.dv == 64) return launch_mfma<64, 64>(a, s);
+  if (a.dk == 128 && a.dv == 128) return launch_mfma<128, 128>(a, s);
+  if (a.dk == 192 && a.dv == 128) return launch_mfma<192, 128>(a, s);
+  if (a.dk == 256 && a.dv == 256) return launch_mfma<256, 256>(a, s);
   const int nwork = a.batch * a.num_kv_heads * a.num_chunks;
   const size_t lds = partition_f32_lds_bytes(a.dk, a.dv, a.hpk);
   if (lds > 65536) {

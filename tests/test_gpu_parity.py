@@ -81,13 +81,15 @@ def test_attend_small(name):
     _attend_vs_oracle(w, x, what=name)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("chunk", [64, 128, 256, 1024, 4096])
-def test_split_independence(chunk):
+def test_split_independence(chunk, dtype):
     """Any chunking of the key axis gives the oracle's answer."""
-    w = wl.RAGGED_BF16.replace(batch=5, max_len=2500, num_q_heads=32)
+    w = wl.RAGGED_BF16.replace(batch=5, max_len=2500, num_q_heads=32,
+                               dtype=dtype)
     x = wl.make_inputs(w, lens_override=[2500, 1, 777, 1024, 1025])
-    say(f"[split] chunk={chunk}")
-    _attend_vs_oracle(w, x, plan_chunk=chunk, what=f"chunk {chunk}")
+    say(f"[split] chunk={chunk} {dtype}")
+    _attend_vs_oracle(w, x, plan_chunk=chunk, what=f"chunk {chunk} {dtype}")
 
 
 def test_padding_never_read():
@@ -123,6 +125,12 @@ EDGE = [
     ("f32_dk96_dv32", wl.TINY_F32.replace(dk=96, dv=32, max_len=130)),
     ("f32_mha", wl.TINY_F32.replace(num_q_heads=4, num_kv_heads=4,
                                     max_len=70)),
+    ("f32_dk192_dv128", wl.TINY_F32.replace(dk=192, dv=128, num_q_heads=16,
+                                            num_kv_heads=2, max_len=400)),
+    ("f32_d256", wl.TINY_F32.replace(dk=256, dv=256, num_q_heads=8,
+                                     num_kv_heads=4, max_len=300, batch=2)),
+    ("f32_valu_dk48_dv80", wl.TINY_F32.replace(dk=48, dv=80, max_len=200,
+                                               batch=2)),
 ]
 
 
