@@ -35,7 +35,12 @@ METRIC = ("KV-cache GB/s streamed (and % HBM peak) in GQA decode; "
           "µs per decode step")
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published figure
 ROTATE_TARGET_BYTES = 1 << 30
-PARTITION_SOURCE = ROOT / "gqa_kv_cache_decode_amd" / "csrc" / "partition_bf16.hip"
+CSRC = ROOT / "gqa_kv_cache_decode_amd" / "csrc"
+# Sources of the dominant (partition) kernel: recorded counter readings are
+# only reported while these are unchanged.
+PARTITION_SOURCES = {"bf16": ["partition_bf16.hip", "device_common.h", "launch.h"],
+                     "f32": ["partition_f32.hip", "device_common.h", "launch.h"]}
+COPY_BYTES = 256 << 20      # calibration copy for the byte counters
 
 
 def log(*a):
@@ -55,6 +60,10 @@ def parse_args():
                    help="budget of the oracle's CPU-baseline timing")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-ceiling", action="store_true")
+    p.add_argument("--profile-pass", action="store_true",
+                   help="no timing: a few eager partition launches and three "
+                        f"{COPY_BYTES >> 20} MiB calibration copies, for "
+                        "hardware-counter runs")
     return p.parse_args()
 
 
@@ -81,8 +90,9 @@ class Branch:
         self.lens_before = (lens_after - 1).clamp_(min=0) if append else None
         self.lens_cur = [lens_after.clone() for _ in range(copies)]
         self.plan = g.attend_plan(self.k[0], self.v[0], w.num_q_heads)
-        self.ws = torch.empty(self.plan.workspace_bytes, dtype=torch.uint8,
-                              device="cuda")
+        # decode_step's workspace (zero-filled once) also serves the plain
+        # partition/combine calls: its head is the split-K partial area
+        self.ws = g.step_workspace(self.k[0], self.v[0], w.num_q_heads)
         self.n_tot = int(lens_after.clamp(0, k.shape[1]).sum().item())
 
 
@@ -132,24 +142,36 @@ def main():
         f"{main_bytes * copies / 2**30:.2f} GiB of K/V resident")
 
     def step(r):
+        """One decode step: the branch holding the new token runs decode_step
+        (append + attend, one launch where the partials fold in-kernel); a
+        long cache without the new token is attended first and hands its
+        carry over."""
         for i, br in enumerate(branches):
-            lens = br.lens_cur[r]
-            if br.append:
-                g.kv_append(br.k[r], br.v[r], k_new, v_new, br.lens_before,
-                            lens_out=lens)
-            g.attend_partition(q, br.k[r], br.v[r], lens, br.plan, br.ws,
-                               w.scale)
             last = i == len(branches) - 1
-            g.attend_combine(Hq, br.k[r], br.v[r], lens, br.plan, br.ws,
-                             carry_in=carry if i > 0 else None,
-                             carry_out=None if last else carry,
-                             out=out if last else None)
+            cin = carry if i > 0 else None
+            cout = None if last else carry
+            o = out if last else None
+            if br.append:
+                g.decode_step(q, br.k[r], br.v[r], k_new, v_new,
+                              br.lens_before, br.lens_cur[r], w.scale,
+                              carry_in=cin, carry_out=cout, out=o,
+                              workspace=br.ws)
+            else:
+                g.attend_partition(q, br.k[r], br.v[r], br.lens_cur[r],
+                                   br.plan, br.ws, w.scale)
+                g.attend_combine(Hq, br.k[r], br.v[r], br.lens_cur[r],
+                                 br.plan, br.ws, carry_in=cin,
+                                 carry_out=cout, out=o)
 
     dom = branches[0]
 
     def partition_only(r):
         g.attend_partition(q, dom.k[r], dom.v[r], dom.lens_cur[r], dom.plan,
                            dom.ws, w.scale)
+
+    if args.profile_pass:
+        profile_pass(torch, step, partition_only, copies, w, dom)
+        return
 
     # warm up eagerly (also fixes lens_cur to the post-append lengths)
     for i in range(args.warmup):
@@ -189,10 +211,22 @@ def main():
     torch.cuda.synchronize()
     ms_step = time_graph(g_step, K)
 
-    g_part = graph_of(partition_only, K)
-    g_part.replay()
+    # the dominant kernel alone: an event pair around each of K eager launches
+    # on the stream they run on.  A bounded spin kernel holds the stream while
+    # the host enqueues them, so the pairs run back to back and none of them
+    # includes host launch latency.
+    pairs = [(torch.cuda.Event(enable_timing=True),
+              torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     torch.cuda.synchronize()
-    ms_part = time_graph(g_part, K)
+    bench_lib().gqa_bench_spin(
+        min(1000000, 20000 + 200 * K),
+        ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    for i, (e0, e1) in enumerate(pairs):
+        e0.record()
+        partition_only(i % copies)
+        e1.record()
+    torch.cuda.synchronize()
+    ms_part = statistics.mean(e0.elapsed_time(e1) for e0, e1 in pairs)
 
     # eager reference timing of one step (diagnostic)
     torch.cuda.synchronize()
@@ -224,19 +258,20 @@ def main():
         ceiling = read_ceiling(torch)
         log(f"[bench] pure-read stream ceiling: {ceiling:.1f} GB/s")
 
-    traffic = measured_traffic(args.workload)
+    traffic = measured_traffic(args.workload, w.dtype)
+    kernel = (f"partition_bf16_kernel<{w.dk}, {w.dv}, 2>" if w.dtype == "bf16"
+              else f"partition_f32_mfma_kernel<{w.dk}, {w.dv}, 2>")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": traffic,
-                "kernel": "partition_bf16_kernel" if w.dtype == "bf16"
-                else "partition_f32_kernel",
+                "kernel": kernel,
                 "algorithmic_bytes_per_launch": part_bytes,
                 "avg_launch_us": round(ms_part * 1e3, 3)}
 
     cpu = None
     if not args.no_cpu_baseline:
-        del branches, dom, g_step, g_part
+        del branches, dom, g_step
         torch.cuda.empty_cache()
         cpu = cpu_baseline(w, args.cpu_seconds)
 
@@ -261,16 +296,33 @@ def main():
     print(json.dumps(line), flush=True)
 
 
+_BENCH_LIB = None
+
+
+def bench_lib():
+    """The measurement helpers (read stream, copy, spin) of libgqa_bench.so."""
+    global _BENCH_LIB
+    if _BENCH_LIB is None:
+        from gqa_kv_cache_decode_amd.build import BENCH_LIB
+        lib = ctypes.CDLL(str(BENCH_LIB))
+        lib.gqa_bench_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_size_t,
+                                              ctypes.c_void_p, ctypes.c_int,
+                                              ctypes.c_void_p]
+        lib.gqa_bench_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_size_t, ctypes.c_int,
+                                       ctypes.c_void_p]
+        lib.gqa_bench_spin.argtypes = [ctypes.c_int, ctypes.c_void_p]
+        _BENCH_LIB = lib
+    return _BENCH_LIB
+
+
 def read_ceiling(torch, nbytes=4 << 30, reps=5):
-    """A plain 16-byte-vector read of 4 GiB: the HBM read rate reachable here."""
-    from gqa_kv_cache_decode_amd.build import BENCH_LIB
-    lib = ctypes.CDLL(str(BENCH_LIB))
-    lib.gqa_bench_read_stream.argtypes = [ctypes.c_void_p, ctypes.c_size_t,
-                                          ctypes.c_void_p, ctypes.c_int,
-                                          ctypes.c_void_p]
+    """A plain nontemporal 16-byte-vector read of 4 GiB: the HBM read rate
+    reachable on this GPU (best of `reps`)."""
+    lib = bench_lib()
     buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     buf.fill_(1)
-    blocks = 256 * 16
+    blocks = 65536  # measured best for this kernel on MI355X
     sink = torch.zeros(blocks, dtype=torch.int32, device="cuda")
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     best = 0.0
@@ -288,17 +340,48 @@ def read_ceiling(torch, nbytes=4 << 30, reps=5):
     return best
 
 
-def measured_traffic(workload):
+def partition_source_hash(dtype):
+    h = hashlib.sha256()
+    for name in PARTITION_SOURCES[dtype]:
+        h.update((CSRC / name).read_bytes())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, dtype):
     """HBM bytes per partition launch from committed counter readings, if they
-    were taken on the current kernel source (else None)."""
+    were taken on the current kernel sources (else None)."""
     path = ROOT / "profiles" / f"traffic_{workload}.json"
     if not path.exists():
         return None
     rec = json.loads(path.read_text())
-    src_hash = hashlib.sha256(PARTITION_SOURCE.read_bytes()).hexdigest()[:16]
-    if rec.get("partition_source_sha256_16") != src_hash:
+    if rec.get("partition_source_sha256_16") != partition_source_hash(dtype):
         return None
     return rec.get("traffic_bytes_per_launch")
+
+
+def profile_pass(torch, step, partition_only, copies, w, dom):
+    """Eager launches for counter collection: 2 warm-up steps, 6 partition
+    launches (the dispatches to read), then 3 plain copies of COPY_BYTES."""
+    for r in range(2):
+        step(r % copies)
+    torch.cuda.synchronize()
+    for i in range(6):
+        partition_only(i % copies)
+    torch.cuda.synchronize()
+    lib = bench_lib()
+    src = torch.ones(COPY_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for _ in range(3):
+        assert lib.gqa_bench_copy(dst.data_ptr(), src.data_ptr(), COPY_BYTES,
+                                  256 * 16, stream) == 0
+    torch.cuda.synchronize()
+    q_bytes = w.batch * w.num_q_heads * w.dk * w.esz
+    print(json.dumps({"profile_pass": w.name,
+                      "partition_algorithmic_bytes": kv_bytes(w, dom.n_tot) +
+                      q_bytes, "copy_bytes": COPY_BYTES,
+                      "source_sha256_16": partition_source_hash(w.dtype)}),
+          flush=True)
 
 
 def cpu_baseline(w, budget_s):

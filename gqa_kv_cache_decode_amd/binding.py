@@ -68,6 +68,10 @@ _SIGNATURES = {
                                   ctypes.c_size_t, _CARRY_P, _CARRY_P, _P, _P]),
     "gqa_softmax_state_merge": (_I32, [_CARRY_P, _CARRY_P, _CARRY_P,
                                        ctypes.c_int64, _I32, _P, _P]),
+    "gqa_decode_step_workspace_bytes": (ctypes.c_size_t, [_CACHE_P, _I32]),
+    "gqa_decode_step": (_I32, [_P, _I32, _CACHE_P, _P, _P, _P, _P, _P,
+                               ctypes.c_float, _CARRY_P, _CARRY_P, _P, _P,
+                               ctypes.c_size_t, _P]),
 }
 
 
@@ -264,6 +268,44 @@ def attend_combine(num_q_heads: int, k_cache, v_cache, lens, plan: Plan,
         num_q_heads, ctypes.byref(c), _ptr(lens), ctypes.byref(plan),
         _ptr(workspace), workspace.numel() * workspace.element_size(), cin,
         cout, _ptr(out), _stream(lens)), "attend_combine")
+    return out
+
+
+def step_workspace(k_cache, v_cache, num_q_heads: int) -> torch.Tensor:
+    """A zero-filled workspace for decode_step (reusable across steps)."""
+    c = _cache(k_cache, v_cache)
+    n = library().gqa_decode_step_workspace_bytes(ctypes.byref(c), num_q_heads)
+    if n == 0:
+        raise GqaError("decode_step: unsupported shape")
+    return torch.zeros(n, dtype=torch.uint8, device=k_cache.device)
+
+
+def decode_step(q, k_cache, v_cache, k_new, v_new, lens_in, lens_out,
+                scale: float = 0.0, carry_in: Optional[Carry] = None,
+                carry_out: Optional[Carry] = None, out=_AUTO,
+                workspace: Optional[torch.Tensor] = None, dropped=None):
+    """kv_append of (k_new, v_new) then attend_decode, as one step.
+
+    lens_out must be a different tensor from lens_in.  ``workspace`` must come
+    from :func:`step_workspace` (zero-filled once, then reused)."""
+    c, hq = _attend_args(q, k_cache, v_cache, lens_in)
+    _need(k_new, "k_new", k_cache.dtype, (c.batch, c.num_kv_heads, c.dk))
+    _need(v_new, "v_new", k_cache.dtype, (c.batch, c.num_kv_heads, c.dv))
+    _need(lens_out, "lens_out", torch.int32, (c.batch,))
+    if dropped is not None:
+        _need(dropped, "dropped", torch.int32, (1,))
+    if out is _AUTO:
+        out = torch.empty(c.batch, hq, c.dv, dtype=torch.float32,
+                          device=q.device)
+    cin, cout = _carries(c, hq, carry_in, carry_out, out)
+    if workspace is None:
+        workspace = step_workspace(k_cache, v_cache, hq)
+    _need(workspace, "workspace")
+    _check(library().gqa_decode_step(
+        _ptr(q), hq, ctypes.byref(c), _ptr(k_new), _ptr(v_new), _ptr(lens_in),
+        _ptr(lens_out), _ptr(dropped), float(scale), cin, cout, _ptr(out),
+        _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(q)), "decode_step")
     return out
 
 

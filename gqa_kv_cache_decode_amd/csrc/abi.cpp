@@ -19,6 +19,13 @@ using gqa::PartitionArgs;
 constexpr size_t kAlign = 256;
 constexpr int kChunkQuantum = 64;
 constexpr int kMaxCombineDv = 256;
+// A decode step folds a KV group's partials inside the step launch (in the
+// group's last work-group to finish) only when the launch is small: there the
+// saved launch outweighs the arrival count every work-group then performs.
+// Larger launches, or partial sets above kFuseBytes per group, use the combine
+// kernel, which spreads the fold over one work-group per query row.
+constexpr size_t kFuseBytes = 64 * 1024;
+constexpr int64_t kFuseMaxGroups = 256;
 // Wavefronts a partition launch should hold: about four per compute unit of an
 // MI355X (256 CUs), each streaming a long run of tiles.
 constexpr int64_t kTargetWaves = 1024;
@@ -202,6 +209,17 @@ gqa_status check_combine_args(int32_t hq, const gqa_cache *c,
   return GQA_OK;
 }
 
+size_t step_counter_bytes(const gqa_cache *c) {
+  return align_up((size_t)c->batch * c->num_kv_heads * sizeof(int));
+}
+
+bool step_fuses(const gqa_cache *c, int32_t hq, const gqa_plan &plan) {
+  const size_t hpk = hq / c->num_kv_heads;
+  const int64_t groups = (int64_t)c->batch * c->num_kv_heads * plan.num_chunks;
+  return groups <= kFuseMaxGroups &&
+         hpk * plan.num_chunks * (c->dv + 2) * sizeof(float) <= kFuseBytes;
+}
+
 }  // namespace
 
 extern "C" {
@@ -336,6 +354,91 @@ gqa_status gqa_softmax_state_merge(const gqa_carry *a, const gqa_carry *b,
   m.rows = rows;
   m.dv = dv;
   return device_status(gqa::launch_merge(m, stream));
+}
+
+size_t gqa_decode_step_workspace_bytes(const gqa_cache *cache,
+                                       int32_t num_q_heads) {
+  gqa_plan p;
+  if (make_plan(cache, num_q_heads, 0, &p) != GQA_OK) return 0;
+  return p.workspace_bytes + step_counter_bytes(cache);
+}
+
+gqa_status gqa_decode_step(const void *q, int32_t num_q_heads,
+                           const gqa_cache *cache, const void *k_new,
+                           const void *v_new, const int32_t *lens_in,
+                           int32_t *lens_out, int32_t *dropped, float scale,
+                           const gqa_carry *carry_in,
+                           const gqa_carry *carry_out, float *out,
+                           void *workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  gqa_status st = check_attend_args(q, num_q_heads, cache, lens_in, scale);
+  if (st != GQA_OK) return st;
+  if ((st = check_combine_args(num_q_heads, cache, lens_in, carry_in,
+                               carry_out, out)) != GQA_OK)
+    return st;
+  if (!k_new || !v_new || !lens_out || lens_out == lens_in)
+    return GQA_ERR_INVALID_ARGUMENT;
+  if (!aligned16(k_new) || !aligned16(v_new)) return GQA_ERR_INVALID_ARGUMENT;
+  gqa_plan plan;
+  if ((st = make_plan(cache, num_q_heads, 0, &plan)) != GQA_OK) return st;
+  if (!workspace || !aligned16(workspace)) return GQA_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < plan.workspace_bytes + step_counter_bytes(cache))
+    return GQA_ERR_WORKSPACE_TOO_SMALL;
+
+  const bool mfma = cache->dtype == GQA_DTYPE_BF16 ||
+                    gqa::partition_f32_uses_mfma(cache->dk, cache->dv);
+  if (!mfma) {  // vector-ALU shapes: the same step as three launches
+    st = gqa_kv_append(cache, k_new, v_new, lens_in, lens_out, dropped, stream);
+    if (st != GQA_OK) return st;
+    st = partition_checked(q, num_q_heads, cache, lens_out, scale, &plan,
+                           workspace, stream);
+    if (st != GQA_OK) return st;
+    return combine_checked(num_q_heads, cache, lens_out, &plan, workspace,
+                           carry_in, carry_out, out, stream);
+  }
+
+  const double sc =
+      scale != 0.0f ? (double)scale : 1.0 / std::sqrt((double)cache->dk);
+  PartitionArgs a;
+  a.q = q;
+  a.k = cache->k;
+  a.v = cache->v;
+  a.lens = lens_in;
+  a.batch = cache->batch;
+  a.max_len = cache->max_len;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.hpk = num_q_heads / cache->num_kv_heads;
+  a.dk = cache->dk;
+  a.dv = cache->dv;
+  a.chunk_tokens = plan.chunk_tokens;
+  a.num_chunks = plan.num_chunks;
+  a.scale_log2 = (float)(sc * 1.4426950408889634);
+  char *base = static_cast<char *>(workspace);
+  a.part_m = reinterpret_cast<float *>(base);
+  a.part_l = reinterpret_cast<float *>(base + plan.off_l);
+  a.part_acc = reinterpret_cast<float *>(base + plan.off_acc);
+
+  gqa::StepParams sp;
+  sp.k_new = k_new;
+  sp.v_new = v_new;
+  sp.lens_in = lens_in;
+  sp.lens_out = lens_out;
+  sp.dropped = dropped;
+  sp.counters = reinterpret_cast<int *>(base + plan.workspace_bytes);
+  sp.in_m = carry_in ? carry_in->m : nullptr;
+  sp.in_l = carry_in ? carry_in->l : nullptr;
+  sp.in_acc = carry_in ? carry_in->acc : nullptr;
+  sp.out_m = carry_out ? carry_out->m : nullptr;
+  sp.out_l = carry_out ? carry_out->l : nullptr;
+  sp.out_acc = carry_out ? carry_out->acc : nullptr;
+  sp.out = out;
+  sp.fuse = step_fuses(cache, num_q_heads, plan) ? 1 : 0;
+  st = device_status(cache->dtype == GQA_DTYPE_BF16
+                         ? gqa::launch_step_bf16(a, sp, stream)
+                         : gqa::launch_step_f32(a, sp, stream));
+  if (st != GQA_OK || sp.fuse) return st;
+  return combine_checked(num_q_heads, cache, lens_out, &plan, workspace,
+                         carry_in, carry_out, out, stream);
 }
 
 }  // extern "C"

@@ -1,6 +1,6 @@
 // Measurement helpers for the benchmark (not part of the decode ABI):
-//  - a pure 16-byte-vector read stream, the practical HBM read ceiling the
-//    decode kernels are compared with;
+//  - a pure 16-byte-vector nontemporal read stream, the practical HBM read
+//    ceiling the decode kernels are compared with;
 //  - a plain copy of known size, whose hardware-counter readings calibrate the
 //    fetch/write byte counters.
 #include <hip/hip_runtime.h>
@@ -11,17 +11,21 @@ namespace {
 
 __global__ __launch_bounds__(256) void read_stream_kernel(
     const uint4 *__restrict__ src, size_t n16, uint32_t *__restrict__ sink) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 *p = reinterpret_cast<const u32x4 *>(src);
   uint32_t acc = 0;
   const size_t stride = (size_t)gridDim.x * blockDim.x;
   size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
   for (; i + 3 * stride < n16; i += 4 * stride) {
-    const uint4 a = src[i], b = src[i + stride];
-    const uint4 c = src[i + 2 * stride], d = src[i + 3 * stride];
+    const u32x4 a = __builtin_nontemporal_load(p + i);
+    const u32x4 b = __builtin_nontemporal_load(p + i + stride);
+    const u32x4 c = __builtin_nontemporal_load(p + i + 2 * stride);
+    const u32x4 d = __builtin_nontemporal_load(p + i + 3 * stride);
     acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w;
     acc ^= c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
   }
   for (; i < n16; i += stride) {
-    const uint4 a = src[i];
+    const u32x4 a = __builtin_nontemporal_load(p + i);
     acc ^= a.x ^ a.y ^ a.z ^ a.w;
   }
   // One word per block, written only if the xor is a value no input makes
@@ -38,9 +42,26 @@ __global__ __launch_bounds__(256) void copy_kernel(uint4 *__restrict__ dst,
     dst[i] = src[i];
 }
 
+// Keeps one wavefront busy for `ticks` of the 100 MHz real-time counter, so
+// that work enqueued behind it runs back to back whatever the host's pace.
+__global__ void spin_kernel(unsigned long long ticks) {
+  const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+  while (__builtin_amdgcn_s_memrealtime() - t0 < ticks) __builtin_amdgcn_s_sleep(64);
+}
+
 }  // namespace
 
 extern "C" {
+
+// Occupies the stream for about `microseconds` (bounded).
+__attribute__((visibility("default"))) int gqa_bench_spin(int microseconds,
+                                                          hipStream_t stream) {
+  if (microseconds <= 0 || microseconds > 1000000) return 1;
+  hipLaunchKernelGGL(spin_kernel, dim3(1), dim3(64), 0, stream,
+                     (unsigned long long)microseconds * 100ull);
+  return hipGetLastError() == hipSuccess ? 0 : 5;
+}
+
 
 // Reads `bytes` (a multiple of 16) from `src`; `sink` needs `blocks` words.
 __attribute__((visibility("default"))) int gqa_bench_read_stream(

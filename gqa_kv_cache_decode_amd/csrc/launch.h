@@ -23,6 +23,20 @@ struct PartitionArgs {
   float *part_acc;      // [rows][num_chunks][dv]
 };
 
+// Extra inputs when a partition launch runs a whole decode step.
+struct StepParams {
+  const void *k_new;        // [B][Hkv][dk]
+  const void *v_new;        // [B][Hkv][dv]
+  const int32_t *lens_in;   // [B]
+  int32_t *lens_out;        // [B], never aliasing lens_in
+  int32_t *dropped;         // [1] or NULL
+  int *counters;            // [B][Hkv], zero on entry and on exit
+  const float *in_m, *in_l, *in_acc;  // carry_in, all NULL if absent
+  float *out_m, *out_l, *out_acc;     // carry_out, all NULL if absent
+  float *out;               // [rows][dv] or NULL
+  int fuse;                 // the last work-group of a group folds partials
+};
+
 struct CombineArgs {
   const int32_t *lens;
   int batch, num_q_heads, max_len, dv, chunk_tokens, num_chunks;
@@ -58,6 +72,12 @@ size_t partition_f32_lds_bytes(int dk, int dv, int hpk);
 
 hipError_t launch_partition_bf16(const PartitionArgs &a, hipStream_t s);
 hipError_t launch_partition_f32(const PartitionArgs &a, hipStream_t s);
+// One launch for append + partition (+ fold, when sp.fuse); matrix-core
+// shapes only.  `a.lens` is unused (lengths come from sp.lens_in).
+hipError_t launch_step_bf16(const PartitionArgs &a, const StepParams &sp,
+                            hipStream_t s);
+hipError_t launch_step_f32(const PartitionArgs &a, const StepParams &sp,
+                           hipStream_t s);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs &a, hipStream_t s);
 hipError_t launch_append(const AppendArgs &a, hipStream_t s);

@@ -2,11 +2,12 @@
 //
 // One work-group handles one (sequence b, KV group g, chunk c) and all
 // heads_per_kv query heads of the group.  Every K/V row of the chunk is read
-// from HBM once, with 16-byte coalesced loads, staged in the wavefront's own
-// LDS slice, and shared by all heads of the group through the MFMA N dimension
-// (needle-core attn.rs module doc: each KV head serves its query heads by
-// broadcast, not repeat-copy; cortiq-engine NystromState: the rows of a group
-// are identical for all its heads, so they are held once per group).
+// from HBM once, with 16-byte coalesced nontemporal loads, staged in the
+// wavefront's own LDS slice, and shared by all heads of the group through the
+// MFMA N dimension (needle-core attn.rs module doc: each KV head serves its
+// query heads by broadcast, not repeat-copy; cortiq-engine NystromState: the
+// rows of a group are identical for all its heads, so they are held once per
+// group).
 //
 // Per 32-token tile a wavefront computes
 //   S^T[token][head] = K_tile[token][:] . q[head][:]         (MFMA, A = K)
@@ -25,8 +26,15 @@
 // Heads are padded to 16 (the MFMA N width); padded heads see q = 0 and are
 // never written.  Tokens of a tile past the chunk end are loaded as zeros and
 // masked to -inf logits, so padding slots of the cache are never read.
+//
+// In STEP mode the same launch is a whole decode step (needle-core
+// self_attn_incremental: push_kv, then attend over the cache including the new
+// token): the wavefront whose tile holds the new slot takes that token's K/V
+// from k_new/v_new, stores them into the cache, and the group's partials are
+// folded by the last work-group to finish when `fuse` is set.
 #include "device_common.h"
 #include "launch.h"
+#include "step_common.h"
 
 namespace gqa {
 namespace {
@@ -47,32 +55,33 @@ struct Bf16Geom {
   static constexpr int waveLdsElems = kTileTokens * (kStride + vStride);
 };
 
-template <int DK, int DV, int NW>
+template <int DK, int DV, int NW, bool STEP>
 __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ K,
-    const uint16_t *__restrict__ V, const int32_t *__restrict__ lens,
-    int batch, int max_len, int Hkv, int hpk, int chunk, int nchunk,
-    float scale_log2, float *__restrict__ part_m, float *__restrict__ part_l,
-    float *__restrict__ part_acc) {
+    PartitionArgs a, StepParams sp) {
   using G = Bf16Geom<DK, DV>;
   constexpr int kMergeFloats = NW * 16 * (DV + 2);
   constexpr int kTileBytes = NW * G::waveLdsElems * 2;
   constexpr int kLdsBytes =
       kTileBytes > kMergeFloats * 4 ? kTileBytes : kMergeFloats * 4;
   __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
+  __shared__ int s_flag;
 
-  const int nwork = batch * Hkv * nchunk;
-  const int item = xcd_local_item(blockIdx.x, nwork);
+  const int Hkv = a.num_kv_heads, hpk = a.hpk, nchunk = a.num_chunks;
+  const int item = xcd_local_item(blockIdx.x, a.batch * Hkv * nchunk);
   const int c = item % nchunk;
   const int bg = item / nchunk;
   const int g = bg % Hkv;
   const int b = bg / Hkv;
 
-  const int n = clamp_len(lens[b], max_len);
-  const int t0 = c * chunk;
-  if (t0 >= n) return;  // whole work-group: nothing of this chunk is live
-  const int t1 = min(t0 + chunk, n);
-  const int ntiles = (t1 - t0 + kTileTokens - 1) / kTileTokens;
+  const SeqLen sl = seq_len<STEP>(a, sp, b);
+  const int n = sl.n;
+  if (STEP && g == 0 && c == 0 && threadIdx.x == 0) step_bookkeeping(sp, b, sl);
+  const int t0 = c * a.chunk_tokens;
+  // A work-group with nothing live exits, except the first of an empty
+  // sequence in a fused step: it still writes the group's outputs.
+  if (t0 >= n && !(STEP && sp.fuse && c == 0)) return;
+  const int t1 = min(t0 + a.chunk_tokens, n);
+  const int ntiles = t1 > t0 ? (t1 - t0 + kTileTokens - 1) / kTileTokens : 0;
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -84,7 +93,8 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
   bf16x8 qf[DK / 32];
   {
     const bool live = hl < hpk;
-    const uint16_t *qrow = q + ((size_t)b * Hq + (size_t)g * hpk + hl) * DK;
+    const uint16_t *qrow = static_cast<const uint16_t *>(a.q) +
+                           ((size_t)b * Hq + (size_t)g * hpk + hl) * DK;
 #pragma unroll
     for (int s = 0; s < DK / 32; ++s) {
       if (live) {
@@ -101,8 +111,20 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
 
   const size_t kTok = (size_t)Hkv * DK;  // elements between tokens
   const size_t vTok = (size_t)Hkv * DV;
-  const uint16_t *Kg = K + ((size_t)b * max_len * Hkv + g) * DK;
-  const uint16_t *Vg = V + ((size_t)b * max_len * Hkv + g) * DV;
+  uint16_t *Kg = static_cast<uint16_t *>(const_cast<void *>(a.k)) +
+                 ((size_t)b * a.max_len * Hkv + g) * DK;
+  uint16_t *Vg = static_cast<uint16_t *>(const_cast<void *>(a.v)) +
+                 ((size_t)b * a.max_len * Hkv + g) * DV;
+
+  // STEP: the work-group whose chunk holds the new slot writes the token's
+  // rows of this group into the cache before any of its tiles is loaded; its
+  // tile loop then reads the slot like any other.
+  if (STEP && sl.fresh && sl.n_old / a.chunk_tokens == c) {
+    append_group_row(static_cast<const u32x4 *>(sp.k_new) + ((size_t)b * Hkv + g) * (DK / 8),
+                     reinterpret_cast<u32x4 *>(Kg + sl.n_old * kTok), DK / 8,
+                     static_cast<const u32x4 *>(sp.v_new) + ((size_t)b * Hkv + g) * (DV / 8),
+                     reinterpret_cast<u32x4 *>(Vg + sl.n_old * vTok), DV / 8);
+  }
 
   // K/V are read exactly once per call, so the loads are nontemporal: they
   // stream through without displacing cached lines.
@@ -134,18 +156,19 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
   int tile = w;
   if (tile < ntiles) issue(tile);
   for (; tile < ntiles; tile += NW) {
+    const int tb = t0 + tile * kTileTokens;
     wave_lds_sync();  // previous tile's LDS reads are done
 #pragma unroll
     for (int i = 0; i < G::kLoads; ++i) {
       const int idx = i * 64 + lane;
-      *reinterpret_cast<u32x4 *>(Ks + (idx / G::kPieces) * G::kStride +
-                                 (idx % G::kPieces) * 8) = kr[i];
+      const int pc = idx % G::kPieces;
+      *reinterpret_cast<u32x4 *>(Ks + (idx / G::kPieces) * G::kStride + pc * 8) = kr[i];
     }
 #pragma unroll
     for (int i = 0; i < G::vLoads; ++i) {
       const int idx = i * 64 + lane;
-      *reinterpret_cast<u32x4 *>(Vs + (idx / G::vPieces) * G::vStride +
-                                 (idx % G::vPieces) * 8) = vr[i];
+      const int pc = idx % G::vPieces;
+      *reinterpret_cast<u32x4 *>(Vs + (idx / G::vPieces) * G::vStride + pc * 8) = vr[i];
     }
     if (tile + NW < ntiles) issue(tile + NW);  // next tile in flight meanwhile
     wave_lds_sync();
@@ -157,14 +180,13 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
       sacc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < DK / 32; ++s) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(
+        const bf16x8 av = *reinterpret_cast<const bf16x8 *>(
             Ks + (rb * 16 + hl) * G::kStride + s * 32 + kg * 8);
-        sacc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[s], sacc[rb],
+        sacc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qf[s], sacc[rb],
                                                            0, 0, 0);
       }
     }
 
-    const int tb = t0 + tile * kTileTokens;
     float x[8];
     float mt = -INFINITY;
 #pragma unroll
@@ -172,7 +194,7 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = tb + rb * 16 + kg * 4 + i;
-        const float v = (t < t1) ? sacc[rb][i] * scale_log2 : -INFINITY;
+        const float v = (t < t1) ? sacc[rb][i] * a.scale_log2 : -INFINITY;
         x[rb * 4 + i] = v;
         mt = fmaxf(mt, v);
       }
@@ -200,15 +222,15 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
     // order of this lane's P values.
 #pragma unroll
     for (int blk = 0; blk < DV / 16; ++blk) {
-      bf16x8 a;
+      bf16x8 av;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int tok = (j < 4) ? (kg * 4 + j) : (16 + kg * 4 + (j - 4));
-        a[j] = __builtin_bit_cast(__bf16, Vs[tok * G::vStride + blk * 16 + hl]);
+        av[j] = __builtin_bit_cast(__bf16, Vs[tok * G::vStride + blk * 16 + hl]);
       }
       o[blk] *= alpha;
-      o[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, phi, o[blk], 0, 0, 0);
-      o[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, plo, o[blk], 0, 0, 0);
+      o[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, phi, o[blk], 0, 0, 0);
+      o[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, plo, o[blk], 0, 0, 0);
     }
   }
 
@@ -221,51 +243,83 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
   float *wm = reinterpret_cast<float *>(lds);
   float *wl = wm + NW * 16;
   float *wacc = wl + NW * 16;
-  if (lane < 16) {
-    wm[w * 16 + lane] = m_run;
-    wl[w * 16 + lane] = l_tot;
+  if (ntiles > 0) {
+    if (lane < 16) {
+      wm[w * 16 + lane] = m_run;
+      wl[w * 16 + lane] = l_tot;
+    }
+#pragma unroll
+    for (int blk = 0; blk < DV / 16; ++blk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        wacc[(w * 16 + hl) * DV + blk * 16 + kg * 4 + i] = o[blk][i];
   }
-#pragma unroll
-  for (int blk = 0; blk < DV / 16; ++blk)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      wacc[(w * 16 + hl) * DV + blk * 16 + kg * 4 + i] = o[blk][i];
   __syncthreads();
 
-  for (int e = threadIdx.x; e < hpk * DV; e += NW * 64) {
-    const int h = e / DV;
-    const int d = e % DV;
-    float M = -INFINITY;
+  if (ntiles > 0) {
+    for (int e = threadIdx.x; e < hpk * DV; e += NW * 64) {
+      const int h = e / DV;
+      const int d = e % DV;
+      float M = -INFINITY;
 #pragma unroll
-    for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, wm[ww * 16 + h]);
-    float acc = 0.0f, L = 0.0f;
+      for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, wm[ww * 16 + h]);
+      float acc = 0.0f, L = 0.0f;
 #pragma unroll
-    for (int ww = 0; ww < NW; ++ww) {
-      const float f = fast_exp2(wm[ww * 16 + h] - M);
-      acc += f * wacc[(ww * 16 + h) * DV + d];
-      L += f * wl[ww * 16 + h];
+      for (int ww = 0; ww < NW; ++ww) {
+        const float f = fast_exp2(wm[ww * 16 + h] - M);
+        acc += f * wacc[(ww * 16 + h) * DV + d];
+        L += f * wl[ww * 16 + h];
+      }
+      const size_t row = (size_t)b * Hq + (size_t)g * hpk + h;
+      float *pa = a.part_acc + (row * nchunk + c) * DV + d;
+      float *pm = a.part_m + row * nchunk + c;
+      float *pl = a.part_l + row * nchunk + c;
+      if (STEP && sp.fuse) {  // read back by this launch's last work-group
+        coherent_store(pa, acc);
+        if (d == 0) {
+          coherent_store(pm, M * kLn2);
+          coherent_store(pl, L);
+        }
+      } else {
+        *pa = acc;
+        if (d == 0) {
+          *pm = M * kLn2;
+          *pl = L;
+        }
+      }
     }
-    const size_t row = (size_t)b * Hq + (size_t)g * hpk + h;
-    part_acc[(row * nchunk + c) * DV + d] = acc;
-    if (d == 0) {
-      part_m[row * nchunk + c] = M * kLn2;
-      part_l[row * nchunk + c] = L;
+  }
+
+  if (STEP && sp.fuse) {
+    const int nc = (n + a.chunk_tokens - 1) / a.chunk_tokens;
+    // an empty sequence has no partials: its first work-group folds alone
+    const bool last = nc == 0 || arrive_last(sp.counters + (size_t)b * Hkv + g,
+                                             nc, &s_flag);
+    if (last) {
+      __syncthreads();  // the LDS merge area is reused below
+      fold_group(a, sp, b, g, nc, reinterpret_cast<float *>(lds));
     }
   }
 }
 
-template <int DK, int DV, int NW>
-hipError_t launch_one(const PartitionArgs &a, hipStream_t s) {
+template <int DK, int DV, int NW, bool STEP>
+hipError_t launch_one(const PartitionArgs &a, const StepParams &sp,
+                      hipStream_t s) {
   const int nwork = a.batch * a.num_kv_heads * a.num_chunks;
-  hipLaunchKernelGGL((partition_bf16_kernel<DK, DV, NW>), dim3(nwork),
-                     dim3(NW * 64), 0, s,
-                     static_cast<const uint16_t *>(a.q),
-                     static_cast<const uint16_t *>(a.k),
-                     static_cast<const uint16_t *>(a.v), a.lens, a.batch,
-                     a.max_len, a.num_kv_heads, a.hpk, a.chunk_tokens,
-                     a.num_chunks, a.scale_log2, a.part_m, a.part_l,
-                     a.part_acc);
+  hipLaunchKernelGGL((partition_bf16_kernel<DK, DV, NW, STEP>), dim3(nwork),
+                     dim3(NW * 64), 0, s, a, sp);
   return hipGetLastError();
+}
+
+template <bool STEP>
+hipError_t dispatch(const PartitionArgs &a, const StepParams &sp,
+                    hipStream_t s) {
+  constexpr int W = kPartitionWaves;
+  if (a.dk == 64 && a.dv == 64) return launch_one<64, 64, W, STEP>(a, sp, s);
+  if (a.dk == 128 && a.dv == 128) return launch_one<128, 128, W, STEP>(a, sp, s);
+  if (a.dk == 192 && a.dv == 128) return launch_one<192, 128, W, STEP>(a, sp, s);
+  if (a.dk == 256 && a.dv == 256) return launch_one<256, 256, W, STEP>(a, sp, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -280,11 +334,12 @@ bool partition_bf16_supported(int dk, int dv, int hpk) {
 // launch holds about a thousand wavefronts, each streaming a long run of
 // tiles, which measured best across the workload shapes on MI355X.
 hipError_t launch_partition_bf16(const PartitionArgs &a, hipStream_t s) {
-  if (a.dk == 64 && a.dv == 64) return launch_one<64, 64, kPartitionWaves>(a, s);
-  if (a.dk == 128 && a.dv == 128) return launch_one<128, 128, kPartitionWaves>(a, s);
-  if (a.dk == 192 && a.dv == 128) return launch_one<192, 128, kPartitionWaves>(a, s);
-  if (a.dk == 256 && a.dv == 256) return launch_one<256, 256, kPartitionWaves>(a, s);
-  return hipErrorInvalidValue;
+  return dispatch<false>(a, StepParams{}, s);
+}
+
+hipError_t launch_step_bf16(const PartitionArgs &a, const StepParams &sp,
+                            hipStream_t s) {
+  return dispatch<true>(a, sp, s);
 }
 
 }  // namespace gqa

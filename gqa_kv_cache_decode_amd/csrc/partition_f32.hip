@@ -16,6 +16,7 @@
 // broadcast).
 #include "device_common.h"
 #include "launch.h"
+#include "step_common.h"
 
 namespace gqa {
 namespace {
@@ -38,30 +39,29 @@ struct F32Geom {
   static constexpr int waveLdsFloats = kF32Tile * (kStride + vStride);
 };
 
-template <int DK, int DV, int NW>
+template <int DK, int DV, int NW, bool STEP>
 __global__ __launch_bounds__(NW * 64) void partition_f32_mfma_kernel(
-    const float *__restrict__ q, const float *__restrict__ K,
-    const float *__restrict__ V, const int32_t *__restrict__ lens, int batch,
-    int max_len, int Hkv, int hpk, int chunk, int nchunk, float scale_log2,
-    float *__restrict__ part_m, float *__restrict__ part_l,
-    float *__restrict__ part_acc) {
+    PartitionArgs a, StepParams sp) {
   using G = F32Geom<DK, DV>;
   constexpr int kMergeFloats = NW * 16 * (DV + 2);
   constexpr int kTileFloats = NW * G::waveLdsFloats;
   constexpr int kLdsFloats = kTileFloats > kMergeFloats ? kTileFloats : kMergeFloats;
   __shared__ __attribute__((aligned(16))) float lds[kLdsFloats];
+  __shared__ int s_flag;
 
-  const int nwork = batch * Hkv * nchunk;
-  const int item = xcd_local_item(blockIdx.x, nwork);
+  const int Hkv = a.num_kv_heads, hpk = a.hpk, nchunk = a.num_chunks;
+  const int item = xcd_local_item(blockIdx.x, a.batch * Hkv * nchunk);
   const int c = item % nchunk;
   const int bg = item / nchunk;
   const int g = bg % Hkv;
   const int b = bg / Hkv;
-  const int n = clamp_len(lens[b], max_len);
-  const int t0 = c * chunk;
-  if (t0 >= n) return;
-  const int t1 = min(t0 + chunk, n);
-  const int ntiles = (t1 - t0 + kF32Tile - 1) / kF32Tile;
+  const SeqLen sl = seq_len<STEP>(a, sp, b);
+  const int n = sl.n;
+  if (STEP && g == 0 && c == 0 && threadIdx.x == 0) step_bookkeeping(sp, b, sl);
+  const int t0 = c * a.chunk_tokens;
+  if (t0 >= n && !(STEP && sp.fuse && c == 0)) return;
+  const int t1 = min(t0 + a.chunk_tokens, n);
+  const int ntiles = t1 > t0 ? (t1 - t0 + kF32Tile - 1) / kF32Tile : 0;
 
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
@@ -73,7 +73,8 @@ __global__ __launch_bounds__(NW * 64) void partition_f32_mfma_kernel(
   // q[head hl][blk*16 + kg*4 + j]; K's A operand uses the same dims.
   f32x4 qf[DK / 16];
   {
-    const float *qrow = q + ((size_t)b * Hq + (size_t)g * hpk + hl) * DK;
+    const float *qrow = static_cast<const float *>(a.q) +
+                        ((size_t)b * Hq + (size_t)g * hpk + hl) * DK;
 #pragma unroll
     for (int blk = 0; blk < DK / 16; ++blk)
       qf[blk] = hl < hpk ? *reinterpret_cast<const f32x4 *>(qrow + blk * 16 + kg * 4)
@@ -83,8 +84,20 @@ __global__ __launch_bounds__(NW * 64) void partition_f32_mfma_kernel(
   float *Ks = lds + w * G::waveLdsFloats;
   float *Vs = Ks + kF32Tile * G::kStride;
   const size_t kTok = (size_t)Hkv * DK, vTok = (size_t)Hkv * DV;
-  const float *Kg = K + ((size_t)b * max_len * Hkv + g) * DK;
-  const float *Vg = V + ((size_t)b * max_len * Hkv + g) * DV;
+  float *Kg = static_cast<float *>(const_cast<void *>(a.k)) +
+              ((size_t)b * a.max_len * Hkv + g) * DK;
+  float *Vg = static_cast<float *>(const_cast<void *>(a.v)) +
+              ((size_t)b * a.max_len * Hkv + g) * DV;
+
+  // STEP: the work-group whose chunk holds the new slot writes the token's
+  // rows of this group into the cache before any of its tiles is loaded; its
+  // tile loop then reads the slot like any other.
+  if (STEP && sl.fresh && sl.n_old / a.chunk_tokens == c) {
+    append_group_row(static_cast<const u32x4 *>(sp.k_new) + ((size_t)b * Hkv + g) * (DK / 4),
+                     reinterpret_cast<u32x4 *>(Kg + sl.n_old * kTok), DK / 4,
+                     static_cast<const u32x4 *>(sp.v_new) + ((size_t)b * Hkv + g) * (DV / 4),
+                     reinterpret_cast<u32x4 *>(Vg + sl.n_old * vTok), DV / 4);
+  }
 
   u32x4 kr[G::kLoads], vr[G::vLoads];
   auto issue = [&](int tile) {
@@ -93,15 +106,15 @@ __global__ __launch_bounds__(NW * 64) void partition_f32_mfma_kernel(
     for (int i = 0; i < G::kLoads; ++i) {
       const int idx = i * 64 + lane;
       const int t = tb + idx / G::kPieces;
-      kr[i] = (t < t1) ? stream_load16(Kg + t * kTok + (idx % G::kPieces) * 4)
-                       : u32x4{0, 0, 0, 0};
+      const int pc = idx % G::kPieces;
+      kr[i] = (t < t1) ? stream_load16(Kg + t * kTok + pc * 4) : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int i = 0; i < G::vLoads; ++i) {
       const int idx = i * 64 + lane;
       const int t = tb + idx / G::vPieces;
-      vr[i] = (t < t1) ? stream_load16(Vg + t * vTok + (idx % G::vPieces) * 4)
-                       : u32x4{0, 0, 0, 0};
+      const int pc = idx % G::vPieces;
+      vr[i] = (t < t1) ? stream_load16(Vg + t * vTok + pc * 4) : u32x4{0, 0, 0, 0};
     }
   };
 
@@ -113,18 +126,19 @@ __global__ __launch_bounds__(NW * 64) void partition_f32_mfma_kernel(
   int tile = w;
   if (tile < ntiles) issue(tile);
   for (; tile < ntiles; tile += NW) {
+    const int tb = t0 + tile * kF32Tile;
     wave_lds_sync();
 #pragma unroll
     for (int i = 0; i < G::kLoads; ++i) {
       const int idx = i * 64 + lane;
-      *reinterpret_cast<u32x4 *>(Ks + (idx / G::kPieces) * G::kStride +
-                                 (idx % G::kPieces) * 4) = kr[i];
+      const int pc = idx % G::kPieces;
+      *reinterpret_cast<u32x4 *>(Ks + (idx / G::kPieces) * G::kStride + pc * 4) = kr[i];
     }
 #pragma unroll
     for (int i = 0; i < G::vLoads; ++i) {
       const int idx = i * 64 + lane;
-      *reinterpret_cast<u32x4 *>(Vs + (idx / G::vPieces) * G::vStride +
-                                 (idx % G::vPieces) * 4) = vr[i];
+      const int pc = idx % G::vPieces;
+      *reinterpret_cast<u32x4 *>(Vs + (idx / G::vPieces) * G::vStride + pc * 4) = vr[i];
     }
     if (tile + NW < ntiles) issue(tile + NW);
     wave_lds_sync();
@@ -133,19 +147,18 @@ __global__ __launch_bounds__(NW * 64) void partition_f32_mfma_kernel(
     f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int blk = 0; blk < DK / 16; ++blk) {
-      const f32x4 a =
+      const f32x4 av =
           *reinterpret_cast<const f32x4 *>(Ks + hl * G::kStride + blk * 16 + kg * 4);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], qf[blk][j], sacc, 0, 0, 0);
+        sacc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[j], qf[blk][j], sacc, 0, 0, 0);
     }
 
-    const int tb = t0 + tile * kF32Tile;
     float x[4];
     float mt = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      x[i] = (tb + kg * 4 + i < t1) ? sacc[i] * scale_log2 : -INFINITY;
+      x[i] = (tb + kg * 4 + i < t1) ? sacc[i] * a.scale_log2 : -INFINITY;
       mt = fmaxf(mt, x[i]);
     }
     mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
@@ -179,50 +192,80 @@ __global__ __launch_bounds__(NW * 64) void partition_f32_mfma_kernel(
   float *wm = lds;
   float *wl = wm + NW * 16;
   float *wacc = wl + NW * 16;
-  if (lane < 16) {
-    wm[w * 16 + lane] = m_run;
-    wl[w * 16 + lane] = l_tot;
+  if (ntiles > 0) {
+    if (lane < 16) {
+      wm[w * 16 + lane] = m_run;
+      wl[w * 16 + lane] = l_tot;
+    }
+#pragma unroll
+    for (int blk = 0; blk < DV / 16; ++blk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        wacc[(w * 16 + hl) * DV + blk * 16 + kg * 4 + i] = o[blk][i];
   }
-#pragma unroll
-  for (int blk = 0; blk < DV / 16; ++blk)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      wacc[(w * 16 + hl) * DV + blk * 16 + kg * 4 + i] = o[blk][i];
   __syncthreads();
 
-  for (int e = threadIdx.x; e < hpk * DV; e += NW * 64) {
-    const int h = e / DV, d = e % DV;
-    float M = -INFINITY;
+  if (ntiles > 0) {
+    for (int e = threadIdx.x; e < hpk * DV; e += NW * 64) {
+      const int h = e / DV, d = e % DV;
+      float M = -INFINITY;
 #pragma unroll
-    for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, wm[ww * 16 + h]);
-    float acc = 0.0f, L = 0.0f;
+      for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, wm[ww * 16 + h]);
+      float acc = 0.0f, L = 0.0f;
 #pragma unroll
-    for (int ww = 0; ww < NW; ++ww) {
-      const float f = fast_exp2(wm[ww * 16 + h] - M);
-      acc += f * wacc[(ww * 16 + h) * DV + d];
-      L += f * wl[ww * 16 + h];
+      for (int ww = 0; ww < NW; ++ww) {
+        const float f = fast_exp2(wm[ww * 16 + h] - M);
+        acc += f * wacc[(ww * 16 + h) * DV + d];
+        L += f * wl[ww * 16 + h];
+      }
+      const size_t row = (size_t)b * Hq + (size_t)g * hpk + h;
+      float *pa = a.part_acc + (row * nchunk + c) * DV + d;
+      float *pm = a.part_m + row * nchunk + c;
+      float *pl = a.part_l + row * nchunk + c;
+      if (STEP && sp.fuse) {  // read back by this launch's last work-group
+        coherent_store(pa, acc);
+        if (d == 0) {
+          coherent_store(pm, M * kLn2);
+          coherent_store(pl, L);
+        }
+      } else {
+        *pa = acc;
+        if (d == 0) {
+          *pm = M * kLn2;
+          *pl = L;
+        }
+      }
     }
-    const size_t row = (size_t)b * Hq + (size_t)g * hpk + h;
-    part_acc[(row * nchunk + c) * DV + d] = acc;
-    if (d == 0) {
-      part_m[row * nchunk + c] = M * kLn2;
-      part_l[row * nchunk + c] = L;
+  }
+
+  if (STEP && sp.fuse) {
+    const int nc = (n + a.chunk_tokens - 1) / a.chunk_tokens;
+    const bool last = nc == 0 || arrive_last(sp.counters + (size_t)b * Hkv + g,
+                                             nc, &s_flag);
+    if (last) {
+      __syncthreads();
+      fold_group(a, sp, b, g, nc, lds);
     }
   }
 }
 
-template <int DK, int DV>
-hipError_t launch_mfma(const PartitionArgs &a, hipStream_t s) {
+template <int DK, int DV, bool STEP>
+hipError_t launch_mfma(const PartitionArgs &a, const StepParams &sp,
+                       hipStream_t s) {
   const int nwork = a.batch * a.num_kv_heads * a.num_chunks;
-  hipLaunchKernelGGL((partition_f32_mfma_kernel<DK, DV, kPartitionWaves>),
-                     dim3(nwork), dim3(kPartitionWaves * 64), 0, s,
-                     static_cast<const float *>(a.q),
-                     static_cast<const float *>(a.k),
-                     static_cast<const float *>(a.v), a.lens, a.batch,
-                     a.max_len, a.num_kv_heads, a.hpk, a.chunk_tokens,
-                     a.num_chunks, a.scale_log2, a.part_m, a.part_l,
-                     a.part_acc);
+  hipLaunchKernelGGL((partition_f32_mfma_kernel<DK, DV, kPartitionWaves, STEP>),
+                     dim3(nwork), dim3(kPartitionWaves * 64), 0, s, a, sp);
   return hipGetLastError();
+}
+
+template <bool STEP>
+hipError_t dispatch_mfma(const PartitionArgs &a, const StepParams &sp,
+                         hipStream_t s) {
+  if (a.dk == 64 && a.dv == 64) return launch_mfma<64, 64, STEP>(a, sp, s);
+  if (a.dk == 128 && a.dv == 128) return launch_mfma<128, 128, STEP>(a, sp, s);
+  if (a.dk == 192 && a.dv == 128) return launch_mfma<192, 128, STEP>(a, sp, s);
+  if (a.dk == 256 && a.dv == 256) return launch_mfma<256, 256, STEP>(a, sp, s);
+  return hipErrorInvalidValue;
 }
 
 bool mfma_shape(int dk, int dv) {
@@ -401,10 +444,7 @@ bool partition_f32_supported(int dk, int dv, int hpk) {
 bool partition_f32_uses_mfma(int dk, int dv) { return mfma_shape(dk, dv); }
 
 hipError_t launch_partition_f32(const PartitionArgs &a, hipStream_t s) {
-  if (a.dk == 64 && a.dv == 64) return launch_mfma<64, 64>(a, s);
-  if (a.dk == 128 && a.dv == 128) return launch_mfma<128, 128>(a, s);
-  if (a.dk == 192 && a.dv == 128) return launch_mfma<192, 128>(a, s);
-  if (a.dk == 256 && a.dv == 256) return launch_mfma<256, 256>(a, s);
+  if (mfma_shape(a.dk, a.dv)) return dispatch_mfma<false>(a, StepParams{}, s);
   const int nwork = a.batch * a.num_kv_heads * a.num_chunks;
   const size_t lds = partition_f32_lds_bytes(a.dk, a.dv, a.hpk);
   if (lds > 65536) {
@@ -421,6 +461,12 @@ hipError_t launch_partition_f32(const PartitionArgs &a, hipStream_t s) {
                      a.chunk_tokens, a.num_chunks, a.scale_log2, a.part_m,
                      a.part_l, a.part_acc);
   return hipGetLastError();
+}
+
+hipError_t launch_step_f32(const PartitionArgs &a, const StepParams &sp,
+                           hipStream_t s) {
+  if (!mfma_shape(a.dk, a.dv)) return hipErrorInvalidValue;
+  return dispatch_mfma<true>(a, sp, s);
 }
 
 }  // namespace gqa

@@ -1,0 +1,145 @@
+// Device helpers shared by the partition kernels when they run a whole decode
+// step in one launch: the append of the new token, the per-sequence length it
+// implies, the arrival count of a KV group's work-groups, and the fold of the
+// group's split-K partials that the last work-group to arrive performs.
+#pragma once
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace gqa {
+
+// s_waitcnt immediate (GFX9 encoding) waiting for vmcnt = 0 only: every
+// vector memory access of the wavefront, stores included, has completed.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+// Keys attended by sequence b, and the slot a decode step appends to.
+struct SeqLen {
+  int n;      // keys attended: [0, n)
+  int n_old;  // slot receiving the new token when `fresh`
+  bool fresh;
+};
+
+// needle-core decode order: push_kv, then attend over the cache including the
+// new token.  A full cache (or a negative length) is left as it is: the step
+// attends over what is there and the drop is counted.
+template <bool STEP>
+__device__ __forceinline__ SeqLen seq_len(const PartitionArgs &a,
+                                          const StepParams &sp, int b) {
+  SeqLen s;
+  if (STEP) {
+    s.n_old = sp.lens_in[b];
+    s.fresh = s.n_old >= 0 && s.n_old < a.max_len;
+    s.n = s.fresh ? s.n_old + 1 : clamp_len(s.n_old, a.max_len);
+  } else {
+    s.n_old = -1;
+    s.fresh = false;
+    s.n = clamp_len(a.lens[b], a.max_len);
+  }
+  return s;
+}
+
+// The new lengths and the drop count, written once per sequence (by its first
+// work-group).  lens_out never aliases lens_in, which every group still reads.
+__device__ __forceinline__ void step_bookkeeping(const StepParams &sp, int b,
+                                                 const SeqLen &s) {
+  sp.lens_out[b] = s.fresh ? s.n_old + 1 : s.n_old;
+  if (!s.fresh && sp.dropped) atomicAdd(sp.dropped, 1);
+}
+
+// Copies one KV group's rows of the new token (16-byte pieces) into the cache
+// slot, then waits until the stores are complete and the whole work-group has
+// passed a barrier, so that the group's own loads of the slot see them.
+__device__ __forceinline__ void append_group_row(const u32x4 *kn, u32x4 *kd,
+                                                 int kpieces, const u32x4 *vn,
+                                                 u32x4 *vd, int vpieces) {
+  for (int e = threadIdx.x; e < kpieces + vpieces; e += blockDim.x) {
+    if (e < kpieces)
+      kd[e] = kn[e];
+    else
+      vd[e - kpieces] = vn[e - kpieces];
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+}
+
+// Stores and loads of split-K partials that another work-group of the same
+// launch may read: device-coherent accesses (agent scope), which go to the
+// coherence point instead of one XCD's L2.  This avoids the L2-wide write-back
+// and invalidate that an agent-scope fence costs on a multi-XCD part.
+__device__ __forceinline__ void coherent_store(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float coherent_load(const float *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Counts this work-group's arrival once its partial is published; true in the
+// last of the `nc` work-groups of group (b, g), which then reads every partial
+// with coherent loads.  Each wavefront first waits for its own coherent
+// partial stores to complete (s_waitcnt vmcnt(0)), so every partial is at the
+// coherence point before the counter moves.  The counter returns to zero for
+// the next call.
+__device__ __forceinline__ bool arrive_last(int *counter, int nc, int *flag) {
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+    const int last = prev == nc - 1;
+    if (last)
+      __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = last;
+  }
+  __syncthreads();
+  return *flag != 0;
+}
+
+// Folds the nc partials of the hpk query rows of group (b, g) and carry_in by
+// log-sum-exp merge (usearch carry: partial-softmax rescaling), then writes
+// out = acc / l and carry_out.  `lds` holds 2 * hpk floats.
+__device__ __forceinline__ void fold_group(const PartitionArgs &a,
+                                           const StepParams &sp, int b, int g,
+                                           int nc, float *lds) {
+  const int Hq = a.num_kv_heads * a.hpk;
+  const size_t row0 = (size_t)b * Hq + (size_t)g * a.hpk;
+  float *in_m = lds, *in_l = lds + a.hpk;
+  for (int h = threadIdx.x; h < a.hpk; h += blockDim.x) {
+    const float l = sp.in_l ? sp.in_l[row0 + h] : 0.0f;
+    in_l[h] = l;
+    in_m[h] = l > 0.0f ? sp.in_m[row0 + h] * kLog2e : -INFINITY;
+  }
+  __syncthreads();  // carry_in m/l are read before carry_out may overwrite them
+  for (int e = threadIdx.x; e < a.hpk * a.dv; e += blockDim.x) {
+    const int h = e / a.dv, d = e % a.dv;
+    const size_t row = row0 + h;
+    const float *pm = a.part_m + row * a.num_chunks;
+    const float *pl = a.part_l + row * a.num_chunks;
+    const float *pa = a.part_acc + row * a.num_chunks * a.dv + d;
+    float m = in_m[h], L = 0.0f, acc = 0.0f;
+    if (in_l[h] > 0.0f) {
+      L = in_l[h];
+      acc = sp.in_acc[row * a.dv + d];
+    }
+#pragma unroll 4
+    for (int i = 0; i < nc; ++i) {
+      const float mi = coherent_load(pm + i) * kLog2e;
+      const float mn = fmaxf(m, mi);
+      const float fo = fast_exp2(m - mn), fi = fast_exp2(mi - mn);
+      acc = acc * fo + coherent_load(pa + (size_t)i * a.dv) * fi;
+      L = L * fo + coherent_load(pl + i) * fi;
+      m = mn;
+    }
+    const bool live = L > 0.0f;
+    if (sp.out) sp.out[row * a.dv + d] = live ? acc / L : 0.0f;
+    if (sp.out_acc) {
+      sp.out_acc[row * a.dv + d] = live ? acc : 0.0f;
+      if (d == 0) {
+        sp.out_m[row] = live ? m * kLn2 : -INFINITY;
+        sp.out_l[row] = live ? L : 0.0f;
+      }
+    }
+  }
+}
+
+}  // namespace gqa

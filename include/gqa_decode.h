@@ -200,6 +200,36 @@ GQA_API gqa_status gqa_attend_combine(int32_t num_q_heads, const gqa_cache *cach
                               hipStream_t stream);
 
 /*
+ * decode_step — kv_append then attend_decode, as one decode step (needle-core
+ * self_attn_incremental: push_kv, then attend over the cache including the new
+ * token), in one kernel launch for the matrix-core shapes.
+ *   For every sequence b with n = lens_in[b]: if 0 <= n < max_len the token's
+ *   K/V rows (k_new [batch][num_kv_heads][dk], v_new [...][dv]) are written to
+ *   slot n and the query attends over [0, n + 1); otherwise nothing is written,
+ *   *dropped (if not NULL) is incremented and the query attends over
+ *   [0, clamp(n, 0, max_len)).  lens_out[b] receives n + 1, or n when nothing
+ *   was written.
+ *   lens_out must NOT alias lens_in (every work-group reads lens_in during the
+ *   call); alternate two length arrays between steps.
+ *   q, scale, carry_in, carry_out, out: as in gqa_attend_decode.
+ *   workspace: at least gqa_decode_step_workspace_bytes() bytes, ZERO-FILLED
+ *   before its first use.  Its tail holds per-(sequence, KV group) arrival
+ *   counters that every completed call leaves at zero again; calls that
+ *   overlap on one workspace race.
+ */
+GQA_API size_t gqa_decode_step_workspace_bytes(const gqa_cache *cache,
+                                               int32_t num_q_heads);
+
+GQA_API gqa_status gqa_decode_step(const void *q, int32_t num_q_heads,
+                                   const gqa_cache *cache, const void *k_new,
+                                   const void *v_new, const int32_t *lens_in,
+                                   int32_t *lens_out, int32_t *dropped,
+                                   float scale, const gqa_carry *carry_in,
+                                   const gqa_carry *carry_out, float *out,
+                                   void *workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
+
+/*
  * softmax_state_merge — dst = merge(a, b) row by row (usearch carry,
  * "partial-softmax rescaling"): m = max(m_a, m_b), l = e^(m_a-m) l_a +
  * e^(m_b-m) l_b, acc = e^(m_a-m) acc_a + e^(m_b-m) acc_b; an empty row
