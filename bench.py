@@ -211,22 +211,22 @@ def main():
     torch.cuda.synchronize()
     ms_step = time_graph(g_step, K)
 
-    # the dominant kernel alone: an event pair around each of K eager launches
-    # on the stream they run on.  A bounded spin kernel holds the stream while
-    # the host enqueues them, so the pairs run back to back and none of them
-    # includes host launch latency.
-    pairs = [(torch.cuda.Event(enable_timing=True),
-              torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    # the dominant kernel alone: K eager launches queued back to back behind a
+    # bounded spin kernel (so host launch latency never shows), one HIP event
+    # pair on their stream around the whole batch; the average per launch
+    # includes the dispatch gap between consecutive launches.
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     bench_lib().gqa_bench_spin(
         min(1000000, 20000 + 200 * K),
         ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
-    for i, (e0, e1) in enumerate(pairs):
-        e0.record()
+    e0.record()
+    for i in range(K):
         partition_only(i % copies)
-        e1.record()
+    e1.record()
     torch.cuda.synchronize()
-    ms_part = statistics.mean(e0.elapsed_time(e1) for e0, e1 in pairs)
+    ms_part = e0.elapsed_time(e1) / K
 
     # eager reference timing of one step (diagnostic)
     torch.cuda.synchronize()

@@ -1,14 +1,14 @@
 // Log-sum-exp combine of split-K partials, and the carry merge.
 //
-// Both fold online-softmax states (usearch DenseAttendConfig.carry: one state
-// per query row folds a call into another over the same queries by
-// partial-softmax rescaling; DenseSoftmaxState: m is the largest logit seen,
-// l the sum of exponentials taken against it).  For states (m_i, l_i, acc_i)
+// Both fold online-softmax states (usearch DenseAttendConfig.carry: a state per
+// query row lets one call continue another over the same queries, rescaling
+// the partial softmaxes; DenseSoftmaxState: m is the maximum logit so far and
+// l the sum of exponentials relative to m).  For states (m_i, l_i, acc_i)
 // with M = max_i m_i:  l = sum_i e^(m_i - M) l_i,  acc = sum_i e^(m_i - M) acc_i.
 // A state with l == 0 is empty and contributes nothing.  The output row is
-// acc / l, already divided by the partition (usearch attend); a row with no
+// acc / l, i.e. normalised by the partition (usearch attend); a row with no
 // keys anywhere gets 0 and the carry (-inf, 0, 0) (the DSA reference's guard:
-// a softmax over nothing has weight 0, not NaN).
+// an empty softmax contributes zero weight instead of a NaN).
 #include "device_common.h"
 #include "launch.h"
 

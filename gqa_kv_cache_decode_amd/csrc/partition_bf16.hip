@@ -4,16 +4,16 @@
 // heads_per_kv query heads of the group.  Every K/V row of the chunk is read
 // from HBM once, with 16-byte coalesced nontemporal loads, staged in the
 // wavefront's own LDS slice, and shared by all heads of the group through the
-// MFMA N dimension (needle-core attn.rs module doc: each KV head serves its
-// query heads by broadcast, not repeat-copy; cortiq-engine NystromState: the
-// rows of a group are identical for all its heads, so they are held once per
-// group).
+// MFMA N dimension (needle-core attn.rs module doc: a KV head serves several
+// query heads directly, without copying its K/V per head; cortiq-engine
+// NystromState: the rows of a group are identical for all its heads, so they
+// are held once per group).
 //
 // Per 32-token tile a wavefront computes
 //   S^T[token][head] = K_tile[token][:] . q[head][:]         (MFMA, A = K)
 // then folds the tile into each head's running maximum m, partition l and
-// weighted value sum acc (usearch attend: every key folds into each head's
-// running maximum, partition and weighted value sum), in base-2 units:
+// weighted value sum acc (usearch attend: each scored key updates these three
+// per-head quantities), in base-2 units:
 //   m' = max(m, max_j s_j), alpha = 2^(m - m'), p_j = 2^(s_j - m'),
 //   l = alpha l + sum_j p_j,  acc = alpha acc + sum_j p_j V_j
 // with acc^T[dv][head] += V_tile^T[dv][token] . P^T[token][head] on MFMA.

@@ -96,7 +96,8 @@ __device__ __forceinline__ bool arrive_last(int *counter, int nc, int *flag) {
 }
 
 // Folds the nc partials of the hpk query rows of group (b, g) and carry_in by
-// log-sum-exp merge (usearch carry: partial-softmax rescaling), then writes
+// log-sum-exp merge (usearch carry: the partial softmaxes are rescaled to a
+// common maximum), then writes
 // out = acc / l and carry_out.  `lds` holds 2 * hpk floats.
 __device__ __forceinline__ void fold_group(const PartitionArgs &a,
                                            const StepParams &sp, int b, int g,

@@ -88,8 +88,9 @@ typedef struct gqa_cache {
 
 /*
  * Online-softmax carry, one row per query row r = b * num_q_heads + h
- * (usearch DenseSoftmaxState, "lent by you", extended with the accumulator):
- *   m   [rows]      largest scaled logit seen, natural-log units
+ * (usearch DenseSoftmaxState, owned by the caller, extended with the
+ * accumulator):
+ *   m   [rows]      maximum scaled logit so far, natural-log units
  *   l   [rows]      sum of exp(s - m) over the keys seen
  *   acc [rows][dv]  sum of exp(s - m) * v, NOT divided by l
  * A row with l == 0 is empty whatever its m (a zero-initialised carry is the
@@ -156,12 +157,13 @@ GQA_API size_t gqa_attend_workspace_bytes(const gqa_cache *cache, int32_t num_q_
  *   q     [batch][num_q_heads][dk], cache dtype.
  *   lens  [batch] device int32; keys attended are [0, clamp(lens[b], 0,
  *         max_len)).
- *   scale logit scale; 0 means 1/sqrt(dk) (usearch score_scale: zero derives
- *         it; conventionally the inverse square root of the head width).
+ *   scale logit scale; 0 means 1/sqrt(dk) (usearch score_scale: a zero value
+ *         asks for the derived scale, by convention one over the square root
+ *         of the head width).
  *         Must be finite.
  *   carry_in   NULL, or a carry over the same query rows folded into this
- *              branch (usearch carry: folds this branch into another over the
- *              same queries, such as a recent window).
+ *              branch (usearch carry: one call continues another over the
+ *              same queries, e.g. a recent-window branch).
  *   carry_out  NULL, or receives the merged carry; may alias carry_in.
  *   out   NULL, or [batch][num_q_heads][dv] fp32: the merged value mix already
  *         divided by the partition; rows with no keys at all get 0.
@@ -231,7 +233,8 @@ GQA_API gqa_status gqa_decode_step(const void *q, int32_t num_q_heads,
 
 /*
  * softmax_state_merge — dst = merge(a, b) row by row (usearch carry,
- * "partial-softmax rescaling"): m = max(m_a, m_b), l = e^(m_a-m) l_a +
+ * partial softmaxes rescaled to a common maximum): m = max(m_a, m_b),
+ * l = e^(m_a-m) l_a +
  * e^(m_b-m) l_b, acc = e^(m_a-m) acc_a + e^(m_b-m) acc_b; an empty row
  * (l == 0) is the identity.  dst may alias a or b.  out, if not NULL,
  * receives acc / l ([rows][dv] fp32, 0 for empty rows).

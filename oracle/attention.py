@@ -14,18 +14,19 @@ against it, their sum and the weighted value sum.  The passages followed:
   scored as ``dot(q_head, k_head) * scale`` with ``scale = head_dim^-0.5``;
   the scores are softmaxed and the value rows are summed with those weights.
   Decode needs no causal mask: the query attends to exactly the cached rows.
-* usearch "linear-algebra", section Attention: every key folds into each head's
-  running maximum, partition and weighted value sum; outputs are divided by the
-  partition; a per-query-row carry folds one branch into another over the same
-  queries.  Struct ``DenseSoftmaxState``: ``maximum_score`` is the largest logit
-  seen (the recurrence's m), ``partition`` the sum of exponentials taken against
-  it (the recurrence's l).  ``score_scale`` of zero means "derive it"; the
-  derived value is the inverse square root of the head width.
+* usearch "linear-algebra", section Attention: each scored key updates the
+  head's running maximum, partition and weighted sum of values; the outputs are
+  normalised by the partition; a carry per query row lets one branch continue
+  another over the same queries.  Struct ``DenseSoftmaxState``:
+  ``maximum_score`` holds the maximum logit so far (m), ``partition`` the sum
+  of exponentials relative to it (l).  A ``score_scale`` of zero asks for the
+  derived scale, whose conventional value is one over the square root of the
+  head width.
 * cortiq-engine ``NystromState``, example ``o1_recovery.rs`` ``trial()``: the
   exact reference takes the maximum logit first and then the exponentials
   ``exp(l - mx)`` in double precision.
-* metrale DSA reference, ``pool_states``: a softmax over an empty set gives
-  weight 0 (a zero result), not NaN.
+* metrale DSA reference, ``pool_states``: a softmax over an empty set
+  contributes zero weight (a zero result) rather than a NaN.
 
 Readings taken where the pages are silent (each listed in the design notes):
 the carry is ``(m, l, acc)`` with ``acc`` the *unnormalised* weighted value sum
@@ -52,7 +53,8 @@ class Carry(NamedTuple):
 
 
 def resolve_scale(scale: float, dk: int) -> float:
-    """usearch DenseAttendConfig.score_scale: zero derives 1/sqrt(head width).
+    """usearch DenseAttendConfig.score_scale: a zero scale is replaced by
+    1/sqrt(head width).
 
     The head width used is the key width dk (it is the width of the dot
     product being scaled)."""
@@ -96,7 +98,8 @@ def softmax_state(s: np.ndarray, vg: np.ndarray) -> Carry:
 def merge(a: Carry, b: Carry) -> Carry:
     """Fold two online-softmax states over the same query rows.
 
-    usearch DenseAttendConfig.carry ("partial-softmax rescaling"): with
+    usearch DenseAttendConfig.carry (partial softmaxes rescaled to a common
+    maximum): with
     m = max(m_a, m_b), alpha = exp(m_a - m), beta = exp(m_b - m):
     l = alpha l_a + beta l_b and acc = alpha acc_a + beta acc_b.
     An empty state (l == 0) is the identity."""
@@ -123,7 +126,7 @@ def merge(a: Carry, b: Carry) -> Carry:
 
 
 def finalize(c: Carry) -> np.ndarray:
-    """Output rows already divided by the partition; 0 for an empty state."""
+    """Output rows normalised by the partition; 0 for an empty state."""
     out = np.zeros_like(c.acc)
     live = c.l > 0.0
     out[live] = c.acc[live] / c.l[live][:, None]

@@ -159,7 +159,8 @@ def pin_recovery_trial(orc):
 
 def pin_gqa_is_repeated_mha(orc):
     """GQA broadcasts each KV head to its group (needle-core module doc:
-    broadcast, not repeat-copy).  It must equal plain multi-head attention on
+    each KV head serves its query heads without per-head copies).  It must
+    equal plain multi-head attention on
     K/V repeat-copied per query head, which torch's fp64 CPU
     scaled_dot_product_attention computes independently.  scale = 0 must give
     torch's default 1/sqrt(key width) (dk != dv here)."""
@@ -229,7 +230,8 @@ def pin_brute_force(orc):
 
 def pin_split_merge(orc):
     """Folding the carries of any split of the keys equals one pass over all
-    of them (usearch carry: partial-softmax rescaling).  Checked for every
+    of them (usearch carry: partial softmaxes rescaled to a common maximum).
+    Checked for every
     split point, through merge() and through carry_in, and for every order of
     a three-way merge; the empty state is the identity."""
     B, Hq, Hkv, dk, dv, T = 2, 4, 2, 8, 6, 23
