@@ -94,6 +94,10 @@ gqa_status make_plan(const gqa_cache *c, int32_t hq, int32_t chunk_tokens,
   if (chunk_tokens < 0 || chunk_tokens % kChunkQuantum != 0)
     return GQA_ERR_INVALID_ARGUMENT;
   const int32_t chunk = chunk_tokens ? chunk_tokens : auto_chunk(c);
+  // a chunk's rows of one KV group are addressed with 32-bit byte offsets
+  const int64_t span = (int64_t)chunk * c->num_kv_heads *
+                       (c->dk > c->dv ? c->dk : c->dv) * esize(c->dtype);
+  if (span >= ((int64_t)1 << 31)) return GQA_ERR_UNSUPPORTED;
   const int64_t nchunk = ((int64_t)c->max_len + chunk - 1) / chunk;
   const int64_t groups = (int64_t)c->batch * c->num_kv_heads * nchunk;
   const int64_t rows = (int64_t)c->batch * hq;

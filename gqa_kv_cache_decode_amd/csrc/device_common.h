@@ -23,6 +23,20 @@ __device__ __forceinline__ u32x4 stream_load16(const void *p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
 }
 
+// Raw buffer view of `bytes` bytes at `base` (the gfx9 descriptor word for
+// untyped 32-bit data).  Loads past `bytes` return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_view(const void *base,
+                                                              uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, bytes,
+                                           0x00020000);
+}
+
+// 16-byte nontemporal load at byte offset `off` of a buffer view.
+__device__ __forceinline__ u32x4 stream_load16(__amdgpu_buffer_rsrc_t v,
+                                               uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(v, off, 0, /*nt*/ 2);
+}
+
 __device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }

@@ -89,21 +89,17 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
   const int kg = lane >> 4;  // lane group: k-slice of MFMA operands
   const int Hq = Hkv * hpk;
 
-  // q as the B operand of S^T = K q^T: lane holds head hl, dims s*32+kg*8..+8
+  // q as the B operand of S^T = K q^T: lane holds head hl, dims s*32+kg*8..+8.
+  // Padding columns (hl >= hpk) repeat the group's last head; they are never
+  // written, and loading them unconditionally keeps the load off the critical
+  // path (no partial-lane write to wait for).
   bf16x8 qf[DK / 32];
   {
-    const bool live = hl < hpk;
     const uint16_t *qrow = static_cast<const uint16_t *>(a.q) +
-                           ((size_t)b * Hq + (size_t)g * hpk + hl) * DK;
+                           ((size_t)b * Hq + (size_t)g * hpk + min(hl, hpk - 1)) * DK;
 #pragma unroll
-    for (int s = 0; s < DK / 32; ++s) {
-      if (live) {
-        qf[s] = *reinterpret_cast<const bf16x8 *>(qrow + s * 32 + kg * 8);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) qf[s][j] = (__bf16)0.0f;
-      }
-    }
+    for (int s = 0; s < DK / 32; ++s)
+      qf[s] = *reinterpret_cast<const bf16x8 *>(qrow + s * 32 + kg * 8);
   }
 
   uint16_t *Ks = reinterpret_cast<uint16_t *>(lds) + w * G::waveLdsElems;
@@ -127,23 +123,28 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
   }
 
   // K/V are read exactly once per call, so the loads are nontemporal: they
-  // stream through without displacing cached lines.
+  // stream through without displacing cached lines.  Tokens of a tile past
+  // the chunk's last live token load that last token again (a finite row
+  // whose logit is masked, so its weight is exactly 0): no branches, and no
+  // slot at or past the length is ever read.
+  const int last = max(t1 - t0 - 1, 0);  // last live token, relative to t0
+  const __amdgpu_buffer_rsrc_t kview = buffer_view(
+      Kg + (size_t)t0 * kTok, (uint32_t)(((size_t)last * kTok + DK) * 2));
+  const __amdgpu_buffer_rsrc_t vview = buffer_view(
+      Vg + (size_t)t0 * vTok, (uint32_t)(((size_t)last * vTok + DV) * 2));
   u32x4 kr[G::kLoads], vr[G::vLoads];
   auto issue = [&](int tile) {
-    const int tb = t0 + tile * kTileTokens;
 #pragma unroll
     for (int i = 0; i < G::kLoads; ++i) {
       const int idx = i * 64 + lane;
-      const int t = tb + idx / G::kPieces;
-      const int pc = idx % G::kPieces;
-      kr[i] = (t < t1) ? stream_load16(Kg + t * kTok + pc * 8) : u32x4{0, 0, 0, 0};
+      const int t = min(tile * kTileTokens + idx / G::kPieces, last);
+      kr[i] = stream_load16(kview, (uint32_t)((t * kTok + (idx % G::kPieces) * 8) * 2));
     }
 #pragma unroll
     for (int i = 0; i < G::vLoads; ++i) {
       const int idx = i * 64 + lane;
-      const int t = tb + idx / G::vPieces;
-      const int pc = idx % G::vPieces;
-      vr[i] = (t < t1) ? stream_load16(Vg + t * vTok + pc * 8) : u32x4{0, 0, 0, 0};
+      const int t = min(tile * kTileTokens + idx / G::vPieces, last);
+      vr[i] = stream_load16(vview, (uint32_t)((t * vTok + (idx % G::vPieces) * 8) * 2));
     }
   };
 

@@ -71,14 +71,14 @@ __global__ __launch_bounds__(NW * 64) void partition_f32_mfma_kernel(
 
   // q as the B operand: for dim block blk and step j the lane holds
   // q[head hl][blk*16 + kg*4 + j]; K's A operand uses the same dims.
+  // Padding columns (hl >= hpk) repeat the group's last head (never written).
   f32x4 qf[DK / 16];
   {
     const float *qrow = static_cast<const float *>(a.q) +
-                        ((size_t)b * Hq + (size_t)g * hpk + hl) * DK;
+                        ((size_t)b * Hq + (size_t)g * hpk + min(hl, hpk - 1)) * DK;
 #pragma unroll
     for (int blk = 0; blk < DK / 16; ++blk)
-      qf[blk] = hl < hpk ? *reinterpret_cast<const f32x4 *>(qrow + blk * 16 + kg * 4)
-                         : f32x4{0.f, 0.f, 0.f, 0.f};
+      qf[blk] = *reinterpret_cast<const f32x4 *>(qrow + blk * 16 + kg * 4);
   }
 
   float *Ks = lds + w * G::waveLdsFloats;
@@ -99,22 +99,26 @@ __global__ __launch_bounds__(NW * 64) void partition_f32_mfma_kernel(
                      reinterpret_cast<u32x4 *>(Vg + sl.n_old * vTok), DV / 4);
   }
 
+  // Tokens past the chunk's last live token load that token again (finite,
+  // masked to weight 0): no branches, and padding slots are never read.
+  const int last = max(t1 - t0 - 1, 0);
+  const __amdgpu_buffer_rsrc_t kview = buffer_view(
+      Kg + (size_t)t0 * kTok, (uint32_t)(((size_t)last * kTok + DK) * 4));
+  const __amdgpu_buffer_rsrc_t vview = buffer_view(
+      Vg + (size_t)t0 * vTok, (uint32_t)(((size_t)last * vTok + DV) * 4));
   u32x4 kr[G::kLoads], vr[G::vLoads];
   auto issue = [&](int tile) {
-    const int tb = t0 + tile * kF32Tile;
 #pragma unroll
     for (int i = 0; i < G::kLoads; ++i) {
       const int idx = i * 64 + lane;
-      const int t = tb + idx / G::kPieces;
-      const int pc = idx % G::kPieces;
-      kr[i] = (t < t1) ? stream_load16(Kg + t * kTok + pc * 4) : u32x4{0, 0, 0, 0};
+      const int t = min(tile * kF32Tile + idx / G::kPieces, last);
+      kr[i] = stream_load16(kview, (uint32_t)((t * kTok + (idx % G::kPieces) * 4) * 4));
     }
 #pragma unroll
     for (int i = 0; i < G::vLoads; ++i) {
       const int idx = i * 64 + lane;
-      const int t = tb + idx / G::vPieces;
-      const int pc = idx % G::vPieces;
-      vr[i] = (t < t1) ? stream_load16(Vg + t * vTok + pc * 4) : u32x4{0, 0, 0, 0};
+      const int t = min(tile * kF32Tile + idx / G::vPieces, last);
+      vr[i] = stream_load16(vview, (uint32_t)((t * vTok + (idx % G::vPieces) * 4) * 4));
     }
   };
 

@@ -85,6 +85,7 @@ def test_plan_layout(lib):
     (dict(dtype=0, dk=256, dv=256), 32, 0, OK),
     (dict(dtype=0, dk=96, dv=32), 32, 0, OK),
     (dict(dk=192, dv=128, H=4), 64, 0, OK),
+    (dict(H=64, dk=256, dv=256, T=1 << 20), 64, 1 << 16, UNSUPPORTED),  # span
 ])
 def test_plan_validation(lib, kw, hq, chunk, want):
     st, _ = _plan(lib, _cache(**kw), hq, chunk)
