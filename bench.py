@@ -38,8 +38,10 @@ ROTATE_TARGET_BYTES = 1 << 30
 CSRC = ROOT / "gqa_kv_cache_decode_amd" / "csrc"
 # Sources of the dominant (partition) kernel: recorded counter readings are
 # only reported while these are unchanged.
-PARTITION_SOURCES = {"bf16": ["partition_bf16.hip", "device_common.h", "launch.h"],
-                     "f32": ["partition_f32.hip", "device_common.h", "launch.h"]}
+PARTITION_SOURCES = {"bf16": ["partition_bf16.hip", "device_common.h", "launch.h",
+                              "step_common.h"],
+                     "f32": ["partition_f32.hip", "device_common.h", "launch.h",
+                             "step_common.h"]}
 COPY_BYTES = 256 << 20      # calibration copy for the byte counters
 
 
@@ -259,8 +261,10 @@ def main():
         log(f"[bench] pure-read stream ceiling: {ceiling:.1f} GB/s")
 
     traffic = measured_traffic(args.workload, w.dtype)
-    kernel = (f"partition_bf16_kernel<{w.dk}, {w.dv}, 2>" if w.dtype == "bf16"
-              else f"partition_f32_mfma_kernel<{w.dk}, {w.dv}, 2>")
+    waves = (4 if w.dk + w.dv <= 256 else 2) if w.dtype == "bf16" else 2
+    kernel = (f"partition_bf16_kernel<{w.dk}, {w.dv}, {waves}, false>"
+              if w.dtype == "bf16" else
+              f"partition_f32_mfma_kernel<{w.dk}, {w.dv}, {waves}, false>")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),

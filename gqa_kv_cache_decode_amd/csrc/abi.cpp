@@ -25,10 +25,13 @@ constexpr int kMaxCombineDv = 256;
 // Larger launches, or partial sets above kFuseBytes per group, use the combine
 // kernel, which spreads the fold over one work-group per query row.
 constexpr size_t kFuseBytes = 64 * 1024;
-constexpr int64_t kFuseMaxGroups = 256;
-// Wavefronts a partition launch should hold: about four per compute unit of an
-// MI355X (256 CUs), each streaming a long run of tiles.
-constexpr int64_t kTargetWaves = 1024;
+constexpr int64_t kFuseMaxGroups = 64;
+// Split-K chunking (measured on MI355X over the workload shapes): every CU
+// gets at least one work-group, and a wavefront streams at most this many
+// tokens of a chunk, in long uninterrupted runs.
+constexpr int64_t kMinGroups = 256;
+constexpr int64_t kMaxTokensPerWave = 2048;
+constexpr int32_t kMaxChunk = 4096;  // longer chunks unbalance ragged batches
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -70,18 +73,33 @@ gqa_status check_carry(const gqa_carry *x) {
   return (x->m && x->l && x->acc) ? GQA_OK : GQA_ERR_INVALID_ARGUMENT;
 }
 
-// Chunk length: the power of two that spreads the cache over kTargetWaves
-// wavefronts, clamped to [min_chunk, 4096] (longer chunks leave ragged
-// batches unbalanced) and to what the cache needs.
+bool uses_mfma(const gqa_cache *c) {
+  return c->dtype == GQA_DTYPE_BF16 || gqa::partition_f32_uses_mfma(c->dk, c->dv);
+}
+
+// Wavefronts per partition work-group (bf16 kernel): four where a
+// wavefront's K/V tile is at most 32 x 256 bf16 values (dk + dv <= 256), two
+// for the wider heads, whose LDS tiles and registers would otherwise leave a
+// compute unit a single work-group.
+int partition_waves(const gqa_cache *c) {
+  if (c->dtype != GQA_DTYPE_BF16) return gqa::kPartitionWaves;
+  return gqa::partition_waves(c->dk, c->dv);
+}
+
+// Chunk length: the largest power of two up to kMaxChunk that still gives
+// every CU a work-group (short caches go down to kChunkQuantum tokens, so a
+// small branch spreads over more work-groups), with at most kMaxTokensPerWave
+// tokens per wavefront, and no longer than the cache needs.  A batch with
+// enough (sequence, KV group) units and short caches gets a single chunk: its
+// partition launch then writes the final results itself.
 int32_t auto_chunk(const gqa_cache *c) {
   const int64_t units = (int64_t)c->batch * c->num_kv_heads;
-  const bool bf16 = c->dtype == GQA_DTYPE_BF16;
-  const bool mfma = bf16 || gqa::partition_f32_uses_mfma(c->dk, c->dv);
-  const int64_t waves_per_group = mfma ? gqa::kPartitionWaves : 1;
-  const int32_t min_chunk = bf16 ? 256 : kChunkQuantum;
-  const int64_t want = units * c->max_len * waves_per_group / kTargetWaves;
-  int32_t chunk = min_chunk;
-  while (chunk < 4096 && chunk < want) chunk *= 2;
+  const int64_t waves = uses_mfma(c) ? partition_waves(c) : 1;
+  int32_t chunk = kMaxChunk;
+  while (chunk > kChunkQuantum &&
+         (chunk / waves > kMaxTokensPerWave ||
+          units * ((c->max_len + chunk - 1) / chunk) < kMinGroups))
+    chunk /= 2;
   while (chunk > kChunkQuantum && chunk / 2 >= c->max_len) chunk /= 2;
   return chunk;
 }
@@ -134,9 +152,27 @@ gqa_status device_status(hipError_t e) {
   return e == hipSuccess ? GQA_OK : GQA_ERR_DEVICE;
 }
 
+// The epilogue of a partition launch that writes final results: carry_in,
+// carry_out and out, with `direct` set when the plan has a single chunk.
+gqa::StepParams final_epilogue(const gqa_cache *c, const gqa_plan &plan,
+                               const gqa_carry *cin, const gqa_carry *cout,
+                               float *out) {
+  gqa::StepParams ep{};
+  ep.in_m = cin ? cin->m : nullptr;
+  ep.in_l = cin ? cin->l : nullptr;
+  ep.in_acc = cin ? cin->acc : nullptr;
+  ep.out_m = cout ? cout->m : nullptr;
+  ep.out_l = cout ? cout->l : nullptr;
+  ep.out_acc = cout ? cout->acc : nullptr;
+  ep.out = out;
+  ep.direct = plan.num_chunks == 1 && uses_mfma(c) ? 1 : 0;
+  return ep;
+}
+
 gqa_status partition_checked(const void *q, int32_t hq, const gqa_cache *c,
                              const int32_t *lens, float scale,
-                             const gqa_plan *plan, void *ws, hipStream_t s) {
+                             const gqa_plan *plan, void *ws,
+                             const gqa::StepParams &ep, hipStream_t s) {
   const int hpk = hq / c->num_kv_heads;
   const double sc = scale != 0.0f ? (double)scale : 1.0 / std::sqrt((double)c->dk);
   PartitionArgs a;
@@ -158,8 +194,8 @@ gqa_status partition_checked(const void *q, int32_t hq, const gqa_cache *c,
   a.part_l = reinterpret_cast<float *>(base + plan->off_l);
   a.part_acc = reinterpret_cast<float *>(base + plan->off_acc);
   return device_status(c->dtype == GQA_DTYPE_BF16
-                           ? gqa::launch_partition_bf16(a, s)
-                           : gqa::launch_partition_f32(a, s));
+                           ? gqa::launch_partition_bf16(a, ep, s)
+                           : gqa::launch_partition_f32(a, ep, s));
 }
 
 gqa_status combine_checked(int32_t hq, const gqa_cache *c, const int32_t *lens,
@@ -292,7 +328,7 @@ gqa_status gqa_attend_partition(const void *q, int32_t num_q_heads,
       GQA_OK)
     return st;
   return partition_checked(q, num_q_heads, cache, lens, scale, plan, workspace,
-                           stream);
+                           gqa::StepParams{}, stream);
 }
 
 gqa_status gqa_attend_combine(int32_t num_q_heads, const gqa_cache *cache,
@@ -327,9 +363,11 @@ gqa_status gqa_attend_decode(const void *q, int32_t num_q_heads,
   if ((st = check_plan(cache, num_q_heads, &plan, workspace_bytes, workspace)) !=
       GQA_OK)
     return st;
+  const gqa::StepParams ep =
+      final_epilogue(cache, plan, carry_in, carry_out, out);
   st = partition_checked(q, num_q_heads, cache, lens, scale, &plan, workspace,
-                         stream);
-  if (st != GQA_OK) return st;
+                         ep, stream);
+  if (st != GQA_OK || ep.direct) return st;
   return combine_checked(num_q_heads, cache, lens, &plan, workspace, carry_in,
                          carry_out, out, stream);
 }
@@ -389,13 +427,11 @@ gqa_status gqa_decode_step(const void *q, int32_t num_q_heads,
   if (workspace_bytes < plan.workspace_bytes + step_counter_bytes(cache))
     return GQA_ERR_WORKSPACE_TOO_SMALL;
 
-  const bool mfma = cache->dtype == GQA_DTYPE_BF16 ||
-                    gqa::partition_f32_uses_mfma(cache->dk, cache->dv);
-  if (!mfma) {  // vector-ALU shapes: the same step as three launches
+  if (!uses_mfma(cache)) {  // vector-ALU shapes: the same step as three launches
     st = gqa_kv_append(cache, k_new, v_new, lens_in, lens_out, dropped, stream);
     if (st != GQA_OK) return st;
     st = partition_checked(q, num_q_heads, cache, lens_out, scale, &plan,
-                           workspace, stream);
+                           workspace, gqa::StepParams{}, stream);
     if (st != GQA_OK) return st;
     return combine_checked(num_q_heads, cache, lens_out, &plan, workspace,
                            carry_in, carry_out, out, stream);
@@ -422,25 +458,18 @@ gqa_status gqa_decode_step(const void *q, int32_t num_q_heads,
   a.part_l = reinterpret_cast<float *>(base + plan.off_l);
   a.part_acc = reinterpret_cast<float *>(base + plan.off_acc);
 
-  gqa::StepParams sp;
+  gqa::StepParams sp = final_epilogue(cache, plan, carry_in, carry_out, out);
   sp.k_new = k_new;
   sp.v_new = v_new;
   sp.lens_in = lens_in;
   sp.lens_out = lens_out;
   sp.dropped = dropped;
   sp.counters = reinterpret_cast<int *>(base + plan.workspace_bytes);
-  sp.in_m = carry_in ? carry_in->m : nullptr;
-  sp.in_l = carry_in ? carry_in->l : nullptr;
-  sp.in_acc = carry_in ? carry_in->acc : nullptr;
-  sp.out_m = carry_out ? carry_out->m : nullptr;
-  sp.out_l = carry_out ? carry_out->l : nullptr;
-  sp.out_acc = carry_out ? carry_out->acc : nullptr;
-  sp.out = out;
-  sp.fuse = step_fuses(cache, num_q_heads, plan) ? 1 : 0;
+  sp.fuse = !sp.direct && step_fuses(cache, num_q_heads, plan) ? 1 : 0;
   st = device_status(cache->dtype == GQA_DTYPE_BF16
                          ? gqa::launch_step_bf16(a, sp, stream)
                          : gqa::launch_step_f32(a, sp, stream));
-  if (st != GQA_OK || sp.fuse) return st;
+  if (st != GQA_OK || sp.fuse || sp.direct) return st;
   return combine_checked(num_q_heads, cache, lens_out, &plan, workspace,
                          carry_in, carry_out, out, stream);
 }

@@ -7,8 +7,14 @@
 
 namespace gqa {
 
-// Wavefronts per work-group of the bf16 partition kernel.
+// Wavefronts per work-group of the fp32 matrix-core partition kernel.
 constexpr int kPartitionWaves = 2;
+
+// Work-group width of the bf16 partition kernel, measured on MI355X over the
+// workload shapes: four wavefronts where a 32-token K/V tile is small
+// (dk + dv <= 256), two for wider heads (their LDS tiles and registers would
+// leave one four-wavefront work-group per compute unit).
+constexpr int partition_waves(int dk, int dv) { return dk + dv <= 256 ? 4 : 2; }
 
 struct PartitionArgs {
   const void *q;        // [B][Hkv*hpk][dk]
@@ -23,7 +29,11 @@ struct PartitionArgs {
   float *part_acc;      // [rows][num_chunks][dv]
 };
 
-// Extra inputs when a partition launch runs a whole decode step.
+// Extra inputs of a partition launch that runs a whole decode step (k_new ..
+// counters), or that writes final results itself (the carry and out fields):
+// with `direct` (a single chunk per sequence) each work-group folds carry_in
+// into its group's state and writes out/carry_out; with `fuse` (decode step
+// only) the last work-group of a group to finish folds the group's partials.
 struct StepParams {
   const void *k_new;        // [B][Hkv][dk]
   const void *v_new;        // [B][Hkv][dv]
@@ -35,6 +45,7 @@ struct StepParams {
   float *out_m, *out_l, *out_acc;     // carry_out, all NULL if absent
   float *out;               // [rows][dv] or NULL
   int fuse;                 // the last work-group of a group folds partials
+  int direct;               // num_chunks == 1: write final results directly
 };
 
 struct CombineArgs {
@@ -70,8 +81,12 @@ bool partition_f32_supported(int dk, int dv, int hpk);
 bool partition_f32_uses_mfma(int dk, int dv);
 size_t partition_f32_lds_bytes(int dk, int dv, int hpk);
 
-hipError_t launch_partition_bf16(const PartitionArgs &a, hipStream_t s);
-hipError_t launch_partition_f32(const PartitionArgs &a, hipStream_t s);
+// `ep` carries the final-result epilogue (ep.direct) or is zero (partials
+// only); the fp32 vector-ALU family always writes partials.
+hipError_t launch_partition_bf16(const PartitionArgs &a, const StepParams &ep,
+                                 hipStream_t s);
+hipError_t launch_partition_f32(const PartitionArgs &a, const StepParams &ep,
+                                hipStream_t s);
 // One launch for append + partition (+ fold, when sp.fuse); matrix-core
 // shapes only.  `a.lens` is unused (lengths come from sp.lens_in).
 hipError_t launch_step_bf16(const PartitionArgs &a, const StepParams &sp,

@@ -29,9 +29,11 @@
 //
 // In STEP mode the same launch is a whole decode step (needle-core
 // self_attn_incremental: push_kv, then attend over the cache including the new
-// token): the wavefront whose tile holds the new slot takes that token's K/V
-// from k_new/v_new, stores them into the cache, and the group's partials are
-// folded by the last work-group to finish when `fuse` is set.
+// token).  The work-group whose chunk holds the new slot stores the token's
+// rows into the cache without waiting for the stores, and the one tile that
+// holds the slot reads those rows from k_new/v_new instead of the cache, so
+// the append never stalls the stream.  The group's partials are folded by the
+// last work-group to finish when `fuse` is set.
 #include "device_common.h"
 #include "launch.h"
 #include "step_common.h"
@@ -65,6 +67,7 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
       kTileBytes > kMergeFloats * 4 ? kTileBytes : kMergeFloats * 4;
   __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
   __shared__ int s_flag;
+  __shared__ float s_in[32];  // carry_in m, l of the group's rows (direct)
 
   const int Hkv = a.num_kv_heads, hpk = a.hpk, nchunk = a.num_chunks;
   const int item = xcd_local_item(blockIdx.x, a.batch * Hkv * nchunk);
@@ -78,8 +81,9 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
   if (STEP && g == 0 && c == 0 && threadIdx.x == 0) step_bookkeeping(sp, b, sl);
   const int t0 = c * a.chunk_tokens;
   // A work-group with nothing live exits, except the first of an empty
-  // sequence in a fused step: it still writes the group's outputs.
-  if (t0 >= n && !(STEP && sp.fuse && c == 0)) return;
+  // sequence when final results are written in this launch: it still writes
+  // the group's outputs.
+  if (t0 >= n && !(c == 0 && (sp.direct || (STEP && sp.fuse)))) return;
   const int t1 = min(t0 + a.chunk_tokens, n);
   const int ntiles = t1 > t0 ? (t1 - t0 + kTileTokens - 1) / kTileTokens : 0;
 
@@ -112,15 +116,22 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
   uint16_t *Vg = static_cast<uint16_t *>(const_cast<void *>(a.v)) +
                  ((size_t)b * a.max_len * Hkv + g) * DV;
 
-  // STEP: the work-group whose chunk holds the new slot writes the token's
-  // rows of this group into the cache before any of its tiles is loaded; its
-  // tile loop then reads the slot like any other.
+  // STEP: the work-group whose chunk holds the new slot stores the token's
+  // rows of this group into the cache.  The stores are not waited for: later
+  // calls read the slot, while this call reads the rows from k_new/v_new (the
+  // slot is the last live token of the chunk, relative position `rel`).
+  const uint16_t *knew = nullptr, *vnew = nullptr;
+  int rel = -1;
   if (STEP && sl.fresh && sl.n_old / a.chunk_tokens == c) {
-    append_group_row(static_cast<const u32x4 *>(sp.k_new) + ((size_t)b * Hkv + g) * (DK / 8),
-                     reinterpret_cast<u32x4 *>(Kg + sl.n_old * kTok), DK / 8,
-                     static_cast<const u32x4 *>(sp.v_new) + ((size_t)b * Hkv + g) * (DV / 8),
-                     reinterpret_cast<u32x4 *>(Vg + sl.n_old * vTok), DV / 8);
+    rel = sl.n_old - t0;
+    knew = static_cast<const uint16_t *>(sp.k_new) + ((size_t)b * Hkv + g) * DK;
+    vnew = static_cast<const uint16_t *>(sp.v_new) + ((size_t)b * Hkv + g) * DV;
+    store_group_row(reinterpret_cast<const u32x4 *>(knew),
+                    reinterpret_cast<u32x4 *>(Kg + (size_t)sl.n_old * kTok), DK / 8,
+                    reinterpret_cast<const u32x4 *>(vnew),
+                    reinterpret_cast<u32x4 *>(Vg + (size_t)sl.n_old * vTok), DV / 8);
   }
+  const int rel_tile = rel >= 0 ? rel / kTileTokens : -1;
 
   // K/V are read exactly once per call, so the loads are nontemporal: they
   // stream through without displacing cached lines.  Tokens of a tile past
@@ -134,6 +145,26 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
       Vg + (size_t)t0 * vTok, (uint32_t)(((size_t)last * vTok + DV) * 2));
   u32x4 kr[G::kLoads], vr[G::vLoads];
   auto issue = [&](int tile) {
+    if (STEP && tile == rel_tile) {
+      // the tile holding the new slot: that token (and the clamped tokens
+      // after it) come from k_new/v_new, the others from the cache
+      const uint16_t *kb = Kg + (size_t)t0 * kTok, *vb = Vg + (size_t)t0 * vTok;
+#pragma unroll
+      for (int i = 0; i < G::kLoads; ++i) {
+        const int idx = i * 64 + lane;
+        const int t = min(tile * kTileTokens + idx / G::kPieces, last);
+        const int pc = (idx % G::kPieces) * 8;
+        kr[i] = stream_load16(t == rel ? knew + pc : kb + (size_t)t * kTok + pc);
+      }
+#pragma unroll
+      for (int i = 0; i < G::vLoads; ++i) {
+        const int idx = i * 64 + lane;
+        const int t = min(tile * kTileTokens + idx / G::vPieces, last);
+        const int pc = (idx % G::vPieces) * 8;
+        vr[i] = stream_load16(t == rel ? vnew + pc : vb + (size_t)t * vTok + pc);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < G::kLoads; ++i) {
       const int idx = i * 64 + lane;
@@ -255,23 +286,32 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
       for (int i = 0; i < 4; ++i)
         wacc[(w * 16 + hl) * DV + blk * 16 + kg * 4 + i] = o[blk][i];
   }
+  if (sp.direct) stage_carry_in(sp, (size_t)b * Hq + (size_t)g * hpk, hpk, s_in);
   __syncthreads();
 
-  if (ntiles > 0) {
+  if (ntiles > 0 || sp.direct) {
     for (int e = threadIdx.x; e < hpk * DV; e += NW * 64) {
       const int h = e / DV;
       const int d = e % DV;
-      float M = -INFINITY;
+      float M = -INFINITY, acc = 0.0f, L = 0.0f;
+      if (ntiles > 0) {
 #pragma unroll
-      for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, wm[ww * 16 + h]);
-      float acc = 0.0f, L = 0.0f;
+        for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, wm[ww * 16 + h]);
 #pragma unroll
-      for (int ww = 0; ww < NW; ++ww) {
-        const float f = fast_exp2(wm[ww * 16 + h] - M);
-        acc += f * wacc[(ww * 16 + h) * DV + d];
-        L += f * wl[ww * 16 + h];
+        for (int ww = 0; ww < NW; ++ww) {
+          const float f = fast_exp2(wm[ww * 16 + h] - M);
+          acc += f * wacc[(ww * 16 + h) * DV + d];
+          L += f * wl[ww * 16 + h];
+        }
       }
       const size_t row = (size_t)b * Hq + (size_t)g * hpk + h;
+      if (sp.direct) {  // the only chunk: fold carry_in, write the results
+        const float l_in = s_in[hpk + h];
+        fold_state(M, L, acc, s_in[h], l_in,
+                   l_in > 0.0f ? sp.in_acc[row * DV + d] : 0.0f);
+        write_final(sp, row, DV, d, M, L, acc);
+        continue;
+      }
       float *pa = a.part_acc + (row * nchunk + c) * DV + d;
       float *pm = a.part_m + row * nchunk + c;
       float *pl = a.part_l + row * nchunk + c;
@@ -312,14 +352,19 @@ hipError_t launch_one(const PartitionArgs &a, const StepParams &sp,
   return hipGetLastError();
 }
 
+template <int DK, int DV, bool STEP>
+hipError_t launch_shape(const PartitionArgs &a, const StepParams &sp,
+                        hipStream_t s) {
+  return launch_one<DK, DV, partition_waves(DK, DV), STEP>(a, sp, s);
+}
+
 template <bool STEP>
 hipError_t dispatch(const PartitionArgs &a, const StepParams &sp,
                     hipStream_t s) {
-  constexpr int W = kPartitionWaves;
-  if (a.dk == 64 && a.dv == 64) return launch_one<64, 64, W, STEP>(a, sp, s);
-  if (a.dk == 128 && a.dv == 128) return launch_one<128, 128, W, STEP>(a, sp, s);
-  if (a.dk == 192 && a.dv == 128) return launch_one<192, 128, W, STEP>(a, sp, s);
-  if (a.dk == 256 && a.dv == 256) return launch_one<256, 256, W, STEP>(a, sp, s);
+  if (a.dk == 64 && a.dv == 64) return launch_shape<64, 64, STEP>(a, sp, s);
+  if (a.dk == 128 && a.dv == 128) return launch_shape<128, 128, STEP>(a, sp, s);
+  if (a.dk == 192 && a.dv == 128) return launch_shape<192, 128, STEP>(a, sp, s);
+  if (a.dk == 256 && a.dv == 256) return launch_shape<256, 256, STEP>(a, sp, s);
   return hipErrorInvalidValue;
 }
 
@@ -331,11 +376,9 @@ bool partition_bf16_supported(int dk, int dv, int hpk) {
          (dk == 192 && dv == 128) || (dk == 256 && dv == 256);
 }
 
-// Two wavefronts per work-group: the split-K plan sizes chunks so that the
-// launch holds about a thousand wavefronts, each streaming a long run of
-// tiles, which measured best across the workload shapes on MI355X.
-hipError_t launch_partition_bf16(const PartitionArgs &a, hipStream_t s) {
-  return dispatch<false>(a, StepParams{}, s);
+hipError_t launch_partition_bf16(const PartitionArgs &a, const StepParams &ep,
+                                 hipStream_t s) {
+  return dispatch<false>(a, ep, s);
 }
 
 hipError_t launch_step_bf16(const PartitionArgs &a, const StepParams &sp,

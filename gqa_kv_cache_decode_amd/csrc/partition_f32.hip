@@ -48,6 +48,7 @@ __global__ __launch_bounds__(NW * 64) void partition_f32_mfma_kernel(
   constexpr int kLdsFloats = kTileFloats > kMergeFloats ? kTileFloats : kMergeFloats;
   __shared__ __attribute__((aligned(16))) float lds[kLdsFloats];
   __shared__ int s_flag;
+  __shared__ float s_in[32];  // carry_in m, l of the group's rows (direct)
 
   const int Hkv = a.num_kv_heads, hpk = a.hpk, nchunk = a.num_chunks;
   const int item = xcd_local_item(blockIdx.x, a.batch * Hkv * nchunk);
@@ -59,7 +60,7 @@ __global__ __launch_bounds__(NW * 64) void partition_f32_mfma_kernel(
   const int n = sl.n;
   if (STEP && g == 0 && c == 0 && threadIdx.x == 0) step_bookkeeping(sp, b, sl);
   const int t0 = c * a.chunk_tokens;
-  if (t0 >= n && !(STEP && sp.fuse && c == 0)) return;
+  if (t0 >= n && !(c == 0 && (sp.direct || (STEP && sp.fuse)))) return;
   const int t1 = min(t0 + a.chunk_tokens, n);
   const int ntiles = t1 > t0 ? (t1 - t0 + kF32Tile - 1) / kF32Tile : 0;
 
@@ -89,15 +90,22 @@ __global__ __launch_bounds__(NW * 64) void partition_f32_mfma_kernel(
   float *Vg = static_cast<float *>(const_cast<void *>(a.v)) +
               ((size_t)b * a.max_len * Hkv + g) * DV;
 
-  // STEP: the work-group whose chunk holds the new slot writes the token's
-  // rows of this group into the cache before any of its tiles is loaded; its
-  // tile loop then reads the slot like any other.
+  // STEP: the work-group whose chunk holds the new slot stores the token's
+  // rows into the cache without waiting; this call reads them from
+  // k_new/v_new in the one tile holding the slot (relative position `rel`,
+  // the chunk's last live token).
+  const float *knew = nullptr, *vnew = nullptr;
+  int rel = -1;
   if (STEP && sl.fresh && sl.n_old / a.chunk_tokens == c) {
-    append_group_row(static_cast<const u32x4 *>(sp.k_new) + ((size_t)b * Hkv + g) * (DK / 4),
-                     reinterpret_cast<u32x4 *>(Kg + sl.n_old * kTok), DK / 4,
-                     static_cast<const u32x4 *>(sp.v_new) + ((size_t)b * Hkv + g) * (DV / 4),
-                     reinterpret_cast<u32x4 *>(Vg + sl.n_old * vTok), DV / 4);
+    rel = sl.n_old - t0;
+    knew = static_cast<const float *>(sp.k_new) + ((size_t)b * Hkv + g) * DK;
+    vnew = static_cast<const float *>(sp.v_new) + ((size_t)b * Hkv + g) * DV;
+    store_group_row(reinterpret_cast<const u32x4 *>(knew),
+                    reinterpret_cast<u32x4 *>(Kg + (size_t)sl.n_old * kTok), DK / 4,
+                    reinterpret_cast<const u32x4 *>(vnew),
+                    reinterpret_cast<u32x4 *>(Vg + (size_t)sl.n_old * vTok), DV / 4);
   }
+  const int rel_tile = rel >= 0 ? rel / kF32Tile : -1;
 
   // Tokens past the chunk's last live token load that token again (finite,
   // masked to weight 0): no branches, and padding slots are never read.
@@ -108,6 +116,24 @@ __global__ __launch_bounds__(NW * 64) void partition_f32_mfma_kernel(
       Vg + (size_t)t0 * vTok, (uint32_t)(((size_t)last * vTok + DV) * 4));
   u32x4 kr[G::kLoads], vr[G::vLoads];
   auto issue = [&](int tile) {
+    if (STEP && tile == rel_tile) {
+      const float *kb = Kg + (size_t)t0 * kTok, *vb = Vg + (size_t)t0 * vTok;
+#pragma unroll
+      for (int i = 0; i < G::kLoads; ++i) {
+        const int idx = i * 64 + lane;
+        const int t = min(tile * kF32Tile + idx / G::kPieces, last);
+        const int pc = (idx % G::kPieces) * 4;
+        kr[i] = stream_load16(t == rel ? knew + pc : kb + (size_t)t * kTok + pc);
+      }
+#pragma unroll
+      for (int i = 0; i < G::vLoads; ++i) {
+        const int idx = i * 64 + lane;
+        const int t = min(tile * kF32Tile + idx / G::vPieces, last);
+        const int pc = (idx % G::vPieces) * 4;
+        vr[i] = stream_load16(t == rel ? vnew + pc : vb + (size_t)t * vTok + pc);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < G::kLoads; ++i) {
       const int idx = i * 64 + lane;
@@ -207,22 +233,31 @@ __global__ __launch_bounds__(NW * 64) void partition_f32_mfma_kernel(
       for (int i = 0; i < 4; ++i)
         wacc[(w * 16 + hl) * DV + blk * 16 + kg * 4 + i] = o[blk][i];
   }
+  if (sp.direct) stage_carry_in(sp, (size_t)b * Hq + (size_t)g * hpk, hpk, s_in);
   __syncthreads();
 
-  if (ntiles > 0) {
+  if (ntiles > 0 || sp.direct) {
     for (int e = threadIdx.x; e < hpk * DV; e += NW * 64) {
       const int h = e / DV, d = e % DV;
-      float M = -INFINITY;
+      float M = -INFINITY, acc = 0.0f, L = 0.0f;
+      if (ntiles > 0) {
 #pragma unroll
-      for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, wm[ww * 16 + h]);
-      float acc = 0.0f, L = 0.0f;
+        for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, wm[ww * 16 + h]);
 #pragma unroll
-      for (int ww = 0; ww < NW; ++ww) {
-        const float f = fast_exp2(wm[ww * 16 + h] - M);
-        acc += f * wacc[(ww * 16 + h) * DV + d];
-        L += f * wl[ww * 16 + h];
+        for (int ww = 0; ww < NW; ++ww) {
+          const float f = fast_exp2(wm[ww * 16 + h] - M);
+          acc += f * wacc[(ww * 16 + h) * DV + d];
+          L += f * wl[ww * 16 + h];
+        }
       }
       const size_t row = (size_t)b * Hq + (size_t)g * hpk + h;
+      if (sp.direct) {  // the only chunk: fold carry_in, write the results
+        const float l_in = s_in[hpk + h];
+        fold_state(M, L, acc, s_in[h], l_in,
+                   l_in > 0.0f ? sp.in_acc[row * DV + d] : 0.0f);
+        write_final(sp, row, DV, d, M, L, acc);
+        continue;
+      }
       float *pa = a.part_acc + (row * nchunk + c) * DV + d;
       float *pm = a.part_m + row * nchunk + c;
       float *pl = a.part_l + row * nchunk + c;
@@ -333,8 +368,7 @@ __global__ __launch_bounds__(64) void partition_f32_kernel(
   float *Ps = Vs + kTok * dv;      // [hpk][kTok]
   float *Qs = Ps + hpk * kTok;     // [hpk][dk]
 
-  const int nwork = batch * Hkv * nchunk;
-  const int item = xcd_local_item(blockIdx.x, nwork);
+  const int item = xcd_local_item(blockIdx.x, batch * Hkv * nchunk);
   const int c = item % nchunk;
   const int bg = item / nchunk;
   const int g = bg % Hkv;
@@ -447,8 +481,10 @@ bool partition_f32_supported(int dk, int dv, int hpk) {
 
 bool partition_f32_uses_mfma(int dk, int dv) { return mfma_shape(dk, dv); }
 
-hipError_t launch_partition_f32(const PartitionArgs &a, hipStream_t s) {
-  if (mfma_shape(a.dk, a.dv)) return dispatch_mfma<false>(a, StepParams{}, s);
+hipError_t launch_partition_f32(const PartitionArgs &a, const StepParams &ep,
+                                hipStream_t s) {
+  if (mfma_shape(a.dk, a.dv)) return dispatch_mfma<false>(a, ep, s);
+  if (ep.direct || ep.fuse) return hipErrorInvalidValue;
   const int nwork = a.batch * a.num_kv_heads * a.num_chunks;
   const size_t lds = partition_f32_lds_bytes(a.dk, a.dv, a.hpk);
   if (lds > 65536) {

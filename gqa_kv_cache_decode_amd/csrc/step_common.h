@@ -47,20 +47,18 @@ __device__ __forceinline__ void step_bookkeeping(const StepParams &sp, int b,
   if (!s.fresh && sp.dropped) atomicAdd(sp.dropped, 1);
 }
 
-// Copies one KV group's rows of the new token (16-byte pieces) into the cache
-// slot, then waits until the stores are complete and the whole work-group has
-// passed a barrier, so that the group's own loads of the slot see them.
-__device__ __forceinline__ void append_group_row(const u32x4 *kn, u32x4 *kd,
-                                                 int kpieces, const u32x4 *vn,
-                                                 u32x4 *vd, int vpieces) {
+// Stores one KV group's rows of the new token (16-byte pieces) into the cache
+// slot.  Nothing in the same launch reads the slot, so the stores are not
+// waited for; the launch's end makes them visible to later calls.
+__device__ __forceinline__ void store_group_row(const u32x4 *kn, u32x4 *kd,
+                                                int kpieces, const u32x4 *vn,
+                                                u32x4 *vd, int vpieces) {
   for (int e = threadIdx.x; e < kpieces + vpieces; e += blockDim.x) {
     if (e < kpieces)
       kd[e] = kn[e];
     else
       vd[e - kpieces] = vn[e - kpieces];
   }
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-  __syncthreads();
 }
 
 // Stores and loads of split-K partials that another work-group of the same
@@ -95,21 +93,60 @@ __device__ __forceinline__ bool arrive_last(int *counter, int nc, int *flag) {
   return *flag != 0;
 }
 
+// carry_in's m (in base-2 units, -inf when empty) and l of the hpk query rows
+// from row0 on, staged in LDS as s_in[h] and s_in[hpk + h].  Callers read them
+// after a work-group barrier, and write carry_out only after that barrier, so
+// carry_out may alias carry_in.
+__device__ __forceinline__ void stage_carry_in(const StepParams &sp,
+                                               size_t row0, int hpk,
+                                               float *s_in) {
+  for (int h = threadIdx.x; h < hpk; h += blockDim.x) {
+    const float l = sp.in_l ? sp.in_l[row0 + h] : 0.0f;
+    s_in[h] = l > 0.0f ? sp.in_m[row0 + h] * kLog2e : -INFINITY;
+    s_in[hpk + h] = l;
+  }
+}
+
+// Log-sum-exp merge of one column of a state (m in base-2 units, partition L,
+// unnormalised acc) with another (usearch carry: both partial softmaxes are
+// rescaled to the common maximum).  An empty state (l == 0) is the identity.
+__device__ __forceinline__ void fold_state(float &m, float &L, float &acc,
+                                           float m_b, float l_b, float acc_b) {
+  if (l_b > 0.0f) {
+    const float mn = fmaxf(m, m_b);
+    const float fa = fast_exp2(m - mn), fb = fast_exp2(m_b - mn);
+    L = L * fa + l_b * fb;
+    acc = acc * fa + acc_b * fb;
+    m = mn;
+  }
+}
+
+// Writes column d of query row `row` from its final state: out = acc / L
+// (usearch: output rows already divided by the partition) and carry_out;
+// an empty state gives out 0 and carry (-inf, 0, 0).
+__device__ __forceinline__ void write_final(const StepParams &sp, size_t row,
+                                            int dv, int d, float m, float L,
+                                            float acc) {
+  const bool live = L > 0.0f;
+  if (sp.out) sp.out[row * dv + d] = live ? acc / L : 0.0f;
+  if (sp.out_acc) {
+    sp.out_acc[row * dv + d] = live ? acc : 0.0f;
+    if (d == 0) {
+      sp.out_m[row] = live ? m * kLn2 : -INFINITY;
+      sp.out_l[row] = live ? L : 0.0f;
+    }
+  }
+}
+
 // Folds the nc partials of the hpk query rows of group (b, g) and carry_in by
-// log-sum-exp merge (usearch carry: the partial softmaxes are rescaled to a
-// common maximum), then writes
-// out = acc / l and carry_out.  `lds` holds 2 * hpk floats.
+// log-sum-exp merge, then writes out and carry_out.  `lds` holds 2 * hpk
+// floats.
 __device__ __forceinline__ void fold_group(const PartitionArgs &a,
                                            const StepParams &sp, int b, int g,
                                            int nc, float *lds) {
   const int Hq = a.num_kv_heads * a.hpk;
   const size_t row0 = (size_t)b * Hq + (size_t)g * a.hpk;
-  float *in_m = lds, *in_l = lds + a.hpk;
-  for (int h = threadIdx.x; h < a.hpk; h += blockDim.x) {
-    const float l = sp.in_l ? sp.in_l[row0 + h] : 0.0f;
-    in_l[h] = l;
-    in_m[h] = l > 0.0f ? sp.in_m[row0 + h] * kLog2e : -INFINITY;
-  }
+  stage_carry_in(sp, row0, a.hpk, lds);
   __syncthreads();  // carry_in m/l are read before carry_out may overwrite them
   for (int e = threadIdx.x; e < a.hpk * a.dv; e += blockDim.x) {
     const int h = e / a.dv, d = e % a.dv;
@@ -117,9 +154,9 @@ __device__ __forceinline__ void fold_group(const PartitionArgs &a,
     const float *pm = a.part_m + row * a.num_chunks;
     const float *pl = a.part_l + row * a.num_chunks;
     const float *pa = a.part_acc + row * a.num_chunks * a.dv + d;
-    float m = in_m[h], L = 0.0f, acc = 0.0f;
-    if (in_l[h] > 0.0f) {
-      L = in_l[h];
+    float m = lds[h], L = 0.0f, acc = 0.0f;
+    if (lds[a.hpk + h] > 0.0f) {
+      L = lds[a.hpk + h];
       acc = sp.in_acc[row * a.dv + d];
     }
 #pragma unroll 4
@@ -131,15 +168,7 @@ __device__ __forceinline__ void fold_group(const PartitionArgs &a,
       L = L * fo + coherent_load(pl + i) * fi;
       m = mn;
     }
-    const bool live = L > 0.0f;
-    if (sp.out) sp.out[row * a.dv + d] = live ? acc / L : 0.0f;
-    if (sp.out_acc) {
-      sp.out_acc[row * a.dv + d] = live ? acc : 0.0f;
-      if (d == 0) {
-        sp.out_m[row] = live ? m * kLn2 : -INFINITY;
-        sp.out_l[row] = live ? L : 0.0f;
-      }
-    }
+    write_final(sp, row, a.dv, d, m, L, acc);
   }
 }
 
