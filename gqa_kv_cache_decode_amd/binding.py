@@ -42,6 +42,7 @@ class Plan(ctypes.Structure):
 
     _fields_ = [("chunk_tokens", ctypes.c_int32), ("num_chunks", ctypes.c_int32),
                 ("off_l", ctypes.c_size_t), ("off_acc", ctypes.c_size_t),
+                ("off_sched", ctypes.c_size_t), ("sched_entries", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_size_t)]
 
 

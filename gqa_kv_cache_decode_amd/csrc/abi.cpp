@@ -32,6 +32,15 @@ constexpr int64_t kFuseMaxGroups = 64;
 constexpr int64_t kMinGroups = 256;
 constexpr int64_t kMaxTokensPerWave = 2048;
 constexpr int32_t kMaxChunk = 4096;  // longer chunks unbalance ragged batches
+// A launch of at least kScheduleMinItems (sequence, KV group, chunk) items runs
+// in several rounds of work-groups; it is scheduled (schedule.hip) so that the
+// eight XCDs get equal shares of live chunks whatever the lengths.  The
+// schedule kernel holds per-sequence state in LDS: up to kScheduleMaxSeqs
+// sequences and kScheduleMaxChunks chunks.
+constexpr int64_t kScheduleMinItems = 1024;
+constexpr int32_t kScheduledMaxChunk = 2048;
+constexpr int64_t kScheduleMaxSeqs = 8192;
+constexpr int64_t kScheduleMaxChunks = 4096;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -101,6 +110,12 @@ int32_t auto_chunk(const gqa_cache *c) {
           units * ((c->max_len + chunk - 1) / chunk) < kMinGroups))
     chunk /= 2;
   while (chunk > kChunkQuantum && chunk / 2 >= c->max_len) chunk /= 2;
+  // A launch big enough to be scheduled runs in several rounds; there the
+  // last round's chunks set the tail, and shorter ones measured faster.
+  const int64_t nchunk = (c->max_len + chunk - 1) / chunk;
+  if (uses_mfma(c) && chunk > kScheduledMaxChunk && nchunk > 1 &&
+      units * nchunk >= kScheduleMinItems)
+    chunk = kScheduledMaxChunk;
   return chunk;
 }
 
@@ -128,6 +143,19 @@ gqa_status make_plan(const gqa_cache *c, int32_t hq, int32_t chunk_tokens,
   p->off_l = align_up(ml);
   p->off_acc = p->off_l + align_up(ml);
   p->workspace_bytes = p->off_acc + align_up(ml * c->dv);
+  // Schedule table: 8 entries per round of XCDs; the snake order keeps every
+  // XCD's list within one sequence's items (num_kv_heads * nchunk) of the
+  // mean, so 8 * (ceil(groups / 8) + num_kv_heads * nchunk) entries suffice.
+  p->off_sched = 0;
+  p->sched_entries = 0;
+  const int64_t entries = 8 * ((groups + 7) / 8 + c->num_kv_heads * nchunk);
+  if (nchunk > 1 && groups >= kScheduleMinItems && uses_mfma(c) &&
+      c->batch <= kScheduleMaxSeqs && nchunk <= kScheduleMaxChunks &&
+      entries <= std::numeric_limits<int32_t>::max()) {
+    p->off_sched = p->workspace_bytes;
+    p->sched_entries = (int32_t)entries;
+    p->workspace_bytes += align_up((size_t)entries * sizeof(int32_t));
+  }
   return GQA_OK;
 }
 
@@ -140,6 +168,8 @@ gqa_status check_plan(const gqa_cache *c, int32_t hq, const gqa_plan *plan,
   if (st != GQA_OK) return st;
   if (plan->chunk_tokens == 0 || want.num_chunks != plan->num_chunks ||
       want.off_l != plan->off_l || want.off_acc != plan->off_acc ||
+      want.off_sched != plan->off_sched ||
+      want.sched_entries != plan->sched_entries ||
       want.workspace_bytes != plan->workspace_bytes)
     return GQA_ERR_SHAPE_MISMATCH;
   if (!ws) return GQA_ERR_INVALID_ARGUMENT;
@@ -150,6 +180,31 @@ gqa_status check_plan(const gqa_cache *c, int32_t hq, const gqa_plan *plan,
 
 gqa_status device_status(hipError_t e) {
   return e == hipSuccess ? GQA_OK : GQA_ERR_DEVICE;
+}
+
+// Enqueues the schedule kernel of a scheduled plan and points the partition
+// launch at its table (a no-op for an unscheduled plan).
+gqa_status schedule_checked(const gqa_cache *c, const gqa_plan &plan,
+                            const int32_t *lens, bool step, void *ws,
+                            PartitionArgs *a, hipStream_t s) {
+  a->sched = nullptr;
+  a->sched_len = 0;
+  if (plan.sched_entries == 0) return GQA_OK;
+  gqa::ScheduleArgs sa;
+  sa.lens = lens;
+  sa.step = step ? 1 : 0;
+  sa.batch = c->batch;
+  sa.max_len = c->max_len;
+  sa.num_kv_heads = c->num_kv_heads;
+  sa.chunk_tokens = plan.chunk_tokens;
+  sa.num_chunks = plan.num_chunks;
+  sa.table = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + plan.off_sched);
+  sa.table_len = plan.sched_entries;
+  gqa_status st = device_status(gqa::launch_schedule(sa, s));
+  if (st != GQA_OK) return st;
+  a->sched = sa.table;
+  a->sched_len = sa.table_len;
+  return GQA_OK;
 }
 
 // The epilogue of a partition launch that writes final results: carry_in,
@@ -193,6 +248,8 @@ gqa_status partition_checked(const void *q, int32_t hq, const gqa_cache *c,
   a.part_m = reinterpret_cast<float *>(base);
   a.part_l = reinterpret_cast<float *>(base + plan->off_l);
   a.part_acc = reinterpret_cast<float *>(base + plan->off_acc);
+  gqa_status st = schedule_checked(c, *plan, lens, false, ws, &a, s);
+  if (st != GQA_OK) return st;
   return device_status(c->dtype == GQA_DTYPE_BF16
                            ? gqa::launch_partition_bf16(a, ep, s)
                            : gqa::launch_partition_f32(a, ep, s));
@@ -458,6 +515,9 @@ gqa_status gqa_decode_step(const void *q, int32_t num_q_heads,
   a.part_l = reinterpret_cast<float *>(base + plan.off_l);
   a.part_acc = reinterpret_cast<float *>(base + plan.off_acc);
 
+  if ((st = schedule_checked(cache, plan, lens_in, true, workspace, &a,
+                             stream)) != GQA_OK)
+    return st;
   gqa::StepParams sp = final_epilogue(cache, plan, carry_in, carry_out, out);
   sp.k_new = k_new;
   sp.v_new = v_new;

@@ -27,6 +27,19 @@ struct PartitionArgs {
   float *part_m;        // [rows][num_chunks]  (natural-log units)
   float *part_l;        // [rows][num_chunks]
   float *part_acc;      // [rows][num_chunks][dv]
+  // Block -> item table of a scheduled launch (schedule.hip), or NULL for the
+  // fixed map; sched_len entries, one per block.
+  const int32_t *sched;
+  int sched_len;
+};
+
+// Inputs of the schedule kernel (one work-group).
+struct ScheduleArgs {
+  const int32_t *lens;  // [B]
+  int step;             // lengths are decode-step inputs (the new token counts)
+  int batch, max_len, num_kv_heads, chunk_tokens, num_chunks;
+  int32_t *table;       // [table_len]
+  int table_len;
 };
 
 // Extra inputs of a partition launch that runs a whole decode step (k_new ..
@@ -94,6 +107,8 @@ hipError_t launch_step_bf16(const PartitionArgs &a, const StepParams &sp,
 hipError_t launch_step_f32(const PartitionArgs &a, const StepParams &sp,
                            hipStream_t s);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
+size_t schedule_lds_bytes(int batch, int num_chunks);
+hipError_t launch_schedule(const ScheduleArgs &a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs &a, hipStream_t s);
 hipError_t launch_append(const AppendArgs &a, hipStream_t s);
 

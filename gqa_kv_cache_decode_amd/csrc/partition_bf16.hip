@@ -70,7 +70,13 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
   __shared__ float s_in[32];  // carry_in m, l of the group's rows (direct)
 
   const int Hkv = a.num_kv_heads, hpk = a.hpk, nchunk = a.num_chunks;
-  const int item = xcd_local_item(blockIdx.x, a.batch * Hkv * nchunk);
+  int item;
+  if (a.sched) {  // scheduled launch: the table entry, or nothing to do
+    item = a.sched[blockIdx.x];
+    if (item < 0) return;
+  } else {
+    item = xcd_local_item(blockIdx.x, a.batch * Hkv * nchunk);
+  }
   const int c = item % nchunk;
   const int bg = item / nchunk;
   const int g = bg % Hkv;
@@ -346,7 +352,8 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
 template <int DK, int DV, int NW, bool STEP>
 hipError_t launch_one(const PartitionArgs &a, const StepParams &sp,
                       hipStream_t s) {
-  const int nwork = a.batch * a.num_kv_heads * a.num_chunks;
+  const int nwork =
+      a.sched ? a.sched_len : a.batch * a.num_kv_heads * a.num_chunks;
   hipLaunchKernelGGL((partition_bf16_kernel<DK, DV, NW, STEP>), dim3(nwork),
                      dim3(NW * 64), 0, s, a, sp);
   return hipGetLastError();

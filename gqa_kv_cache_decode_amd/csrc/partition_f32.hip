@@ -51,7 +51,13 @@ __global__ __launch_bounds__(NW * 64) void partition_f32_mfma_kernel(
   __shared__ float s_in[32];  // carry_in m, l of the group's rows (direct)
 
   const int Hkv = a.num_kv_heads, hpk = a.hpk, nchunk = a.num_chunks;
-  const int item = xcd_local_item(blockIdx.x, a.batch * Hkv * nchunk);
+  int item;
+  if (a.sched) {  // scheduled launch: the table entry, or nothing to do
+    item = a.sched[blockIdx.x];
+    if (item < 0) return;
+  } else {
+    item = xcd_local_item(blockIdx.x, a.batch * Hkv * nchunk);
+  }
   const int c = item % nchunk;
   const int bg = item / nchunk;
   const int g = bg % Hkv;
@@ -291,7 +297,8 @@ __global__ __launch_bounds__(NW * 64) void partition_f32_mfma_kernel(
 template <int DK, int DV, bool STEP>
 hipError_t launch_mfma(const PartitionArgs &a, const StepParams &sp,
                        hipStream_t s) {
-  const int nwork = a.batch * a.num_kv_heads * a.num_chunks;
+  const int nwork =
+      a.sched ? a.sched_len : a.batch * a.num_kv_heads * a.num_chunks;
   hipLaunchKernelGGL((partition_f32_mfma_kernel<DK, DV, kPartitionWaves, STEP>),
                      dim3(nwork), dim3(kPartitionWaves * 64), 0, s, a, sp);
   return hipGetLastError();
@@ -484,7 +491,7 @@ bool partition_f32_uses_mfma(int dk, int dv) { return mfma_shape(dk, dv); }
 hipError_t launch_partition_f32(const PartitionArgs &a, const StepParams &ep,
                                 hipStream_t s) {
   if (mfma_shape(a.dk, a.dv)) return dispatch_mfma<false>(a, ep, s);
-  if (ep.direct || ep.fuse) return hipErrorInvalidValue;
+  if (ep.direct || ep.fuse || a.sched) return hipErrorInvalidValue;
   const int nwork = a.batch * a.num_kv_heads * a.num_chunks;
   const size_t lds = partition_f32_lds_bytes(a.dk, a.dv, a.hpk);
   if (lds > 65536) {

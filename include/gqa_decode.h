@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define GQA_ABI_VERSION 1
+#define GQA_ABI_VERSION 2
 
 /* Only the entry points below are exported from the shared library. */
 #define GQA_API __attribute__((visibility("default")))
@@ -110,12 +110,20 @@ typedef struct gqa_carry {
  *   part_l   [rows][num_chunks]       at off_l
  *   part_acc [rows][num_chunks][dv]   at off_acc
  * Only chunks c < ceil(min(lens[b], max_len) / chunk_tokens) are written.
+ * A plan with many (sequence, KV group, chunk) items (sched_entries > 0) also
+ * holds the work schedule the library computes on the device before each
+ * partition launch: sched_entries int32 at off_sched (a block -> item table
+ * that gives the GPU's eight XCDs equal shares of the live chunks).
+ * The workspace needs no initialisation and is only scratch between the
+ * partition and combine of one call.
  */
 typedef struct gqa_plan {
   int32_t chunk_tokens;
   int32_t num_chunks;
   size_t off_l;
   size_t off_acc;
+  size_t off_sched;
+  int32_t sched_entries;
   size_t workspace_bytes;
 } gqa_plan;
 

@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.gqa_abi_version() == 1
+    assert lib.gqa_abi_version() == 2
     names = [lib.gqa_status_string(i).decode() for i in range(7)]
     assert names == ["GQA_OK", "GQA_ERR_INVALID_ARGUMENT",
                      "GQA_ERR_SHAPE_MISMATCH", "GQA_ERR_UNSUPPORTED",
