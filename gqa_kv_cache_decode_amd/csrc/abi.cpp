@@ -104,6 +104,12 @@ int partition_waves(const gqa_cache *c) {
 int32_t auto_chunk(const gqa_cache *c) {
   const int64_t units = (int64_t)c->batch * c->num_kv_heads;
   const int64_t waves = uses_mfma(c) ? partition_waves(c) : 1;
+  // A cache of at most two tiles per wavefront is one chunk: its launch is
+  // latency-bound, and a single chunk writes the results directly instead of
+  // passing partials through a second kernel or an arrival count.
+  const int64_t tile = c->dtype == GQA_DTYPE_BF16 ? 32 : 16;
+  if (uses_mfma(c) && c->max_len <= 2 * waves * tile)
+    return (c->max_len + kChunkQuantum - 1) / kChunkQuantum * kChunkQuantum;
   int32_t chunk = kMaxChunk;
   while (chunk > kChunkQuantum &&
          (chunk / waves > kMaxTokensPerWave ||
