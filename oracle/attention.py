@@ -27,13 +27,18 @@ against it, their sum and the weighted value sum.  The passages followed:
   ``exp(l - mx)`` in double precision.
 * metrale DSA reference, ``pool_states``: a softmax over an empty set
   contributes zero weight (a zero result) rather than a NaN.
+* needle-core ``self_attn_incremental``, argument ``attn_bias``: an optional
+  additive term per cached position, added to the scaled dot product of every
+  head before the softmax.
 
 Readings taken where the pages are silent (each listed in the design notes):
 the carry is ``(m, l, acc)`` with ``acc`` the *unnormalised* weighted value sum
 ``sum_j exp(s_j - m) v_j``; ``m`` is in natural-log units of the scaled logit;
 a state with ``l == 0`` is empty whatever its ``m``; an empty result has output
 0 and carry ``(-inf, 0, 0)``; lengths are clamped to ``[0, max_len]``; the
-scale defaults to ``1/sqrt(dk)`` (the key width) when given as 0.
+scale defaults to ``1/sqrt(dk)`` (the key width) when given as 0; the bias
+is one fp32 value per (sequence, position), shared by the sequence's heads, and
+a bias of -inf removes the key, so a row whose every key is removed is empty.
 """
 
 from __future__ import annotations
@@ -78,20 +83,42 @@ def group_logits(qg: np.ndarray, kg: np.ndarray, scale: float) -> np.ndarray:
     return scale * (qg.astype(np.float64) @ kg.astype(np.float64).T)
 
 
+def bias_row_of(bias, b: int, n: int) -> np.ndarray:
+    """The additive bias of sequence b's first n positions (fp64)."""
+    return np.asarray(bias[b][:n], dtype=np.float64)
+
+
+def biased_logits(qg: np.ndarray, kg: np.ndarray, scale: float,
+                  bias_row) -> np.ndarray:
+    """needle-core self_attn_incremental: score = dot(q, k) * scale, then
+    score += bias[t] when a bias is given (the same term for every head)."""
+    s = group_logits(qg, kg, scale)
+    if bias_row is not None:
+        s = s + np.asarray(bias_row, dtype=np.float64)[None, :]
+    return s
+
+
 def softmax_state(s: np.ndarray, vg: np.ndarray) -> Carry:
     """Two-pass softmax state of a logit matrix s [heads, n] over values vg [n, dv].
 
     Pass 1: m = max_j s_j.  Pass 2: l = sum_j exp(s_j - m),
-    acc = sum_j exp(s_j - m) v_j.  With no keys the state is empty."""
+    acc = sum_j exp(s_j - m) v_j.  With no keys, or no key with a finite
+    logit (all removed by a -inf bias), the state is empty."""
     heads, n = s.shape
     dv = vg.shape[1]
+    m = np.full(heads, -np.inf)
+    l = np.zeros(heads)
+    acc = np.zeros((heads, dv))
     if n == 0:
-        return Carry(np.full(heads, -np.inf), np.zeros(heads),
-                     np.zeros((heads, dv)))
-    m = s.max(axis=1)
-    e = np.exp(s - m[:, None])
-    l = e.sum(axis=1)
-    acc = e @ vg.astype(np.float64)
+        return Carry(m, l, acc)
+    mx = s.max(axis=1)
+    for h in range(heads):
+        if mx[h] == -np.inf:
+            continue
+        e = np.exp(s[h] - mx[h])
+        m[h] = mx[h]
+        l[h] = e.sum()
+        acc[h] = e @ vg.astype(np.float64)
     return Carry(m, l, acc)
 
 
@@ -138,11 +165,12 @@ def empty_carry(rows: int, dv: int) -> Carry:
 
 
 def attend(q, k, v, lens, scale: float = 0.0,
-           carry_in: Optional[Carry] = None):
+           carry_in: Optional[Carry] = None, bias=None):
     """Exact GQA decode attention of one query token per sequence.
 
     q [B, Hq, dk]; k [B, max_len, Hkv, dk]; v [B, max_len, Hkv, dv];
-    lens [B] (live keys per sequence).  Rows of the result are b * Hq + h.
+    lens [B] (live keys per sequence); bias None or [B, >= n] additive
+    logit terms.  Rows of the result are b * Hq + h.
     With ``carry_in`` the result is merge(carry_in, this branch).
     Returns (out [B, Hq, dv], Carry with m [B*Hq], l [B*Hq], acc [B*Hq, dv]).
     """
@@ -163,7 +191,9 @@ def attend(q, k, v, lens, scale: float = 0.0,
             heads = [h for h in range(Hq) if kv_head_of(h, hpk) == g]
             kg = np.asarray(k[b, :n, g, :])
             vg = np.asarray(v[b, :n, g, :])
-            st = softmax_state(group_logits(q[b, heads, :], kg, s_scale), vg)
+            brow = None if bias is None else bias_row_of(bias, b, n)
+            st = softmax_state(biased_logits(q[b, heads, :], kg, s_scale,
+                                             brow), vg)
             rows = [b * Hq + h for h in heads]
             m[rows], l[rows], acc[rows] = st.m, st.l, st.acc
     c = Carry(m, l, acc)

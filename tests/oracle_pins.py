@@ -345,3 +345,93 @@ def pin_kv_append(orc):
 ALL_PINS = [pin_equal_keys, pin_dominant_key, pin_recovery_trial,
             pin_gqa_is_repeated_mha, pin_brute_force, pin_split_merge,
             pin_special_cases, pin_kv_append]
+
+
+# --- additive logit bias (needle-core attn_bias) ---------------------------
+
+def pin_bias(orc):
+    """The additive bias of needle-core self_attn_incremental, one value per
+    (sequence, position) shared by all heads and added to the scaled dot
+    product:
+    * bias_j = ln w_j (w_j > 0) weights key j by w_j: checked at 50 digits
+      straight from out = sum_j w_j e^(s_j) v_j / sum_j w_j e^(s_j), with m
+      the largest biased logit and l the partition against it;
+    * a constant bias leaves out and l unchanged and shifts m by it;
+    * a bias of -inf on a set of keys equals attending over the other keys
+      (a cache with those rows taken out);
+    * a row whose every key is removed is empty (out 0, carry (-inf, 0, 0)),
+      and with a carry_in it returns the carry_in."""
+    B, Hq, Hkv, dk, dv, T = 2, 4, 2, 3, 3, 6
+    q, k, v, lens = _problem(11, B, Hq, Hkv, dk, dv, T, lens=[6, 5],
+                             dyadic=True)
+    scale = 0.75
+    rng = np.random.default_rng(12)
+    w = rng.uniform(0.2, 3.0, (B, T))
+    bias = np.log(w)
+    out, c = orc.attend(q, k, v, lens, scale=scale, bias=bias)
+    hpk = Hq // Hkv
+    with localcontext() as ctx:
+        ctx.prec = 50
+        for b in range(B):
+            n = int(lens[b])
+            for h in range(Hq):
+                g = h // hpk
+                s = [Decimal(scale) * sum(Decimal(float(q[b, h, i])) *
+                                          Decimal(float(k[b, j, g, i]))
+                                          for i in range(dk))
+                     for j in range(n)]
+                ww = [Decimal(float(w[b, j])) for j in range(n)]
+                ex = [wj * x.exp() for wj, x in zip(ww, s)]
+                z = sum(ex)
+                for ch in range(dv):
+                    want = sum(e * Decimal(float(v[b, j, g, ch]))
+                               for j, e in enumerate(ex)) / z
+                    assert abs(Decimal(float(out[b, h, ch])) - want) <= \
+                        Decimal("1e-13"), f"weighted keys b={b} h={h}"
+                sb = [x + Decimal(float(bias[b, j])) for j, x in enumerate(s)]
+                mx = max(sb)
+                r = b * Hq + h
+                assert abs(Decimal(float(c.m[r])) - mx) <= Decimal("1e-13"), \
+                    "m is the largest biased logit"
+                lw = sum((x - mx).exp() for x in sb)
+                assert abs(Decimal(float(c.l[r])) - lw) <= Decimal("1e-12"), \
+                    "l against the biased maximum"
+
+    # constant bias: shift invariance
+    q, k, v, lens = _problem(13, 2, 8, 4, 16, 8, 29, lens=[29, 11])
+    out0, c0 = orc.attend(q, k, v, lens, scale=0.4)
+    outc, cc = orc.attend(q, k, v, lens, scale=0.4,
+                          bias=np.full((2, 29), 2.5))
+    _close(outc, out0, 1e-13, "constant bias: out")
+    _close(cc.l, c0.l, 1e-11, "constant bias: l")
+    _close(cc.m, c0.m + 2.5, 1e-13, "constant bias: m shifts")
+
+    # -inf on a key set == the cache without those keys; one row all removed
+    q, k, v, lens = _problem(14, 3, 8, 4, 16, 8, 21, lens=[21, 13, 7])
+    keep = np.ones((3, 21), dtype=bool)
+    keep[0, [0, 5, 6, 20]] = False
+    keep[1, 3:9] = False
+    keep[2, :7] = False            # every key of sequence 2 removed
+    bias = np.where(keep, 0.0, -np.inf)
+    outm, cm = orc.attend(q, k, v, lens, scale=0.3, bias=bias)
+    for b in range(3):
+        n = int(lens[b])
+        idx = [j for j in range(n) if keep[b, j]]
+        kk = np.full_like(k[b:b + 1], np.nan)
+        vv = np.full_like(v[b:b + 1], np.nan)
+        kk[0, :len(idx)] = k[b, idx]
+        vv[0, :len(idx)] = v[b, idx]
+        want, cw = orc.attend(q[b:b + 1], kk, vv, [len(idx)], scale=0.3)
+        _close(outm[b], want[0], 1e-14, f"masked keys b={b}")
+        rows = slice(b * 8, (b + 1) * 8)
+        _close(cm.m[rows], cw.m, 1e-14, f"masked m b={b}")
+        _close(cm.l[rows], cw.l, 1e-12, f"masked l b={b}")
+    assert np.all(outm[2] == 0.0) and np.all(np.isneginf(cm.m[16:24])) and \
+        np.all(cm.l[16:24] == 0.0), "all keys removed: empty"
+    cin = orc.Carry(np.full(24, 0.7), np.full(24, 2.0), np.ones((24, 8)))
+    outi, ci = orc.attend(q, k, v, lens, scale=0.3, bias=bias, carry_in=cin)
+    _close(outi[2], np.full((8, 8), 0.5), 1e-15, "removed row returns carry_in")
+    _close(ci.m[16:24], np.full(8, 0.7), 0.0, "removed row keeps carry_in m")
+
+
+ALL_PINS.append(pin_bias)

@@ -76,8 +76,30 @@ def _kv_append_no_increment(k_cache, v_cache, k_new, v_new, lens):
     return k, v, np.asarray(lens, dtype=np.int32), dropped
 
 
+def _softmax_state_unguarded(s, vg):
+    if s.shape[1] == 0:
+        return orc.Carry(np.full(s.shape[0], -np.inf), np.zeros(s.shape[0]),
+                         np.zeros((s.shape[0], vg.shape[1])))
+    m = s.max(axis=1)                               # -inf rows give NaN
+    with np.errstate(invalid="ignore"):
+        e = np.exp(s - m[:, None])
+    return orc.Carry(m, e.sum(axis=1), e @ vg.astype(np.float64))
+
+
+def _biased_logits_scaled(qg, kg, scale, bias_row):
+    s = qg.astype(np.float64) @ kg.astype(np.float64).T
+    if bias_row is not None:
+        s = s + np.asarray(bias_row)[None, :]
+    return scale * s                                # bias scaled too
+
+
+def _biased_logits_ignored(qg, kg, scale, bias_row):
+    return _real_group_logits(qg, kg, scale)
+
+
 _real_attend = orc.attend
 _real_append = orc.kv_append
+_real_group_logits = orc.group_logits
 
 MUTANTS = {
     "scale_dropped": ("group_logits",
@@ -99,6 +121,12 @@ MUTANTS = {
     "carry_in_ignored": ("attend", _attend_ignores_carry),
     "values_of_wrong_group": ("attend", _attend_wrong_value_group),
     "append_keeps_length": ("kv_append", _kv_append_no_increment),
+    "removed_keys_give_nan": ("softmax_state", _softmax_state_unguarded),
+    "bias_scaled_with_logits": ("biased_logits", _biased_logits_scaled),
+    "bias_ignored": ("biased_logits", _biased_logits_ignored),
+    "bias_of_wrong_sequence": ("bias_row_of",
+                               lambda bias, b, n: np.asarray(
+                                   bias[b - 1][:n], dtype=np.float64)),
 }
 
 
