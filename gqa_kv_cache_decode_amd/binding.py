@@ -61,18 +61,19 @@ _SIGNATURES = {
     "gqa_attend_plan": (_I32, [_CACHE_P, _I32, _I32, _PLAN_P]),
     "gqa_attend_workspace_bytes": (ctypes.c_size_t, [_CACHE_P, _I32]),
     "gqa_attend_decode": (_I32, [_P, _I32, _CACHE_P, _P, ctypes.c_float,
-                                 _CARRY_P, _CARRY_P, _P, _P, ctypes.c_size_t,
-                                 _P]),
+                                 _P, ctypes.c_int64, _CARRY_P, _CARRY_P, _P,
+                                 _P, ctypes.c_size_t, _P]),
     "gqa_attend_partition": (_I32, [_P, _I32, _CACHE_P, _P, ctypes.c_float,
-                                    _PLAN_P, _P, ctypes.c_size_t, _P]),
+                                    _P, ctypes.c_int64, _PLAN_P, _P,
+                                    ctypes.c_size_t, _P]),
     "gqa_attend_combine": (_I32, [_I32, _CACHE_P, _P, _PLAN_P, _P,
                                   ctypes.c_size_t, _CARRY_P, _CARRY_P, _P, _P]),
     "gqa_softmax_state_merge": (_I32, [_CARRY_P, _CARRY_P, _CARRY_P,
                                        ctypes.c_int64, _I32, _P, _P]),
     "gqa_decode_step_workspace_bytes": (ctypes.c_size_t, [_CACHE_P, _I32]),
     "gqa_decode_step": (_I32, [_P, _I32, _CACHE_P, _P, _P, _P, _P, _P,
-                               ctypes.c_float, _CARRY_P, _CARRY_P, _P, _P,
-                               ctypes.c_size_t, _P]),
+                               ctypes.c_float, _P, ctypes.c_int64, _CARRY_P,
+                               _CARRY_P, _P, _P, ctypes.c_size_t, _P]),
 }
 
 
@@ -204,6 +205,23 @@ def _attend_args(q, k_cache, v_cache, lens):
     return c, q.shape[1]
 
 
+def _bias(c, bias):
+    """(pointer, row stride) of an optional additive logit bias: fp32
+    [batch, >= max_len] on the GPU with unit column stride (its row stride is
+    passed as is: a multiple of 4, 16-byte aligned rows)."""
+    if bias is None:
+        return None, 0
+    if not isinstance(bias, torch.Tensor) or not bias.is_cuda:
+        raise GqaError("bias must be a GPU tensor")
+    if bias.dtype != torch.float32 or bias.dim() != 2:
+        raise GqaError("bias must be fp32 [batch, positions]")
+    if bias.shape[0] != c.batch or bias.shape[1] < c.max_len or \
+            bias.stride(1) != 1:
+        raise GqaError(f"bias must be [batch={c.batch}, >= max_len="
+                       f"{c.max_len}] with unit column stride")
+    return ctypes.c_void_p(bias.data_ptr()), int(bias.stride(0))
+
+
 def _carries(c, hq, carry_in, carry_out, out):
     rows = c.batch * hq
     cin = None if carry_in is None else carry_in._struct(rows, c.dv, "carry_in")
@@ -219,12 +237,14 @@ def attend_decode(q, k_cache, v_cache, lens, scale: float = 0.0,
                   carry_in: Optional[Carry] = None,
                   carry_out: Optional[Carry] = None,
                   out=_AUTO,
-                  workspace: Optional[torch.Tensor] = None):
+                  workspace: Optional[torch.Tensor] = None, bias=None):
     """Exact GQA decode attention: q [B, Hq, dk] over the caches.
 
     Returns ``out`` [B, Hq, dv] fp32: allocated unless given; pass
-    ``out=None`` together with ``carry_out`` to get the carry only."""
+    ``out=None`` together with ``carry_out`` to get the carry only.
+    ``bias``: optional fp32 [B, >= max_len] additive logit terms."""
     c, hq = _attend_args(q, k_cache, v_cache, lens)
+    bp, bs = _bias(c, bias)
     if out is _AUTO:
         out = torch.empty(c.batch, hq, c.dv, dtype=torch.float32,
                           device=q.device)
@@ -234,19 +254,22 @@ def attend_decode(q, k_cache, v_cache, lens, scale: float = 0.0,
         workspace = _workspace(need, q.device)
     _need(workspace, "workspace")
     _check(library().gqa_attend_decode(
-        _ptr(q), hq, ctypes.byref(c), _ptr(lens), float(scale), cin, cout,
+        _ptr(q), hq, ctypes.byref(c), _ptr(lens), float(scale), bp, bs, cin,
+        cout,
         _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(q)), "attend_decode")
     return out
 
 
 def attend_partition(q, k_cache, v_cache, lens, plan: Plan,
-                     workspace: torch.Tensor, scale: float = 0.0) -> None:
+                     workspace: torch.Tensor, scale: float = 0.0,
+                     bias=None) -> None:
     """Split-K partials of every live (query row, chunk) into ``workspace``."""
     c, hq = _attend_args(q, k_cache, v_cache, lens)
+    bp, bs = _bias(c, bias)
     _need(workspace, "workspace")
     _check(library().gqa_attend_partition(
-        _ptr(q), hq, ctypes.byref(c), _ptr(lens), float(scale),
+        _ptr(q), hq, ctypes.byref(c), _ptr(lens), float(scale), bp, bs,
         ctypes.byref(plan), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream(q)),
         "attend_partition")
@@ -284,12 +307,14 @@ def step_workspace(k_cache, v_cache, num_q_heads: int) -> torch.Tensor:
 def decode_step(q, k_cache, v_cache, k_new, v_new, lens_in, lens_out,
                 scale: float = 0.0, carry_in: Optional[Carry] = None,
                 carry_out: Optional[Carry] = None, out=_AUTO,
-                workspace: Optional[torch.Tensor] = None, dropped=None):
+                workspace: Optional[torch.Tensor] = None, dropped=None,
+                bias=None):
     """kv_append of (k_new, v_new) then attend_decode, as one step.
 
     lens_out must be a different tensor from lens_in.  ``workspace`` must come
     from :func:`step_workspace` (zero-filled once, then reused)."""
     c, hq = _attend_args(q, k_cache, v_cache, lens_in)
+    bp, bs = _bias(c, bias)
     _need(k_new, "k_new", k_cache.dtype, (c.batch, c.num_kv_heads, c.dk))
     _need(v_new, "v_new", k_cache.dtype, (c.batch, c.num_kv_heads, c.dv))
     _need(lens_out, "lens_out", torch.int32, (c.batch,))
@@ -304,7 +329,8 @@ def decode_step(q, k_cache, v_cache, k_new, v_new, lens_in, lens_out,
     _need(workspace, "workspace")
     _check(library().gqa_decode_step(
         _ptr(q), hq, ctypes.byref(c), _ptr(k_new), _ptr(v_new), _ptr(lens_in),
-        _ptr(lens_out), _ptr(dropped), float(scale), cin, cout, _ptr(out),
+        _ptr(lens_out), _ptr(dropped), float(scale), bp, bs, cin, cout,
+        _ptr(out),
         _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(q)), "decode_step")
     return out

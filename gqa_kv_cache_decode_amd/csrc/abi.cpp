@@ -232,6 +232,7 @@ gqa::StepParams final_epilogue(const gqa_cache *c, const gqa_plan &plan,
 
 gqa_status partition_checked(const void *q, int32_t hq, const gqa_cache *c,
                              const int32_t *lens, float scale,
+                             const float *bias, int64_t bias_stride,
                              const gqa_plan *plan, void *ws,
                              const gqa::StepParams &ep, hipStream_t s) {
   const int hpk = hq / c->num_kv_heads;
@@ -250,6 +251,8 @@ gqa_status partition_checked(const void *q, int32_t hq, const gqa_cache *c,
   a.chunk_tokens = plan->chunk_tokens;
   a.num_chunks = plan->num_chunks;
   a.scale_log2 = (float)(sc * 1.4426950408889634);
+  a.bias = bias;
+  a.bias_stride = bias ? bias_stride : 0;
   char *base = static_cast<char *>(ws);
   a.part_m = reinterpret_cast<float *>(base);
   a.part_l = reinterpret_cast<float *>(base + plan->off_l);
@@ -296,6 +299,16 @@ gqa_status check_attend_args(const void *q, int32_t hq, const gqa_cache *c,
   if (!q || !lens) return GQA_ERR_INVALID_ARGUMENT;
   if (!aligned16(q)) return GQA_ERR_INVALID_ARGUMENT;
   if (!std::isfinite(scale)) return GQA_ERR_INVALID_ARGUMENT;
+  return GQA_OK;
+}
+
+// The additive bias: NULL, or fp32 rows of bias_stride >= max_len values per
+// sequence, 16-byte aligned rows (the kernels read four positions at once).
+gqa_status check_bias(const gqa_cache *c, const float *bias,
+                      int64_t bias_stride) {
+  if (!bias) return GQA_OK;
+  if (bias_stride < c->max_len || bias_stride % 4 != 0 || !aligned16(bias))
+    return GQA_ERR_INVALID_ARGUMENT;
   return GQA_OK;
 }
 
@@ -382,16 +395,19 @@ size_t gqa_attend_workspace_bytes(const gqa_cache *cache, int32_t num_q_heads) {
 
 gqa_status gqa_attend_partition(const void *q, int32_t num_q_heads,
                                 const gqa_cache *cache, const int32_t *lens,
-                                float scale, const gqa_plan *plan,
+                                float scale, const float *bias,
+                                int64_t bias_stride, const gqa_plan *plan,
                                 void *workspace, size_t workspace_bytes,
                                 hipStream_t stream) {
   gqa_status st = check_attend_args(q, num_q_heads, cache, lens, scale);
   if (st != GQA_OK) return st;
+  if ((st = check_bias(cache, bias, bias_stride)) != GQA_OK) return st;
   if ((st = check_plan(cache, num_q_heads, plan, workspace_bytes, workspace)) !=
       GQA_OK)
     return st;
-  return partition_checked(q, num_q_heads, cache, lens, scale, plan, workspace,
-                           gqa::StepParams{}, stream);
+  return partition_checked(q, num_q_heads, cache, lens, scale, bias,
+                           bias_stride, plan, workspace, gqa::StepParams{},
+                           stream);
 }
 
 gqa_status gqa_attend_combine(int32_t num_q_heads, const gqa_cache *cache,
@@ -412,12 +428,14 @@ gqa_status gqa_attend_combine(int32_t num_q_heads, const gqa_cache *cache,
 
 gqa_status gqa_attend_decode(const void *q, int32_t num_q_heads,
                              const gqa_cache *cache, const int32_t *lens,
-                             float scale, const gqa_carry *carry_in,
+                             float scale, const float *bias,
+                             int64_t bias_stride, const gqa_carry *carry_in,
                              const gqa_carry *carry_out, float *out,
                              void *workspace, size_t workspace_bytes,
                              hipStream_t stream) {
   gqa_status st = check_attend_args(q, num_q_heads, cache, lens, scale);
   if (st != GQA_OK) return st;
+  if ((st = check_bias(cache, bias, bias_stride)) != GQA_OK) return st;
   if ((st = check_combine_args(num_q_heads, cache, lens, carry_in, carry_out,
                                out)) != GQA_OK)
     return st;
@@ -428,8 +446,8 @@ gqa_status gqa_attend_decode(const void *q, int32_t num_q_heads,
     return st;
   const gqa::StepParams ep =
       final_epilogue(cache, plan, carry_in, carry_out, out);
-  st = partition_checked(q, num_q_heads, cache, lens, scale, &plan, workspace,
-                         ep, stream);
+  st = partition_checked(q, num_q_heads, cache, lens, scale, bias, bias_stride,
+                         &plan, workspace, ep, stream);
   if (st != GQA_OK || ep.direct) return st;
   return combine_checked(num_q_heads, cache, lens, &plan, workspace, carry_in,
                          carry_out, out, stream);
@@ -472,6 +490,7 @@ gqa_status gqa_decode_step(const void *q, int32_t num_q_heads,
                            const gqa_cache *cache, const void *k_new,
                            const void *v_new, const int32_t *lens_in,
                            int32_t *lens_out, int32_t *dropped, float scale,
+                           const float *bias, int64_t bias_stride,
                            const gqa_carry *carry_in,
                            const gqa_carry *carry_out, float *out,
                            void *workspace, size_t workspace_bytes,
@@ -481,6 +500,7 @@ gqa_status gqa_decode_step(const void *q, int32_t num_q_heads,
   if ((st = check_combine_args(num_q_heads, cache, lens_in, carry_in,
                                carry_out, out)) != GQA_OK)
     return st;
+  if ((st = check_bias(cache, bias, bias_stride)) != GQA_OK) return st;
   if (!k_new || !v_new || !lens_out || lens_out == lens_in)
     return GQA_ERR_INVALID_ARGUMENT;
   if (!aligned16(k_new) || !aligned16(v_new)) return GQA_ERR_INVALID_ARGUMENT;
@@ -493,8 +513,9 @@ gqa_status gqa_decode_step(const void *q, int32_t num_q_heads,
   if (!uses_mfma(cache)) {  // vector-ALU shapes: the same step as three launches
     st = gqa_kv_append(cache, k_new, v_new, lens_in, lens_out, dropped, stream);
     if (st != GQA_OK) return st;
-    st = partition_checked(q, num_q_heads, cache, lens_out, scale, &plan,
-                           workspace, gqa::StepParams{}, stream);
+    st = partition_checked(q, num_q_heads, cache, lens_out, scale, bias,
+                           bias_stride, &plan, workspace, gqa::StepParams{},
+                           stream);
     if (st != GQA_OK) return st;
     return combine_checked(num_q_heads, cache, lens_out, &plan, workspace,
                            carry_in, carry_out, out, stream);
@@ -516,6 +537,8 @@ gqa_status gqa_decode_step(const void *q, int32_t num_q_heads,
   a.chunk_tokens = plan.chunk_tokens;
   a.num_chunks = plan.num_chunks;
   a.scale_log2 = (float)(sc * 1.4426950408889634);
+  a.bias = bias;
+  a.bias_stride = bias ? bias_stride : 0;
   char *base = static_cast<char *>(workspace);
   a.part_m = reinterpret_cast<float *>(base);
   a.part_l = reinterpret_cast<float *>(base + plan.off_l);

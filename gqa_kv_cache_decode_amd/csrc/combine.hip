@@ -52,8 +52,9 @@ __global__ __launch_bounds__(THREADS) void combine_kernel(CombineArgs a) {
       const float mi = pm[i] * kLog2e;
       const float li = pl[i];
       const float ai = pa[(size_t)i * a.dv + col];
-      const float mn = fmaxf(m, mi);
-      const float fo = fast_exp2(m - mn), fi = fast_exp2(mi - mn);
+      // a chunk whose keys were all removed by the bias has m = -inf, l = 0
+      const float mn = fmaxf(m, mi), ref = exp_ref(mn);
+      const float fo = fast_exp2(m - ref), fi = fast_exp2(mi - ref);
       acc = acc * fo + ai * fi;
       L = L * fo + li * fi;
       m = mn;

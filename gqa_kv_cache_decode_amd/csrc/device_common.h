@@ -37,6 +37,18 @@ __device__ __forceinline__ u32x4 stream_load16(__amdgpu_buffer_rsrc_t v,
   return __builtin_amdgcn_raw_buffer_load_b128(v, off, 0, /*nt*/ 2);
 }
 
+// 16-byte (four fp32) load at byte offset `off` of a buffer view; zeros past
+// the view's end.
+__device__ __forceinline__ f32x4 load4f(__amdgpu_buffer_rsrc_t v, uint32_t off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(v, off, 0, 0));
+}
+
+// The running maximum used as the exponent reference: a state that has seen
+// no finite logit yet (m = -inf) takes 0, so exp2(x - ref) is 0, not NaN.
+__device__ __forceinline__ float exp_ref(float m) {
+  return m == -INFINITY ? 0.0f : m;
+}
+
 __device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }

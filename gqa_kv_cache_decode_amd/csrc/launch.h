@@ -24,6 +24,8 @@ struct PartitionArgs {
   int batch, max_len, num_kv_heads, hpk, dk, dv;
   int chunk_tokens, num_chunks;
   float scale_log2;     // logit scale times log2(e)
+  const float *bias;    // [B][bias_stride] additive logit terms, or NULL
+  long long bias_stride;
   float *part_m;        // [rows][num_chunks]  (natural-log units)
   float *part_l;        // [rows][num_chunks]
   float *part_acc;      // [rows][num_chunks][dv]

@@ -57,7 +57,7 @@ struct Bf16Geom {
   static constexpr int waveLdsElems = kTileTokens * (kStride + vStride);
 };
 
-template <int DK, int DV, int NW, bool STEP>
+template <int DK, int DV, int NW, bool STEP, bool BIAS>
 __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
     PartitionArgs a, StepParams sp) {
   using G = Bf16Geom<DK, DV>;
@@ -149,8 +149,21 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
       Kg + (size_t)t0 * kTok, (uint32_t)(((size_t)last * kTok + DK) * 2));
   const __amdgpu_buffer_rsrc_t vview = buffer_view(
       Vg + (size_t)t0 * vTok, (uint32_t)(((size_t)last * vTok + DV) * 2));
+  // The additive bias of the chunk's live tokens (needle-core attn_bias: one
+  // term per position, shared by the heads); loads past the view return 0.
+  const __amdgpu_buffer_rsrc_t bview =
+      BIAS ? buffer_view(a.bias + (size_t)b * a.bias_stride + t0,
+                         (uint32_t)((t1 - t0) * 4))
+           : buffer_view(nullptr, 0);
   u32x4 kr[G::kLoads], vr[G::vLoads];
+  f32x4 br[2];  // bias of tokens rb*16 + kg*4 + i, i < 4
+  br[0] = br[1] = f32x4{0.f, 0.f, 0.f, 0.f};
   auto issue = [&](int tile) {
+    if (BIAS) {
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+        br[rb] = load4f(bview, (uint32_t)((tile * kTileTokens + rb * 16 + kg * 4) * 4));
+    }
     if (STEP && tile == rel_tile) {
       // the tile holding the new slot: that token (and the clamped tokens
       // after it) come from k_new/v_new, the others from the cache
@@ -208,6 +221,7 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
       const int pc = idx % G::vPieces;
       *reinterpret_cast<u32x4 *>(Vs + (idx / G::vPieces) * G::vStride + pc * 8) = vr[i];
     }
+    const f32x4 bcur[2] = {br[0], br[1]};
     if (tile + NW < ntiles) issue(tile + NW);  // next tile in flight meanwhile
     wave_lds_sync();
 
@@ -232,7 +246,9 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = tb + rb * 16 + kg * 4 + i;
-        const float v = (t < t1) ? sacc[rb][i] * a.scale_log2 : -INFINITY;
+        float v = sacc[rb][i] * a.scale_log2;
+        if (BIAS) v += bcur[rb][i] * kLog2e;
+        v = (t < t1) ? v : -INFINITY;
         x[rb * 4 + i] = v;
         mt = fmaxf(mt, v);
       }
@@ -240,14 +256,15 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
     mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
     const float m_new = fmaxf(m_run, mt);
-    const float alpha = fast_exp2(m_run - m_new);
+    const float ref = exp_ref(m_new);  // -inf only while every key is removed
+    const float alpha = fast_exp2(m_run - ref);
     m_run = m_new;
 
     bf16x8 phi, plo;
     float psum = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float p = fast_exp2(x[j] - m_new);
+      const float p = fast_exp2(x[j] - ref);
       psum += p;
       const __bf16 h = (__bf16)p;
       phi[j] = h;
@@ -303,9 +320,10 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
       if (ntiles > 0) {
 #pragma unroll
         for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, wm[ww * 16 + h]);
+        const float ref = exp_ref(M);
 #pragma unroll
         for (int ww = 0; ww < NW; ++ww) {
-          const float f = fast_exp2(wm[ww * 16 + h] - M);
+          const float f = fast_exp2(wm[ww * 16 + h] - ref);
           acc += f * wacc[(ww * 16 + h) * DV + d];
           L += f * wl[ww * 16 + h];
         }
@@ -354,8 +372,12 @@ hipError_t launch_one(const PartitionArgs &a, const StepParams &sp,
                       hipStream_t s) {
   const int nwork =
       a.sched ? a.sched_len : a.batch * a.num_kv_heads * a.num_chunks;
-  hipLaunchKernelGGL((partition_bf16_kernel<DK, DV, NW, STEP>), dim3(nwork),
-                     dim3(NW * 64), 0, s, a, sp);
+  if (a.bias)
+    hipLaunchKernelGGL((partition_bf16_kernel<DK, DV, NW, STEP, true>),
+                       dim3(nwork), dim3(NW * 64), 0, s, a, sp);
+  else
+    hipLaunchKernelGGL((partition_bf16_kernel<DK, DV, NW, STEP, false>),
+                       dim3(nwork), dim3(NW * 64), 0, s, a, sp);
   return hipGetLastError();
 }
 

@@ -39,7 +39,7 @@ struct F32Geom {
   static constexpr int waveLdsFloats = kF32Tile * (kStride + vStride);
 };
 
-template <int DK, int DV, int NW, bool STEP>
+template <int DK, int DV, int NW, bool STEP, bool BIAS>
 __global__ __launch_bounds__(NW * 64) void partition_f32_mfma_kernel(
     PartitionArgs a, StepParams sp) {
   using G = F32Geom<DK, DV>;
@@ -120,8 +120,16 @@ __global__ __launch_bounds__(NW * 64) void partition_f32_mfma_kernel(
       Kg + (size_t)t0 * kTok, (uint32_t)(((size_t)last * kTok + DK) * 4));
   const __amdgpu_buffer_rsrc_t vview = buffer_view(
       Vg + (size_t)t0 * vTok, (uint32_t)(((size_t)last * vTok + DV) * 4));
+  // additive bias of the chunk's live tokens (loads past the view return 0)
+  const __amdgpu_buffer_rsrc_t bview =
+      BIAS ? buffer_view(a.bias + (size_t)b * a.bias_stride + t0,
+                         (uint32_t)((t1 - t0) * 4))
+           : buffer_view(nullptr, 0);
   u32x4 kr[G::kLoads], vr[G::vLoads];
+  f32x4 br;  // bias of tokens kg*4 + i
+  br = f32x4{0.f, 0.f, 0.f, 0.f};
   auto issue = [&](int tile) {
+    if (BIAS) br = load4f(bview, (uint32_t)((tile * kF32Tile + kg * 4) * 4));
     if (STEP && tile == rel_tile) {
       const float *kb = Kg + (size_t)t0 * kTok, *vb = Vg + (size_t)t0 * vTok;
 #pragma unroll
@@ -176,6 +184,7 @@ __global__ __launch_bounds__(NW * 64) void partition_f32_mfma_kernel(
       const int pc = idx % G::vPieces;
       *reinterpret_cast<u32x4 *>(Vs + (idx / G::vPieces) * G::vStride + pc * 4) = vr[i];
     }
+    const f32x4 bcur = br;
     if (tile + NW < ntiles) issue(tile + NW);
     wave_lds_sync();
 
@@ -194,18 +203,21 @@ __global__ __launch_bounds__(NW * 64) void partition_f32_mfma_kernel(
     float mt = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      x[i] = (tb + kg * 4 + i < t1) ? sacc[i] * a.scale_log2 : -INFINITY;
+      float v = sacc[i] * a.scale_log2;
+      if (BIAS) v += bcur[i] * kLog2e;
+      x[i] = (tb + kg * 4 + i < t1) ? v : -INFINITY;
       mt = fmaxf(mt, x[i]);
     }
     mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
     const float m_new = fmaxf(m_run, mt);
-    const float alpha = fast_exp2(m_run - m_new);
+    const float ref = exp_ref(m_new);  // -inf only while every key is removed
+    const float alpha = fast_exp2(m_run - ref);
     m_run = m_new;
     float p[4], psum = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      p[i] = fast_exp2(x[i] - m_new);
+      p[i] = fast_exp2(x[i] - ref);
       psum += p[i];
     }
     l_run = l_run * alpha + psum;
@@ -249,9 +261,10 @@ __global__ __launch_bounds__(NW * 64) void partition_f32_mfma_kernel(
       if (ntiles > 0) {
 #pragma unroll
         for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, wm[ww * 16 + h]);
+        const float ref = exp_ref(M);
 #pragma unroll
         for (int ww = 0; ww < NW; ++ww) {
-          const float f = fast_exp2(wm[ww * 16 + h] - M);
+          const float f = fast_exp2(wm[ww * 16 + h] - ref);
           acc += f * wacc[(ww * 16 + h) * DV + d];
           L += f * wl[ww * 16 + h];
         }
@@ -299,8 +312,14 @@ hipError_t launch_mfma(const PartitionArgs &a, const StepParams &sp,
                        hipStream_t s) {
   const int nwork =
       a.sched ? a.sched_len : a.batch * a.num_kv_heads * a.num_chunks;
-  hipLaunchKernelGGL((partition_f32_mfma_kernel<DK, DV, kPartitionWaves, STEP>),
-                     dim3(nwork), dim3(kPartitionWaves * 64), 0, s, a, sp);
+  if (a.bias)
+    hipLaunchKernelGGL(
+        (partition_f32_mfma_kernel<DK, DV, kPartitionWaves, STEP, true>),
+        dim3(nwork), dim3(kPartitionWaves * 64), 0, s, a, sp);
+  else
+    hipLaunchKernelGGL(
+        (partition_f32_mfma_kernel<DK, DV, kPartitionWaves, STEP, false>),
+        dim3(nwork), dim3(kPartitionWaves * 64), 0, s, a, sp);
   return hipGetLastError();
 }
 
@@ -366,7 +385,8 @@ __global__ __launch_bounds__(64) void partition_f32_kernel(
     const float *__restrict__ q, const float *__restrict__ K,
     const float *__restrict__ V, const int32_t *__restrict__ lens, int batch,
     int max_len, int Hkv, int hpk, int dk, int dv, int chunk, int nchunk,
-    float scale_log2, float *__restrict__ part_m, float *__restrict__ part_l,
+    float scale_log2, const float *__restrict__ bias, long long bias_stride,
+    float *__restrict__ part_m, float *__restrict__ part_l,
     float *__restrict__ part_acc) {
   extern __shared__ __attribute__((aligned(16))) float smem[];
   const int ks = dk + 1;           // odd stride: column reads hit 64 banks
@@ -419,13 +439,16 @@ __global__ __launch_bounds__(64) void partition_f32_kernel(
         if (h < hpk) s[h] = fmaf(Qs[h * dk + cc], kv, s[h]);
     }
     const bool live = tb + lane < t1;
+    const float bl =
+        (live && bias) ? bias[(size_t)b * bias_stride + tb + lane] * kLog2e : 0.0f;
 #pragma unroll
     for (int h = 0; h < kMaxHeads; ++h) {
       if (h < hpk) {
-        const float x = live ? s[h] * scale_log2 : -INFINITY;
+        const float x = live ? s[h] * scale_log2 + bl : -INFINITY;
         const float m_new = fmaxf(m[h], wave_max(x));
-        const float alpha = fast_exp2(m[h] - m_new);
-        const float p = fast_exp2(x - m_new);
+        const float ref = exp_ref(m_new);
+        const float alpha = fast_exp2(m[h] - ref);
+        const float p = fast_exp2(x - ref);
         l[h] = l[h] * alpha + wave_sum(p);
         m[h] = m_new;
         Ps[h * kTok + lane] = p;
@@ -505,7 +528,8 @@ hipError_t launch_partition_f32(const PartitionArgs &a, const StepParams &ep,
                      static_cast<const float *>(a.k),
                      static_cast<const float *>(a.v), a.lens, a.batch,
                      a.max_len, a.num_kv_heads, a.hpk, a.dk, a.dv,
-                     a.chunk_tokens, a.num_chunks, a.scale_log2, a.part_m,
+                     a.chunk_tokens, a.num_chunks, a.scale_log2, a.bias,
+                     a.bias_stride, a.part_m,
                      a.part_l, a.part_acc);
   return hipGetLastError();
 }

@@ -162,8 +162,8 @@ __device__ __forceinline__ void fold_group(const PartitionArgs &a,
 #pragma unroll 4
     for (int i = 0; i < nc; ++i) {
       const float mi = coherent_load(pm + i) * kLog2e;
-      const float mn = fmaxf(m, mi);
-      const float fo = fast_exp2(m - mn), fi = fast_exp2(mi - mn);
+      const float mn = fmaxf(m, mi), ref = exp_ref(mn);
+      const float fo = fast_exp2(m - ref), fi = fast_exp2(mi - ref);
       acc = acc * fo + coherent_load(pa + (size_t)i * a.dv) * fi;
       L = L * fo + coherent_load(pl + i) * fi;
       m = mn;

@@ -169,6 +169,13 @@ GQA_API size_t gqa_attend_workspace_bytes(const gqa_cache *cache, int32_t num_q_
  *         asks for the derived scale, by convention one over the square root
  *         of the head width).
  *         Must be finite.
+ *   bias  NULL, or additive logit terms (needle-core self_attn_incremental,
+ *         attn_bias: one term per cached position, added to the scaled dot
+ *         product of every head): fp32, bias[b * bias_stride + t] for key t of
+ *         sequence b.  bias_stride >= max_len and a multiple of 4; bias 16-byte
+ *         aligned.  A term of -inf removes the key; a row whose keys are all
+ *         removed is empty (out 0, carry (-inf, 0, 0), or carry_in).  Terms
+ *         must not be NaN or +inf.  Ignored (with bias_stride) when NULL.
  *   carry_in   NULL, or a carry over the same query rows folded into this
  *              branch (usearch carry: one call continues another over the
  *              same queries, e.g. a recent-window branch).
@@ -177,11 +184,14 @@ GQA_API size_t gqa_attend_workspace_bytes(const gqa_cache *cache, int32_t num_q_
  *         divided by the partition; rows with no keys at all get 0.
  *   At least one of out / carry_out must be given.
  *   workspace  device buffer of at least gqa_attend_workspace_bytes().
- * Enqueues the split-K partition kernel and the log-sum-exp combine kernel.
+ * Enqueues the split-K partition kernel (preceded by the schedule kernel for
+ * a plan with sched_entries > 0) and the log-sum-exp combine kernel; a plan
+ * with a single chunk writes out and carry_out from the partition launch.
  */
 GQA_API gqa_status gqa_attend_decode(const void *q, int32_t num_q_heads,
                              const gqa_cache *cache, const int32_t *lens,
-                             float scale, const gqa_carry *carry_in,
+                             float scale, const float *bias,
+                             int64_t bias_stride, const gqa_carry *carry_in,
                              const gqa_carry *carry_out, float *out,
                              void *workspace, size_t workspace_bytes,
                              hipStream_t stream);
@@ -193,7 +203,8 @@ GQA_API gqa_status gqa_attend_decode(const void *q, int32_t num_q_heads,
  */
 GQA_API gqa_status gqa_attend_partition(const void *q, int32_t num_q_heads,
                                 const gqa_cache *cache, const int32_t *lens,
-                                float scale, const gqa_plan *plan,
+                                float scale, const float *bias,
+                                int64_t bias_stride, const gqa_plan *plan,
                                 void *workspace, size_t workspace_bytes,
                                 hipStream_t stream);
 
@@ -221,7 +232,8 @@ GQA_API gqa_status gqa_attend_combine(int32_t num_q_heads, const gqa_cache *cach
  *   was written.
  *   lens_out must NOT alias lens_in (every work-group reads lens_in during the
  *   call); alternate two length arrays between steps.
- *   q, scale, carry_in, carry_out, out: as in gqa_attend_decode.
+ *   q, scale, bias, carry_in, carry_out, out: as in gqa_attend_decode (the
+ *   bias row covers the new token's position too).
  *   workspace: at least gqa_decode_step_workspace_bytes() bytes, ZERO-FILLED
  *   before its first use.  Its tail holds per-(sequence, KV group) arrival
  *   counters that every completed call leaves at zero again; calls that
@@ -234,7 +246,9 @@ GQA_API gqa_status gqa_decode_step(const void *q, int32_t num_q_heads,
                                    const gqa_cache *cache, const void *k_new,
                                    const void *v_new, const int32_t *lens_in,
                                    int32_t *lens_out, int32_t *dropped,
-                                   float scale, const gqa_carry *carry_in,
+                                   float scale, const float *bias,
+                                   int64_t bias_stride,
+                                   const gqa_carry *carry_in,
                                    const gqa_carry *carry_out, float *out,
                                    void *workspace, size_t workspace_bytes,
                                    hipStream_t stream);

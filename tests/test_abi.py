@@ -99,49 +99,62 @@ def test_attend_rejects_before_launch(lib):
     q, lens, ws, out = (ctypes.c_void_p(x) for x in
                         (0x30000, 0x40000, 0x50000, 0x60000))
     nbytes = p.workspace_bytes
-    f = lib.gqa_attend_decode
     carry = bd._Carry(0x70000, 0x80000, 0x90000)
+
+    def f(q_, hq_, c_, lens_, scale, cin, cout, out_, ws_, nbytes_, bias=None,
+          stride=0):
+        return lib.gqa_attend_decode(q_, hq_, ctypes.byref(c_), lens_, scale,
+                                     bias, stride, cin, cout, out_, ws_,
+                                     nbytes_, None)
+
     # null q, null lens
-    assert f(None, hq, ctypes.byref(c), lens, 0.0, None, None, out, ws, nbytes,
-             None) == INVALID
-    assert f(q, hq, ctypes.byref(c), None, 0.0, None, None, out, ws, nbytes,
-             None) == INVALID
+    assert f(None, hq, c, lens, 0.0, None, None, out, ws, nbytes) == INVALID
+    assert f(q, hq, c, None, 0.0, None, None, out, ws, nbytes) == INVALID
     # neither out nor carry_out
-    assert f(q, hq, ctypes.byref(c), lens, 0.0, None, None, None, ws, nbytes,
-             None) == INVALID
+    assert f(q, hq, c, lens, 0.0, None, None, None, ws, nbytes) == INVALID
     # non-finite scale
     for s in (float("nan"), float("inf")):
-        assert f(q, hq, ctypes.byref(c), lens, s, None, None, out, ws, nbytes,
-                 None) == INVALID
+        assert f(q, hq, c, lens, s, None, None, out, ws, nbytes) == INVALID
     # misaligned q
-    assert f(ctypes.c_void_p(0x30002), hq, ctypes.byref(c), lens, 0.0, None,
-             None, out, ws, nbytes, None) == INVALID
+    assert f(ctypes.c_void_p(0x30002), hq, c, lens, 0.0, None, None, out, ws,
+             nbytes) == INVALID
     # workspace too small
-    assert f(q, hq, ctypes.byref(c), lens, 0.0, None, None, out, ws,
-             nbytes - 1, None) == WORKSPACE
+    assert f(q, hq, c, lens, 0.0, None, None, out, ws, nbytes - 1) == WORKSPACE
     # a carry with a null member
     bad = bd._Carry(0x70000, None, 0x90000)
-    assert f(q, hq, ctypes.byref(c), lens, 0.0, ctypes.byref(bad), None, out,
-             ws, nbytes, None) == INVALID
-    assert f(q, 30, ctypes.byref(c), lens, 0.0, ctypes.byref(carry), None,
-             out, ws, nbytes, None) == SHAPE
+    assert f(q, hq, c, lens, 0.0, ctypes.byref(bad), None, out, ws,
+             nbytes) == INVALID
+    assert f(q, 30, c, lens, 0.0, ctypes.byref(carry), None, out, ws,
+             nbytes) == SHAPE
+    # the additive bias: short rows, a row stride not a multiple of 4, a
+    # misaligned pointer; a well-formed one passes the checks (it is the
+    # workspace size that is then wrong here)
+    bias = ctypes.c_void_p(0xA0000)
+    for ptr, stride in ((bias, c.max_len - 4), (bias, c.max_len + 2),
+                        (ctypes.c_void_p(0xA0004), c.max_len)):
+        assert f(q, hq, c, lens, 0.0, None, None, out, ws, nbytes, ptr,
+                 stride) == INVALID
+    assert f(q, hq, c, lens, 0.0, None, None, out, ws, nbytes - 1, bias,
+             c.max_len) == WORKSPACE
     # null cache data
     c0 = _cache(k=0)
-    assert f(q, hq, ctypes.byref(c0), lens, 0.0, None, None, out, ws, nbytes,
-             None) == INVALID
+    assert f(q, hq, c0, lens, 0.0, None, None, out, ws, nbytes) == INVALID
 
 
 def test_partition_combine_plan_checks(lib):
     c = _cache()
     _, p = _plan(lib, c, 32)
     q, lens, ws = (ctypes.c_void_p(x) for x in (0x30000, 0x40000, 0x50000))
-    bad = bd.Plan(p.chunk_tokens, p.num_chunks + 1, p.off_l, p.off_acc,
-                  p.workspace_bytes)
-    assert lib.gqa_attend_partition(q, 32, ctypes.byref(c), lens, 0.0,
-                                    ctypes.byref(bad), ws, p.workspace_bytes,
-                                    None) == SHAPE
+    bad = bd.Plan(chunk_tokens=p.chunk_tokens, num_chunks=p.num_chunks + 1,
+                  off_l=p.off_l, off_acc=p.off_acc, off_sched=p.off_sched,
+                  sched_entries=p.sched_entries,
+                  workspace_bytes=p.workspace_bytes)
     assert lib.gqa_attend_partition(q, 32, ctypes.byref(c), lens, 0.0, None,
-                                    ws, p.workspace_bytes, None) == INVALID
+                                    0, ctypes.byref(bad), ws,
+                                    p.workspace_bytes, None) == SHAPE
+    assert lib.gqa_attend_partition(q, 32, ctypes.byref(c), lens, 0.0, None,
+                                    0, None, ws, p.workspace_bytes,
+                                    None) == INVALID
     assert lib.gqa_attend_combine(32, ctypes.byref(c), lens, ctypes.byref(p),
                                   ws, p.workspace_bytes, None, None, None,
                                   None) == INVALID
