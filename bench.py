@@ -62,6 +62,9 @@ def parse_args():
                    help="budget of the oracle's CPU-baseline timing")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-ceiling", action="store_true")
+    p.add_argument("--bias", action="store_true",
+                   help="attend with an additive logit bias (fp32 per "
+                        "sequence and position, N(0, 1))")
     p.add_argument("--profile-pass", action="store_true",
                    help="no timing: a few eager partition launches and three "
                         f"{COPY_BYTES >> 20} MiB calibration copies, for "
@@ -83,8 +86,16 @@ def kv_bytes(w, lens_total, hkv=None):
 class Branch:
     """One attend branch: R cache copies, lens before/after the append."""
 
-    def __init__(self, g, torch, w, k, v, lens_after, copies, append):
+    def __init__(self, g, torch, w, k, v, lens_after, copies, append,
+                 bias=False, seed=0):
         self.w = w
+        # optional additive bias, one fp32 term per (sequence, position)
+        self.bias = None
+        if bias:
+            gen = torch.Generator().manual_seed(seed)
+            pad = (k.shape[1] + 3) // 4 * 4
+            self.bias = torch.randn(k.shape[0], pad, generator=gen).to(
+                k.device)
         self.k = [k] + [k.clone() for _ in range(copies - 1)]
         self.v = [v] + [v.clone() for _ in range(copies - 1)]
         self.append = append
@@ -130,13 +141,16 @@ def main():
     if w.window:
         # the long cache is attended as is; the new token enters the window
         branches.append(Branch(g, torch, w, x["k"].to(dev), x["v"].to(dev),
-                               x["lens"].to(dev), copies, append=False))
+                               x["lens"].to(dev), copies, append=False,
+                               bias=args.bias, seed=w.seed + 2000))
         branches.append(Branch(g, torch, w, x["wk"].to(dev), x["wv"].to(dev),
-                               x["wlens"].to(dev), copies, append=True))
+                               x["wlens"].to(dev), copies, append=True,
+                               bias=args.bias, seed=w.seed + 2001))
         carry = g.empty_carry(B * Hq, w.dv)
     else:
         branches.append(Branch(g, torch, w, x["k"].to(dev), x["v"].to(dev),
-                               x["lens"].to(dev), copies, append=True))
+                               x["lens"].to(dev), copies, append=True,
+                               bias=args.bias, seed=w.seed + 2000))
         carry = None
     del x
     torch.cuda.synchronize()
@@ -157,10 +171,10 @@ def main():
                 g.decode_step(q, br.k[r], br.v[r], k_new, v_new,
                               br.lens_before, br.lens_cur[r], w.scale,
                               carry_in=cin, carry_out=cout, out=o,
-                              workspace=br.ws)
+                              workspace=br.ws, bias=br.bias)
             else:
                 g.attend_partition(q, br.k[r], br.v[r], br.lens_cur[r],
-                                   br.plan, br.ws, w.scale)
+                                   br.plan, br.ws, w.scale, bias=br.bias)
                 g.attend_combine(Hq, br.k[r], br.v[r], br.lens_cur[r],
                                  br.plan, br.ws, carry_in=cin,
                                  carry_out=cout, out=o)
@@ -169,7 +183,7 @@ def main():
 
     def partition_only(r):
         g.attend_partition(q, dom.k[r], dom.v[r], dom.lens_cur[r], dom.plan,
-                           dom.ws, w.scale)
+                           dom.ws, w.scale, bias=dom.bias)
 
     if args.profile_pass:
         profile_pass(torch, step, partition_only, copies, w, dom)
@@ -243,12 +257,14 @@ def main():
     out_bytes = B * Hq * w.dv * 4
     carry_bytes = B * Hq * (w.dv + 2) * 4
     step_bytes = 0
+    # a bias term counts once per attended (sequence, position)
+    bias_bytes = (lambda br: 4 * br.n_tot if br.bias is not None else 0)
     for i, br in enumerate(branches):
-        step_bytes += kv_bytes(w, br.n_tot) + q_bytes
+        step_bytes += kv_bytes(w, br.n_tot) + q_bytes + bias_bytes(br)
         if br.append:
             step_bytes += 2 * B * Hkv * (w.dk + w.dv) * w.esz + 2 * B * 4
     step_bytes += out_bytes + (2 * carry_bytes if len(branches) > 1 else 0)
-    part_bytes = kv_bytes(w, dom.n_tot) + q_bytes
+    part_bytes = kv_bytes(w, dom.n_tot) + q_bytes + bias_bytes(dom)
     value = step_bytes / (ms_step * 1e-3) / 1e9
     achieved = part_bytes / (ms_part * 1e-3) / 1e9
     log(f"[bench] step {ms_step * 1e3:.2f} us (graph), eager {ms_eager * 1e3:.1f}"
@@ -260,11 +276,11 @@ def main():
         ceiling = read_ceiling(torch)
         log(f"[bench] pure-read stream ceiling: {ceiling:.1f} GB/s")
 
-    traffic = measured_traffic(args.workload, w.dtype)
+    traffic = measured_traffic(profile_name(args), w.dtype)
     waves = (4 if w.dk + w.dv <= 256 else 2) if w.dtype == "bf16" else 2
-    kernel = (f"partition_bf16_kernel<{w.dk}, {w.dv}, {waves}, false>"
-              if w.dtype == "bf16" else
-              f"partition_f32_mfma_kernel<{w.dk}, {w.dv}, {waves}, false>")
+    tmpl = f"{w.dk}, {w.dv}, {waves}, false, {'true' if args.bias else 'false'}"
+    kernel = (f"partition_bf16_kernel<{tmpl}>" if w.dtype == "bf16" else
+              f"partition_f32_mfma_kernel<{tmpl}>")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -289,6 +305,7 @@ def main():
                    "num_kv_heads": Hkv, "dk": w.dk, "dv": w.dv,
                    "seq_len": w.max_len, "window": w.window,
                    "kv_dtype": w.dtype, "rotating_cache_copies": copies,
+                   "additive_bias": bool(args.bias),
                    "timing": "HIP graph of K steps"},
         "us_per_step": round(ms_step * 1e3, 2),
         "hbm_frac_per_step": round(value / HBM_PEAK_GBS, 4),
@@ -351,6 +368,11 @@ def partition_source_hash(dtype):
     return h.hexdigest()[:16]
 
 
+def profile_name(args):
+    """Name of the workload's counter readings under profiles/."""
+    return args.workload + ("_bias" if args.bias else "")
+
+
 def measured_traffic(workload, dtype):
     """HBM bytes per partition launch from committed counter readings, if they
     were taken on the current kernel sources (else None)."""
@@ -381,9 +403,10 @@ def profile_pass(torch, step, partition_only, copies, w, dom):
                                   256 * 16, stream) == 0
     torch.cuda.synchronize()
     q_bytes = w.batch * w.num_q_heads * w.dk * w.esz
+    b_bytes = 4 * dom.n_tot if dom.bias is not None else 0
     print(json.dumps({"profile_pass": w.name,
                       "partition_algorithmic_bytes": kv_bytes(w, dom.n_tot) +
-                      q_bytes, "copy_bytes": COPY_BYTES,
+                      q_bytes + b_bytes, "copy_bytes": COPY_BYTES,
                       "source_sha256_16": partition_source_hash(w.dtype)}),
           flush=True)
 
