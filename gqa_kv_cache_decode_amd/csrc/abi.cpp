@@ -188,6 +188,14 @@ gqa_status device_status(hipError_t e) {
   return e == hipSuccess ? GQA_OK : GQA_ERR_DEVICE;
 }
 
+// The partial layout and work items of a one-cache launch.
+void single_branch(PartitionArgs *a) {
+  a->total_cols = a->num_chunks;
+  a->col_base = 0;
+  a->total_items = a->batch * a->num_kv_heads * a->num_chunks;
+  a->num_extra = 0;
+}
+
 // Enqueues the schedule kernel of a scheduled plan and points the partition
 // launch at its table (a no-op for an unscheduled plan).
 gqa_status schedule_checked(const gqa_cache *c, const gqa_plan &plan,
@@ -250,6 +258,7 @@ gqa_status partition_checked(const void *q, int32_t hq, const gqa_cache *c,
   a.dv = c->dv;
   a.chunk_tokens = plan->chunk_tokens;
   a.num_chunks = plan->num_chunks;
+  single_branch(&a);
   a.scale_log2 = (float)(sc * 1.4426950408889634);
   a.bias = bias;
   a.bias_stride = bias ? bias_stride : 0;
@@ -269,13 +278,12 @@ gqa_status combine_checked(int32_t hq, const gqa_cache *c, const int32_t *lens,
                            const gqa_carry *cin, const gqa_carry *cout,
                            float *out, hipStream_t s) {
   CombineArgs a;
-  a.lens = lens;
   a.batch = c->batch;
   a.num_q_heads = hq;
-  a.max_len = c->max_len;
   a.dv = c->dv;
-  a.chunk_tokens = plan->chunk_tokens;
-  a.num_chunks = plan->num_chunks;
+  a.total_cols = plan->num_chunks;
+  a.num_branches = 1;
+  a.br[0] = gqa::CombineBranch{lens, c->max_len, plan->chunk_tokens, 0};
   const char *base = static_cast<const char *>(ws);
   a.part_m = reinterpret_cast<const float *>(base);
   a.part_l = reinterpret_cast<const float *>(base + plan->off_l);
@@ -536,6 +544,7 @@ gqa_status gqa_decode_step(const void *q, int32_t num_q_heads,
   a.dv = cache->dv;
   a.chunk_tokens = plan.chunk_tokens;
   a.num_chunks = plan.num_chunks;
+  single_branch(&a);
   a.scale_log2 = (float)(sc * 1.4426950408889634);
   a.bias = bias;
   a.bias_stride = bias ? bias_stride : 0;

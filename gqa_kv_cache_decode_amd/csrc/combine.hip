@@ -39,25 +39,29 @@ __global__ __launch_bounds__(THREADS) void combine_kernel(CombineArgs a) {
   const float in_acc =
       (has_in && worker) ? a.in_acc[(size_t)row * a.dv + col] : 0.0f;
 
-  const int n = clamp_len(a.lens[b], a.max_len);
-  const int nc = (n + a.chunk_tokens - 1) / a.chunk_tokens;
-  const float *pm = a.part_m + (size_t)row * a.num_chunks;
-  const float *pl = a.part_l + (size_t)row * a.num_chunks;
-  const float *pa = a.part_acc + (size_t)row * a.num_chunks * a.dv;
+  const float *pm = a.part_m + (size_t)row * a.total_cols;
+  const float *pl = a.part_l + (size_t)row * a.total_cols;
+  const float *pa = a.part_acc + (size_t)row * a.total_cols * a.dv;
 
   float m = -INFINITY, L = 0.0f, acc = 0.0f;  // base-2 running state
   if (worker) {
+    // every branch's live chunks: columns col_base .. col_base + nc - 1
+    for (int br = 0; br < a.num_branches; ++br) {
+      const CombineBranch &x = a.br[br];
+      const int n = clamp_len(x.lens[b], x.max_len);
+      const int nc = (n + x.chunk_tokens - 1) / x.chunk_tokens;
 #pragma unroll 4
-    for (int i = slice; i < nc; i += nslice) {
-      const float mi = pm[i] * kLog2e;
-      const float li = pl[i];
-      const float ai = pa[(size_t)i * a.dv + col];
-      // a chunk whose keys were all removed by the bias has m = -inf, l = 0
-      const float mn = fmaxf(m, mi), ref = exp_ref(mn);
-      const float fo = fast_exp2(m - ref), fi = fast_exp2(mi - ref);
-      acc = acc * fo + ai * fi;
-      L = L * fo + li * fi;
-      m = mn;
+      for (int i = x.col_base + slice; i < x.col_base + nc; i += nslice) {
+        const float mi = pm[i] * kLog2e;
+        const float li = pl[i];
+        const float ai = pa[(size_t)i * a.dv + col];
+        // a chunk whose keys were all removed by the bias has m = -inf, l = 0
+        const float mn = fmaxf(m, mi), ref = exp_ref(mn);
+        const float fo = fast_exp2(m - ref), fi = fast_exp2(mi - ref);
+        acc = acc * fo + ai * fi;
+        L = L * fo + li * fi;
+        m = mn;
+      }
     }
   }
   sm[threadIdx.x] = m;
@@ -122,7 +126,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s) {
   const int rows = a.batch * a.num_q_heads;
-  if (a.num_chunks >= 32)
+  if (a.total_cols >= 32)
     hipLaunchKernelGGL(combine_kernel<1024>, dim3(rows), dim3(1024), 0, s, a);
   else
     hipLaunchKernelGGL(combine_kernel<256>, dim3(rows), dim3(256), 0, s, a);

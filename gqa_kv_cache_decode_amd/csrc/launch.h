@@ -16,6 +16,21 @@ constexpr int kPartitionWaves = 2;
 // leave one four-wavefront work-group per compute unit).
 constexpr int partition_waves(int dk, int dv) { return dk + dv <= 256 ? 4 : 2; }
 
+// A further cache attended by the same launch (multi-branch attention: the
+// branches' partials share one partial row per query row and one combine).
+// Every branch has the launch's batch, heads and head widths.
+struct ExtraBranch {
+  const void *k, *v;
+  const int32_t *lens;
+  const float *bias;
+  long long bias_stride;
+  int max_len, chunk_tokens, num_chunks;
+  int col_base;   // first partial column of the branch
+  int item_base;  // first work item of the branch
+};
+
+constexpr int kMaxExtraBranches = 3;
+
 struct PartitionArgs {
   const void *q;        // [B][Hkv*hpk][dk]
   const void *k;        // [B][max_len][Hkv][dk]
@@ -23,6 +38,12 @@ struct PartitionArgs {
   const int32_t *lens;  // [B]
   int batch, max_len, num_kv_heads, hpk, dk, dv;
   int chunk_tokens, num_chunks;
+  // Partial layout and work items over all branches of the launch: a single
+  // branch has total_cols = num_chunks, col_base = 0 and total_items =
+  // batch * num_kv_heads * num_chunks.
+  int total_cols, col_base, total_items;
+  int num_extra;        // branches after the first, 0..kMaxExtraBranches
+  ExtraBranch extra[kMaxExtraBranches];
   float scale_log2;     // logit scale times log2(e)
   const float *bias;    // [B][bias_stride] additive logit terms, or NULL
   long long bias_stride;
@@ -63,9 +84,17 @@ struct StepParams {
   int direct;               // num_chunks == 1: write final results directly
 };
 
-struct CombineArgs {
+// One branch's partial columns for the combine kernel.
+struct CombineBranch {
   const int32_t *lens;
-  int batch, num_q_heads, max_len, dv, chunk_tokens, num_chunks;
+  int max_len, chunk_tokens, col_base;
+};
+
+struct CombineArgs {
+  int batch, num_q_heads, dv;
+  int total_cols;  // partial columns per query row
+  int num_branches;
+  CombineBranch br[1 + kMaxExtraBranches];
   const float *part_m, *part_l, *part_acc;
   const float *in_m, *in_l, *in_acc;   // carry_in, all NULL if absent
   float *out_m, *out_l, *out_acc;      // carry_out, all NULL if absent

@@ -59,7 +59,7 @@ struct Bf16Geom {
 
 template <int DK, int DV, int NW, bool STEP, bool BIAS>
 __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
-    PartitionArgs a, StepParams sp) {
+    PartitionArgs args, StepParams sp) {
   using G = Bf16Geom<DK, DV>;
   constexpr int kMergeFloats = NW * 16 * (DV + 2);
   constexpr int kTileBytes = NW * G::waveLdsElems * 2;
@@ -69,14 +69,16 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
   __shared__ int s_flag;
   __shared__ float s_in[32];  // carry_in m, l of the group's rows (direct)
 
-  const int Hkv = a.num_kv_heads, hpk = a.hpk, nchunk = a.num_chunks;
+  PartitionArgs a = args;
   int item;
   if (a.sched) {  // scheduled launch: the table entry, or nothing to do
     item = a.sched[blockIdx.x];
     if (item < 0) return;
   } else {
-    item = xcd_local_item(blockIdx.x, a.batch * Hkv * nchunk);
+    item = xcd_local_item(blockIdx.x, a.total_items);
   }
+  select_branch(a, item);  // multi-branch launch: the item's cache
+  const int Hkv = a.num_kv_heads, hpk = a.hpk, nchunk = a.num_chunks;
   const int c = item % nchunk;
   const int bg = item / nchunk;
   const int g = bg % Hkv;
@@ -152,9 +154,9 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
   // The additive bias of the chunk's live tokens (needle-core attn_bias: one
   // term per position, shared by the heads); loads past the view return 0.
   const __amdgpu_buffer_rsrc_t bview =
-      BIAS ? buffer_view(a.bias + (size_t)b * a.bias_stride + t0,
+      BIAS && a.bias ? buffer_view(a.bias + (size_t)b * a.bias_stride + t0,
                          (uint32_t)((t1 - t0) * 4))
-           : buffer_view(nullptr, 0);
+                     : buffer_view(nullptr, 0);
   u32x4 kr[G::kLoads], vr[G::vLoads];
   f32x4 br[2];  // bias of tokens rb*16 + kg*4 + i, i < 4
   br[0] = br[1] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -336,9 +338,10 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
         write_final(sp, row, DV, d, M, L, acc);
         continue;
       }
-      float *pa = a.part_acc + (row * nchunk + c) * DV + d;
-      float *pm = a.part_m + row * nchunk + c;
-      float *pl = a.part_l + row * nchunk + c;
+      const size_t col = row * a.total_cols + a.col_base + c;
+      float *pa = a.part_acc + col * DV + d;
+      float *pm = a.part_m + col;
+      float *pl = a.part_l + col;
       if (STEP && sp.fuse) {  // read back by this launch's last work-group
         coherent_store(pa, acc);
         if (d == 0) {
@@ -370,8 +373,7 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
 template <int DK, int DV, int NW, bool STEP>
 hipError_t launch_one(const PartitionArgs &a, const StepParams &sp,
                       hipStream_t s) {
-  const int nwork =
-      a.sched ? a.sched_len : a.batch * a.num_kv_heads * a.num_chunks;
+  const int nwork = a.sched ? a.sched_len : a.total_items;
   if (a.bias)
     hipLaunchKernelGGL((partition_bf16_kernel<DK, DV, NW, STEP, true>),
                        dim3(nwork), dim3(NW * 64), 0, s, a, sp);

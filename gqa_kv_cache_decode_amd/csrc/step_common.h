@@ -13,6 +13,29 @@ namespace gqa {
 // vector memory access of the wavefront, stores included, has completed.
 constexpr int kWaitVmcnt0 = 0x0F70;
 
+// Points `a` at the branch that owns work item `item` of a multi-branch
+// launch (branches hold ascending item ranges) and makes `item` local to it.
+__device__ __forceinline__ void select_branch(PartitionArgs &a, int &item) {
+  int base = 0;
+#pragma unroll
+  for (int e = 0; e < kMaxExtraBranches; ++e) {
+    if (e < a.num_extra && item >= a.extra[e].item_base) {
+      const ExtraBranch &x = a.extra[e];
+      a.k = x.k;
+      a.v = x.v;
+      a.lens = x.lens;
+      a.bias = x.bias;
+      a.bias_stride = x.bias_stride;
+      a.max_len = x.max_len;
+      a.chunk_tokens = x.chunk_tokens;
+      a.num_chunks = x.num_chunks;
+      a.col_base = x.col_base;
+      base = x.item_base;
+    }
+  }
+  item -= base;
+}
+
 // Keys attended by sequence b, and the slot a decode step appends to.
 struct SeqLen {
   int n;      // keys attended: [0, n)
@@ -151,9 +174,9 @@ __device__ __forceinline__ void fold_group(const PartitionArgs &a,
   for (int e = threadIdx.x; e < a.hpk * a.dv; e += blockDim.x) {
     const int h = e / a.dv, d = e % a.dv;
     const size_t row = row0 + h;
-    const float *pm = a.part_m + row * a.num_chunks;
-    const float *pl = a.part_l + row * a.num_chunks;
-    const float *pa = a.part_acc + row * a.num_chunks * a.dv + d;
+    const float *pm = a.part_m + row * a.total_cols;
+    const float *pl = a.part_l + row * a.total_cols;
+    const float *pa = a.part_acc + row * a.total_cols * a.dv + d;
     float m = lds[h], L = 0.0f, acc = 0.0f;
     if (lds[a.hpk + h] > 0.0f) {
       L = lds[a.hpk + h];
