@@ -37,6 +37,11 @@ class _Carry(ctypes.Structure):
                 ("acc", ctypes.c_void_p)]
 
 
+class _Branch(ctypes.Structure):
+    _fields_ = [("cache", _Cache), ("lens", ctypes.c_void_p),
+                ("bias", ctypes.c_void_p), ("bias_stride", ctypes.c_int64)]
+
+
 class Plan(ctypes.Structure):
     """gqa_plan: split-K chunking and workspace layout of one attend call."""
 
@@ -54,7 +59,14 @@ _CACHE_P = ctypes.POINTER(_Cache)
 _CARRY_P = ctypes.POINTER(_Carry)
 _PLAN_P = ctypes.POINTER(Plan)
 
+_BRANCH_P = ctypes.POINTER(_Branch)
+
 _SIGNATURES = {
+    "gqa_attend_branches_workspace_bytes": (ctypes.c_size_t,
+                                            [_BRANCH_P, _I32, _I32]),
+    "gqa_attend_branches": (_I32, [_P, _I32, _BRANCH_P, _I32, ctypes.c_float,
+                                   _CARRY_P, _CARRY_P, _P, _P,
+                                   ctypes.c_size_t, _P]),
     "gqa_abi_version": (_I32, []),
     "gqa_status_string": (ctypes.c_char_p, [_I32]),
     "gqa_kv_append": (_I32, [_CACHE_P, _P, _P, _P, _P, _P, _P]),
@@ -353,3 +365,46 @@ def softmax_state_merge(a: Carry, b: Carry, dst: Optional[Carry] = None,
         ctypes.byref(sa), ctypes.byref(sb), ctypes.byref(sd), rows, dv,
         _ptr(out), _stream(a.m)), "softmax_state_merge")
     return dst
+
+
+def _branches(branches, q):
+    """ctypes array of gqa_branch from (k, v, lens[, bias]) tuples."""
+    if not 1 <= len(branches) <= 4:
+        raise GqaError("attend_branches takes 1 to 4 branches")
+    arr = (_Branch * len(branches))()
+    for i, br in enumerate(branches):
+        k, v, lens = br[:3]
+        bias = br[3] if len(br) > 3 else None
+        c = _cache(k, v)
+        _need(lens, f"branch {i} lens", torch.int32, (c.batch,))
+        bp, bs = _bias(c, bias)
+        arr[i] = _Branch(c, lens.data_ptr(), bp, bs)
+    return arr
+
+
+def attend_branches(q, branches, scale: float = 0.0,
+                    carry_in: Optional[Carry] = None,
+                    carry_out: Optional[Carry] = None, out=_AUTO,
+                    workspace: Optional[torch.Tensor] = None):
+    """Attention of q over the union of several caches' live keys, one
+    partition launch and one combine.  ``branches``: a list of
+    (k_cache, v_cache, lens) or (k_cache, v_cache, lens, bias) tuples with the
+    same batch, KV heads, head widths and dtype."""
+    arr = _branches(branches, q)
+    k0 = branches[0][0]
+    c0, hq = _attend_args(q, k0, branches[0][1], branches[0][2])
+    if out is _AUTO:
+        out = torch.empty(c0.batch, hq, c0.dv, dtype=torch.float32,
+                          device=q.device)
+    cin, cout = _carries(c0, hq, carry_in, carry_out, out)
+    need = library().gqa_attend_branches_workspace_bytes(arr, len(arr), hq)
+    if need == 0:
+        raise GqaError("attend_branches: invalid or unsupported branches")
+    if workspace is None:
+        workspace = _workspace(need, q.device)
+    _need(workspace, "workspace")
+    _check(library().gqa_attend_branches(
+        _ptr(q), hq, arr, len(arr), float(scale), cin, cout, _ptr(out),
+        _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(q)), "attend_branches")
+    return out

@@ -262,6 +262,7 @@ gqa_status partition_checked(const void *q, int32_t hq, const gqa_cache *c,
   a.scale_log2 = (float)(sc * 1.4426950408889634);
   a.bias = bias;
   a.bias_stride = bias ? bias_stride : 0;
+  a.has_bias = bias ? 1 : 0;
   char *base = static_cast<char *>(ws);
   a.part_m = reinterpret_cast<float *>(base);
   a.part_l = reinterpret_cast<float *>(base + plan->off_l);
@@ -342,6 +343,56 @@ bool step_fuses(const gqa_cache *c, int32_t hq, const gqa_plan &plan) {
   const int64_t groups = (int64_t)c->batch * c->num_kv_heads * plan.num_chunks;
   return groups <= kFuseMaxGroups &&
          hpk * plan.num_chunks * (c->dv + 2) * sizeof(float) <= kFuseBytes;
+}
+
+// Chunking and workspace layout of a multi-branch attend: per-branch chunk
+// lengths (each branch's own plan rule), the partial columns of all
+// branches, and the partial arrays' offsets.
+struct BranchesPlan {
+  int32_t chunk[GQA_MAX_BRANCHES];
+  int32_t num_chunks[GQA_MAX_BRANCHES];
+  int32_t col_base[GQA_MAX_BRANCHES];
+  int64_t item_base[GQA_MAX_BRANCHES];
+  int32_t total_cols;
+  int64_t total_items;
+  size_t off_l, off_acc, workspace_bytes;
+};
+
+gqa_status plan_branches(const gqa_branch *br, int32_t n, int32_t hq,
+                         BranchesPlan *p) {
+  if (!br || n < 1 || n > GQA_MAX_BRANCHES) return GQA_ERR_INVALID_ARGUMENT;
+  int64_t cols = 0, items = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const gqa_cache *c = &br[i].cache;
+    gqa_status st = check_cache_dims(c);
+    if (st != GQA_OK) return st;
+    const gqa_cache *c0 = &br[0].cache;
+    if (c->batch != c0->batch || c->num_kv_heads != c0->num_kv_heads ||
+        c->dk != c0->dk || c->dv != c0->dv || c->dtype != c0->dtype)
+      return GQA_ERR_SHAPE_MISMATCH;
+    if ((st = check_heads(c, hq)) != GQA_OK) return st;
+    if (!uses_mfma(c)) return GQA_ERR_UNSUPPORTED;
+    gqa_plan one;
+    if ((st = make_plan(c, hq, 0, &one)) != GQA_OK) return st;
+    p->chunk[i] = one.chunk_tokens;
+    p->num_chunks[i] = one.num_chunks;
+    p->col_base[i] = (int32_t)cols;
+    p->item_base[i] = items;
+    cols += one.num_chunks;
+    items += (int64_t)c->batch * c->num_kv_heads * one.num_chunks;
+  }
+  const int64_t rows = (int64_t)br[0].cache.batch * hq;
+  if (cols > std::numeric_limits<int32_t>::max() ||
+      items > std::numeric_limits<int32_t>::max() ||
+      rows * cols > std::numeric_limits<int32_t>::max())
+    return GQA_ERR_UNSUPPORTED;
+  p->total_cols = (int32_t)cols;
+  p->total_items = items;
+  const size_t ml = (size_t)rows * cols * sizeof(float);
+  p->off_l = align_up(ml);
+  p->off_acc = p->off_l + align_up(ml);
+  p->workspace_bytes = p->off_acc + align_up(ml * br[0].cache.dv);
+  return GQA_OK;
 }
 
 }  // namespace
@@ -487,6 +538,111 @@ gqa_status gqa_softmax_state_merge(const gqa_carry *a, const gqa_carry *b,
   return device_status(gqa::launch_merge(m, stream));
 }
 
+size_t gqa_attend_branches_workspace_bytes(const gqa_branch *branches,
+                                           int32_t num_branches,
+                                           int32_t num_q_heads) {
+  BranchesPlan p;
+  return plan_branches(branches, num_branches, num_q_heads, &p) == GQA_OK
+             ? p.workspace_bytes
+             : 0;
+}
+
+gqa_status gqa_attend_branches(const void *q, int32_t num_q_heads,
+                               const gqa_branch *branches,
+                               int32_t num_branches, float scale,
+                               const gqa_carry *carry_in,
+                               const gqa_carry *carry_out, float *out,
+                               void *workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  BranchesPlan p;
+  gqa_status st = plan_branches(branches, num_branches, num_q_heads, &p);
+  if (st != GQA_OK) return st;
+  bool any_bias = false;
+  for (int32_t i = 0; i < num_branches; ++i) {
+    const gqa_branch &b = branches[i];
+    if ((st = check_attend_args(q, num_q_heads, &b.cache, b.lens, scale)) !=
+        GQA_OK)
+      return st;
+    if ((st = check_bias(&b.cache, b.bias, b.bias_stride)) != GQA_OK) return st;
+    any_bias = any_bias || b.bias != nullptr;
+  }
+  const gqa_cache *c0 = &branches[0].cache;
+  if ((st = check_combine_args(num_q_heads, c0, branches[0].lens, carry_in,
+                               carry_out, out)) != GQA_OK)
+    return st;
+  if (!workspace || !aligned16(workspace)) return GQA_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < p.workspace_bytes) return GQA_ERR_WORKSPACE_TOO_SMALL;
+
+  const double sc =
+      scale != 0.0f ? (double)scale : 1.0 / std::sqrt((double)c0->dk);
+  PartitionArgs a;
+  a.q = q;
+  a.k = c0->k;
+  a.v = c0->v;
+  a.lens = branches[0].lens;
+  a.batch = c0->batch;
+  a.max_len = c0->max_len;
+  a.num_kv_heads = c0->num_kv_heads;
+  a.hpk = num_q_heads / c0->num_kv_heads;
+  a.dk = c0->dk;
+  a.dv = c0->dv;
+  a.chunk_tokens = p.chunk[0];
+  a.num_chunks = p.num_chunks[0];
+  a.total_cols = p.total_cols;
+  a.col_base = 0;
+  a.total_items = (int)p.total_items;
+  a.num_extra = num_branches - 1;
+  for (int32_t i = 1; i < num_branches; ++i) {
+    const gqa_branch &b = branches[i];
+    gqa::ExtraBranch &x = a.extra[i - 1];
+    x.k = b.cache.k;
+    x.v = b.cache.v;
+    x.lens = b.lens;
+    x.bias = b.bias;
+    x.bias_stride = b.bias ? b.bias_stride : 0;
+    x.max_len = b.cache.max_len;
+    x.chunk_tokens = p.chunk[i];
+    x.num_chunks = p.num_chunks[i];
+    x.col_base = p.col_base[i];
+    x.item_base = (int)p.item_base[i];
+  }
+  a.scale_log2 = (float)(sc * 1.4426950408889634);
+  a.bias = branches[0].bias;
+  a.bias_stride = a.bias ? branches[0].bias_stride : 0;
+  a.has_bias = any_bias ? 1 : 0;
+  char *base = static_cast<char *>(workspace);
+  a.part_m = reinterpret_cast<float *>(base);
+  a.part_l = reinterpret_cast<float *>(base + p.off_l);
+  a.part_acc = reinterpret_cast<float *>(base + p.off_acc);
+  a.sched = nullptr;
+  a.sched_len = 0;
+  st = device_status(c0->dtype == GQA_DTYPE_BF16
+                         ? gqa::launch_partition_bf16(a, gqa::StepParams{}, stream)
+                         : gqa::launch_partition_f32(a, gqa::StepParams{}, stream));
+  if (st != GQA_OK) return st;
+
+  CombineArgs cb;
+  cb.batch = c0->batch;
+  cb.num_q_heads = num_q_heads;
+  cb.dv = c0->dv;
+  cb.total_cols = p.total_cols;
+  cb.num_branches = num_branches;
+  for (int32_t i = 0; i < num_branches; ++i)
+    cb.br[i] = gqa::CombineBranch{branches[i].lens, branches[i].cache.max_len,
+                                  p.chunk[i], p.col_base[i]};
+  cb.part_m = a.part_m;
+  cb.part_l = a.part_l;
+  cb.part_acc = a.part_acc;
+  cb.in_m = carry_in ? carry_in->m : nullptr;
+  cb.in_l = carry_in ? carry_in->l : nullptr;
+  cb.in_acc = carry_in ? carry_in->acc : nullptr;
+  cb.out_m = carry_out ? carry_out->m : nullptr;
+  cb.out_l = carry_out ? carry_out->l : nullptr;
+  cb.out_acc = carry_out ? carry_out->acc : nullptr;
+  cb.out = out;
+  return device_status(gqa::launch_combine(cb, stream));
+}
+
 size_t gqa_decode_step_workspace_bytes(const gqa_cache *cache,
                                        int32_t num_q_heads) {
   gqa_plan p;
@@ -548,6 +704,7 @@ gqa_status gqa_decode_step(const void *q, int32_t num_q_heads,
   a.scale_log2 = (float)(sc * 1.4426950408889634);
   a.bias = bias;
   a.bias_stride = bias ? bias_stride : 0;
+  a.has_bias = bias ? 1 : 0;
   char *base = static_cast<char *>(workspace);
   a.part_m = reinterpret_cast<float *>(base);
   a.part_l = reinterpret_cast<float *>(base + plan.off_l);

@@ -47,6 +47,7 @@ struct PartitionArgs {
   float scale_log2;     // logit scale times log2(e)
   const float *bias;    // [B][bias_stride] additive logit terms, or NULL
   long long bias_stride;
+  int has_bias;         // any branch of the launch has a bias
   float *part_m;        // [rows][num_chunks]  (natural-log units)
   float *part_l;        // [rows][num_chunks]
   float *part_acc;      // [rows][num_chunks][dv]

@@ -374,7 +374,7 @@ template <int DK, int DV, int NW, bool STEP>
 hipError_t launch_one(const PartitionArgs &a, const StepParams &sp,
                       hipStream_t s) {
   const int nwork = a.sched ? a.sched_len : a.total_items;
-  if (a.bias)
+  if (a.has_bias)
     hipLaunchKernelGGL((partition_bf16_kernel<DK, DV, NW, STEP, true>),
                        dim3(nwork), dim3(NW * 64), 0, s, a, sp);
   else

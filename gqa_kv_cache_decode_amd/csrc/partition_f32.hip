@@ -314,7 +314,7 @@ template <int DK, int DV, bool STEP>
 hipError_t launch_mfma(const PartitionArgs &a, const StepParams &sp,
                        hipStream_t s) {
   const int nwork = a.sched ? a.sched_len : a.total_items;
-  if (a.bias)
+  if (a.has_bias)
     hipLaunchKernelGGL(
         (partition_f32_mfma_kernel<DK, DV, kPartitionWaves, STEP, true>),
         dim3(nwork), dim3(kPartitionWaves * 64), 0, s, a, sp);

@@ -254,6 +254,46 @@ GQA_API gqa_status gqa_decode_step(const void *q, int32_t num_q_heads,
                                    hipStream_t stream);
 
 /*
+ * One cache of a multi-branch attend: its own K/V (and max_len), lengths and
+ * optional bias (as in gqa_attend_decode).  Every branch of a call has the
+ * same batch, num_kv_heads, dk, dv and dtype.
+ */
+typedef struct gqa_branch {
+  gqa_cache cache;
+  const int32_t *lens;   /* [batch] device int32 */
+  const float *bias;     /* NULL or [batch][bias_stride] fp32 */
+  int64_t bias_stride;
+} gqa_branch;
+
+#define GQA_MAX_BRANCHES 4
+
+/* Workspace bytes gqa_attend_branches needs; 0 if the branches are invalid. */
+GQA_API size_t gqa_attend_branches_workspace_bytes(const gqa_branch *branches,
+                                                   int32_t num_branches,
+                                                   int32_t num_q_heads);
+
+/*
+ * attend_branches — the queries attend over the union of several caches'
+ * live keys (branch i: keys [0, clamp(lens_i[b], 0, max_len_i)) of its own
+ * cache), folded with carry_in, in one partition launch and one combine.
+ * The branches' partial softmax states merge exactly as carries do (usearch
+ * carry: one branch continues another over the same queries), so the result
+ * is one pass over the concatenated keys: e.g. permanent sink keys, a recent
+ * window and a main cache (cortiq-engine NystromState: exact window ring and
+ * sink buffer, kept once per KV group).
+ *   1 <= num_branches <= GQA_MAX_BRANCHES; matrix-core head shapes only
+ *   (GQA_ERR_UNSUPPORTED otherwise).  Other arguments as in
+ *   gqa_attend_decode; workspace: gqa_attend_branches_workspace_bytes().
+ */
+GQA_API gqa_status gqa_attend_branches(const void *q, int32_t num_q_heads,
+                                       const gqa_branch *branches,
+                                       int32_t num_branches, float scale,
+                                       const gqa_carry *carry_in,
+                                       const gqa_carry *carry_out, float *out,
+                                       void *workspace, size_t workspace_bytes,
+                                       hipStream_t stream);
+
+/*
  * softmax_state_merge — dst = merge(a, b) row by row (usearch carry,
  * partial softmaxes rescaled to a common maximum): m = max(m_a, m_b),
  * l = e^(m_a-m) l_a +

@@ -435,3 +435,116 @@ def pin_bias(orc):
 
 
 ALL_PINS.append(pin_bias)
+
+
+# --- several caches as one; the sink / ring / main layout -----------------
+
+def pin_branches(orc_stream):
+    """attend_branches over caches of different lengths (some empty) equals
+    one pass over each sequence's concatenated live keys, in any order, and
+    folds carry_in like a single branch does."""
+    import oracle.attention as att
+    rng = np.random.default_rng(21)
+    B, Hq, Hkv, dk, dv = 3, 8, 4, 16, 8
+    q = rng.uniform(-1, 1, (B, Hq, dk))
+    branches = []
+    for T, lens in ((5, [5, 0, 3]), (9, [2, 9, 0]), (13, [13, 7, 0])):
+        k = rng.uniform(-1, 1, (B, T, Hkv, dk))
+        v = rng.uniform(-1, 1, (B, T, Hkv, dv))
+        branches.append((k, v, np.array(lens)))
+    out, c = orc_stream.attend_branches(q, branches, scale=0.4)
+    for perm in ((0, 1, 2), (2, 0, 1)):
+        total = [sum(int(branches[i][2][b]) for i in range(3))
+                 for b in range(B)]
+        T = max(total)
+        kc = np.full((B, T, Hkv, dk), np.nan)
+        vc = np.full((B, T, Hkv, dv), np.nan)
+        for b in range(B):
+            rows_k = [branches[i][0][b, :branches[i][2][b]] for i in perm]
+            rows_v = [branches[i][1][b, :branches[i][2][b]] for i in perm]
+            n = total[b]
+            if n:
+                kc[b, :n] = np.concatenate(rows_k)
+                vc[b, :n] = np.concatenate(rows_v)
+        want, cw = att.attend(q, kc, vc, total, scale=0.4)
+        _close(out, want, 1e-14, f"branches = one pass, order {perm}")
+        _close(c.m, cw.m, 1e-14, "branches m")
+        _close(c.l, cw.l, 1e-12, "branches l")
+    cin = att.Carry(rng.uniform(-1, 1, B * Hq), rng.uniform(0.5, 2, B * Hq),
+                    rng.uniform(-1, 1, (B * Hq, dv)))
+    out2, c2 = orc_stream.attend_branches(q, branches, scale=0.4,
+                                          carry_in=cin)
+    want2 = att.finalize(att.merge(cin, c)).reshape(B, Hq, dv)
+    _close(out2, want2, 1e-13, "branches fold carry_in")
+
+
+def pin_stream(orc_stream):
+    """The sink / ring / main layout over a run of decode steps: the sink
+    holds the first S tokens, ring slot (p - S) % W holds token p for the
+    last W tokens, main holds the evicted tokens in order; attending the
+    three parts equals attending the whole history; a full main cache drops
+    the new token; with no main cache the evicted tokens leave attention;
+    with no sink the ring starts at token 0."""
+    import oracle.attention as att
+    rng = np.random.default_rng(22)
+    B, Hq, Hkv, dk, dv = 3, 4, 2, 8, 8
+    for S, W, M, use_main in ((4, 8, 20, True), (0, 6, 10, True),
+                              (3, 5, 0, False)):
+        sk = np.zeros((B, max(S, 1), Hkv, dk)) if S else None
+        sv = np.zeros((B, max(S, 1), Hkv, dv)) if S else None
+        rk = np.zeros((B, W, Hkv, dk))
+        rv = np.zeros((B, W, Hkv, dv))
+        mk = np.zeros((B, max(M, 1), Hkv, dk)) if use_main else None
+        mv = np.zeros((B, max(M, 1), Hkv, dv)) if use_main else None
+        count = np.array([0, 0, -1])           # sequence 2 is invalid
+        hist_k = [[] for _ in range(B)]
+        hist_v = [[] for _ in range(B)]
+        for step in range(S + W + M + 3):
+            kn = rng.uniform(-1, 1, (B, Hkv, dk))
+            vn = rng.uniform(-1, 1, (B, Hkv, dv))
+            before = count.copy()
+            sk, sv, rk, rv, mk, mv, count, dropped = orc_stream.stream_append(
+                sk, sv, rk, rv, mk, mv, kn, vn, count)
+            exp_drop = 1                       # the invalid sequence
+            for b in range(2):
+                full = use_main and before[b] - S - W >= M
+                if full:
+                    exp_drop += 1
+                    assert count[b] == before[b], "full main: no change"
+                else:
+                    assert count[b] == before[b] + 1, "count advances"
+                    hist_k[b].append(kn[b])
+                    hist_v[b].append(vn[b])
+            assert count[2] == -1 and dropped == exp_drop, "drop count"
+            q = rng.uniform(-1, 1, (B, Hq, dk))
+            for b in range(2):
+                t = int(count[b])
+                ns, nw, nm = orc_stream.stream_lengths(t, S, W, M)
+                assert ns + nw + nm == (t if use_main else min(t, S + W))
+                for p in range(min(t, S)):
+                    assert np.array_equal(sk[b, p], hist_k[b][p]), "sink"
+                for p in range(max(S, t - W), t):
+                    assert np.array_equal(rk[b, (p - S) % W], hist_k[b][p]) \
+                        and np.array_equal(rv[b, (p - S) % W], hist_v[b][p]), \
+                        "ring slot"
+                for j in range(nm):
+                    assert np.array_equal(mk[b, j], hist_k[b][S + j]) and \
+                        np.array_equal(mv[b, j], hist_v[b][S + j]), "main"
+                kept = list(range(min(t, S))) + \
+                    list(range(max(S, t - W), t)) + \
+                    (list(range(S, S + nm)) if use_main else [])
+                if not kept:
+                    continue
+                kc = np.stack([hist_k[b][p] for p in kept])[None]
+                vc = np.stack([hist_v[b][p] for p in kept])[None]
+                want, _ = att.attend(q[b:b + 1], kc, vc, [len(kept)], 0.5)
+                parts = [(rk[b:b + 1], rv[b:b + 1], [nw])]
+                if S:
+                    parts.insert(0, (sk[b:b + 1], sv[b:b + 1], [ns]))
+                if use_main and nm:
+                    parts.append((mk[b:b + 1], mv[b:b + 1], [nm]))
+                got, _ = orc_stream.attend_branches(q[b:b + 1], parts, 0.5)
+                _close(got, want, 1e-14, f"stream S={S} W={W} t={t}")
+
+
+STREAM_PINS = [pin_branches, pin_stream]

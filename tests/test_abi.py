@@ -30,7 +30,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 11, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(lib, n), f"missing export {n}"
     assert set(names) == set(bd._SIGNATURES), "binding covers the header"
@@ -180,3 +180,50 @@ def test_append_and_merge_reject(lib):
     assert lib.gqa_softmax_state_merge(ctypes.byref(a), ctypes.byref(a),
                                        ctypes.byref(a), 4, 0, None, None) == \
         INVALID
+
+
+def _branch(c, lens=0x40000, bias=None, stride=0):
+    return bd._Branch(c, lens, bias, stride)
+
+
+def test_branches_layout_and_checks(lib):
+    """Multi-branch attend: per-branch chunking, one partial row over all
+    branches' chunks, and the argument checks (before any launch)."""
+    main = _cache(B=1, T=262144, H=4)
+    win = _cache(B=1, T=128, H=4, k=0x30000, v=0x38000)
+    arr = (bd._Branch * 2)(_branch(main), _branch(win, lens=0x48000))
+    nbytes = lib.gqa_attend_branches_workspace_bytes(arr, 2, 32)
+    # main: 64 chunks of 4096; window: one chunk; rows = 32
+    ml = 32 * (64 + 1) * 4
+    al = lambda x: (x + 255) // 256 * 256
+    assert nbytes == 2 * al(ml) + al(ml * 128)
+    q, out, ws = (ctypes.c_void_p(x) for x in (0x50000, 0x60000, 0x70000))
+    f = lib.gqa_attend_branches
+    assert f(q, 32, arr, 2, 0.0, None, None, out, ws, nbytes - 1,
+             None) == WORKSPACE
+    # branch count outside 1..4
+    assert f(q, 32, arr, 0, 0.0, None, None, out, ws, nbytes, None) == INVALID
+    arr5 = (bd._Branch * 5)(*[_branch(main)] * 5)
+    assert f(q, 32, arr5, 5, 0.0, None, None, out, ws, nbytes,
+             None) == INVALID
+    # branches must agree on batch, heads, widths and dtype
+    for bad in (_cache(B=2, T=128, H=4), _cache(B=1, T=128, H=8),
+                _cache(B=1, T=128, H=4, dv=64), _cache(B=1, T=128, H=4,
+                                                       dtype=0)):
+        arr_bad = (bd._Branch * 2)(_branch(main), _branch(bad))
+        assert f(q, 32, arr_bad, 2, 0.0, None, None, out, ws, nbytes,
+                 None) == SHAPE
+    # the vector-ALU head widths are not supported here
+    odd = _cache(B=1, T=128, H=4, dk=48, dv=80, dtype=0)
+    arr_odd = (bd._Branch * 1)(_branch(odd))
+    assert f(q, 32, arr_odd, 1, 0.0, None, None, out, ws, nbytes,
+             None) == UNSUPPORTED
+    # a branch with a null lens, a bad bias
+    arr_nl = (bd._Branch * 2)(_branch(main), _branch(win, lens=None))
+    assert f(q, 32, arr_nl, 2, 0.0, None, None, out, ws, nbytes,
+             None) == INVALID
+    arr_bb = (bd._Branch * 2)(_branch(main),
+                              _branch(win, bias=0xA0000, stride=64))
+    assert f(q, 32, arr_bb, 2, 0.0, None, None, out, ws, nbytes,
+             None) == INVALID
+
