@@ -62,6 +62,8 @@ _PLAN_P = ctypes.POINTER(Plan)
 _BRANCH_P = ctypes.POINTER(_Branch)
 
 _SIGNATURES = {
+    "gqa_stream_append": (_I32, [_CACHE_P, _CACHE_P, _CACHE_P, _P, _P, _P, _P,
+                                 _P, _P, _P, _P, _P]),
     "gqa_attend_branches_workspace_bytes": (ctypes.c_size_t,
                                             [_BRANCH_P, _I32, _I32]),
     "gqa_attend_branches": (_I32, [_P, _I32, _BRANCH_P, _I32, ctypes.c_float,
@@ -408,3 +410,36 @@ def attend_branches(q, branches, scale: float = 0.0,
         _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(q)), "attend_branches")
     return out
+
+
+def stream_append(ring_k, ring_v, k_new, v_new, count_in, count_out=None,
+                  sink=None, main=None, dropped=None):
+    """One token per sequence into the sink / ring / main layout.
+
+    ``sink`` and ``main`` are optional (k, v) cache pairs.  Returns
+    (count_out, lens_sink, lens_ring, lens_main): device int32 [batch]
+    tensors (lens_sink / lens_main None without that part), the lengths
+    :func:`attend_branches` takes."""
+    rc = _cache(ring_k, ring_v)
+    sc = None if sink is None else _cache(*sink)
+    mc = None if main is None else _cache(*main)
+    _need(k_new, "k_new", ring_k.dtype, (rc.batch, rc.num_kv_heads, rc.dk))
+    _need(v_new, "v_new", ring_k.dtype, (rc.batch, rc.num_kv_heads, rc.dv))
+    _need(count_in, "count_in", torch.int32, (rc.batch,))
+    dev = ring_k.device
+    new = lambda: torch.empty(rc.batch, dtype=torch.int32, device=dev)
+    if count_out is None:
+        count_out = new()
+    _need(count_out, "count_out", torch.int32, (rc.batch,))
+    ls = None if sc is None else new()
+    lr = new()
+    lm = None if mc is None else new()
+    if dropped is not None:
+        _need(dropped, "dropped", torch.int32, (1,))
+    _check(library().gqa_stream_append(
+        None if sc is None else ctypes.byref(sc), ctypes.byref(rc),
+        None if mc is None else ctypes.byref(mc), _ptr(k_new), _ptr(v_new),
+        _ptr(count_in), _ptr(count_out), _ptr(ls), _ptr(lr), _ptr(lm),
+        _ptr(dropped), _stream(ring_k)), "stream_append")
+    return count_out, ls, lr, lm
+

@@ -441,6 +441,58 @@ gqa_status gqa_kv_append(const gqa_cache *cache, const void *k_new,
   return device_status(gqa::launch_append(a, stream));
 }
 
+gqa_status gqa_stream_append(const gqa_cache *sink, const gqa_cache *ring,
+                             const gqa_cache *main_cache, const void *k_new,
+                             const void *v_new, const int32_t *count_in,
+                             int32_t *count_out, int32_t *lens_sink,
+                             int32_t *lens_ring, int32_t *lens_main,
+                             int32_t *dropped, hipStream_t stream) {
+  gqa_status st = check_cache_dims(ring);
+  if (st != GQA_OK) return st;
+  if ((st = check_cache_data(ring)) != GQA_OK) return st;
+  for (const gqa_cache *c : {sink, main_cache}) {
+    if (!c) continue;
+    if ((st = check_cache_dims(c)) != GQA_OK) return st;
+    if ((st = check_cache_data(c)) != GQA_OK) return st;
+    if (c->batch != ring->batch || c->num_kv_heads != ring->num_kv_heads ||
+        c->dk != ring->dk || c->dv != ring->dv || c->dtype != ring->dtype)
+      return GQA_ERR_SHAPE_MISMATCH;
+  }
+  if (!k_new || !v_new || !count_in || !count_out || !lens_ring ||
+      (sink && !lens_sink) || (main_cache && !lens_main))
+    return GQA_ERR_INVALID_ARGUMENT;
+  const int64_t rk = (int64_t)ring->num_kv_heads * ring->dk * esize(ring->dtype);
+  const int64_t rv = (int64_t)ring->num_kv_heads * ring->dv * esize(ring->dtype);
+  if (rk % 4 || rv % 4 || rk > std::numeric_limits<int32_t>::max() ||
+      rv > std::numeric_limits<int32_t>::max())
+    return GQA_ERR_UNSUPPORTED;
+  const uintptr_t bits = reinterpret_cast<uintptr_t>(k_new) |
+                         reinterpret_cast<uintptr_t>(v_new);
+  if (bits & 3) return GQA_ERR_INVALID_ARGUMENT;
+  gqa::StreamAppendArgs a;
+  a.sink_k = sink ? sink->k : nullptr;
+  a.sink_v = sink ? sink->v : nullptr;
+  a.ring_k = ring->k;
+  a.ring_v = ring->v;
+  a.main_k = main_cache ? main_cache->k : nullptr;
+  a.main_v = main_cache ? main_cache->v : nullptr;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.count_in = count_in;
+  a.count_out = count_out;
+  a.lens_sink = sink ? lens_sink : nullptr;
+  a.lens_ring = lens_ring;
+  a.lens_main = main_cache ? lens_main : nullptr;
+  a.dropped = dropped;
+  a.batch = ring->batch;
+  a.sink = sink ? sink->max_len : 0;
+  a.window = ring->max_len;
+  a.main_len = main_cache ? main_cache->max_len : 0;
+  a.row_bytes_k = (int)rk;
+  a.row_bytes_v = (int)rv;
+  return device_status(gqa::launch_stream_append(a, stream));
+}
+
 gqa_status gqa_attend_plan(const gqa_cache *cache, int32_t num_q_heads,
                            int32_t chunk_tokens, gqa_plan *plan) {
   if (!plan) return GQA_ERR_INVALID_ARGUMENT;

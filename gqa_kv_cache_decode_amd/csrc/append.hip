@@ -76,10 +76,78 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
   }
 }
 
+// Streaming layout (cortiq-engine NystromState: permanent exact sink keys and
+// an exact window ring per KV group; the key a full ring evicts moves into
+// the exact main cache here, where the page feeds an approximate far field).
+// With t = count_in[b]:
+//   t < 0: nothing changes, the drop is counted;
+//   t < S: the token goes to sink slot t;
+//   else:  ring slot r = (t - S) % W; when the ring is full (t - S >= W) its
+//          token there (position t - W) first moves to main slot t - S - W
+//          (a full main cache drops the new token instead; without a main
+//          cache the old token simply leaves), then the new token takes r.
+// count_out = t + 1 unless dropped; lens_* = the live keys of each part.
+// One work-group per sequence; each thread copies its own 4-byte words, so
+// the old ring word is read before the same thread overwrites it.
+__global__ __launch_bounds__(kThreads) void stream_append_kernel(
+    StreamAppendArgs a) {
+  const int b = blockIdx.x;
+  const int t = a.count_in[b];
+  const int S = a.sink, W = a.window, M = a.main_len;
+  bool ok = t >= 0;
+  uint32_t *kd = nullptr, *vd = nullptr;   // destination of the new token
+  uint32_t *ek = nullptr, *ev = nullptr;   // main slot of the evicted token
+  if (ok && t < S) {
+    kd = static_cast<uint32_t *>(a.sink_k) + ((size_t)b * S + t) * (a.row_bytes_k / 4);
+    vd = static_cast<uint32_t *>(a.sink_v) + ((size_t)b * S + t) * (a.row_bytes_v / 4);
+  } else if (ok) {
+    const int r = (t - S) % W;
+    if (t - S >= W && a.main_k) {
+      const int j = t - S - W;
+      if (j >= M) {
+        ok = false;
+      } else {
+        ek = static_cast<uint32_t *>(a.main_k) + ((size_t)b * M + j) * (a.row_bytes_k / 4);
+        ev = static_cast<uint32_t *>(a.main_v) + ((size_t)b * M + j) * (a.row_bytes_v / 4);
+      }
+    }
+    kd = static_cast<uint32_t *>(a.ring_k) + ((size_t)b * W + r) * (a.row_bytes_k / 4);
+    vd = static_cast<uint32_t *>(a.ring_v) + ((size_t)b * W + r) * (a.row_bytes_v / 4);
+  }
+  if (ok) {
+    const uint32_t *kn = static_cast<const uint32_t *>(a.k_new) + (size_t)b * (a.row_bytes_k / 4);
+    const uint32_t *vn = static_cast<const uint32_t *>(a.v_new) + (size_t)b * (a.row_bytes_v / 4);
+    for (int i = threadIdx.x; i < a.row_bytes_k / 4; i += kThreads) {
+      if (ek) ek[i] = kd[i];
+      kd[i] = kn[i];
+    }
+    for (int i = threadIdx.x; i < a.row_bytes_v / 4; i += kThreads) {
+      if (ev) ev[i] = vd[i];
+      vd[i] = vn[i];
+    }
+  }
+  __syncthreads();  // count_in is read by every thread before count_out is set
+  if (threadIdx.x == 0) {
+    const int t1 = ok ? t + 1 : t;
+    const int tc = t1 < 0 ? 0 : t1;
+    a.count_out[b] = t1;
+    if (a.lens_sink) a.lens_sink[b] = min(tc, S);
+    a.lens_ring[b] = min(max(tc - S, 0), W);
+    if (a.lens_main) a.lens_main[b] = min(max(tc - S - W, 0), M);
+    if (!ok && a.dropped) atomicAdd(a.dropped, 1);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_append(const AppendArgs &a, hipStream_t s) {
   hipLaunchKernelGGL(append_kernel, dim3(a.batch), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_append(const StreamAppendArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL(stream_append_kernel, dim3(a.batch), dim3(kThreads), 0, s,
+                     a);
   return hipGetLastError();
 }
 

@@ -120,6 +120,21 @@ struct AppendArgs {
   int batch, max_len, row_bytes_k, row_bytes_v;  // bytes of one token's K/V row
 };
 
+// One token per sequence into a streaming layout: permanent sink slots, a
+// window ring, and a main cache receiving the keys the full ring evicts.
+struct StreamAppendArgs {
+  void *sink_k, *sink_v;  // [B][S][Hkv][d] or NULL (S = 0)
+  void *ring_k, *ring_v;  // [B][W][Hkv][d]
+  void *main_k, *main_v;  // [B][M][Hkv][d] or NULL (evicted keys dropped)
+  const void *k_new, *v_new;
+  const int32_t *count_in;
+  int32_t *count_out;
+  int32_t *lens_sink, *lens_ring, *lens_main;  // live keys after the append
+  int32_t *dropped;
+  int batch, sink, window, main_len;
+  int row_bytes_k, row_bytes_v;  // bytes of one token's K/V row (multiple of 4)
+};
+
 // Kernel families compiled into the library.
 bool partition_bf16_supported(int dk, int dv, int hpk);
 bool partition_f32_supported(int dk, int dv, int hpk);
@@ -143,5 +158,6 @@ size_t schedule_lds_bytes(int batch, int num_chunks);
 hipError_t launch_schedule(const ScheduleArgs &a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs &a, hipStream_t s);
 hipError_t launch_append(const AppendArgs &a, hipStream_t s);
+hipError_t launch_stream_append(const StreamAppendArgs &a, hipStream_t s);
 
 }  // namespace gqa

@@ -150,6 +150,37 @@ GQA_API gqa_status gqa_kv_append(const gqa_cache *cache, const void *k_new,
                          hipStream_t stream);
 
 /*
+ * stream_append — one token per sequence into a streaming decoder's layout
+ * (cortiq-engine NystromState: permanent exact sink keys and an exact window
+ * ring per KV group, shared by the group's query heads; here the key that a
+ * full ring evicts moves, exactly, into a main cache instead of the page's
+ * approximate far field).
+ *   sink  NULL (no sinks) or a cache of S slots; ring: a cache of W slots;
+ *   main_cache  NULL (evicted keys leave attention) or a cache of M slots.
+ *   All three share batch, num_kv_heads, dk, dv and dtype; K/V rows of
+ *   num_kv_heads * d elements must be a multiple of 4 bytes.
+ *   count_in [batch]: tokens seen so far by each sequence.  With t =
+ *   count_in[b]: t < S puts the token in sink slot t; otherwise it takes ring
+ *   slot (t - S) % W, and if the ring was full (t - S >= W) the token it held
+ *   (position t - W) first moves to main slot t - S - W.  A negative t, or a
+ *   full main cache, changes nothing and increments *dropped (if not NULL).
+ *   count_out[b] = t + 1 (t when dropped); may alias count_in.
+ *   lens_sink / lens_ring / lens_main [batch] receive each part's live keys
+ *   (min(t', S), min(max(t' - S, 0), W), min(max(t' - S - W, 0), M)), the
+ *   lengths gqa_attend_branches takes; lens_sink / lens_main are ignored
+ *   without a sink / main cache.  Attending the three parts then equals
+ *   attending the whole history (or sinks + window without a main cache).
+ */
+GQA_API gqa_status gqa_stream_append(const gqa_cache *sink,
+                                     const gqa_cache *ring,
+                                     const gqa_cache *main_cache,
+                                     const void *k_new, const void *v_new,
+                                     const int32_t *count_in,
+                                     int32_t *count_out, int32_t *lens_sink,
+                                     int32_t *lens_ring, int32_t *lens_main,
+                                     int32_t *dropped, hipStream_t stream);
+
+/*
  * Plan the split-K decomposition for `cache` and `num_q_heads` query heads.
  * chunk_tokens = 0 picks the library's choice; otherwise it must be a
  * positive multiple of 64.  Pure host computation (no HIP calls).

@@ -30,7 +30,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(lib, n), f"missing export {n}"
     assert set(names) == set(bd._SIGNATURES), "binding covers the header"
@@ -227,3 +227,30 @@ def test_branches_layout_and_checks(lib):
     assert f(q, 32, arr_bb, 2, 0.0, None, None, out, ws, nbytes,
              None) == INVALID
 
+
+
+def test_stream_append_checks(lib):
+    """stream_append rejects bad layouts before any launch."""
+    ring = _cache(B=4, T=128, H=2)
+    sink = _cache(B=4, T=4, H=2, k=0x30000, v=0x38000)
+    main = _cache(B=4, T=4096, H=2, k=0x40000, v=0x48000)
+    p = [ctypes.c_void_p(0x50000 + 0x1000 * i) for i in range(8)]
+    f = lib.gqa_stream_append
+
+    def call(s_, r_, m_, ls=p[4], lm=p[6], kn=p[0]):
+        return f(None if s_ is None else ctypes.byref(s_),
+                 None if r_ is None else ctypes.byref(r_),
+                 None if m_ is None else ctypes.byref(m_), kn, p[1], p[2],
+                 p[3], ls, p[5], lm, None, None)
+
+    assert call(sink, None, main) == INVALID              # no ring
+    assert call(sink, ring, main, ls=None) == INVALID     # sink without lens
+    assert call(sink, ring, main, lm=None) == INVALID     # main without lens
+    assert call(sink, ring, main, kn=None) == INVALID
+    assert call(sink, ring, main, kn=ctypes.c_void_p(0x50002)) == INVALID
+    for bad in (_cache(B=5, T=4, H=2), _cache(B=4, T=4, H=1),
+                _cache(B=4, T=4, H=2, dv=64), _cache(B=4, T=4, H=2, dtype=0)):
+        assert call(bad, ring, main) == SHAPE
+        assert call(None, ring, bad) == SHAPE
+    odd = _cache(B=4, T=16, H=1, dk=3, dv=3)   # 6-byte rows
+    assert call(None, odd, None) == UNSUPPORTED
