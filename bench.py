@@ -25,6 +25,7 @@ import os
 import statistics
 import sys
 import time
+import types
 from pathlib import Path
 
 ROOT = Path(__file__).resolve().parent
@@ -55,7 +56,12 @@ def parse_args():
     p.add_argument("--steps", type=int, default=60)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="batched",
-                   choices=["tiny", "batched", "ragged", "long", "spike"])
+                   choices=["tiny", "batched", "ragged", "long", "spike",
+                            "stream"],
+                   help="stream: the long-context shapes kept as 4 sink "
+                        "keys + a 128-key window ring + a main cache; each "
+                        "step appends (evicting the ring's oldest key into "
+                        "main) and attends the three parts in one launch")
     p.add_argument("--rotate", type=int, default=0,
                    help="cache copies to rotate over (0 = enough for 1 GiB)")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -76,7 +82,47 @@ def workload_by_name(name):
     from gqa_kv_cache_decode_amd import workloads as wl
     return {"tiny": wl.TINY_F32, "batched": wl.BATCHED_BF16,
             "ragged": wl.RAGGED_BF16, "long": wl.LONG_WINDOW_BF16,
-            "spike": wl.WIDE_SPIKE_BF16}[name]
+            "spike": wl.WIDE_SPIKE_BF16, "stream": wl.LONG_WINDOW_BF16}[name]
+
+
+STREAM_SINK = 4            # permanent sink keys (cortiq-engine default)
+STREAM_ROOM = 256          # free main slots, so the first steps grow main
+
+
+class StreamState:
+    """The long-context history kept as sink / window ring / main cache, R
+    copies.  Main holds max_len - STREAM_SINK - window - STREAM_ROOM keys."""
+
+    def __init__(self, g, torch, w, x, copies, dev):
+        S, W, T = STREAM_SINK, w.window, w.max_len
+        mn = T - S - W - STREAM_ROOM
+        self.count0 = S + W + mn
+        mk, mv = x["k"].to(dev), x["v"].to(dev)
+        self.main = [(mk, mv)] + [(mk.clone(), mv.clone())
+                                  for _ in range(copies - 1)]
+        self.sink = [(m[0][:, :S].clone(), m[1][:, :S].clone())
+                     for m in self.main]
+        rk, rv = x["wk"].to(dev), x["wv"].to(dev)
+        self.ring = [(rk.clone(), rv.clone()) for _ in range(copies)]
+        B = w.batch
+        i32 = lambda v: torch.full((B,), v, dtype=torch.int32, device=dev)
+        self.count = [i32(self.count0) for _ in range(copies)]
+        self.lens = [(i32(S), i32(W), i32(mn)) for _ in range(copies)]
+        self.ws = torch.empty(g.library().gqa_attend_branches_workspace_bytes(
+            self.branch_array(g, 0), 3, w.num_q_heads), dtype=torch.uint8,
+            device=dev)
+        self.plan = g.attend_plan(mk, mv, w.num_q_heads)
+        self.pws = torch.empty(self.plan.workspace_bytes, dtype=torch.uint8,
+                               device=dev)
+        self.n_main = mn
+
+    def branches(self, r):
+        ls, lr, lm = self.lens[r]
+        return [(*self.sink[r], ls), (*self.ring[r], lr), (*self.main[r], lm)]
+
+    def branch_array(self, g, r):
+        from gqa_kv_cache_decode_amd import binding as bd
+        return bd._branches(self.branches(r), None)
 
 
 def kv_bytes(w, lens_total, hkv=None):
@@ -119,6 +165,7 @@ def main():
 
     import torch
     import gqa_kv_cache_decode_amd as g
+    from gqa_kv_cache_decode_amd import binding
     from gqa_kv_cache_decode_amd import workloads as wl
 
     w = workload_by_name(args.workload)
@@ -137,8 +184,12 @@ def main():
     v_new = torch.randn(B, Hkv, w.dv, generator=gen).to(w.torch_dtype).to(dev)
     out = torch.empty(B, Hq, w.dv, dtype=torch.float32, device=dev)
 
+    stream = args.workload == "stream"
     branches = []
-    if w.window:
+    if stream:
+        st = StreamState(g, torch, w, x, copies, dev)
+        carry = None
+    elif w.window:
         # the long cache is attended as is; the new token enters the window
         branches.append(Branch(g, torch, w, x["k"].to(dev), x["v"].to(dev),
                                x["lens"].to(dev), copies, append=False,
@@ -157,11 +208,38 @@ def main():
     log(f"[bench] {copies} rotating cache copies, "
         f"{main_bytes * copies / 2**30:.2f} GiB of K/V resident")
 
+    def stream_step(r):
+        """One streaming decode step: the new token enters the ring (its
+        oldest key moving to main), then the three parts are attended in one
+        partition launch and one combine."""
+        g.stream_append(st.ring[r][0], st.ring[r][1], k_new, v_new,
+                        st.count[r], count_out=st.count[r], sink=st.sink[r],
+                        main=st.main[r], lens=st.lens[r])
+        g.attend_branches(q, st.branches(r), w.scale, out=out,
+                          workspace=st.ws)
+
+    if w.window and not stream:
+        # the long cache and the window taking the new token: one partition
+        # launch over both branches, one combine folding their partials
+        mb, wb = branches
+        bws = torch.empty(g.library().gqa_attend_branches_workspace_bytes(
+            binding._branches([(mb.k[0], mb.v[0], mb.lens_cur[0]),
+                               (wb.k[0], wb.v[0], wb.lens_before)], None),
+            2, Hq), dtype=torch.uint8, device=dev)
+
     def step(r):
         """One decode step: the branch holding the new token runs decode_step
-        (append + attend, one launch where the partials fold in-kernel); a
-        long cache without the new token is attended first and hands its
-        carry over."""
+        (append + attend, one launch where the partials fold in-kernel); with
+        a long cache beside the window, both branches run in one
+        decode_step_branches (two launches)."""
+        if w.window:
+            mb, wb = branches
+            g.decode_step_branches(
+                q, [(mb.k[r], mb.v[r], mb.lens_cur[r], mb.bias),
+                    (wb.k[r], wb.v[r], wb.lens_before, wb.bias)], 1,
+                k_new, v_new, wb.lens_cur[r], w.scale, out=out,
+                workspace=bws)
+            return
         for i, br in enumerate(branches):
             last = i == len(branches) - 1
             cin = carry if i > 0 else None
@@ -179,11 +257,19 @@ def main():
                                  br.plan, br.ws, carry_in=cin,
                                  carry_out=cout, out=o)
 
-    dom = branches[0]
+    if stream:
+        step = stream_step
+        dom = types.SimpleNamespace(n_tot=B * st.n_main, bias=None)
 
-    def partition_only(r):
-        g.attend_partition(q, dom.k[r], dom.v[r], dom.lens_cur[r], dom.plan,
-                           dom.ws, w.scale, bias=dom.bias)
+        def partition_only(r):
+            g.attend_partition(q, *st.main[r], st.lens[r][2], st.plan, st.pws,
+                               w.scale)
+    else:
+        dom = branches[0]
+
+        def partition_only(r):
+            g.attend_partition(q, dom.k[r], dom.v[r], dom.lens_cur[r],
+                               dom.plan, dom.ws, w.scale, bias=dom.bias)
 
     if args.profile_pass:
         profile_pass(torch, step, partition_only, copies, w, dom)
@@ -255,15 +341,22 @@ def main():
     # bytes
     q_bytes = B * Hq * w.dk * w.esz
     out_bytes = B * Hq * w.dv * 4
-    carry_bytes = B * Hq * (w.dv + 2) * 4
     step_bytes = 0
     # a bias term counts once per attended (sequence, position)
     bias_bytes = (lambda br: 4 * br.n_tot if br.bias is not None else 0)
     for i, br in enumerate(branches):
-        step_bytes += kv_bytes(w, br.n_tot) + q_bytes + bias_bytes(br)
+        # q counts once per step (one launch reads it for every branch)
+        step_bytes += kv_bytes(w, br.n_tot) + bias_bytes(br) + \
+            (q_bytes if i == 0 else 0)
         if br.append:
             step_bytes += 2 * B * Hkv * (w.dk + w.dv) * w.esz + 2 * B * 4
-    step_bytes += out_bytes + (2 * carry_bytes if len(branches) > 1 else 0)
+    if stream:
+        # sink + ring + main keys, q once; the new row written, the evicted
+        # row read and written; counts and the three lengths
+        step_bytes += (kv_bytes(w, B * (STREAM_SINK + w.window + st.n_main)) +
+                       q_bytes + 3 * B * Hkv * (w.dk + w.dv) * w.esz +
+                       5 * B * 4)
+    step_bytes += out_bytes
     part_bytes = kv_bytes(w, dom.n_tot) + q_bytes + bias_bytes(dom)
     value = step_bytes / (ms_step * 1e-3) / 1e9
     achieved = part_bytes / (ms_part * 1e-3) / 1e9
@@ -301,7 +394,9 @@ def main():
         "ms_per_step": round(ms_step, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic (seeded; shapes and distributions of the workload)",
-        "config": {"workload": w.name, "batch": B, "num_q_heads": Hq,
+        "config": {"workload": (f"stream_sink{STREAM_SINK}_ring{w.window}_"
+                                f"main_of_{w.name}" if stream else w.name),
+                   "batch": B, "num_q_heads": Hq,
                    "num_kv_heads": Hkv, "dk": w.dk, "dv": w.dv,
                    "seq_len": w.max_len, "window": w.window,
                    "kv_dtype": w.dtype, "rotating_cache_copies": copies,

@@ -62,6 +62,10 @@ _PLAN_P = ctypes.POINTER(Plan)
 _BRANCH_P = ctypes.POINTER(_Branch)
 
 _SIGNATURES = {
+    "gqa_decode_step_branches": (_I32, [_P, _I32, _BRANCH_P, _I32, _I32, _P,
+                                        _P, _P, _P, ctypes.c_float, _CARRY_P,
+                                        _CARRY_P, _P, _P, ctypes.c_size_t,
+                                        _P]),
     "gqa_stream_append": (_I32, [_CACHE_P, _CACHE_P, _CACHE_P, _P, _P, _P, _P,
                                  _P, _P, _P, _P, _P]),
     "gqa_attend_branches_workspace_bytes": (ctypes.c_size_t,
@@ -370,7 +374,8 @@ def softmax_state_merge(a: Carry, b: Carry, dst: Optional[Carry] = None,
 
 
 def _branches(branches, q):
-    """ctypes array of gqa_branch from (k, v, lens[, bias]) tuples."""
+    """ctypes array of gqa_branch from (k, v, lens[, bias]) tuples (a bias
+    of None means none)."""
     if not 1 <= len(branches) <= 4:
         raise GqaError("attend_branches takes 1 to 4 branches")
     arr = (_Branch * len(branches))()
@@ -413,13 +418,14 @@ def attend_branches(q, branches, scale: float = 0.0,
 
 
 def stream_append(ring_k, ring_v, k_new, v_new, count_in, count_out=None,
-                  sink=None, main=None, dropped=None):
+                  sink=None, main=None, dropped=None, lens=None):
     """One token per sequence into the sink / ring / main layout.
 
     ``sink`` and ``main`` are optional (k, v) cache pairs.  Returns
     (count_out, lens_sink, lens_ring, lens_main): device int32 [batch]
     tensors (lens_sink / lens_main None without that part), the lengths
-    :func:`attend_branches` takes."""
+    :func:`attend_branches` takes; ``lens`` may give those three tensors to
+    fill (e.g. under graph capture)."""
     rc = _cache(ring_k, ring_v)
     sc = None if sink is None else _cache(*sink)
     mc = None if main is None else _cache(*main)
@@ -431,9 +437,15 @@ def stream_append(ring_k, ring_v, k_new, v_new, count_in, count_out=None,
     if count_out is None:
         count_out = new()
     _need(count_out, "count_out", torch.int32, (rc.batch,))
-    ls = None if sc is None else new()
-    lr = new()
-    lm = None if mc is None else new()
+    if lens is not None:
+        ls, lr, lm = lens
+        for t, nm in ((ls, "lens_sink"), (lr, "lens_ring"), (lm, "lens_main")):
+            if t is not None:
+                _need(t, nm, torch.int32, (rc.batch,))
+    else:
+        ls = None if sc is None else new()
+        lr = new()
+        lm = None if mc is None else new()
     if dropped is not None:
         _need(dropped, "dropped", torch.int32, (1,))
     _check(library().gqa_stream_append(
@@ -442,4 +454,40 @@ def stream_append(ring_k, ring_v, k_new, v_new, count_in, count_out=None,
         _ptr(count_in), _ptr(count_out), _ptr(ls), _ptr(lr), _ptr(lm),
         _ptr(dropped), _stream(ring_k)), "stream_append")
     return count_out, ls, lr, lm
+
+
+def decode_step_branches(q, branches, append_branch: int, k_new, v_new,
+                         lens_out, scale: float = 0.0,
+                         carry_in: Optional[Carry] = None,
+                         carry_out: Optional[Carry] = None, out=_AUTO,
+                         workspace: Optional[torch.Tensor] = None,
+                         dropped=None):
+    """decode_step over several caches: (k_new, v_new) is appended to branch
+    ``append_branch`` (whose lens is the step's lens_in; ``lens_out`` gets
+    the new lengths) and q attends every branch, two launches in all."""
+    arr = _branches(branches, q)
+    c0, hq = _attend_args(q, branches[0][0], branches[0][1], branches[0][2])
+    ab = branches[append_branch]
+    ca = _cache(ab[0], ab[1])
+    _need(k_new, "k_new", ab[0].dtype, (ca.batch, ca.num_kv_heads, ca.dk))
+    _need(v_new, "v_new", ab[0].dtype, (ca.batch, ca.num_kv_heads, ca.dv))
+    _need(lens_out, "lens_out", torch.int32, (ca.batch,))
+    if dropped is not None:
+        _need(dropped, "dropped", torch.int32, (1,))
+    if out is _AUTO:
+        out = torch.empty(c0.batch, hq, c0.dv, dtype=torch.float32,
+                          device=q.device)
+    cin, cout = _carries(c0, hq, carry_in, carry_out, out)
+    need = library().gqa_attend_branches_workspace_bytes(arr, len(arr), hq)
+    if need == 0:
+        raise GqaError("decode_step_branches: invalid or unsupported branches")
+    if workspace is None:
+        workspace = _workspace(need, q.device)
+    _need(workspace, "workspace")
+    _check(library().gqa_decode_step_branches(
+        _ptr(q), hq, arr, len(arr), int(append_branch), _ptr(k_new),
+        _ptr(v_new), _ptr(lens_out), _ptr(dropped), float(scale), cin, cout,
+        _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(q)), "decode_step_branches")
+    return out
 

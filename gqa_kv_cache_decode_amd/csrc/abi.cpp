@@ -194,6 +194,7 @@ void single_branch(PartitionArgs *a) {
   a->col_base = 0;
   a->total_items = a->batch * a->num_kv_heads * a->num_chunks;
   a->num_extra = 0;
+  a->append_branch = 0;
 }
 
 // Enqueues the schedule kernel of a scheduled plan and points the partition
@@ -377,6 +378,9 @@ gqa_status plan_branches(const gqa_branch *br, int32_t n, int32_t hq,
     p->chunk[i] = one.chunk_tokens;
     p->num_chunks[i] = one.num_chunks;
     p->col_base[i] = (int32_t)cols;
+    // each branch's blocks start at a multiple of 8 so that its items spread
+    // evenly over the eight XCDs (block i runs on XCD i % 8)
+    items = (items + 7) / 8 * 8;
     p->item_base[i] = items;
     cols += one.num_chunks;
     items += (int64_t)c->batch * c->num_kv_heads * one.num_chunks;
@@ -393,6 +397,133 @@ gqa_status plan_branches(const gqa_branch *br, int32_t n, int32_t hq,
   p->off_acc = p->off_l + align_up(ml);
   p->workspace_bytes = p->off_acc + align_up(ml * br[0].cache.dv);
   return GQA_OK;
+}
+
+// Inputs of a multi-branch decode step: the new token goes to one branch.
+struct BranchStep {
+  int32_t append_branch;
+  const void *k_new, *v_new;
+  int32_t *lens_out, *dropped;
+};
+
+gqa_status branches_checked(const void *q, int32_t num_q_heads,
+                            const gqa_branch *branches, int32_t num_branches,
+                            float scale, const gqa_carry *carry_in,
+                            const gqa_carry *carry_out, float *out,
+                            void *workspace, size_t workspace_bytes,
+                            const BranchStep *step, hipStream_t stream) {
+  BranchesPlan p;
+  gqa_status st = plan_branches(branches, num_branches, num_q_heads, &p);
+  if (st != GQA_OK) return st;
+  bool any_bias = false;
+  for (int32_t i = 0; i < num_branches; ++i) {
+    const gqa_branch &b = branches[i];
+    if ((st = check_attend_args(q, num_q_heads, &b.cache, b.lens, scale)) !=
+        GQA_OK)
+      return st;
+    if ((st = check_cache_data(&b.cache)) != GQA_OK) return st;
+    if ((st = check_bias(&b.cache, b.bias, b.bias_stride)) != GQA_OK) return st;
+    any_bias = any_bias || b.bias != nullptr;
+  }
+  const gqa_cache *c0 = &branches[0].cache;
+  if ((st = check_combine_args(num_q_heads, c0, branches[0].lens, carry_in,
+                               carry_out, out)) != GQA_OK)
+    return st;
+  if (step) {
+    const int32_t ab = step->append_branch;
+    if (ab < 0 || ab >= num_branches) return GQA_ERR_INVALID_ARGUMENT;
+    if (!step->k_new || !step->v_new || !step->lens_out ||
+        step->lens_out == branches[ab].lens)
+      return GQA_ERR_INVALID_ARGUMENT;
+    if (!aligned16(step->k_new) || !aligned16(step->v_new))
+      return GQA_ERR_INVALID_ARGUMENT;
+  }
+  if (!workspace || !aligned16(workspace)) return GQA_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < p.workspace_bytes) return GQA_ERR_WORKSPACE_TOO_SMALL;
+
+  const double sc =
+      scale != 0.0f ? (double)scale : 1.0 / std::sqrt((double)c0->dk);
+  PartitionArgs a;
+  a.q = q;
+  a.k = c0->k;
+  a.v = c0->v;
+  a.lens = branches[0].lens;
+  a.batch = c0->batch;
+  a.max_len = c0->max_len;
+  a.num_kv_heads = c0->num_kv_heads;
+  a.hpk = num_q_heads / c0->num_kv_heads;
+  a.dk = c0->dk;
+  a.dv = c0->dv;
+  a.chunk_tokens = p.chunk[0];
+  a.num_chunks = p.num_chunks[0];
+  a.total_cols = p.total_cols;
+  a.col_base = 0;
+  a.total_items = (int)p.total_items;
+  a.num_extra = num_branches - 1;
+  a.append_branch = step ? step->append_branch : -1;
+  for (int32_t i = 1; i < num_branches; ++i) {
+    const gqa_branch &b = branches[i];
+    gqa::ExtraBranch &x = a.extra[i - 1];
+    x.k = b.cache.k;
+    x.v = b.cache.v;
+    x.lens = b.lens;
+    x.bias = b.bias;
+    x.bias_stride = b.bias ? b.bias_stride : 0;
+    x.max_len = b.cache.max_len;
+    x.chunk_tokens = p.chunk[i];
+    x.num_chunks = p.num_chunks[i];
+    x.col_base = p.col_base[i];
+    x.item_base = (int)p.item_base[i];
+  }
+  a.scale_log2 = (float)(sc * 1.4426950408889634);
+  a.bias = branches[0].bias;
+  a.bias_stride = a.bias ? branches[0].bias_stride : 0;
+  a.has_bias = any_bias ? 1 : 0;
+  char *base = static_cast<char *>(workspace);
+  a.part_m = reinterpret_cast<float *>(base);
+  a.part_l = reinterpret_cast<float *>(base + p.off_l);
+  a.part_acc = reinterpret_cast<float *>(base + p.off_acc);
+  a.sched = nullptr;
+  a.sched_len = 0;
+  const bool bf16 = c0->dtype == GQA_DTYPE_BF16;
+  if (step) {
+    gqa::StepParams sp{};
+    sp.k_new = step->k_new;
+    sp.v_new = step->v_new;
+    sp.lens_in = branches[step->append_branch].lens;
+    sp.lens_out = step->lens_out;
+    sp.dropped = step->dropped;
+    st = device_status(bf16 ? gqa::launch_step_bf16(a, sp, stream)
+                            : gqa::launch_step_f32(a, sp, stream));
+  } else {
+    st = device_status(bf16 ? gqa::launch_partition_bf16(a, gqa::StepParams{}, stream)
+                            : gqa::launch_partition_f32(a, gqa::StepParams{}, stream));
+  }
+  if (st != GQA_OK) return st;
+
+  CombineArgs cb;
+  cb.batch = c0->batch;
+  cb.num_q_heads = num_q_heads;
+  cb.dv = c0->dv;
+  cb.total_cols = p.total_cols;
+  cb.num_branches = num_branches;
+  for (int32_t i = 0; i < num_branches; ++i) {
+    const int32_t *lens = branches[i].lens;
+    if (step && i == step->append_branch) lens = step->lens_out;
+    cb.br[i] = gqa::CombineBranch{lens, branches[i].cache.max_len, p.chunk[i],
+                                  p.col_base[i]};
+  }
+  cb.part_m = a.part_m;
+  cb.part_l = a.part_l;
+  cb.part_acc = a.part_acc;
+  cb.in_m = carry_in ? carry_in->m : nullptr;
+  cb.in_l = carry_in ? carry_in->l : nullptr;
+  cb.in_acc = carry_in ? carry_in->acc : nullptr;
+  cb.out_m = carry_out ? carry_out->m : nullptr;
+  cb.out_l = carry_out ? carry_out->l : nullptr;
+  cb.out_acc = carry_out ? carry_out->acc : nullptr;
+  cb.out = out;
+  return device_status(gqa::launch_combine(cb, stream));
 }
 
 }  // namespace
@@ -606,93 +737,21 @@ gqa_status gqa_attend_branches(const void *q, int32_t num_q_heads,
                                const gqa_carry *carry_out, float *out,
                                void *workspace, size_t workspace_bytes,
                                hipStream_t stream) {
-  BranchesPlan p;
-  gqa_status st = plan_branches(branches, num_branches, num_q_heads, &p);
-  if (st != GQA_OK) return st;
-  bool any_bias = false;
-  for (int32_t i = 0; i < num_branches; ++i) {
-    const gqa_branch &b = branches[i];
-    if ((st = check_attend_args(q, num_q_heads, &b.cache, b.lens, scale)) !=
-        GQA_OK)
-      return st;
-    if ((st = check_bias(&b.cache, b.bias, b.bias_stride)) != GQA_OK) return st;
-    any_bias = any_bias || b.bias != nullptr;
-  }
-  const gqa_cache *c0 = &branches[0].cache;
-  if ((st = check_combine_args(num_q_heads, c0, branches[0].lens, carry_in,
-                               carry_out, out)) != GQA_OK)
-    return st;
-  if (!workspace || !aligned16(workspace)) return GQA_ERR_INVALID_ARGUMENT;
-  if (workspace_bytes < p.workspace_bytes) return GQA_ERR_WORKSPACE_TOO_SMALL;
+  return branches_checked(q, num_q_heads, branches, num_branches, scale,
+                          carry_in, carry_out, out, workspace,
+                          workspace_bytes, nullptr, stream);
+}
 
-  const double sc =
-      scale != 0.0f ? (double)scale : 1.0 / std::sqrt((double)c0->dk);
-  PartitionArgs a;
-  a.q = q;
-  a.k = c0->k;
-  a.v = c0->v;
-  a.lens = branches[0].lens;
-  a.batch = c0->batch;
-  a.max_len = c0->max_len;
-  a.num_kv_heads = c0->num_kv_heads;
-  a.hpk = num_q_heads / c0->num_kv_heads;
-  a.dk = c0->dk;
-  a.dv = c0->dv;
-  a.chunk_tokens = p.chunk[0];
-  a.num_chunks = p.num_chunks[0];
-  a.total_cols = p.total_cols;
-  a.col_base = 0;
-  a.total_items = (int)p.total_items;
-  a.num_extra = num_branches - 1;
-  for (int32_t i = 1; i < num_branches; ++i) {
-    const gqa_branch &b = branches[i];
-    gqa::ExtraBranch &x = a.extra[i - 1];
-    x.k = b.cache.k;
-    x.v = b.cache.v;
-    x.lens = b.lens;
-    x.bias = b.bias;
-    x.bias_stride = b.bias ? b.bias_stride : 0;
-    x.max_len = b.cache.max_len;
-    x.chunk_tokens = p.chunk[i];
-    x.num_chunks = p.num_chunks[i];
-    x.col_base = p.col_base[i];
-    x.item_base = (int)p.item_base[i];
-  }
-  a.scale_log2 = (float)(sc * 1.4426950408889634);
-  a.bias = branches[0].bias;
-  a.bias_stride = a.bias ? branches[0].bias_stride : 0;
-  a.has_bias = any_bias ? 1 : 0;
-  char *base = static_cast<char *>(workspace);
-  a.part_m = reinterpret_cast<float *>(base);
-  a.part_l = reinterpret_cast<float *>(base + p.off_l);
-  a.part_acc = reinterpret_cast<float *>(base + p.off_acc);
-  a.sched = nullptr;
-  a.sched_len = 0;
-  st = device_status(c0->dtype == GQA_DTYPE_BF16
-                         ? gqa::launch_partition_bf16(a, gqa::StepParams{}, stream)
-                         : gqa::launch_partition_f32(a, gqa::StepParams{}, stream));
-  if (st != GQA_OK) return st;
-
-  CombineArgs cb;
-  cb.batch = c0->batch;
-  cb.num_q_heads = num_q_heads;
-  cb.dv = c0->dv;
-  cb.total_cols = p.total_cols;
-  cb.num_branches = num_branches;
-  for (int32_t i = 0; i < num_branches; ++i)
-    cb.br[i] = gqa::CombineBranch{branches[i].lens, branches[i].cache.max_len,
-                                  p.chunk[i], p.col_base[i]};
-  cb.part_m = a.part_m;
-  cb.part_l = a.part_l;
-  cb.part_acc = a.part_acc;
-  cb.in_m = carry_in ? carry_in->m : nullptr;
-  cb.in_l = carry_in ? carry_in->l : nullptr;
-  cb.in_acc = carry_in ? carry_in->acc : nullptr;
-  cb.out_m = carry_out ? carry_out->m : nullptr;
-  cb.out_l = carry_out ? carry_out->l : nullptr;
-  cb.out_acc = carry_out ? carry_out->acc : nullptr;
-  cb.out = out;
-  return device_status(gqa::launch_combine(cb, stream));
+gqa_status gqa_decode_step_branches(
+    const void *q, int32_t num_q_heads, const gqa_branch *branches,
+    int32_t num_branches, int32_t append_branch, const void *k_new,
+    const void *v_new, int32_t *lens_out, int32_t *dropped, float scale,
+    const gqa_carry *carry_in, const gqa_carry *carry_out, float *out,
+    void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  const BranchStep step{append_branch, k_new, v_new, lens_out, dropped};
+  return branches_checked(q, num_q_heads, branches, num_branches, scale,
+                          carry_in, carry_out, out, workspace,
+                          workspace_bytes, &step, stream);
 }
 
 size_t gqa_decode_step_workspace_bytes(const gqa_cache *cache,

@@ -26,7 +26,7 @@ struct ExtraBranch {
   long long bias_stride;
   int max_len, chunk_tokens, num_chunks;
   int col_base;   // first partial column of the branch
-  int item_base;  // first work item of the branch
+  int item_base;  // first block of the branch (a multiple of 8)
 };
 
 constexpr int kMaxExtraBranches = 3;
@@ -43,6 +43,7 @@ struct PartitionArgs {
   // batch * num_kv_heads * num_chunks.
   int total_cols, col_base, total_items;
   int num_extra;        // branches after the first, 0..kMaxExtraBranches
+  int append_branch;    // decode step: the branch receiving the new token
   ExtraBranch extra[kMaxExtraBranches];
   float scale_log2;     // logit scale times log2(e)
   const float *bias;    // [B][bias_stride] additive logit terms, or NULL

@@ -70,23 +70,30 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
   __shared__ float s_in[32];  // carry_in m, l of the group's rows (direct)
 
   PartitionArgs a = args;
-  int item;
+  int item, branch = 0;
   if (a.sched) {  // scheduled launch: the table entry, or nothing to do
     item = a.sched[blockIdx.x];
     if (item < 0) return;
   } else {
-    item = xcd_local_item(blockIdx.x, a.total_items);
+    // the block's branch (multi-branch launch: each branch owns a block
+    // range starting at a multiple of 8), then its item within the branch
+    item = blockIdx.x;
+    branch = select_branch(a, item);
+    const int nitems = a.batch * a.num_kv_heads * a.num_chunks;
+    if (item >= nitems) return;  // padding up to the next branch
+    item = xcd_local_item(item, nitems);
   }
-  select_branch(a, item);  // multi-branch launch: the item's cache
   const int Hkv = a.num_kv_heads, hpk = a.hpk, nchunk = a.num_chunks;
   const int c = item % nchunk;
   const int bg = item / nchunk;
   const int g = bg % Hkv;
   const int b = bg / Hkv;
 
-  const SeqLen sl = seq_len<STEP>(a, sp, b);
+  // decode step: this branch takes the new token (the others attend as is)
+  const bool stepping = STEP && branch == a.append_branch;
+  const SeqLen sl = seq_len(a, sp, b, stepping);
   const int n = sl.n;
-  if (STEP && g == 0 && c == 0 && threadIdx.x == 0) step_bookkeeping(sp, b, sl);
+  if (stepping && g == 0 && c == 0 && threadIdx.x == 0) step_bookkeeping(sp, b, sl);
   const int t0 = c * a.chunk_tokens;
   // A work-group with nothing live exits, except the first of an empty
   // sequence when final results are written in this launch: it still writes
@@ -130,7 +137,7 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
   // slot is the last live token of the chunk, relative position `rel`).
   const uint16_t *knew = nullptr, *vnew = nullptr;
   int rel = -1;
-  if (STEP && sl.fresh && sl.n_old / a.chunk_tokens == c) {
+  if (stepping && sl.fresh && sl.n_old / a.chunk_tokens == c) {
     rel = sl.n_old - t0;
     knew = static_cast<const uint16_t *>(sp.k_new) + ((size_t)b * Hkv + g) * DK;
     vnew = static_cast<const uint16_t *>(sp.v_new) + ((size_t)b * Hkv + g) * DV;

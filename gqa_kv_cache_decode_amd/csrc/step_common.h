@@ -13,13 +13,14 @@ namespace gqa {
 // vector memory access of the wavefront, stores included, has completed.
 constexpr int kWaitVmcnt0 = 0x0F70;
 
-// Points `a` at the branch that owns work item `item` of a multi-branch
-// launch (branches hold ascending item ranges) and makes `item` local to it.
-__device__ __forceinline__ void select_branch(PartitionArgs &a, int &item) {
-  int base = 0;
+// Points `a` at the branch that owns block `item` of a multi-branch launch
+// (branches hold ascending block ranges) and makes `item` local to it.
+__device__ __forceinline__ int select_branch(PartitionArgs &a, int &item) {
+  int base = 0, branch = 0;
 #pragma unroll
   for (int e = 0; e < kMaxExtraBranches; ++e) {
     if (e < a.num_extra && item >= a.extra[e].item_base) {
+      branch = e + 1;
       const ExtraBranch &x = a.extra[e];
       a.k = x.k;
       a.v = x.v;
@@ -34,6 +35,7 @@ __device__ __forceinline__ void select_branch(PartitionArgs &a, int &item) {
     }
   }
   item -= base;
+  return branch;
 }
 
 // Keys attended by sequence b, and the slot a decode step appends to.
@@ -44,13 +46,13 @@ struct SeqLen {
 };
 
 // needle-core decode order: push_kv, then attend over the cache including the
-// new token.  A full cache (or a negative length) is left as it is: the step
+// new token (`stepping`: this branch receives the token of a decode step).  A full cache (or a negative length) is left as it is: the step
 // attends over what is there and the drop is counted.
-template <bool STEP>
 __device__ __forceinline__ SeqLen seq_len(const PartitionArgs &a,
-                                          const StepParams &sp, int b) {
+                                          const StepParams &sp, int b,
+                                          bool stepping) {
   SeqLen s;
-  if (STEP) {
+  if (stepping) {
     s.n_old = sp.lens_in[b];
     s.fresh = s.n_old >= 0 && s.n_old < a.max_len;
     s.n = s.fresh ? s.n_old + 1 : clamp_len(s.n_old, a.max_len);

@@ -325,6 +325,24 @@ GQA_API gqa_status gqa_attend_branches(const void *q, int32_t num_q_heads,
                                        hipStream_t stream);
 
 /*
+ * decode_step_branches — decode_step over several caches: the new token
+ * (k_new, v_new) is appended to branch `append_branch` at slot lens[b] of
+ * that branch (its `lens` field is the lens_in of gqa_decode_step; a full
+ * cache or negative length drops the token and counts it in *dropped), and
+ * the queries attend over every branch's keys including the new token, in
+ * one partition launch and one combine.  lens_out [batch] receives the
+ * append branch's new lengths and must not alias its lens.  The workspace
+ * is that of gqa_attend_branches (no initialisation needed).  E.g. a long
+ * cache attended as is plus the recent window taking the new token.
+ */
+GQA_API gqa_status gqa_decode_step_branches(
+    const void *q, int32_t num_q_heads, const gqa_branch *branches,
+    int32_t num_branches, int32_t append_branch, const void *k_new,
+    const void *v_new, int32_t *lens_out, int32_t *dropped, float scale,
+    const gqa_carry *carry_in, const gqa_carry *carry_out, float *out,
+    void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * softmax_state_merge — dst = merge(a, b) row by row (usearch carry,
  * partial softmaxes rescaled to a common maximum): m = max(m_a, m_b),
  * l = e^(m_a-m) l_a +

@@ -30,7 +30,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(lib, n), f"missing export {n}"
     assert set(names) == set(bd._SIGNATURES), "binding covers the header"
@@ -254,3 +254,25 @@ def test_stream_append_checks(lib):
         assert call(None, ring, bad) == SHAPE
     odd = _cache(B=4, T=16, H=1, dk=3, dv=3)   # 6-byte rows
     assert call(None, odd, None) == UNSUPPORTED
+
+
+def test_decode_step_branches_checks(lib):
+    main = _cache(B=1, T=262144, H=4)
+    win = _cache(B=1, T=128, H=4, k=0x30000, v=0x38000)
+    arr = (bd._Branch * 2)(_branch(main), _branch(win, lens=0x48000))
+    nbytes = lib.gqa_attend_branches_workspace_bytes(arr, 2, 32)
+    q, kn, vn, lo, out, ws = (ctypes.c_void_p(x) for x in
+                              (0x50000, 0x51000, 0x52000, 0x53000, 0x60000,
+                               0x70000))
+    f = lib.gqa_decode_step_branches
+
+    def call(ab, lo_=lo, kn_=kn, n=nbytes):
+        return f(q, 32, arr, 2, ab, kn_, vn, lo_, None, 0.0, None, None, out,
+                 ws, n, None)
+
+    assert call(2) == INVALID                       # no such branch
+    assert call(-1) == INVALID
+    assert call(1, lo_=ctypes.c_void_p(0x48000)) == INVALID  # lens_out = lens
+    assert call(1, lo_=None) == INVALID
+    assert call(1, kn_=ctypes.c_void_p(0x51004)) == INVALID  # misaligned
+    assert call(1, n=nbytes - 1) == WORKSPACE

@@ -185,3 +185,50 @@ def test_attend_branches(dt, dk, dv, Hq, Hkv, nbr):
     check_out(out.cpu().numpy(), want, vmax, dt, f"branches x{nbr}")
     check_carry(carry.m.cpu().numpy(), carry.l.cpu().numpy(), cw.m, cw.l, dt,
                 f"branches x{nbr} carry")
+
+
+@pytest.mark.parametrize("dt,dk,dv,Hq,Hkv", [("bf16", 128, 128, 32, 4),
+                                             ("bf16", 192, 128, 16, 1),
+                                             ("f32", 64, 64, 8, 4)])
+def test_decode_step_branches(dt, dk, dv, Hq, Hkv):
+    """A long cache attended as is plus a window taking the new token (with a
+    bias on the window), one partition launch and one combine: the window
+    after the append bit for bit, lens and drops exactly, out and carry
+    against the oracle (append, then attend over both branches)."""
+    g = _gqa()
+    B = 4
+    gen = torch.Generator().manual_seed(63)
+    tdt = wl.DTYPES[dt]
+    q = torch.randn(B, Hq, dk, generator=gen).to(tdt)
+    mk, mv = _cache(B, 3000, Hkv, dk, dt, 91), _cache(B, 3000, Hkv, dv, dt, 92)
+    wk, wv = _cache(B, 128, Hkv, dk, dt, 93), _cache(B, 128, Hkv, dv, dt, 94)
+    mlens = torch.tensor([3000, 1, 0, 2047], dtype=torch.int32)
+    wlens = torch.tensor([127, 0, 128, -1], dtype=torch.int32)  # 2 drops
+    kn = torch.randn(B, Hkv, dk, generator=gen).to(tdt)
+    vn = torch.randn(B, Hkv, dv, generator=gen).to(tdt)
+    bias = torch.randn(B, 128, generator=gen)
+    wkd, wvd = wk.cuda(), wv.cuda()
+    lo = torch.full((B,), -7, dtype=torch.int32, device="cuda")
+    dropped = torch.zeros(1, dtype=torch.int32, device="cuda")
+    cout = g.empty_carry(B * Hq, dv)
+    out = g.decode_step_branches(
+        q.cuda(), [(mk.cuda(), mv.cuda(), mlens.cuda()),
+                   (wkd, wvd, wlens.cuda(), bias.cuda())], 1, kn.cuda(),
+        vn.cuda(), lo, 0.0, carry_out=cout, dropped=dropped)
+    torch.cuda.synchronize()
+    k_ref, v_ref, l_ref, drop_ref = oracle.kv_append(
+        _bits(wk).numpy(), _bits(wv).numpy(), _bits(kn).numpy(),
+        _bits(vn).numpy(), wlens.numpy())
+    assert np.array_equal(_bits(wkd.cpu()).numpy(), k_ref), "window K"
+    assert np.array_equal(_bits(wvd.cpu()).numpy(), v_ref), "window V"
+    assert lo.cpu().tolist() == l_ref.tolist(), "lens_out"
+    assert int(dropped.item()) == drop_ref == 2, "dropped"
+    wk2 = torch.from_numpy(k_ref).view(tdt)
+    wv2 = torch.from_numpy(v_ref).view(tdt)
+    want, cw = ost.attend_branches(
+        np64(q), [(np64(mk), np64(mv), mlens.numpy()),
+                  (np64(wk2), np64(wv2), l_ref, bias.double().numpy())], 0.0)
+    vmax = max(float(mv.float().abs().max()), float(wv2.float().abs().max()))
+    check_out(out.cpu().numpy(), want, vmax, dt, "decode_step_branches")
+    check_carry(cout.m.cpu().numpy(), cout.l.cpu().numpy(), cw.m, cw.l, dt,
+                "decode_step_branches carry")
