@@ -96,3 +96,34 @@ def stream_append(sink_k, sink_v, ring_k, ring_v, main_k, main_v,
         rv[b, r] = v_new[b]
         out[b] = t + 1
     return sk, sv, rk, rv, mk, mv, out.astype(np.int32), dropped
+
+
+def selection_mask(idx_row, kv_len: int) -> np.ndarray:
+    """metrale DSA ``topk_to_mask`` for one query row: key i is visible when
+    some entry equals i with 0 <= i < kv_len; duplicates collapse to one
+    visible key and out-of-range or INVALID (negative) entries are dropped."""
+    mask = np.zeros(max(int(kv_len), 0), dtype=bool)
+    for i in np.asarray(idx_row).ravel():
+        i = int(i)
+        if 0 <= i < kv_len:
+            mask[i] = True
+    return mask
+
+
+def attend_gathered(q, k, v, lens, idx, scale: float = 0.0,
+                    carry_in: Optional[Carry] = None):
+    """Attention of each sequence's query over the keys its index row
+    selects (``selection_mask`` with kv_len = the sequence's live length),
+    taken in ascending position order.  idx [B, width] int."""
+    B = np.asarray(q).shape[0]
+    T = np.asarray(k).shape[1]
+    kc = np.full_like(np.asarray(k, dtype=np.float64), np.nan)
+    vc = np.full_like(np.asarray(v, dtype=np.float64), np.nan)
+    n_sel = np.zeros(B, dtype=np.int64)
+    for b in range(B):
+        n = int(min(max(int(lens[b]), 0), T))
+        sel = np.nonzero(selection_mask(idx[b], n))[0]
+        n_sel[b] = len(sel)
+        kc[b, :len(sel)] = np.asarray(k[b], dtype=np.float64)[sel]
+        vc[b, :len(sel)] = np.asarray(v[b], dtype=np.float64)[sel]
+    return attend(q, kc, vc, n_sel, scale, carry_in=carry_in)

@@ -548,3 +548,45 @@ def pin_stream(orc_stream):
 
 
 STREAM_PINS = [pin_branches, pin_stream]
+
+
+def pin_gathered(orc_stream):
+    """Index-gathered decode (metrale DSA topk_to_mask): equals attention
+    with a -inf bias on every unselected key (the bias path is pinned on its
+    own); duplicates collapse (a row with repeats equals the deduplicated
+    row); order does not matter; INVALID and out-of-range entries drop; a
+    row selecting [0, n) equals plain attention over n keys; a row selecting
+    nothing is empty."""
+    import oracle.attention as att
+    rng = np.random.default_rng(23)
+    B, Hq, Hkv, dk, dv, T = 4, 8, 4, 16, 8, 40
+    q, k, v, lens = _problem(24, B, Hq, Hkv, dk, dv, T, lens=[40, 25, 7, 30])
+    width = 12
+    idx = rng.integers(0, 40, (B, width))
+    idx[0, :3] = -1                  # INVALID padding
+    idx[1, 4] = idx[1, 5] = 3        # a duplicate
+    idx[1, 6] = 38                   # past the live length (25)
+    idx[2] = -1                      # selects nothing
+    idx[3] = np.r_[np.arange(10), -1, -1]   # the prefix [0, 10)
+    out, c = orc_stream.attend_gathered(q, k, v, lens, idx, scale=0.4)
+    bias = np.full((B, T), -np.inf)
+    for b in range(B):
+        for i in idx[b]:
+            if 0 <= i < min(lens[b], T):
+                bias[b, i] = 0.0
+    want, cw = att.attend(q, k, v, lens, scale=0.4, bias=bias)
+    _close(out, want, 1e-14, "gathered = masked by a -inf bias")
+    _close(c.l, cw.l, 1e-12, "gathered l")
+    assert np.all(out[2] == 0.0) and np.all(c.l[16:24] == 0.0), \
+        "nothing selected: empty"
+    want3, _ = att.attend(q[3:4], k[3:4], v[3:4], [10], scale=0.4)
+    _close(out[3], want3[0], 1e-14, "prefix selection = plain attention")
+    dedup = idx.copy()
+    dedup[1, 5] = -1
+    perm = rng.permutation(width)
+    out2, _ = orc_stream.attend_gathered(q, k, v, lens, dedup[:, perm],
+                                         scale=0.4)
+    _close(out2, out, 1e-14, "duplicates collapse; order is free")
+
+
+STREAM_PINS.append(pin_gathered)

@@ -15,6 +15,20 @@ def test_stream_pin(pin):
 
 _real_append = st.stream_append
 _real_lengths = st.stream_lengths
+_real_mask = st.selection_mask
+
+
+def _mask_counts_dups(row, n):
+    """a duplicated entry selects the next key too (no collapse)"""
+    m = _real_mask(row, n)
+    seen = set()
+    for i in np.asarray(row).ravel():
+        i = int(i)
+        if 0 <= i < n:
+            if i in seen and i + 1 < n:
+                m[i + 1] = True
+            seen.add(i)
+    return m
 
 
 def _ring_slot_shifted(sk, sv, rk, rv, mk, mv, kn, vn, count):
@@ -49,6 +63,9 @@ MUTANTS = {
     "main_off_by_one": ("stream_lengths",
                         lambda c, s, w, m: _real_lengths(c, s, w, m)[:2] +
                         (max(_real_lengths(c, s, w, m)[2] - 1, 0),)),
+    "selection_keeps_duplicates": ("selection_mask", _mask_counts_dups),
+    "selection_ignores_length": ("selection_mask",
+                                 lambda row, n: _real_mask(row, 10 ** 6)),
     "branches_drop_carry": ("attend_branches",
                             lambda q, brs, scale=0.0, carry_in=None:
                             _real_branches(q, brs, scale)),
