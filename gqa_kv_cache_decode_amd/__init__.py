@@ -9,7 +9,7 @@ library is loaded on first use and a missing build raises at once.
 
 __all__ = ["kv_append", "attend_decode", "softmax_state_merge",
            "decode_step", "step_workspace", "attend_branches",
-           "stream_append", "decode_step_branches",
+           "stream_append", "decode_step_branches", "attend_gathered",
            "attend_partition", "attend_combine", "attend_plan",
            "workspace_bytes", "Carry", "empty_carry", "GqaError", "library"]
 

@@ -62,6 +62,11 @@ _PLAN_P = ctypes.POINTER(Plan)
 _BRANCH_P = ctypes.POINTER(_Branch)
 
 _SIGNATURES = {
+    "gqa_attend_gathered_workspace_bytes": (ctypes.c_size_t,
+                                            [_CACHE_P, _I32, _I32]),
+    "gqa_attend_gathered": (_I32, [_P, _I32, _CACHE_P, _P, _P, _I32,
+                                   ctypes.c_float, _CARRY_P, _CARRY_P, _P, _P,
+                                   ctypes.c_size_t, _P]),
     "gqa_decode_step_branches": (_I32, [_P, _I32, _BRANCH_P, _I32, _I32, _P,
                                         _P, _P, _P, ctypes.c_float, _CARRY_P,
                                         _CARRY_P, _P, _P, ctypes.c_size_t,
@@ -489,5 +494,36 @@ def decode_step_branches(q, branches, append_branch: int, k_new, v_new,
         _ptr(v_new), _ptr(lens_out), _ptr(dropped), float(scale), cin, cout,
         _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(q)), "decode_step_branches")
+    return out
+
+
+def attend_gathered(q, k_cache, v_cache, lens, idx, scale: float = 0.0,
+                    carry_in: Optional[Carry] = None,
+                    carry_out: Optional[Carry] = None, out=_AUTO,
+                    workspace: Optional[torch.Tensor] = None):
+    """Index-gathered decode: each sequence attends only the cache slots its
+    row of ``idx`` [B, width] (device int32) names; duplicates collapse,
+    negative and out-of-range entries drop."""
+    c, hq = _attend_args(q, k_cache, v_cache, lens)
+    _need(idx, "idx", torch.int32)
+    if idx.dim() != 2 or idx.shape[0] != c.batch:
+        raise GqaError(f"idx must be [batch={c.batch}, width]")
+    width = int(idx.shape[1])
+    if out is _AUTO:
+        out = torch.empty(c.batch, hq, c.dv, dtype=torch.float32,
+                          device=q.device)
+    cin, cout = _carries(c, hq, carry_in, carry_out, out)
+    need = library().gqa_attend_gathered_workspace_bytes(ctypes.byref(c), hq,
+                                                         width)
+    if need == 0:
+        raise GqaError("attend_gathered: unsupported shape")
+    if workspace is None:
+        workspace = _workspace(need, q.device)
+    _need(workspace, "workspace")
+    _check(library().gqa_attend_gathered(
+        _ptr(q), hq, ctypes.byref(c), _ptr(lens), _ptr(idx), width,
+        float(scale), cin, cout, _ptr(out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(q)),
+        "attend_gathered")
     return out
 

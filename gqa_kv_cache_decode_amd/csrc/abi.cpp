@@ -195,6 +195,8 @@ void single_branch(PartitionArgs *a) {
   a->total_items = a->batch * a->num_kv_heads * a->num_chunks;
   a->num_extra = 0;
   a->append_branch = 0;
+  a->sel = nullptr;
+  a->cache_len = a->max_len;
 }
 
 // Enqueues the schedule kernel of a scheduled plan and points the partition
@@ -461,6 +463,8 @@ gqa_status branches_checked(const void *q, int32_t num_q_heads,
   a.total_items = (int)p.total_items;
   a.num_extra = num_branches - 1;
   a.append_branch = step ? step->append_branch : -1;
+  a.sel = nullptr;
+  a.cache_len = c0->max_len;
   for (int32_t i = 1; i < num_branches; ++i) {
     const gqa_branch &b = branches[i];
     gqa::ExtraBranch &x = a.extra[i - 1];
@@ -524,6 +528,44 @@ gqa_status branches_checked(const void *q, int32_t num_q_heads,
   cb.out_acc = carry_out ? carry_out->acc : nullptr;
   cb.out = out;
   return device_status(gqa::launch_combine(cb, stream));
+}
+
+// Layout of an index-gathered attend: the split-K plan of the selection
+// (a cache of min(width, max_len) slots per sequence, chunks of at most
+// kGatherChunk), then the selected slots [batch][sel_cap] and their counts.
+struct GatherPlan {
+  gqa_cache vcache;
+  gqa_plan plan;
+  int32_t sel_cap;
+  size_t off_sel, off_count, workspace_bytes;
+};
+
+constexpr int32_t kGatherMaxLen = 1 << 20;  // LDS bitmap of the selection
+
+gqa_status plan_gathered(const gqa_cache *c, int32_t hq, int32_t width,
+                         GatherPlan *g) {
+  gqa_status st = check_cache_dims(c);
+  if (st != GQA_OK) return st;
+  if ((st = check_heads(c, hq)) != GQA_OK) return st;
+  if (width < 1) return GQA_ERR_INVALID_ARGUMENT;
+  if (!uses_mfma(c) || c->max_len > kGatherMaxLen) return GQA_ERR_UNSUPPORTED;
+  // gathered rows are addressed with 32-bit offsets from the sequence start
+  const int64_t span = (int64_t)c->max_len * c->num_kv_heads *
+                       (c->dk > c->dv ? c->dk : c->dv) * esize(c->dtype);
+  if (span >= ((int64_t)1 << 31)) return GQA_ERR_UNSUPPORTED;
+  g->sel_cap = width < c->max_len ? width : c->max_len;
+  g->vcache = *c;
+  g->vcache.max_len = g->sel_cap;
+  if ((st = make_plan(&g->vcache, hq, 0, &g->plan)) != GQA_OK) return st;
+  if (g->plan.chunk_tokens > gqa::kGatherChunk &&
+      (st = make_plan(&g->vcache, hq, gqa::kGatherChunk, &g->plan)) != GQA_OK)
+    return st;
+  g->off_sel = g->plan.workspace_bytes;
+  g->off_count =
+      g->off_sel + align_up((size_t)c->batch * g->sel_cap * sizeof(int32_t));
+  g->workspace_bytes =
+      g->off_count + align_up((size_t)c->batch * sizeof(int32_t));
+  return GQA_OK;
 }
 
 }  // namespace
@@ -752,6 +794,86 @@ gqa_status gqa_decode_step_branches(
   return branches_checked(q, num_q_heads, branches, num_branches, scale,
                           carry_in, carry_out, out, workspace,
                           workspace_bytes, &step, stream);
+}
+
+size_t gqa_attend_gathered_workspace_bytes(const gqa_cache *cache,
+                                           int32_t num_q_heads,
+                                           int32_t width) {
+  GatherPlan g;
+  return plan_gathered(cache, num_q_heads, width, &g) == GQA_OK
+             ? g.workspace_bytes
+             : 0;
+}
+
+gqa_status gqa_attend_gathered(const void *q, int32_t num_q_heads,
+                               const gqa_cache *cache, const int32_t *lens,
+                               const int32_t *idx, int32_t width, float scale,
+                               const gqa_carry *carry_in,
+                               const gqa_carry *carry_out, float *out,
+                               void *workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  gqa_status st = check_attend_args(q, num_q_heads, cache, lens, scale);
+  if (st != GQA_OK) return st;
+  if ((st = check_combine_args(num_q_heads, cache, lens, carry_in, carry_out,
+                               out)) != GQA_OK)
+    return st;
+  if (!idx) return GQA_ERR_INVALID_ARGUMENT;
+  GatherPlan g;
+  if ((st = plan_gathered(cache, num_q_heads, width, &g)) != GQA_OK) return st;
+  if (!workspace || !aligned16(workspace)) return GQA_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < g.workspace_bytes) return GQA_ERR_WORKSPACE_TOO_SMALL;
+  char *base = static_cast<char *>(workspace);
+  int32_t *sel = reinterpret_cast<int32_t *>(base + g.off_sel);
+  int32_t *count = reinterpret_cast<int32_t *>(base + g.off_count);
+
+  gqa::SelectArgs sa;
+  sa.idx = idx;
+  sa.width = width;
+  sa.lens = lens;
+  sa.batch = cache->batch;
+  sa.max_len = cache->max_len;
+  sa.sel = sel;
+  sa.sel_stride = g.sel_cap;
+  sa.count = count;
+  if ((st = device_status(gqa::launch_select(sa, stream))) != GQA_OK) return st;
+
+  // the selection attended as a cache of sel_cap slots whose token t is
+  // cache slot sel[b][t]
+  const gqa::StepParams ep =
+      final_epilogue(&g.vcache, g.plan, carry_in, carry_out, out);
+  const double sc =
+      scale != 0.0f ? (double)scale : 1.0 / std::sqrt((double)cache->dk);
+  PartitionArgs a;
+  a.q = q;
+  a.k = cache->k;
+  a.v = cache->v;
+  a.lens = count;
+  a.batch = cache->batch;
+  a.max_len = g.sel_cap;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.hpk = num_q_heads / cache->num_kv_heads;
+  a.dk = cache->dk;
+  a.dv = cache->dv;
+  a.chunk_tokens = g.plan.chunk_tokens;
+  a.num_chunks = g.plan.num_chunks;
+  single_branch(&a);
+  a.sel = sel;
+  a.cache_len = cache->max_len;
+  a.scale_log2 = (float)(sc * 1.4426950408889634);
+  a.bias = nullptr;
+  a.bias_stride = 0;
+  a.has_bias = 0;
+  a.part_m = reinterpret_cast<float *>(base);
+  a.part_l = reinterpret_cast<float *>(base + g.plan.off_l);
+  a.part_acc = reinterpret_cast<float *>(base + g.plan.off_acc);
+  a.sched = nullptr;
+  a.sched_len = 0;
+  st = device_status(cache->dtype == GQA_DTYPE_BF16
+                         ? gqa::launch_partition_bf16(a, ep, stream)
+                         : gqa::launch_partition_f32(a, ep, stream));
+  if (st != GQA_OK || ep.direct) return st;
+  return combine_checked(num_q_heads, &g.vcache, count, &g.plan, workspace,
+                         carry_in, carry_out, out, stream);
 }
 
 size_t gqa_decode_step_workspace_bytes(const gqa_cache *cache,

@@ -49,6 +49,12 @@ struct PartitionArgs {
   const float *bias;    // [B][bias_stride] additive logit terms, or NULL
   long long bias_stride;
   int has_bias;         // any branch of the launch has a bias
+  // Index-gathered launch: token t < lens[b] of sequence b is cache slot
+  // sel[b * max_len + t] (max_len is then the selection's row width) of a
+  // cache holding cache_len slots per sequence.  NULL otherwise, with
+  // cache_len = max_len.
+  const int32_t *sel;
+  int cache_len;
   float *part_m;        // [rows][num_chunks]  (natural-log units)
   float *part_l;        // [rows][num_chunks]
   float *part_acc;      // [rows][num_chunks][dv]
@@ -136,6 +142,22 @@ struct StreamAppendArgs {
   int row_bytes_k, row_bytes_v;  // bytes of one token's K/V row (multiple of 4)
 };
 
+// Index-row selection (DSA topk_to_mask): per sequence, the distinct cache
+// slots s < clamp(lens[b], 0, max_len) named by idx[b][0..width), ascending,
+// into sel[b][0..count[b]) (row stride sel_stride).
+struct SelectArgs {
+  const int32_t *idx;
+  int width;
+  const int32_t *lens;
+  int batch, max_len;
+  int32_t *sel;
+  int sel_stride;
+  int32_t *count;
+};
+
+// Longest chunk of an index-gathered launch (its slots are staged in LDS).
+constexpr int kGatherChunk = 2048;
+
 // Kernel families compiled into the library.
 bool partition_bf16_supported(int dk, int dv, int hpk);
 bool partition_f32_supported(int dk, int dv, int hpk);
@@ -160,5 +182,7 @@ hipError_t launch_schedule(const ScheduleArgs &a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs &a, hipStream_t s);
 hipError_t launch_append(const AppendArgs &a, hipStream_t s);
 hipError_t launch_stream_append(const StreamAppendArgs &a, hipStream_t s);
+size_t select_lds_bytes(int max_len);
+hipError_t launch_select(const SelectArgs &a, hipStream_t s);
 
 }  // namespace gqa

@@ -57,7 +57,7 @@ struct Bf16Geom {
   static constexpr int waveLdsElems = kTileTokens * (kStride + vStride);
 };
 
-template <int DK, int DV, int NW, bool STEP, bool BIAS>
+template <int DK, int DV, int NW, bool STEP, bool BIAS, bool GATHER>
 __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
     PartitionArgs args, StepParams sp) {
   using G = Bf16Geom<DK, DV>;
@@ -68,6 +68,7 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
   __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
   __shared__ int s_flag;
   __shared__ float s_in[32];  // carry_in m, l of the group's rows (direct)
+  __shared__ int s_slot[GATHER ? kGatherChunk : 1];  // gathered cache slots
 
   PartitionArgs a = args;
   int item, branch = 0;
@@ -127,9 +128,9 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
   const size_t kTok = (size_t)Hkv * DK;  // elements between tokens
   const size_t vTok = (size_t)Hkv * DV;
   uint16_t *Kg = static_cast<uint16_t *>(const_cast<void *>(a.k)) +
-                 ((size_t)b * a.max_len * Hkv + g) * DK;
+                 ((size_t)b * a.cache_len * Hkv + g) * DK;
   uint16_t *Vg = static_cast<uint16_t *>(const_cast<void *>(a.v)) +
-                 ((size_t)b * a.max_len * Hkv + g) * DV;
+                 ((size_t)b * a.cache_len * Hkv + g) * DV;
 
   // STEP: the work-group whose chunk holds the new slot stores the token's
   // rows of this group into the cache.  The stores are not waited for: later
@@ -158,6 +159,17 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
       Kg + (size_t)t0 * kTok, (uint32_t)(((size_t)last * kTok + DK) * 2));
   const __amdgpu_buffer_rsrc_t vview = buffer_view(
       Vg + (size_t)t0 * vTok, (uint32_t)(((size_t)last * vTok + DV) * 2));
+  // Index-gathered: the chunk's cache slots, staged in LDS; the views then
+  // span the sequence's whole cache (slots are absolute)
+  const __amdgpu_buffer_rsrc_t gkview = buffer_view(
+      Kg, GATHER ? (uint32_t)(((size_t)(a.cache_len - 1) * kTok + DK) * 2) : 0u);
+  const __amdgpu_buffer_rsrc_t gvview = buffer_view(
+      Vg, GATHER ? (uint32_t)(((size_t)(a.cache_len - 1) * vTok + DV) * 2) : 0u);
+  if (GATHER) {
+    for (int e = threadIdx.x; e <= last && t1 > t0; e += NW * 64)
+      s_slot[e] = a.sel[(size_t)b * a.max_len + t0 + e];
+    __syncthreads();
+  }
   // The additive bias of the chunk's live tokens (needle-core attn_bias: one
   // term per position, shared by the heads); loads past the view return 0.
   const __amdgpu_buffer_rsrc_t bview =
@@ -190,6 +202,21 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
         const int t = min(tile * kTileTokens + idx / G::vPieces, last);
         const int pc = (idx % G::vPieces) * 8;
         vr[i] = stream_load16(t == rel ? vnew + pc : vb + (size_t)t * vTok + pc);
+      }
+      return;
+    }
+    if (GATHER) {
+#pragma unroll
+      for (int i = 0; i < G::kLoads; ++i) {
+        const int idx = i * 64 + lane;
+        const int s = s_slot[min(tile * kTileTokens + idx / G::kPieces, last)];
+        kr[i] = stream_load16(gkview, (uint32_t)((s * kTok + (idx % G::kPieces) * 8) * 2));
+      }
+#pragma unroll
+      for (int i = 0; i < G::vLoads; ++i) {
+        const int idx = i * 64 + lane;
+        const int s = s_slot[min(tile * kTileTokens + idx / G::vPieces, last)];
+        vr[i] = stream_load16(gvview, (uint32_t)((s * vTok + (idx % G::vPieces) * 8) * 2));
       }
       return;
     }
@@ -381,12 +408,17 @@ template <int DK, int DV, int NW, bool STEP>
 hipError_t launch_one(const PartitionArgs &a, const StepParams &sp,
                       hipStream_t s) {
   const int nwork = a.sched ? a.sched_len : a.total_items;
-  if (a.has_bias)
-    hipLaunchKernelGGL((partition_bf16_kernel<DK, DV, NW, STEP, true>),
+  if (a.sel) {  // index-gathered: attend only, no bias
+    if (STEP || a.has_bias) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((partition_bf16_kernel<DK, DV, NW, false, false, true>),
                        dim3(nwork), dim3(NW * 64), 0, s, a, sp);
-  else
-    hipLaunchKernelGGL((partition_bf16_kernel<DK, DV, NW, STEP, false>),
+  } else if (a.has_bias) {
+    hipLaunchKernelGGL((partition_bf16_kernel<DK, DV, NW, STEP, true, false>),
                        dim3(nwork), dim3(NW * 64), 0, s, a, sp);
+  } else {
+    hipLaunchKernelGGL((partition_bf16_kernel<DK, DV, NW, STEP, false, false>),
+                       dim3(nwork), dim3(NW * 64), 0, s, a, sp);
+  }
   return hipGetLastError();
 }
 

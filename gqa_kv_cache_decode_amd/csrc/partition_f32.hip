@@ -39,7 +39,7 @@ struct F32Geom {
   static constexpr int waveLdsFloats = kF32Tile * (kStride + vStride);
 };
 
-template <int DK, int DV, int NW, bool STEP, bool BIAS>
+template <int DK, int DV, int NW, bool STEP, bool BIAS, bool GATHER>
 __global__ __launch_bounds__(NW * 64) void partition_f32_mfma_kernel(
     PartitionArgs args, StepParams sp) {
   using G = F32Geom<DK, DV>;
@@ -49,6 +49,7 @@ __global__ __launch_bounds__(NW * 64) void partition_f32_mfma_kernel(
   __shared__ __attribute__((aligned(16))) float lds[kLdsFloats];
   __shared__ int s_flag;
   __shared__ float s_in[32];  // carry_in m, l of the group's rows (direct)
+  __shared__ int s_slot[GATHER ? kGatherChunk : 1];  // gathered cache slots
 
   PartitionArgs a = args;
   int item, branch = 0;
@@ -101,9 +102,9 @@ __global__ __launch_bounds__(NW * 64) void partition_f32_mfma_kernel(
   float *Vs = Ks + kF32Tile * G::kStride;
   const size_t kTok = (size_t)Hkv * DK, vTok = (size_t)Hkv * DV;
   float *Kg = static_cast<float *>(const_cast<void *>(a.k)) +
-              ((size_t)b * a.max_len * Hkv + g) * DK;
+              ((size_t)b * a.cache_len * Hkv + g) * DK;
   float *Vg = static_cast<float *>(const_cast<void *>(a.v)) +
-              ((size_t)b * a.max_len * Hkv + g) * DV;
+              ((size_t)b * a.cache_len * Hkv + g) * DV;
 
   // STEP: the work-group whose chunk holds the new slot stores the token's
   // rows into the cache without waiting; this call reads them from
@@ -129,6 +130,17 @@ __global__ __launch_bounds__(NW * 64) void partition_f32_mfma_kernel(
       Kg + (size_t)t0 * kTok, (uint32_t)(((size_t)last * kTok + DK) * 4));
   const __amdgpu_buffer_rsrc_t vview = buffer_view(
       Vg + (size_t)t0 * vTok, (uint32_t)(((size_t)last * vTok + DV) * 4));
+  // Index-gathered: the chunk's cache slots, staged in LDS; the views then
+  // span the sequence's whole cache (slots are absolute)
+  const __amdgpu_buffer_rsrc_t gkview = buffer_view(
+      Kg, GATHER ? (uint32_t)(((size_t)(a.cache_len - 1) * kTok + DK) * 4) : 0u);
+  const __amdgpu_buffer_rsrc_t gvview = buffer_view(
+      Vg, GATHER ? (uint32_t)(((size_t)(a.cache_len - 1) * vTok + DV) * 4) : 0u);
+  if (GATHER) {
+    for (int e = threadIdx.x; e <= last && t1 > t0; e += NW * 64)
+      s_slot[e] = a.sel[(size_t)b * a.max_len + t0 + e];
+    __syncthreads();
+  }
   // additive bias of the chunk's live tokens (loads past the view return 0)
   const __amdgpu_buffer_rsrc_t bview =
       BIAS && a.bias ? buffer_view(a.bias + (size_t)b * a.bias_stride + t0,
@@ -154,6 +166,21 @@ __global__ __launch_bounds__(NW * 64) void partition_f32_mfma_kernel(
         const int t = min(tile * kF32Tile + idx / G::vPieces, last);
         const int pc = (idx % G::vPieces) * 4;
         vr[i] = stream_load16(t == rel ? vnew + pc : vb + (size_t)t * vTok + pc);
+      }
+      return;
+    }
+    if (GATHER) {
+#pragma unroll
+      for (int i = 0; i < G::kLoads; ++i) {
+        const int idx = i * 64 + lane;
+        const int s = s_slot[min(tile * kF32Tile + idx / G::kPieces, last)];
+        kr[i] = stream_load16(gkview, (uint32_t)((s * kTok + (idx % G::kPieces) * 4) * 4));
+      }
+#pragma unroll
+      for (int i = 0; i < G::vLoads; ++i) {
+        const int idx = i * 64 + lane;
+        const int s = s_slot[min(tile * kF32Tile + idx / G::vPieces, last)];
+        vr[i] = stream_load16(gvview, (uint32_t)((s * vTok + (idx % G::vPieces) * 4) * 4));
       }
       return;
     }
@@ -321,14 +348,20 @@ template <int DK, int DV, bool STEP>
 hipError_t launch_mfma(const PartitionArgs &a, const StepParams &sp,
                        hipStream_t s) {
   const int nwork = a.sched ? a.sched_len : a.total_items;
-  if (a.has_bias)
+  if (a.sel) {  // index-gathered: attend only, no bias
+    if (STEP || a.has_bias) return hipErrorInvalidValue;
     hipLaunchKernelGGL(
-        (partition_f32_mfma_kernel<DK, DV, kPartitionWaves, STEP, true>),
+        (partition_f32_mfma_kernel<DK, DV, kPartitionWaves, false, false, true>),
         dim3(nwork), dim3(kPartitionWaves * 64), 0, s, a, sp);
-  else
+  } else if (a.has_bias) {
     hipLaunchKernelGGL(
-        (partition_f32_mfma_kernel<DK, DV, kPartitionWaves, STEP, false>),
+        (partition_f32_mfma_kernel<DK, DV, kPartitionWaves, STEP, true, false>),
         dim3(nwork), dim3(kPartitionWaves * 64), 0, s, a, sp);
+  } else {
+    hipLaunchKernelGGL(
+        (partition_f32_mfma_kernel<DK, DV, kPartitionWaves, STEP, false, false>),
+        dim3(nwork), dim3(kPartitionWaves * 64), 0, s, a, sp);
+  }
   return hipGetLastError();
 }
 
@@ -523,7 +556,7 @@ bool partition_f32_uses_mfma(int dk, int dv) { return mfma_shape(dk, dv); }
 hipError_t launch_partition_f32(const PartitionArgs &a, const StepParams &ep,
                                 hipStream_t s) {
   if (mfma_shape(a.dk, a.dv)) return dispatch_mfma<false>(a, ep, s);
-  if (ep.direct || ep.fuse || a.sched) return hipErrorInvalidValue;
+  if (ep.direct || ep.fuse || a.sched || a.sel) return hipErrorInvalidValue;
   const int nwork = a.batch * a.num_kv_heads * a.num_chunks;
   const size_t lds = partition_f32_lds_bytes(a.dk, a.dv, a.hpk);
   if (lds > 65536) {

@@ -28,6 +28,7 @@ __device__ __forceinline__ int select_branch(PartitionArgs &a, int &item) {
       a.bias = x.bias;
       a.bias_stride = x.bias_stride;
       a.max_len = x.max_len;
+      a.cache_len = x.max_len;
       a.chunk_tokens = x.chunk_tokens;
       a.num_chunks = x.num_chunks;
       a.col_base = x.col_base;

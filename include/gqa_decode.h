@@ -343,6 +343,31 @@ GQA_API gqa_status gqa_decode_step_branches(
     void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * attend_gathered — index-gathered decode (the sparse attention the metrale
+ * DSA reference feeds from its selection): sequence b's query attends only
+ * the cache slots its index row names.  idx [batch][width] device int32;
+ * as in topk_to_mask, duplicates collapse (a repeated slot is attended
+ * once), and negative (INVALID) entries and slots at or past
+ * clamp(lens[b], 0, max_len) are dropped.  The selected rows are gathered
+ * in ascending slot order.  Matrix-core head shapes, max_len <= 2^20, and a
+ * sequence's K or V rows spanning less than 2 GiB; other arguments as in
+ * gqa_attend_decode (no bias).  Workspace:
+ * gqa_attend_gathered_workspace_bytes(); it needs no initialisation.
+ */
+GQA_API size_t gqa_attend_gathered_workspace_bytes(const gqa_cache *cache,
+                                                   int32_t num_q_heads,
+                                                   int32_t width);
+
+GQA_API gqa_status gqa_attend_gathered(const void *q, int32_t num_q_heads,
+                                       const gqa_cache *cache,
+                                       const int32_t *lens, const int32_t *idx,
+                                       int32_t width, float scale,
+                                       const gqa_carry *carry_in,
+                                       const gqa_carry *carry_out, float *out,
+                                       void *workspace, size_t workspace_bytes,
+                                       hipStream_t stream);
+
+/*
  * softmax_state_merge — dst = merge(a, b) row by row (usearch carry,
  * partial softmaxes rescaled to a common maximum): m = max(m_a, m_b),
  * l = e^(m_a-m) l_a +

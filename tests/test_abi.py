@@ -30,7 +30,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 15, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(lib, n), f"missing export {n}"
     assert set(names) == set(bd._SIGNATURES), "binding covers the header"
@@ -276,3 +276,29 @@ def test_decode_step_branches_checks(lib):
     assert call(1, lo_=None) == INVALID
     assert call(1, kn_=ctypes.c_void_p(0x51004)) == INVALID  # misaligned
     assert call(1, n=nbytes - 1) == WORKSPACE
+
+
+def test_gathered_checks(lib):
+    c = _cache(B=4, T=8192, H=8)
+    nbytes = lib.gqa_attend_gathered_workspace_bytes(ctypes.byref(c), 32, 2048)
+    assert nbytes > 0
+    assert lib.gqa_attend_gathered_workspace_bytes(ctypes.byref(c), 32, 0) == 0
+    odd = _cache(B=4, T=8192, H=8, dk=48, dv=80, dtype=0)
+    assert lib.gqa_attend_gathered_workspace_bytes(ctypes.byref(odd), 32,
+                                                   64) == 0
+    huge = _cache(B=1, T=(1 << 20) + 64, H=1)
+    assert lib.gqa_attend_gathered_workspace_bytes(ctypes.byref(huge), 8,
+                                                   64) == 0
+    q, lens, idx, out, ws = (ctypes.c_void_p(x) for x in
+                             (0x30000, 0x40000, 0x41000, 0x60000, 0x70000))
+    f = lib.gqa_attend_gathered
+
+    def call(c_, idx_=idx, width=2048, n=nbytes):
+        return f(q, 32, ctypes.byref(c_), lens, idx_, width, 0.0, None, None,
+                 out, ws, n, None)
+
+    assert call(c, idx_=None) == INVALID
+    assert call(c, width=0) == INVALID
+    assert call(odd) == UNSUPPORTED
+    assert call(huge) in (UNSUPPORTED, SHAPE)   # 8 q heads over 1 KV head ok
+    assert call(c, n=nbytes - 1) == WORKSPACE
