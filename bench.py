@@ -57,11 +57,13 @@ def parse_args():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="batched",
                    choices=["tiny", "batched", "ragged", "long", "spike",
-                            "stream"],
+                            "stream", "gather"],
                    help="stream: the long-context shapes kept as 4 sink "
                         "keys + a 128-key window ring + a main cache; each "
                         "step appends (evicting the ring's oldest key into "
-                        "main) and attends the three parts in one launch")
+                        "main) and attends the three parts in one launch.  "
+                        "gather: index-gathered decode of 2048 selected "
+                        "slots (pools of 64) per sequence of a 32K cache")
     p.add_argument("--rotate", type=int, default=0,
                    help="cache copies to rotate over (0 = enough for 1 GiB)")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -82,7 +84,8 @@ def workload_by_name(name):
     from gqa_kv_cache_decode_amd import workloads as wl
     return {"tiny": wl.TINY_F32, "batched": wl.BATCHED_BF16,
             "ragged": wl.RAGGED_BF16, "long": wl.LONG_WINDOW_BF16,
-            "spike": wl.WIDE_SPIKE_BF16, "stream": wl.LONG_WINDOW_BF16}[name]
+            "spike": wl.WIDE_SPIKE_BF16, "stream": wl.LONG_WINDOW_BF16,
+            "gather": wl.GATHER_BF16}[name]
 
 
 STREAM_SINK = 4            # permanent sink keys (cortiq-engine default)
@@ -185,8 +188,26 @@ def main():
     out = torch.empty(B, Hq, w.dv, dtype=torch.float32, device=dev)
 
     stream = args.workload == "stream"
+    gather = args.workload == "gather"
     branches = []
-    if stream:
+    if gather:
+        # one cache; the steps rotate over index sets that select disjoint
+        # enough rows (>= 1 GiB in all) that no step hits the 256 MB MALL
+        gk, gv, glens = x["k"].to(dev), x["v"].to(dev), x["lens"].to(dev)
+        sel_bytes = (w.batch * wl.GATHER_WIDTH * Hkv * (w.dk + w.dv) * w.esz)
+        copies = args.rotate or max(1, min(16, math.ceil(ROTATE_TARGET_BYTES /
+                                                         sel_bytes)))
+        gidx, gsel = [], []
+        for r in range(copies):
+            rows = wl.make_index_rows(w, x["lens"], wl.GATHER_WIDTH,
+                                      wl.GATHER_POOL, w.seed + 3000 + r)
+            gidx.append(rows.to(dev))
+            gsel.append(sum(len(set(rr.tolist()) - {-1}) for rr in rows))
+        gws = torch.empty(binding.library().gqa_attend_gathered_workspace_bytes(
+            ctypes.byref(binding._cache(gk, gv)), Hq, wl.GATHER_WIDTH),
+            dtype=torch.uint8, device=dev)
+        carry = None
+    elif stream:
         st = StreamState(g, torch, w, x, copies, dev)
         carry = None
     elif w.window:
@@ -205,8 +226,12 @@ def main():
         carry = None
     del x
     torch.cuda.synchronize()
-    log(f"[bench] {copies} rotating cache copies, "
-        f"{main_bytes * copies / 2**30:.2f} GiB of K/V resident")
+    if gather:
+        log(f"[bench] {copies} rotating index sets over one cache of "
+            f"{main_bytes / 2**30:.2f} GiB")
+    else:
+        log(f"[bench] {copies} rotating cache copies, "
+            f"{main_bytes * copies / 2**30:.2f} GiB of K/V resident")
 
     def stream_step(r):
         """One streaming decode step: the new token enters the ring (its
@@ -257,7 +282,16 @@ def main():
                                  br.plan, br.ws, carry_in=cin,
                                  carry_out=cout, out=o)
 
-    if stream:
+    if gather:
+        def gather_step(r):
+            g.attend_gathered(q, gk, gv, glens, gidx[r], w.scale, out=out,
+                              workspace=gws)
+        step = gather_step
+        # the whole call (selection, gathered partition, combine) is timed
+        # as the dominant launch: there is no separate partition entry
+        partition_only = gather_step
+        dom = types.SimpleNamespace(n_tot=sum(gsel) // len(gsel), bias=None)
+    elif stream:
         step = stream_step
         dom = types.SimpleNamespace(n_tot=B * st.n_main, bias=None)
 
@@ -356,6 +390,11 @@ def main():
         step_bytes += (kv_bytes(w, B * (STREAM_SINK + w.window + st.n_main)) +
                        q_bytes + 3 * B * Hkv * (w.dk + w.dv) * w.esz +
                        5 * B * 4)
+    if gather:
+        # the distinct selected rows (mean over the index sets), q, and the
+        # index rows read by the selection kernel
+        step_bytes += (kv_bytes(w, dom.n_tot) + q_bytes +
+                       B * wl.GATHER_WIDTH * 4)
     step_bytes += out_bytes
     part_bytes = kv_bytes(w, dom.n_tot) + q_bytes + bias_bytes(dom)
     value = step_bytes / (ms_step * 1e-3) / 1e9
@@ -371,9 +410,12 @@ def main():
 
     traffic = measured_traffic(profile_name(args), w.dtype)
     waves = (4 if w.dk + w.dv <= 256 else 2) if w.dtype == "bf16" else 2
-    tmpl = f"{w.dk}, {w.dv}, {waves}, false, {'true' if args.bias else 'false'}"
+    tmpl = (f"{w.dk}, {w.dv}, {waves}, false, "
+            f"{'true' if args.bias else 'false'}, {'true' if gather else 'false'}")
     kernel = (f"partition_bf16_kernel<{tmpl}>" if w.dtype == "bf16" else
               f"partition_f32_mfma_kernel<{tmpl}>")
+    if gather:
+        kernel = f"attend_gathered call: select_kernel + {kernel} + combine"
     roofline = {"bound": "hbm", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -396,6 +438,8 @@ def main():
         "data": "synthetic (seeded; shapes and distributions of the workload)",
         "config": {"workload": (f"stream_sink{STREAM_SINK}_ring{w.window}_"
                                 f"main_of_{w.name}" if stream else w.name),
+                   "selected_per_sequence": (wl.GATHER_WIDTH if gather
+                                             else None),
                    "batch": B, "num_q_heads": Hq,
                    "num_kv_heads": Hkv, "dk": w.dk, "dv": w.dv,
                    "seq_len": w.max_len, "window": w.window,

@@ -107,6 +107,48 @@ WIDE_SPIKE_BF16 = DecodeWorkload(
 WORKLOADS = [TINY_F32, BATCHED_BF16, RAGGED_BF16, LONG_WINDOW_BF16,
              WIDE_SPIKE_BF16]
 
+# Index-gathered decode (a "next" shape, not one of the five above): a
+# DSA-style selection of GATHER_WIDTH slots per sequence out of a 32K cache,
+# GATHER_POOL consecutive slots per selected pool (metrale DSA expand_selection
+# turns selected pools of index_kpool tokens into raw token indices).
+GATHER_BF16 = DecodeWorkload(
+    "gather_bf16_b16_hq32_hkv8_d128_t32768_sel2048", batch=16,
+    num_q_heads=32, num_kv_heads=8, dk=128, dv=128, max_len=32768,
+    dtype="bf16", dist="normal", seed_index=6)
+GATHER_WIDTH = 2048
+GATHER_POOL = 64
+
+
+def make_index_rows(w: DecodeWorkload, lens, width: int, pool: int,
+                    seed: int, invalid_frac: float = 0.02,
+                    dup_frac: float = 0.02) -> torch.Tensor:
+    """Index rows [B, width] int32 in the shape of a pooled top-k
+    selection: width // pool distinct pools of `pool` consecutive slots each
+    (pool starts drawn without replacement among the live pools), then a
+    fraction of entries replaced by duplicates of other entries and by -1
+    (INVALID), in a shuffled order.  Holds no attention arithmetic."""
+    g = torch.Generator().manual_seed(seed)
+    rows = torch.full((w.batch, width), -1, dtype=torch.int32)
+    for b in range(w.batch):
+        n = int(min(max(int(lens[b]), 0), w.max_len))
+        npool = max(n // pool, 1)
+        k = min(width // pool, npool)
+        starts = torch.randperm(npool, generator=g)[:k] * pool
+        row = (starts[:, None] + torch.arange(pool)[None, :]).reshape(-1)
+        row = row[row < n][:width]
+        full = torch.full((width,), -1, dtype=torch.int64)
+        full[:row.numel()] = row
+        m = int(width * dup_frac)
+        if m and row.numel():
+            src = torch.randint(0, row.numel(), (m,), generator=g)
+            dst = torch.randint(0, width, (m,), generator=g)
+            full[dst] = full[src]
+        m = int(width * invalid_frac)
+        if m:
+            full[torch.randint(0, width, (m,), generator=g)] = -1
+        rows[b] = full[torch.randperm(width, generator=g)].to(torch.int32)
+    return rows
+
 
 def _uniform(g: torch.Generator, shape, lo: float, hi: float) -> torch.Tensor:
     return torch.empty(shape, dtype=torch.float32).uniform_(lo, hi, generator=g)
