@@ -590,3 +590,149 @@ def pin_gathered(orc_stream):
 
 
 STREAM_PINS.append(pin_gathered)
+
+
+# --- fp8 (E4M3) KV caches -----------------------------------------------------
+# The format's definition fixes every value below: bias 7, 3 mantissa bits,
+# subnormals m * 2^-9, NaN at S.1111.111 only, 448 the largest finite value.
+
+_E4M3_KNOWN = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9,
+               0x08: 2.0 ** -6, 0x38: 1.0, 0x39: 1.125, 0x3A: 1.25,
+               0x3C: 1.5, 0x40: 2.0, 0x48: 4.0, 0x4B: 5.5, 0x77: 240.0,
+               0x78: 256.0, 0x7E: 448.0, 0xB8: -1.0, 0xFE: -448.0}
+
+
+def pin_fp8_format(orc8):
+    """E4M3 decode: the known codes, NaN exactly at 0x7F and 0xFF, sign
+    symmetry (0x80 is -0), and the spacing of consecutive non-negative codes:
+    2^-9 through the subnormals and the first binade, then doubling with each
+    exponent step (so the values rise strictly up to 448)."""
+    vals = [orc8.e4m3_decode(c) for c in range(256)]
+    for c, want in _E4M3_KNOWN.items():
+        assert vals[c] == want, f"code {c:#04x}: {vals[c]} != {want}"
+    assert [c for c in range(256) if math.isnan(vals[c])] == [0x7F, 0xFF]
+    assert vals[0x80] == 0.0 and math.copysign(1.0, vals[0x80]) < 0, "-0"
+    for c in range(0x7F):
+        assert vals[c | 0x80] == -vals[c], f"sign of {c:#04x}"
+    for c in range(0x7E):
+        step = vals[c + 1] - vals[c]
+        assert step == 2.0 ** (max(c >> 3, 1) - 10), f"spacing at {c:#04x}"
+    assert np.array_equal(orc8.decode(np.arange(256, dtype=np.uint8)),
+                          np.array(vals), equal_nan=True), "array decode"
+
+
+def pin_fp8_encode(orc8):
+    """Nearest finite code, ties to the even mantissa, saturation at 448, sign
+    kept: every finite code round-trips; midpoints of adjacent codes go to
+    the even one; the error of any value is at most half the local spacing."""
+    finite = [c for c in range(256) if c not in (0x7F, 0xFF)]
+    vals = orc8.decode(np.array(finite, dtype=np.uint8))
+    assert orc8.encode(vals).tolist() == finite, "round trip of every code"
+    cases = [(1.0625, 0x38), (1.1875, 0x3A), (2.0 ** -10, 0x00),
+             (3 * 2.0 ** -10, 0x02), (5 * 2.0 ** -10, 0x02),
+             (2.0 ** -6 + 2.0 ** -10, 0x08), (464.0, 0x7E), (-1.0625, 0xB8),
+             (1.07, 0x39), (1.05, 0x38), (5.75, 0x4C), (449.0, 0x7E),
+             (1e6, 0x7E), (-1e30, 0xFE), (np.inf, 0x7E),
+             (-2.0 ** -12, 0x80), (-0.0, 0x80), (0.0, 0x00)]
+    got = orc8.encode(np.array([x for x, _ in cases]))
+    for (x, want), c in zip(cases, got.tolist()):
+        assert c == want, f"encode({x}) = {c:#04x}, want {want:#04x}"
+    rng = np.random.default_rng(31)
+    x = np.exp2(rng.uniform(-12, np.log2(448.0), 4000))
+    c = orc8.encode(x)
+    err = np.abs(orc8.decode(c) - x)
+    e = np.maximum(np.floor(np.log2(x)), -6)
+    assert np.all(err <= np.exp2(e - 3) / 2), "more than half a spacing off"
+    assert np.array_equal(orc8.encode(-x), c | 0x80), "sign symmetry"
+
+
+def pin_fp8_quantize(orc8):
+    """quantize(x, s) encodes x / s: with s a power of two every code
+    round-trips from its scaled value; 3 / 0.75 = 4 and 17 / 3 rounds to 5.5
+    (its nearest code)."""
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)],
+                      dtype=np.uint8)
+    for s in (0.125, 1.0, 32.0):
+        x = (orc8.decode(finite) * s).astype(np.float32)
+        assert np.array_equal(orc8.quantize(x, np.float32(s)), finite), \
+            f"scale {s}"
+    assert orc8.quantize(np.float32(3.0), np.float32(0.75)) == 0x48
+    assert orc8.quantize(np.float32(17.0), np.float32(3.0)) == 0x4B
+
+
+def _fp8_codes(rng, shape):
+    """Random finite E4M3 codes of magnitude up to 4."""
+    c = rng.integers(0, 0x49, shape)          # 0 .. 4.0
+    return (c | (rng.integers(0, 2, shape) << 7)).astype(np.uint8)
+
+
+def pin_fp8_attend(orc8):
+    """Attention over fp8 caches, in closed form: (1) equal keys give each
+    head the plain mean of its group's decoded values times the group's V
+    scale; (2) two keys with known codes give sigmoid weights of the logit gap
+    scale * k_scale * (q . (k1 - k0)).  Scales differ per (sequence, KV head)
+    and between K and V; slots past each length hold NaN codes."""
+    rng = np.random.default_rng(32)
+    B, Hkv, hpk, dk, dv, T = 2, 3, 2, 16, 8, 10
+    lens = np.array([7, 4])
+    ks = np.array([[0.5, 1.5, 3.0], [0.25, 2.0, 5.0]])
+    vs = np.array([[1.25, 0.5, 4.0], [3.0, 0.125, 1.5]])
+    q = rng.uniform(-1, 1, (B, Hkv * hpk, dk))
+    kc = np.repeat(_fp8_codes(rng, (B, 1, Hkv, dk)), T, axis=1)
+    vc = _fp8_codes(rng, (B, T, Hkv, dv))
+    for b in range(B):
+        kc[b, lens[b]:] = 0x7F
+        vc[b, lens[b]:] = 0xFF
+    out, _ = orc8.attend_fp8(q, kc, vc, ks, vs, lens, scale=0.7)
+    for b in range(B):
+        for h in range(Hkv * hpk):
+            g = h // hpk
+            want = vs[b, g] * orc8.decode(vc[b, :lens[b], g]).mean(axis=0)
+            _close(out[b, h], want, 1e-14, f"equal keys b{b} h{h}")
+    # two keys: k0 = (1, 0, 0, 0), k1 = (2, 1, 0, 0)
+    B, Hkv, hpk, d = 2, 3, 2, 4
+    kc = np.zeros((B, 2, Hkv, d), dtype=np.uint8)
+    kc[:, 0, :, 0] = 0x38
+    kc[:, 1, :, 0] = 0x40
+    kc[:, 1, :, 1] = 0x38
+    vc = _fp8_codes(rng, (B, 2, Hkv, d))
+    q = rng.uniform(-1, 1, (B, Hkv * hpk, d))
+    out, _ = orc8.attend_fp8(q, kc, vc, ks, vs, [2, 2], scale=0.5)
+    for b in range(B):
+        for h in range(Hkv * hpk):
+            g = h // hpk
+            gap = 0.5 * ks[b, g] * (q[b, h, 0] + q[b, h, 1])
+            w1 = 1.0 / (1.0 + math.exp(-gap))
+            v0, v1 = orc8.decode(vc[b, 0, g]), orc8.decode(vc[b, 1, g])
+            want = vs[b, g] * ((1 - w1) * v0 + w1 * v1)
+            _close(out[b, h], want, 1e-14, f"two keys b{b} h{h}")
+
+
+def pin_fp8_append(orc8):
+    """Quantising append: rows whose values are codes times power-of-two
+    scales (different for K and V and per KV head) land as those codes in
+    slot lens[b]; a full cache drops the token; nothing else changes."""
+    rng = np.random.default_rng(33)
+    B, T, Hkv, d = 3, 5, 2, 8
+    k = _fp8_codes(rng, (B, T, Hkv, d))
+    v = _fp8_codes(rng, (B, T, Hkv, d))
+    lens = np.array([0, 4, 5])
+    ks = np.array([[0.25, 2.0], [8.0, 0.5], [1.0, 4.0]], dtype=np.float32)
+    vs = np.array([[16.0, 0.125], [1.0, 2.0], [0.5, 0.25]], dtype=np.float32)
+    kcode = _fp8_codes(rng, (B, Hkv, d))
+    vcode = _fp8_codes(rng, (B, Hkv, d))
+    kn = (orc8.decode(kcode) * ks[:, :, None]).astype(np.float32)
+    vn = (orc8.decode(vcode) * vs[:, :, None]).astype(np.float32)
+    k2, v2, l2, dropped = orc8.kv_append_fp8(k, v, kn, vn, ks, vs, lens)
+    assert l2.tolist() == [1, 5, 5] and dropped == 1, "lengths, drops"
+    for b, slot in ((0, 0), (1, 4)):
+        assert np.array_equal(k2[b, slot], kcode[b]), f"K codes b{b}"
+        assert np.array_equal(v2[b, slot], vcode[b]), f"V codes b{b}"
+    keep = np.ones((B, T), dtype=bool)
+    keep[0, 0] = keep[1, 4] = False
+    assert np.array_equal(k2[keep], k[keep]) and \
+        np.array_equal(v2[keep], v[keep]), "other slots untouched"
+
+
+FP8_PINS = [pin_fp8_format, pin_fp8_encode, pin_fp8_quantize,
+            pin_fp8_attend, pin_fp8_append]
