@@ -39,8 +39,10 @@ ROTATE_TARGET_BYTES = 1 << 30
 CSRC = ROOT / "gqa_kv_cache_decode_amd" / "csrc"
 # Sources of the dominant (partition) kernel: recorded counter readings are
 # only reported while these are unchanged.
-PARTITION_SOURCES = {"bf16": ["partition_bf16.hip", "device_common.h", "launch.h",
-                              "step_common.h"],
+_MFMA16 = ["partition_mfma16.h", "fp8_common.h", "device_common.h", "launch.h",
+           "step_common.h"]
+PARTITION_SOURCES = {"bf16": ["partition_bf16.hip"] + _MFMA16,
+                     "fp8": ["partition_fp8.hip"] + _MFMA16,
                      "f32": ["partition_f32.hip", "device_common.h", "launch.h",
                              "step_common.h"]}
 COPY_BYTES = 256 << 20      # calibration copy for the byte counters
@@ -57,13 +59,15 @@ def parse_args():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="batched",
                    choices=["tiny", "batched", "ragged", "long", "spike",
-                            "stream", "gather"],
+                            "stream", "gather", "fp8"],
                    help="stream: the long-context shapes kept as 4 sink "
                         "keys + a 128-key window ring + a main cache; each "
                         "step appends (evicting the ring's oldest key into "
                         "main) and attends the three parts in one launch.  "
                         "gather: index-gathered decode of 2048 selected "
-                        "slots (pools of 64) per sequence of a 32K cache")
+                        "slots (pools of 64) per sequence of a 32K cache.  "
+                        "fp8: the batched shape over fp8 (E4M3) caches with "
+                        "per-(sequence, KV head) scales")
     p.add_argument("--rotate", type=int, default=0,
                    help="cache copies to rotate over (0 = enough for 1 GiB)")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -85,7 +89,7 @@ def workload_by_name(name):
     return {"tiny": wl.TINY_F32, "batched": wl.BATCHED_BF16,
             "ragged": wl.RAGGED_BF16, "long": wl.LONG_WINDOW_BF16,
             "spike": wl.WIDE_SPIKE_BF16, "stream": wl.LONG_WINDOW_BF16,
-            "gather": wl.GATHER_BF16}[name]
+            "gather": wl.GATHER_BF16, "fp8": wl.BATCHED_FP8}[name]
 
 
 STREAM_SINK = 4            # permanent sink keys (cortiq-engine default)
@@ -132,6 +136,14 @@ def kv_bytes(w, lens_total, hkv=None):
     return lens_total * (hkv or w.num_kv_heads) * (w.dk + w.dv) * w.esz
 
 
+def clone_cache(c):
+    """A copy of a K or V cache (an fp8 cache keeps sharing its scales)."""
+    from gqa_kv_cache_decode_amd import Fp8Cache
+    if isinstance(c, Fp8Cache):
+        return Fp8Cache(c.codes.clone(), c.scale)
+    return c.clone()
+
+
 class Branch:
     """One attend branch: R cache copies, lens before/after the append."""
 
@@ -145,8 +157,8 @@ class Branch:
             pad = (k.shape[1] + 3) // 4 * 4
             self.bias = torch.randn(k.shape[0], pad, generator=gen).to(
                 k.device)
-        self.k = [k] + [k.clone() for _ in range(copies - 1)]
-        self.v = [v] + [v.clone() for _ in range(copies - 1)]
+        self.k = [k] + [clone_cache(k) for _ in range(copies - 1)]
+        self.v = [v] + [clone_cache(v) for _ in range(copies - 1)]
         self.append = append
         self.lens_after = lens_after
         self.lens_before = (lens_after - 1).clamp_(min=0) if append else None
@@ -172,8 +184,9 @@ def main():
     from gqa_kv_cache_decode_amd import workloads as wl
 
     w = workload_by_name(args.workload)
+    fp8 = w.dtype == "fp8"
     t_gen = time.time()
-    x = wl.make_inputs(w)
+    x = wl.make_fp8_inputs(w) if fp8 else wl.make_inputs(w)
     log(f"[bench] workload {w.name}: inputs drawn in {time.time() - t_gen:.1f}s")
     dev = torch.device("cuda")
     B, Hq, Hkv = w.batch, w.num_q_heads, w.num_kv_heads
@@ -183,8 +196,9 @@ def main():
                                                     main_bytes)))
     q = x["q"].to(dev)
     gen = torch.Generator().manual_seed(w.seed + 1000)
-    k_new = torch.randn(B, Hkv, w.dk, generator=gen).to(w.torch_dtype).to(dev)
-    v_new = torch.randn(B, Hkv, w.dv, generator=gen).to(w.torch_dtype).to(dev)
+    io_dt = torch.bfloat16 if fp8 else w.torch_dtype   # q and new rows
+    k_new = torch.randn(B, Hkv, w.dk, generator=gen).to(io_dt).to(dev)
+    v_new = torch.randn(B, Hkv, w.dv, generator=gen).to(io_dt).to(dev)
     out = torch.empty(B, Hq, w.dv, dtype=torch.float32, device=dev)
 
     stream = args.workload == "stream"
@@ -220,9 +234,13 @@ def main():
                                bias=args.bias, seed=w.seed + 2001))
         carry = g.empty_carry(B * Hq, w.dv)
     else:
-        branches.append(Branch(g, torch, w, x["k"].to(dev), x["v"].to(dev),
-                               x["lens"].to(dev), copies, append=True,
-                               bias=args.bias, seed=w.seed + 2000))
+        kc, vc = x["k"].to(dev), x["v"].to(dev)
+        if fp8:
+            kc = g.Fp8Cache(kc, x["k_scale"].to(dev))
+            vc = g.Fp8Cache(vc, x["v_scale"].to(dev))
+        branches.append(Branch(g, torch, w, kc, vc, x["lens"].to(dev), copies,
+                               append=True, bias=args.bias,
+                               seed=w.seed + 2000))
         carry = None
     del x
     torch.cuda.synchronize()
@@ -373,7 +391,9 @@ def main():
     ms_eager = (time.perf_counter() - t0) * 1e3 / K
 
     # bytes
-    q_bytes = B * Hq * w.dk * w.esz
+    q_bytes = B * Hq * w.dk * w.q_esz
+    # fp8: the K and V scale of every (sequence, KV head), read per launch
+    scale_bytes = 2 * B * Hkv * 4 if fp8 else 0
     out_bytes = B * Hq * w.dv * 4
     step_bytes = 0
     # a bias term counts once per attended (sequence, position)
@@ -383,7 +403,9 @@ def main():
         step_bytes += kv_bytes(w, br.n_tot) + bias_bytes(br) + \
             (q_bytes if i == 0 else 0)
         if br.append:
-            step_bytes += 2 * B * Hkv * (w.dk + w.dv) * w.esz + 2 * B * 4
+            # the new rows read (bf16 for fp8 caches) and written, the lengths
+            step_bytes += (B * Hkv * (w.dk + w.dv) * (w.q_esz + w.esz) +
+                           2 * B * 4)
     if stream:
         # sink + ring + main keys, q once; the new row written, the evicted
         # row read and written; counts and the three lengths
@@ -395,8 +417,9 @@ def main():
         # index rows read by the selection kernel
         step_bytes += (kv_bytes(w, dom.n_tot) + q_bytes +
                        B * wl.GATHER_WIDTH * 4)
-    step_bytes += out_bytes
-    part_bytes = kv_bytes(w, dom.n_tot) + q_bytes + bias_bytes(dom)
+    step_bytes += out_bytes + scale_bytes
+    part_bytes = kv_bytes(w, dom.n_tot) + q_bytes + bias_bytes(dom) + \
+        scale_bytes
     value = step_bytes / (ms_step * 1e-3) / 1e9
     achieved = part_bytes / (ms_part * 1e-3) / 1e9
     log(f"[bench] step {ms_step * 1e3:.2f} us (graph), eager {ms_eager * 1e3:.1f}"
@@ -409,11 +432,12 @@ def main():
         log(f"[bench] pure-read stream ceiling: {ceiling:.1f} GB/s")
 
     traffic = measured_traffic(profile_name(args), w.dtype)
-    waves = (4 if w.dk + w.dv <= 256 else 2) if w.dtype == "bf16" else 2
+    mfma16 = w.dtype in ("bf16", "fp8")
+    waves = (4 if w.dk + w.dv <= 256 else 2) if mfma16 else 2
     tmpl = (f"{w.dk}, {w.dv}, {waves}, false, "
             f"{'true' if args.bias else 'false'}, {'true' if gather else 'false'}")
-    kernel = (f"partition_bf16_kernel<{tmpl}>" if w.dtype == "bf16" else
-              f"partition_f32_mfma_kernel<{tmpl}>")
+    kernel = (f"partition_bf16_kernel<{tmpl}, {'true' if fp8 else 'false'}>"
+              if mfma16 else f"partition_f32_mfma_kernel<{tmpl}>")
     if gather:
         kernel = f"attend_gathered call: select_kernel + {kernel} + combine"
     roofline = {"bound": "hbm", "achieved": round(achieved, 1),
@@ -434,7 +458,9 @@ def main():
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s",
         "n_gpus": 1, "steps": K, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "scaling": "weak", "vs_baseline": None,
+        # fp8 codes are decoded to bf16 for the matrix cores
+        "dtype": "bf16" if fp8 else w.dtype,
         "data": "synthetic (seeded; shapes and distributions of the workload)",
         "config": {"workload": (f"stream_sink{STREAM_SINK}_ring{w.window}_"
                                 f"main_of_{w.name}" if stream else w.name),
@@ -443,7 +469,8 @@ def main():
                    "batch": B, "num_q_heads": Hq,
                    "num_kv_heads": Hkv, "dk": w.dk, "dv": w.dv,
                    "seq_len": w.max_len, "window": w.window,
-                   "kv_dtype": w.dtype, "rotating_cache_copies": copies,
+                   "kv_dtype": "fp8_e4m3" if fp8 else w.dtype,
+                   "rotating_cache_copies": copies,
                    "additive_bias": bool(args.bias),
                    "timing": "HIP graph of K steps"},
         "us_per_step": round(ms_step * 1e3, 2),
@@ -541,11 +568,12 @@ def profile_pass(torch, step, partition_only, copies, w, dom):
         assert lib.gqa_bench_copy(dst.data_ptr(), src.data_ptr(), COPY_BYTES,
                                   256 * 16, stream) == 0
     torch.cuda.synchronize()
-    q_bytes = w.batch * w.num_q_heads * w.dk * w.esz
+    q_bytes = w.batch * w.num_q_heads * w.dk * w.q_esz
     b_bytes = 4 * dom.n_tot if dom.bias is not None else 0
+    s_bytes = 2 * w.batch * w.num_kv_heads * 4 if w.dtype == "fp8" else 0
     print(json.dumps({"profile_pass": w.name,
                       "partition_algorithmic_bytes": kv_bytes(w, dom.n_tot) +
-                      q_bytes + b_bytes, "copy_bytes": COPY_BYTES,
+                      q_bytes + b_bytes + s_bytes, "copy_bytes": COPY_BYTES,
                       "source_sha256_16": partition_source_hash(w.dtype)}),
           flush=True)
 
@@ -556,9 +584,11 @@ def cpu_baseline(w, budget_s):
     time budget is spent (a small workload is evaluated several times over)."""
     import numpy as np
     import oracle
+    import oracle.fp8 as ofp8
     from gqa_kv_cache_decode_amd import workloads as wl
     from threadpoolctl import threadpool_limits
-    x = wl.make_inputs(w)
+    fp8 = w.dtype == "fp8"
+    x = wl.make_fp8_inputs(w) if fp8 else wl.make_inputs(w)
     hpk = w.hpk
     units = [(b, gg) for b in range(w.batch) for gg in range(w.num_kv_heads)]
     order = np.random.default_rng(0).permutation(len(units))
@@ -571,18 +601,26 @@ def cpu_baseline(w, budget_s):
             b, gg = units[idx]
             n = int(min(max(int(x["lens"][b]), 0), w.max_len))
             q = x["q"][b:b + 1, gg * hpk:(gg + 1) * hpk].float().numpy()
-            k = x["k"][b:b + 1, :n, gg:gg + 1].float().numpy()
-            v = x["v"][b:b + 1, :n, gg:gg + 1].float().numpy()
-            oracle.attend(q, k, v, [n], w.scale)
+            if fp8:
+                ofp8.attend_fp8(q, x["k"][b:b + 1, :n, gg:gg + 1].numpy(),
+                                x["v"][b:b + 1, :n, gg:gg + 1].numpy(),
+                                x["k_scale"][b:b + 1, gg:gg + 1].numpy(),
+                                x["v_scale"][b:b + 1, gg:gg + 1].numpy(),
+                                [n], w.scale)
+            else:
+                k = x["k"][b:b + 1, :n, gg:gg + 1].float().numpy()
+                v = x["v"][b:b + 1, :n, gg:gg + 1].float().numpy()
+                oracle.attend(q, k, v, [n], w.scale)
             done_bytes += (n * (w.dk + w.dv) * w.esz +
-                           hpk * (w.dk * w.esz + w.dv * 4))
+                           hpk * (w.dk * w.q_esz + w.dv * 4))
             done += 1
         el = time.perf_counter() - t0
     return {"value": round(done_bytes / el / 1e9, 4), "unit": "GB/s",
             "cores": 1, "kind": "oracle",
             "sample": f"{done} (sequence, KV group) unit evaluations "
                       f"({done / len(units):.2f} passes over the "
-                      f"{len(units)} units) of {w.name}, fp64 numpy oracle, "
+                      f"{len(units)} units) of {w.name}, fp64 numpy oracle"
+                      f"{' (codes decoded in fp64)' if fp8 else ''}, "
                       f"1 thread, {el:.1f} s wall"}
 
 

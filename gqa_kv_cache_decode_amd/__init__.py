@@ -11,7 +11,8 @@ __all__ = ["kv_append", "attend_decode", "softmax_state_merge",
            "decode_step", "step_workspace", "attend_branches",
            "stream_append", "decode_step_branches", "attend_gathered",
            "attend_partition", "attend_combine", "attend_plan",
-           "workspace_bytes", "Carry", "empty_carry", "GqaError", "library"]
+           "workspace_bytes", "Carry", "Fp8Cache", "empty_carry", "GqaError",
+           "library"]
 
 
 def __getattr__(name):

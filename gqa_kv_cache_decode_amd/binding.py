@@ -19,6 +19,8 @@ import torch
 LIB_PATH = Path(__file__).resolve().with_name("libgqa_decode.so")
 
 DTYPE_CODES = {torch.float32: 0, torch.bfloat16: 1}
+FP8_E4M3 = 2                       # gqa_dtype of an Fp8Cache
+FP8_STORAGE = (torch.uint8, torch.float8_e4m3fn)
 
 
 class GqaError(RuntimeError):
@@ -29,7 +31,8 @@ class _Cache(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
                 ("batch", ctypes.c_int32), ("max_len", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("dk", ctypes.c_int32),
-                ("dv", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("dv", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p)]
 
 
 class _Carry(ctypes.Structure):
@@ -145,7 +148,52 @@ def _need(t: torch.Tensor, name: str, dtype=None, shape=None):
                        f"{tuple(t.shape)}")
 
 
-def _cache(k: torch.Tensor, v: torch.Tensor) -> _Cache:
+@dataclasses.dataclass
+class Fp8Cache:
+    """An fp8 K or V cache: ``codes`` [B, max_len, Hkv, d] (torch.uint8 or
+    torch.float8_e4m3fn holding OCP E4M3 codes) and fp32 ``scale`` [B, Hkv]
+    on the GPU; code c of KV head g of sequence b stands for
+    decode(c) * scale[b, g].  Goes wherever a k_cache / v_cache tensor goes;
+    queries and new K/V rows are then bf16."""
+
+    codes: torch.Tensor
+    scale: torch.Tensor
+
+    @property
+    def device(self):
+        return self.codes.device
+
+    @property
+    def shape(self):
+        return self.codes.shape
+
+
+def _io_dtype(cache) -> torch.dtype:
+    """dtype of the queries and new rows that go with a cache."""
+    return torch.bfloat16 if isinstance(cache, Fp8Cache) else cache.dtype
+
+
+def _fp8_cache(k: Fp8Cache, v: Fp8Cache) -> _Cache:
+    if not (isinstance(k, Fp8Cache) and isinstance(v, Fp8Cache)):
+        raise GqaError("K and V caches must both be Fp8Cache, or neither")
+    for t, name in ((k.codes, "k_cache.codes"), (v.codes, "v_cache.codes")):
+        _need(t, name)
+        if t.dtype not in FP8_STORAGE:
+            raise GqaError(f"{name} must be uint8 or float8_e4m3fn codes")
+    kc, vc = k.codes, v.codes
+    if kc.dim() != 4 or vc.dim() != 4 or kc.shape[:3] != vc.shape[:3]:
+        raise GqaError("caches must be [batch, max_len, num_kv_heads, d] with "
+                       "matching batch, max_len and heads")
+    B, T, H, dk = kc.shape
+    _need(k.scale, "k_cache.scale", torch.float32, (B, H))
+    _need(v.scale, "v_cache.scale", torch.float32, (B, H))
+    return _Cache(kc.data_ptr(), vc.data_ptr(), B, T, H, dk, vc.shape[3],
+                  FP8_E4M3, k.scale.data_ptr(), v.scale.data_ptr())
+
+
+def _cache(k, v) -> _Cache:
+    if isinstance(k, Fp8Cache) or isinstance(v, Fp8Cache):
+        return _fp8_cache(k, v)
     _need(k, "k_cache")
     _need(v, "v_cache", dtype=k.dtype)
     if k.dtype not in DTYPE_CODES:
@@ -155,7 +203,7 @@ def _cache(k: torch.Tensor, v: torch.Tensor) -> _Cache:
                        "matching batch, max_len and heads")
     B, T, H, dk = k.shape
     return _Cache(k.data_ptr(), v.data_ptr(), B, T, H, dk, v.shape[3],
-                  DTYPE_CODES[k.dtype])
+                  DTYPE_CODES[k.dtype], None, None)
 
 
 @dataclasses.dataclass
@@ -183,12 +231,14 @@ def kv_append(k_cache, v_cache, k_new, v_new, lens, lens_out=None,
               dropped=None):
     """Append one token per sequence (needle-core KvCache::push_kv).
 
-    k_new [B, Hkv, dk], v_new [B, Hkv, dv] in the cache dtype; lens [B] int32.
-    Writes lens_out (default: lens itself, updated in place); a full cache is
-    left untouched and counted in ``dropped`` (int32 [1]) if given."""
+    k_new [B, Hkv, dk], v_new [B, Hkv, dv] in the cache dtype (bf16 for an
+    Fp8Cache, quantised on the way in); lens [B] int32.  Writes lens_out
+    (default: lens itself, updated in place); a full cache is left untouched
+    and counted in ``dropped`` (int32 [1]) if given."""
     c = _cache(k_cache, v_cache)
-    _need(k_new, "k_new", k_cache.dtype, (c.batch, c.num_kv_heads, c.dk))
-    _need(v_new, "v_new", k_cache.dtype, (c.batch, c.num_kv_heads, c.dv))
+    io = _io_dtype(k_cache)
+    _need(k_new, "k_new", io, (c.batch, c.num_kv_heads, c.dk))
+    _need(v_new, "v_new", io, (c.batch, c.num_kv_heads, c.dv))
     _need(lens, "lens", torch.int32, (c.batch,))
     if lens_out is None:
         lens_out = lens
@@ -221,7 +271,7 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
 
 def _attend_args(q, k_cache, v_cache, lens):
     c = _cache(k_cache, v_cache)
-    _need(q, "q", k_cache.dtype)
+    _need(q, "q", _io_dtype(k_cache))
     if q.dim() != 3 or q.shape[0] != c.batch or q.shape[2] != c.dk:
         raise GqaError(f"q must be [batch={c.batch}, num_q_heads, dk={c.dk}]")
     _need(lens, "lens", torch.int32, (c.batch,))
@@ -338,8 +388,9 @@ def decode_step(q, k_cache, v_cache, k_new, v_new, lens_in, lens_out,
     from :func:`step_workspace` (zero-filled once, then reused)."""
     c, hq = _attend_args(q, k_cache, v_cache, lens_in)
     bp, bs = _bias(c, bias)
-    _need(k_new, "k_new", k_cache.dtype, (c.batch, c.num_kv_heads, c.dk))
-    _need(v_new, "v_new", k_cache.dtype, (c.batch, c.num_kv_heads, c.dv))
+    io = _io_dtype(k_cache)
+    _need(k_new, "k_new", io, (c.batch, c.num_kv_heads, c.dk))
+    _need(v_new, "v_new", io, (c.batch, c.num_kv_heads, c.dv))
     _need(lens_out, "lens_out", torch.int32, (c.batch,))
     if dropped is not None:
         _need(dropped, "dropped", torch.int32, (1,))
@@ -434,8 +485,9 @@ def stream_append(ring_k, ring_v, k_new, v_new, count_in, count_out=None,
     rc = _cache(ring_k, ring_v)
     sc = None if sink is None else _cache(*sink)
     mc = None if main is None else _cache(*main)
-    _need(k_new, "k_new", ring_k.dtype, (rc.batch, rc.num_kv_heads, rc.dk))
-    _need(v_new, "v_new", ring_k.dtype, (rc.batch, rc.num_kv_heads, rc.dv))
+    io = _io_dtype(ring_k)
+    _need(k_new, "k_new", io, (rc.batch, rc.num_kv_heads, rc.dk))
+    _need(v_new, "v_new", io, (rc.batch, rc.num_kv_heads, rc.dv))
     _need(count_in, "count_in", torch.int32, (rc.batch,))
     dev = ring_k.device
     new = lambda: torch.empty(rc.batch, dtype=torch.int32, device=dev)
@@ -474,8 +526,9 @@ def decode_step_branches(q, branches, append_branch: int, k_new, v_new,
     c0, hq = _attend_args(q, branches[0][0], branches[0][1], branches[0][2])
     ab = branches[append_branch]
     ca = _cache(ab[0], ab[1])
-    _need(k_new, "k_new", ab[0].dtype, (ca.batch, ca.num_kv_heads, ca.dk))
-    _need(v_new, "v_new", ab[0].dtype, (ca.batch, ca.num_kv_heads, ca.dv))
+    io = _io_dtype(ab[0])
+    _need(k_new, "k_new", io, (ca.batch, ca.num_kv_heads, ca.dk))
+    _need(v_new, "v_new", io, (ca.batch, ca.num_kv_heads, ca.dv))
     _need(lens_out, "lens_out", torch.int32, (ca.batch,))
     if dropped is not None:
         _need(dropped, "dropped", torch.int32, (1,))

@@ -24,7 +24,8 @@ LIB = PKG / "libgqa_decode.so"
 BENCH_LIB = PKG / "libgqa_bench.so"   # measurement helpers, not the decode ABI
 ARCH = "gfx950"
 
-SOURCES = ["abi.cpp", "append.hip", "partition_bf16.hip", "partition_f32.hip",
+SOURCES = ["abi.cpp", "append.hip", "partition_bf16.hip", "partition_fp8.hip",
+           "partition_f32.hip",
            "combine.hip", "schedule.hip"]
 BENCH_SOURCES = ["bench_kernels.hip"]
 

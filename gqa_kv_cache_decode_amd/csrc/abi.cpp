@@ -48,14 +48,17 @@ bool aligned16(const void *p) {
   return (reinterpret_cast<uintptr_t>(p) & 15) == 0;
 }
 
-int esize(int32_t dtype) { return dtype == GQA_DTYPE_F32 ? 4 : 2; }
+int esize(int32_t dtype) {
+  return dtype == GQA_DTYPE_F32 ? 4 : dtype == GQA_DTYPE_BF16 ? 2 : 1;
+}
 
 gqa_status check_cache_dims(const gqa_cache *c) {
   if (!c) return GQA_ERR_INVALID_ARGUMENT;
   if (c->batch <= 0 || c->max_len <= 0 || c->num_kv_heads <= 0 || c->dk <= 0 ||
       c->dv <= 0)
     return GQA_ERR_INVALID_ARGUMENT;
-  if (c->dtype != GQA_DTYPE_F32 && c->dtype != GQA_DTYPE_BF16)
+  if (c->dtype != GQA_DTYPE_F32 && c->dtype != GQA_DTYPE_BF16 &&
+      c->dtype != GQA_DTYPE_FP8_E4M3)
     return GQA_ERR_INVALID_ARGUMENT;
   return GQA_OK;
 }
@@ -63,6 +66,12 @@ gqa_status check_cache_dims(const gqa_cache *c) {
 gqa_status check_cache_data(const gqa_cache *c) {
   if (!c->k || !c->v) return GQA_ERR_INVALID_ARGUMENT;
   if (!aligned16(c->k) || !aligned16(c->v)) return GQA_ERR_INVALID_ARGUMENT;
+  if (c->dtype == GQA_DTYPE_FP8_E4M3) {
+    if (!c->k_scale || !c->v_scale) return GQA_ERR_INVALID_ARGUMENT;
+    if ((reinterpret_cast<uintptr_t>(c->k_scale) |
+         reinterpret_cast<uintptr_t>(c->v_scale)) & 3)
+      return GQA_ERR_INVALID_ARGUMENT;
+  }
   return GQA_OK;
 }
 
@@ -71,9 +80,10 @@ gqa_status check_heads(const gqa_cache *c, int32_t hq) {
   if (hq % c->num_kv_heads != 0) return GQA_ERR_SHAPE_MISMATCH;
   const int hpk = hq / c->num_kv_heads;
   if (c->dv > kMaxCombineDv) return GQA_ERR_UNSUPPORTED;
-  const bool ok = c->dtype == GQA_DTYPE_BF16
-                      ? gqa::partition_bf16_supported(c->dk, c->dv, hpk)
-                      : gqa::partition_f32_supported(c->dk, c->dv, hpk);
+  // fp8 caches run the bf16 kernel family (codes decoded to bf16)
+  const bool ok = c->dtype == GQA_DTYPE_F32
+                      ? gqa::partition_f32_supported(c->dk, c->dv, hpk)
+                      : gqa::partition_bf16_supported(c->dk, c->dv, hpk);
   return ok ? GQA_OK : GQA_ERR_UNSUPPORTED;
 }
 
@@ -83,15 +93,15 @@ gqa_status check_carry(const gqa_carry *x) {
 }
 
 bool uses_mfma(const gqa_cache *c) {
-  return c->dtype == GQA_DTYPE_BF16 || gqa::partition_f32_uses_mfma(c->dk, c->dv);
+  return c->dtype != GQA_DTYPE_F32 || gqa::partition_f32_uses_mfma(c->dk, c->dv);
 }
 
-// Wavefronts per partition work-group (bf16 kernel): four where a
+// Wavefronts per partition work-group (bf16 / fp8 kernel): four where a
 // wavefront's K/V tile is at most 32 x 256 bf16 values (dk + dv <= 256), two
 // for the wider heads, whose LDS tiles and registers would otherwise leave a
 // compute unit a single work-group.
 int partition_waves(const gqa_cache *c) {
-  if (c->dtype != GQA_DTYPE_BF16) return gqa::kPartitionWaves;
+  if (c->dtype == GQA_DTYPE_F32) return gqa::kPartitionWaves;
   return gqa::partition_waves(c->dk, c->dv);
 }
 
@@ -107,7 +117,7 @@ int32_t auto_chunk(const gqa_cache *c) {
   // A cache of at most two tiles per wavefront is one chunk: its launch is
   // latency-bound, and a single chunk writes the results directly instead of
   // passing partials through a second kernel or an arrival count.
-  const int64_t tile = c->dtype == GQA_DTYPE_BF16 ? 32 : 16;
+  const int64_t tile = c->dtype == GQA_DTYPE_F32 ? 16 : 32;
   if (uses_mfma(c) && c->max_len <= 2 * waves * tile)
     return (c->max_len + kChunkQuantum - 1) / kChunkQuantum * kChunkQuantum;
   int32_t chunk = kMaxChunk;
@@ -188,6 +198,33 @@ gqa_status device_status(hipError_t e) {
   return e == hipSuccess ? GQA_OK : GQA_ERR_DEVICE;
 }
 
+// The storage fields of a partition launch (fp8 flag and scales).
+void set_storage(PartitionArgs *a, const gqa_cache *c) {
+  const bool fp8 = c->dtype == GQA_DTYPE_FP8_E4M3;
+  a->fp8 = fp8 ? 1 : 0;
+  a->k_scale = fp8 ? c->k_scale : nullptr;
+  a->v_scale = fp8 ? c->v_scale : nullptr;
+}
+
+// The partition (or whole decode step) kernel family of the cache's dtype.
+hipError_t launch_partition(const gqa_cache *c, const PartitionArgs &a,
+                            const gqa::StepParams &ep, hipStream_t s) {
+  switch (c->dtype) {
+    case GQA_DTYPE_BF16: return gqa::launch_partition_bf16(a, ep, s);
+    case GQA_DTYPE_FP8_E4M3: return gqa::launch_partition_fp8(a, ep, s);
+    default: return gqa::launch_partition_f32(a, ep, s);
+  }
+}
+
+hipError_t launch_step(const gqa_cache *c, const PartitionArgs &a,
+                       const gqa::StepParams &sp, hipStream_t s) {
+  switch (c->dtype) {
+    case GQA_DTYPE_BF16: return gqa::launch_step_bf16(a, sp, s);
+    case GQA_DTYPE_FP8_E4M3: return gqa::launch_step_fp8(a, sp, s);
+    default: return gqa::launch_step_f32(a, sp, s);
+  }
+}
+
 // The partial layout and work items of a one-cache launch.
 void single_branch(PartitionArgs *a) {
   a->total_cols = a->num_chunks;
@@ -262,6 +299,7 @@ gqa_status partition_checked(const void *q, int32_t hq, const gqa_cache *c,
   a.chunk_tokens = plan->chunk_tokens;
   a.num_chunks = plan->num_chunks;
   single_branch(&a);
+  set_storage(&a, c);
   a.scale_log2 = (float)(sc * 1.4426950408889634);
   a.bias = bias;
   a.bias_stride = bias ? bias_stride : 0;
@@ -272,9 +310,7 @@ gqa_status partition_checked(const void *q, int32_t hq, const gqa_cache *c,
   a.part_acc = reinterpret_cast<float *>(base + plan->off_acc);
   gqa_status st = schedule_checked(c, *plan, lens, false, ws, &a, s);
   if (st != GQA_OK) return st;
-  return device_status(c->dtype == GQA_DTYPE_BF16
-                           ? gqa::launch_partition_bf16(a, ep, s)
-                           : gqa::launch_partition_f32(a, ep, s));
+  return device_status(launch_partition(c, a, ep, s));
 }
 
 gqa_status combine_checked(int32_t hq, const gqa_cache *c, const int32_t *lens,
@@ -465,11 +501,14 @@ gqa_status branches_checked(const void *q, int32_t num_q_heads,
   a.append_branch = step ? step->append_branch : -1;
   a.sel = nullptr;
   a.cache_len = c0->max_len;
+  set_storage(&a, c0);
   for (int32_t i = 1; i < num_branches; ++i) {
     const gqa_branch &b = branches[i];
     gqa::ExtraBranch &x = a.extra[i - 1];
     x.k = b.cache.k;
     x.v = b.cache.v;
+    x.k_scale = a.fp8 ? b.cache.k_scale : nullptr;
+    x.v_scale = a.fp8 ? b.cache.v_scale : nullptr;
     x.lens = b.lens;
     x.bias = b.bias;
     x.bias_stride = b.bias ? b.bias_stride : 0;
@@ -489,7 +528,6 @@ gqa_status branches_checked(const void *q, int32_t num_q_heads,
   a.part_acc = reinterpret_cast<float *>(base + p.off_acc);
   a.sched = nullptr;
   a.sched_len = 0;
-  const bool bf16 = c0->dtype == GQA_DTYPE_BF16;
   if (step) {
     gqa::StepParams sp{};
     sp.k_new = step->k_new;
@@ -497,11 +535,9 @@ gqa_status branches_checked(const void *q, int32_t num_q_heads,
     sp.lens_in = branches[step->append_branch].lens;
     sp.lens_out = step->lens_out;
     sp.dropped = step->dropped;
-    st = device_status(bf16 ? gqa::launch_step_bf16(a, sp, stream)
-                            : gqa::launch_step_f32(a, sp, stream));
+    st = device_status(launch_step(c0, a, sp, stream));
   } else {
-    st = device_status(bf16 ? gqa::launch_partition_bf16(a, gqa::StepParams{}, stream)
-                            : gqa::launch_partition_f32(a, gqa::StepParams{}, stream));
+    st = device_status(launch_partition(c0, a, gqa::StepParams{}, stream));
   }
   if (st != GQA_OK) return st;
 
@@ -594,11 +630,17 @@ gqa_status gqa_kv_append(const gqa_cache *cache, const void *k_new,
   if (st != GQA_OK) return st;
   if ((st = check_cache_data(cache)) != GQA_OK) return st;
   if (!k_new || !v_new || !lens_in || !lens_out) return GQA_ERR_INVALID_ARGUMENT;
+  const bool fp8 = cache->dtype == GQA_DTYPE_FP8_E4M3;
   const int64_t rk = (int64_t)cache->num_kv_heads * cache->dk * esize(cache->dtype);
   const int64_t rv = (int64_t)cache->num_kv_heads * cache->dv * esize(cache->dtype);
-  if (rk > std::numeric_limits<int32_t>::max() ||
-      rv > std::numeric_limits<int32_t>::max())
+  // (bf16 rows of an fp8 cache are read twice as wide as the code rows)
+  if (2 * rk > std::numeric_limits<int32_t>::max() ||
+      2 * rv > std::numeric_limits<int32_t>::max())
     return GQA_ERR_UNSUPPORTED;
+  if (fp8) {  // sixteen codes per 16-byte piece, from 16-byte bf16 pieces
+    if (cache->dk % 16 || cache->dv % 16) return GQA_ERR_UNSUPPORTED;
+    if (!aligned16(k_new) || !aligned16(v_new)) return GQA_ERR_INVALID_ARGUMENT;
+  }
   AppendArgs a;
   a.k = cache->k;
   a.v = cache->v;
@@ -611,6 +653,10 @@ gqa_status gqa_kv_append(const gqa_cache *cache, const void *k_new,
   a.max_len = cache->max_len;
   a.row_bytes_k = (int)rk;
   a.row_bytes_v = (int)rv;
+  a.fp8 = fp8 ? 1 : 0;
+  a.num_kv_heads = cache->num_kv_heads;
+  a.k_scale = fp8 ? cache->k_scale : nullptr;
+  a.v_scale = fp8 ? cache->v_scale : nullptr;
   return device_status(gqa::launch_append(a, stream));
 }
 
@@ -623,6 +669,7 @@ gqa_status gqa_stream_append(const gqa_cache *sink, const gqa_cache *ring,
   gqa_status st = check_cache_dims(ring);
   if (st != GQA_OK) return st;
   if ((st = check_cache_data(ring)) != GQA_OK) return st;
+  if (ring->dtype == GQA_DTYPE_FP8_E4M3) return GQA_ERR_UNSUPPORTED;
   for (const gqa_cache *c : {sink, main_cache}) {
     if (!c) continue;
     if ((st = check_cache_dims(c)) != GQA_OK) return st;
@@ -857,6 +904,7 @@ gqa_status gqa_attend_gathered(const void *q, int32_t num_q_heads,
   a.chunk_tokens = g.plan.chunk_tokens;
   a.num_chunks = g.plan.num_chunks;
   single_branch(&a);
+  set_storage(&a, cache);
   a.sel = sel;
   a.cache_len = cache->max_len;
   a.scale_log2 = (float)(sc * 1.4426950408889634);
@@ -868,9 +916,7 @@ gqa_status gqa_attend_gathered(const void *q, int32_t num_q_heads,
   a.part_acc = reinterpret_cast<float *>(base + g.plan.off_acc);
   a.sched = nullptr;
   a.sched_len = 0;
-  st = device_status(cache->dtype == GQA_DTYPE_BF16
-                         ? gqa::launch_partition_bf16(a, ep, stream)
-                         : gqa::launch_partition_f32(a, ep, stream));
+  st = device_status(launch_partition(cache, a, ep, stream));
   if (st != GQA_OK || ep.direct) return st;
   return combine_checked(num_q_heads, &g.vcache, count, &g.plan, workspace,
                          carry_in, carry_out, out, stream);
@@ -934,6 +980,7 @@ gqa_status gqa_decode_step(const void *q, int32_t num_q_heads,
   a.chunk_tokens = plan.chunk_tokens;
   a.num_chunks = plan.num_chunks;
   single_branch(&a);
+  set_storage(&a, cache);
   a.scale_log2 = (float)(sc * 1.4426950408889634);
   a.bias = bias;
   a.bias_stride = bias ? bias_stride : 0;
@@ -954,9 +1001,7 @@ gqa_status gqa_decode_step(const void *q, int32_t num_q_heads,
   sp.dropped = dropped;
   sp.counters = reinterpret_cast<int *>(base + plan.workspace_bytes);
   sp.fuse = !sp.direct && step_fuses(cache, num_q_heads, plan) ? 1 : 0;
-  st = device_status(cache->dtype == GQA_DTYPE_BF16
-                         ? gqa::launch_step_bf16(a, sp, stream)
-                         : gqa::launch_step_f32(a, sp, stream));
+  st = device_status(launch_step(cache, a, sp, stream));
   if (st != GQA_OK || sp.fuse || sp.direct) return st;
   return combine_checked(num_q_heads, cache, lens_out, &plan, workspace,
                          carry_in, carry_out, out, stream);

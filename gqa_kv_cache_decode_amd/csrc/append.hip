@@ -6,6 +6,7 @@
 // and the drop is counted: the page warns that the cache is full and returns
 // without writing.
 #include "device_common.h"
+#include "fp8_common.h"
 #include "launch.h"
 
 namespace gqa {
@@ -69,6 +70,38 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
                          (uintptr_t)a.row_bytes_k | (uintptr_t)a.row_bytes_v) &
                         15) == 0;
   copy_rows(kd, ks, a.row_bytes_k, vd, vs, a.row_bytes_v, aligned, ok);
+  __syncthreads();  // lens_in is read by every thread before lens_out is set
+  if (threadIdx.x == 0) {
+    a.lens_out[b] = ok ? n + 1 : n;
+    if (!ok && a.dropped) atomicAdd(a.dropped, 1);
+  }
+}
+
+// kv_append into fp8 caches: the new bf16 rows are quantised (fp32 quotient
+// by the sequence's scale of that KV head, nearest E4M3 code, ties to even,
+// saturating at 448) into slot n, sixteen codes per thread and piece.
+__global__ __launch_bounds__(kThreads) void append_e4m3_kernel(AppendArgs a) {
+  const int b = blockIdx.x;
+  const int n = a.lens_in[b];
+  const bool ok = n >= 0 && n < a.max_len;
+  if (ok) {
+    const size_t slot = (size_t)b * a.max_len + n;
+    const size_t sb = (size_t)b * a.num_kv_heads;
+    const int dk = a.row_bytes_k / a.num_kv_heads;
+    const int dv = a.row_bytes_v / a.num_kv_heads;
+    u32x4 *kd = reinterpret_cast<u32x4 *>(static_cast<unsigned char *>(a.k) +
+                                          slot * a.row_bytes_k);
+    u32x4 *vd = reinterpret_cast<u32x4 *>(static_cast<unsigned char *>(a.v) +
+                                          slot * a.row_bytes_v);
+    const uint16_t *kn = static_cast<const uint16_t *>(a.k_new) +
+                         (size_t)b * a.row_bytes_k;
+    const uint16_t *vn = static_cast<const uint16_t *>(a.v_new) +
+                         (size_t)b * a.row_bytes_v;
+    for (int e = threadIdx.x; e < a.row_bytes_k / 16; e += kThreads)
+      kd[e] = e4m3_quantize16(kn + e * 16, a.k_scale[sb + e * 16 / dk]);
+    for (int e = threadIdx.x; e < a.row_bytes_v / 16; e += kThreads)
+      vd[e] = e4m3_quantize16(vn + e * 16, a.v_scale[sb + e * 16 / dv]);
+  }
   __syncthreads();  // lens_in is read by every thread before lens_out is set
   if (threadIdx.x == 0) {
     a.lens_out[b] = ok ? n + 1 : n;
@@ -141,7 +174,10 @@ __global__ __launch_bounds__(kThreads) void stream_append_kernel(
 }  // namespace
 
 hipError_t launch_append(const AppendArgs &a, hipStream_t s) {
-  hipLaunchKernelGGL(append_kernel, dim3(a.batch), dim3(kThreads), 0, s, a);
+  if (a.fp8)
+    hipLaunchKernelGGL(append_e4m3_kernel, dim3(a.batch), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(append_kernel, dim3(a.batch), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -1,0 +1,99 @@
+// E4M3 (OCP 8-bit floating point, "E4M3FN") codes on gfx950: decode to
+// bf16 for the matrix cores, and the quantisation of new rows.
+//
+// A cache of codes carries one fp32 scale per (sequence, KV head) for K and
+// one for V; code c stands for decode(c) * scale.  Every E4M3 value has at
+// most four significant bits and an exponent within bf16's range, so it is
+// exact in bf16: the kernels decode codes to bf16 and run the bf16 loop
+// unchanged, folding the K scale into the logit scale and the V scale into
+// the weighted value sum.
+#pragma once
+
+#include "device_common.h"
+
+namespace gqa {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kE4m3Max = 448.0f;
+
+// Four codes (the bytes of w, lowest first) as four bf16 values in two
+// words.  The hardware conversion decodes E4M3 exactly to fp32; the bf16 is
+// the upper half of that fp32 (its lower half is zero).
+__device__ __forceinline__ uint2 e4m3x4_to_bf16(uint32_t w) {
+  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);  // bytes 0, 1
+  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);   // bytes 2, 3
+  uint2 r;
+  r.x = __builtin_amdgcn_perm(__float_as_uint(a.y), __float_as_uint(a.x),
+                              0x07060302u);
+  r.y = __builtin_amdgcn_perm(__float_as_uint(b.y), __float_as_uint(b.x),
+                              0x07060302u);
+  return r;
+}
+
+// Sixteen codes as sixteen bf16 values, in order: p0 holds elements 0..7,
+// p1 elements 8..15.
+__device__ __forceinline__ void e4m3x16_to_bf16(u32x4 c, u32x4 &p0,
+                                                u32x4 &p1) {
+  const uint2 a = e4m3x4_to_bf16(c.x), b = e4m3x4_to_bf16(c.y);
+  const uint2 d = e4m3x4_to_bf16(c.z), e = e4m3x4_to_bf16(c.w);
+  p0 = u32x4{a.x, a.y, b.x, b.y};
+  p1 = u32x4{d.x, d.y, e.x, e.y};
+}
+
+// The code of x: nearest E4M3 value, ties to the even mantissa, magnitudes
+// above 448 saturated.  The hardware conversion rounds to nearest even but
+// does not saturate (it gives NaN from 480 up), hence the clamp first; the
+// clamp keeps the sign of zero.
+__device__ __forceinline__ float e4m3_clamp(float x) {
+  return fminf(fmaxf(x, -kE4m3Max), kE4m3Max);
+}
+
+// Codes of four fp32 values packed into a word (element 0 in the low byte).
+__device__ __forceinline__ uint32_t e4m3_pack4(float x0, float x1, float x2,
+                                               float x3) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(x0), e4m3_clamp(x1), 0,
+                                          false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(x2), e4m3_clamp(x3), w, true);
+  return (uint32_t)w;
+}
+
+// Codes of eight bf16 values (one 16-byte piece) divided by `scale`: the
+// quotient is the correctly rounded fp32 division.
+__device__ __forceinline__ uint2 e4m3_quantize8(u32x4 x, float scale) {
+  float f[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(x[i] << 16) / scale;
+    f[2 * i + 1] = __uint_as_float(x[i] & 0xFFFF0000u) / scale;
+  }
+  uint2 r;
+  r.x = e4m3_pack4(f[0], f[1], f[2], f[3]);
+  r.y = e4m3_pack4(f[4], f[5], f[6], f[7]);
+  return r;
+}
+
+// Codes of sixteen bf16 values at `src` (two 16-byte pieces).
+__device__ __forceinline__ u32x4 e4m3_quantize16(const uint16_t *src,
+                                                 float scale) {
+  const uint2 a = e4m3_quantize8(stream_load16(src), scale);
+  const uint2 b = e4m3_quantize8(stream_load16(src + 8), scale);
+  return u32x4{a.x, a.y, b.x, b.y};
+}
+
+// Stores one KV group's rows of the new token (bf16 [d] each) into the cache
+// slot as codes, 16 codes per 16-byte piece, spread over the work-group's
+// threads.  As for bf16 rows, nothing in the same launch reads the slot, so
+// the stores are not waited for.
+__device__ __forceinline__ void store_group_row_e4m3(
+    const uint16_t *kn, u32x4 *kd, int kpieces, float kscale,
+    const uint16_t *vn, u32x4 *vd, int vpieces, float vscale) {
+  for (int e = threadIdx.x; e < kpieces + vpieces; e += blockDim.x) {
+    if (e < kpieces)
+      kd[e] = e4m3_quantize16(kn + e * 16, kscale);
+    else
+      vd[e - kpieces] = e4m3_quantize16(vn + (e - kpieces) * 16, vscale);
+  }
+}
+
+}  // namespace gqa

@@ -21,6 +21,7 @@ constexpr int partition_waves(int dk, int dv) { return dk + dv <= 256 ? 4 : 2; }
 // Every branch has the launch's batch, heads and head widths.
 struct ExtraBranch {
   const void *k, *v;
+  const float *k_scale, *v_scale;  // fp8 launches: [B][Hkv] each
   const int32_t *lens;
   const float *bias;
   long long bias_stride;
@@ -35,6 +36,10 @@ struct PartitionArgs {
   const void *q;        // [B][Hkv*hpk][dk]
   const void *k;        // [B][max_len][Hkv][dk]
   const void *v;        // [B][max_len][Hkv][dv]
+  // fp8 (E4M3) storage: code c of (b, g) stands for decode(c) * scale[b][g];
+  // fp8 = 0 (bf16 / fp32 storage) leaves the scales unused.
+  int fp8;
+  const float *k_scale, *v_scale;  // [B][Hkv] each
   const int32_t *lens;  // [B]
   int batch, max_len, num_kv_heads, hpk, dk, dv;
   int chunk_tokens, num_chunks;
@@ -125,6 +130,10 @@ struct AppendArgs {
   int32_t *lens_out;
   int32_t *dropped;
   int batch, max_len, row_bytes_k, row_bytes_v;  // bytes of one token's K/V row
+  // fp8 caches: k_new / v_new are bf16 rows [Hkv][d], quantised with the
+  // sequence's scales (row_bytes_* are then the code rows' bytes, Hkv * d)
+  int fp8, num_kv_heads;
+  const float *k_scale, *v_scale;  // [B][Hkv] each
 };
 
 // One token per sequence into a streaming layout: permanent sink slots, a
@@ -174,6 +183,11 @@ hipError_t launch_partition_f32(const PartitionArgs &a, const StepParams &ep,
 // shapes only.  `a.lens` is unused (lengths come from sp.lens_in).
 hipError_t launch_step_bf16(const PartitionArgs &a, const StepParams &sp,
                             hipStream_t s);
+// fp8 (E4M3) caches: the bf16 family's shapes, a.fp8 set, q and new rows bf16.
+hipError_t launch_partition_fp8(const PartitionArgs &a, const StepParams &ep,
+                                hipStream_t s);
+hipError_t launch_step_fp8(const PartitionArgs &a, const StepParams &sp,
+                           hipStream_t s);
 hipError_t launch_step_f32(const PartitionArgs &a, const StepParams &sp,
                            hipStream_t s);
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s);

@@ -1,444 +1,7 @@
-// Split-K partition kernel for bf16 caches on gfx950 (MFMA 16x16x32 bf16).
-//
-// One work-group handles one (sequence b, KV group g, chunk c) and all
-// heads_per_kv query heads of the group.  Every K/V row of the chunk is read
-// from HBM once, with 16-byte coalesced nontemporal loads, staged in the
-// wavefront's own LDS slice, and shared by all heads of the group through the
-// MFMA N dimension (needle-core attn.rs module doc: a KV head serves several
-// query heads directly, without copying its K/V per head; cortiq-engine
-// NystromState: the rows of a group are identical for all its heads, so they
-// are held once per group).
-//
-// Per 32-token tile a wavefront computes
-//   S^T[token][head] = K_tile[token][:] . q[head][:]         (MFMA, A = K)
-// then folds the tile into each head's running maximum m, partition l and
-// weighted value sum acc (usearch attend: each scored key updates these three
-// per-head quantities), in base-2 units:
-//   m' = max(m, max_j s_j), alpha = 2^(m - m'), p_j = 2^(s_j - m'),
-//   l = alpha l + sum_j p_j,  acc = alpha acc + sum_j p_j V_j
-// with acc^T[dv][head] += V_tile^T[dv][token] . P^T[token][head] on MFMA.
-// The S^T accumulator layout (lane = head column, 4 consecutive tokens per
-// lane group) is exactly the B-operand layout the P.V product needs, so P never
-// leaves registers.  P is split as p = hi + lo with hi, lo bf16 so that the
-// product keeps ~16 bits of each weight (two MFMAs instead of one; the matrix
-// cores are far from busy on this HBM-bound loop).
-//
-// Heads are padded to 16 (the MFMA N width); padded heads see q = 0 and are
-// never written.  Tokens of a tile past the chunk end are loaded as zeros and
-// masked to -inf logits, so padding slots of the cache are never read.
-//
-// In STEP mode the same launch is a whole decode step (needle-core
-// self_attn_incremental: push_kv, then attend over the cache including the new
-// token).  The work-group whose chunk holds the new slot stores the token's
-// rows into the cache without waiting for the stores, and the one tile that
-// holds the slot reads those rows from k_new/v_new instead of the cache, so
-// the append never stalls the stream.  The group's partials are folded by the
-// last work-group to finish when `fuse` is set.
-#include "device_common.h"
-#include "launch.h"
-#include "step_common.h"
+// Partition launches for bf16 caches (kernel in partition_mfma16.h).
+#include "partition_mfma16.h"
 
 namespace gqa {
-namespace {
-
-constexpr int kTileTokens = 32;
-
-template <int DK, int DV>
-struct Bf16Geom {
-  static_assert(DK % 32 == 0 && DV % 16 == 0, "head widths");
-  static constexpr int kPieces = DK / 8;  // 16-byte pieces per K row
-  static constexpr int vPieces = DV / 8;
-  static constexpr int kLoads = kTileTokens * kPieces / 64;  // per lane
-  static constexpr int vLoads = kTileTokens * vPieces / 64;
-  static_assert(kTileTokens * kPieces % 64 == 0, "K tile split");
-  static_assert(kTileTokens * vPieces % 64 == 0, "V tile split");
-  static constexpr int kStride = DK + 8;  // LDS row stride in bf16 (+16 B pad)
-  static constexpr int vStride = DV + 8;
-  static constexpr int waveLdsElems = kTileTokens * (kStride + vStride);
-};
-
-template <int DK, int DV, int NW, bool STEP, bool BIAS, bool GATHER>
-__global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
-    PartitionArgs args, StepParams sp) {
-  using G = Bf16Geom<DK, DV>;
-  constexpr int kMergeFloats = NW * 16 * (DV + 2);
-  constexpr int kTileBytes = NW * G::waveLdsElems * 2;
-  constexpr int kLdsBytes =
-      kTileBytes > kMergeFloats * 4 ? kTileBytes : kMergeFloats * 4;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
-  __shared__ int s_flag;
-  __shared__ float s_in[32];  // carry_in m, l of the group's rows (direct)
-  __shared__ int s_slot[GATHER ? kGatherChunk : 1];  // gathered cache slots
-
-  PartitionArgs a = args;
-  int item, branch = 0;
-  if (a.sched) {  // scheduled launch: the table entry, or nothing to do
-    item = a.sched[blockIdx.x];
-    if (item < 0) return;
-  } else {
-    // the block's branch (multi-branch launch: each branch owns a block
-    // range starting at a multiple of 8), then its item within the branch
-    item = blockIdx.x;
-    branch = select_branch(a, item);
-    const int nitems = a.batch * a.num_kv_heads * a.num_chunks;
-    if (item >= nitems) return;  // padding up to the next branch
-    item = xcd_local_item(item, nitems);
-  }
-  const int Hkv = a.num_kv_heads, hpk = a.hpk, nchunk = a.num_chunks;
-  const int c = item % nchunk;
-  const int bg = item / nchunk;
-  const int g = bg % Hkv;
-  const int b = bg / Hkv;
-
-  // decode step: this branch takes the new token (the others attend as is)
-  const bool stepping = STEP && branch == a.append_branch;
-  const SeqLen sl = seq_len(a, sp, b, stepping);
-  const int n = sl.n;
-  if (stepping && g == 0 && c == 0 && threadIdx.x == 0) step_bookkeeping(sp, b, sl);
-  const int t0 = c * a.chunk_tokens;
-  // A work-group with nothing live exits, except the first of an empty
-  // sequence when final results are written in this launch: it still writes
-  // the group's outputs.
-  if (t0 >= n && !(c == 0 && (sp.direct || (STEP && sp.fuse)))) return;
-  const int t1 = min(t0 + a.chunk_tokens, n);
-  const int ntiles = t1 > t0 ? (t1 - t0 + kTileTokens - 1) / kTileTokens : 0;
-
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const int hl = lane & 15;  // head column of this lane
-  const int kg = lane >> 4;  // lane group: k-slice of MFMA operands
-  const int Hq = Hkv * hpk;
-
-  // q as the B operand of S^T = K q^T: lane holds head hl, dims s*32+kg*8..+8.
-  // Padding columns (hl >= hpk) repeat the group's last head; they are never
-  // written, and loading them unconditionally keeps the load off the critical
-  // path (no partial-lane write to wait for).
-  bf16x8 qf[DK / 32];
-  {
-    const uint16_t *qrow = static_cast<const uint16_t *>(a.q) +
-                           ((size_t)b * Hq + (size_t)g * hpk + min(hl, hpk - 1)) * DK;
-#pragma unroll
-    for (int s = 0; s < DK / 32; ++s)
-      qf[s] = *reinterpret_cast<const bf16x8 *>(qrow + s * 32 + kg * 8);
-  }
-
-  uint16_t *Ks = reinterpret_cast<uint16_t *>(lds) + w * G::waveLdsElems;
-  uint16_t *Vs = Ks + kTileTokens * G::kStride;
-
-  const size_t kTok = (size_t)Hkv * DK;  // elements between tokens
-  const size_t vTok = (size_t)Hkv * DV;
-  uint16_t *Kg = static_cast<uint16_t *>(const_cast<void *>(a.k)) +
-                 ((size_t)b * a.cache_len * Hkv + g) * DK;
-  uint16_t *Vg = static_cast<uint16_t *>(const_cast<void *>(a.v)) +
-                 ((size_t)b * a.cache_len * Hkv + g) * DV;
-
-  // STEP: the work-group whose chunk holds the new slot stores the token's
-  // rows of this group into the cache.  The stores are not waited for: later
-  // calls read the slot, while this call reads the rows from k_new/v_new (the
-  // slot is the last live token of the chunk, relative position `rel`).
-  const uint16_t *knew = nullptr, *vnew = nullptr;
-  int rel = -1;
-  if (stepping && sl.fresh && sl.n_old / a.chunk_tokens == c) {
-    rel = sl.n_old - t0;
-    knew = static_cast<const uint16_t *>(sp.k_new) + ((size_t)b * Hkv + g) * DK;
-    vnew = static_cast<const uint16_t *>(sp.v_new) + ((size_t)b * Hkv + g) * DV;
-    store_group_row(reinterpret_cast<const u32x4 *>(knew),
-                    reinterpret_cast<u32x4 *>(Kg + (size_t)sl.n_old * kTok), DK / 8,
-                    reinterpret_cast<const u32x4 *>(vnew),
-                    reinterpret_cast<u32x4 *>(Vg + (size_t)sl.n_old * vTok), DV / 8);
-  }
-  const int rel_tile = rel >= 0 ? rel / kTileTokens : -1;
-
-  // K/V are read exactly once per call, so the loads are nontemporal: they
-  // stream through without displacing cached lines.  Tokens of a tile past
-  // the chunk's last live token load that last token again (a finite row
-  // whose logit is masked, so its weight is exactly 0): no branches, and no
-  // slot at or past the length is ever read.
-  const int last = max(t1 - t0 - 1, 0);  // last live token, relative to t0
-  const __amdgpu_buffer_rsrc_t kview = buffer_view(
-      Kg + (size_t)t0 * kTok, (uint32_t)(((size_t)last * kTok + DK) * 2));
-  const __amdgpu_buffer_rsrc_t vview = buffer_view(
-      Vg + (size_t)t0 * vTok, (uint32_t)(((size_t)last * vTok + DV) * 2));
-  // Index-gathered: the chunk's cache slots, staged in LDS; the views then
-  // span the sequence's whole cache (slots are absolute)
-  const __amdgpu_buffer_rsrc_t gkview = buffer_view(
-      Kg, GATHER ? (uint32_t)(((size_t)(a.cache_len - 1) * kTok + DK) * 2) : 0u);
-  const __amdgpu_buffer_rsrc_t gvview = buffer_view(
-      Vg, GATHER ? (uint32_t)(((size_t)(a.cache_len - 1) * vTok + DV) * 2) : 0u);
-  if (GATHER) {
-    for (int e = threadIdx.x; e <= last && t1 > t0; e += NW * 64)
-      s_slot[e] = a.sel[(size_t)b * a.max_len + t0 + e];
-    __syncthreads();
-  }
-  // The additive bias of the chunk's live tokens (needle-core attn_bias: one
-  // term per position, shared by the heads); loads past the view return 0.
-  const __amdgpu_buffer_rsrc_t bview =
-      BIAS && a.bias ? buffer_view(a.bias + (size_t)b * a.bias_stride + t0,
-                         (uint32_t)((t1 - t0) * 4))
-                     : buffer_view(nullptr, 0);
-  u32x4 kr[G::kLoads], vr[G::vLoads];
-  f32x4 br[2];  // bias of tokens rb*16 + kg*4 + i, i < 4
-  br[0] = br[1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  auto issue = [&](int tile) {
-    if (BIAS) {
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
-        br[rb] = load4f(bview, (uint32_t)((tile * kTileTokens + rb * 16 + kg * 4) * 4));
-    }
-    if (STEP && tile == rel_tile) {
-      // the tile holding the new slot: that token (and the clamped tokens
-      // after it) come from k_new/v_new, the others from the cache
-      const uint16_t *kb = Kg + (size_t)t0 * kTok, *vb = Vg + (size_t)t0 * vTok;
-#pragma unroll
-      for (int i = 0; i < G::kLoads; ++i) {
-        const int idx = i * 64 + lane;
-        const int t = min(tile * kTileTokens + idx / G::kPieces, last);
-        const int pc = (idx % G::kPieces) * 8;
-        kr[i] = stream_load16(t == rel ? knew + pc : kb + (size_t)t * kTok + pc);
-      }
-#pragma unroll
-      for (int i = 0; i < G::vLoads; ++i) {
-        const int idx = i * 64 + lane;
-        const int t = min(tile * kTileTokens + idx / G::vPieces, last);
-        const int pc = (idx % G::vPieces) * 8;
-        vr[i] = stream_load16(t == rel ? vnew + pc : vb + (size_t)t * vTok + pc);
-      }
-      return;
-    }
-    if (GATHER) {
-#pragma unroll
-      for (int i = 0; i < G::kLoads; ++i) {
-        const int idx = i * 64 + lane;
-        const int s = s_slot[min(tile * kTileTokens + idx / G::kPieces, last)];
-        kr[i] = stream_load16(gkview, (uint32_t)((s * kTok + (idx % G::kPieces) * 8) * 2));
-      }
-#pragma unroll
-      for (int i = 0; i < G::vLoads; ++i) {
-        const int idx = i * 64 + lane;
-        const int s = s_slot[min(tile * kTileTokens + idx / G::vPieces, last)];
-        vr[i] = stream_load16(gvview, (uint32_t)((s * vTok + (idx % G::vPieces) * 8) * 2));
-      }
-      return;
-    }
-#pragma unroll
-    for (int i = 0; i < G::kLoads; ++i) {
-      const int idx = i * 64 + lane;
-      const int t = min(tile * kTileTokens + idx / G::kPieces, last);
-      kr[i] = stream_load16(kview, (uint32_t)((t * kTok + (idx % G::kPieces) * 8) * 2));
-    }
-#pragma unroll
-    for (int i = 0; i < G::vLoads; ++i) {
-      const int idx = i * 64 + lane;
-      const int t = min(tile * kTileTokens + idx / G::vPieces, last);
-      vr[i] = stream_load16(vview, (uint32_t)((t * vTok + (idx % G::vPieces) * 8) * 2));
-    }
-  };
-
-  float m_run = -INFINITY;  // base-2 running max of head hl
-  float l_run = 0.0f;       // this lane's share of the partition
-  f32x4 o[DV / 16];         // acc^T: head hl, dv rows blk*16 + kg*4 + i
-#pragma unroll
-  for (int blk = 0; blk < DV / 16; ++blk) o[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  int tile = w;
-  if (tile < ntiles) issue(tile);
-  for (; tile < ntiles; tile += NW) {
-    const int tb = t0 + tile * kTileTokens;
-    wave_lds_sync();  // previous tile's LDS reads are done
-#pragma unroll
-    for (int i = 0; i < G::kLoads; ++i) {
-      const int idx = i * 64 + lane;
-      const int pc = idx % G::kPieces;
-      *reinterpret_cast<u32x4 *>(Ks + (idx / G::kPieces) * G::kStride + pc * 8) = kr[i];
-    }
-#pragma unroll
-    for (int i = 0; i < G::vLoads; ++i) {
-      const int idx = i * 64 + lane;
-      const int pc = idx % G::vPieces;
-      *reinterpret_cast<u32x4 *>(Vs + (idx / G::vPieces) * G::vStride + pc * 8) = vr[i];
-    }
-    const f32x4 bcur[2] = {br[0], br[1]};
-    if (tile + NW < ntiles) issue(tile + NW);  // next tile in flight meanwhile
-    wave_lds_sync();
-
-    // S^T for tokens rb*16 + kg*4 + i (i < 4), head hl
-    f32x4 sacc[2];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      sacc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < DK / 32; ++s) {
-        const bf16x8 av = *reinterpret_cast<const bf16x8 *>(
-            Ks + (rb * 16 + hl) * G::kStride + s * 32 + kg * 8);
-        sacc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qf[s], sacc[rb],
-                                                           0, 0, 0);
-      }
-    }
-
-    float x[8];
-    float mt = -INFINITY;
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = tb + rb * 16 + kg * 4 + i;
-        float v = sacc[rb][i] * a.scale_log2;
-        if (BIAS) v += bcur[rb][i] * kLog2e;
-        v = (t < t1) ? v : -INFINITY;
-        x[rb * 4 + i] = v;
-        mt = fmaxf(mt, v);
-      }
-    }
-    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const float m_new = fmaxf(m_run, mt);
-    const float ref = exp_ref(m_new);  // -inf only while every key is removed
-    const float alpha = fast_exp2(m_run - ref);
-    m_run = m_new;
-
-    bf16x8 phi, plo;
-    float psum = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float p = fast_exp2(x[j] - ref);
-      psum += p;
-      const __bf16 h = (__bf16)p;
-      phi[j] = h;
-      plo[j] = (__bf16)(p - (float)h);
-    }
-    l_run = l_run * alpha + psum;
-
-    // acc^T += V^T P^T; the A operand gathers V[token(kg, j)][blk*16 + hl]
-    // with token(kg, j) = j < 4 ? kg*4 + j : 16 + kg*4 + (j - 4), the token
-    // order of this lane's P values.
-#pragma unroll
-    for (int blk = 0; blk < DV / 16; ++blk) {
-      bf16x8 av;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int tok = (j < 4) ? (kg * 4 + j) : (16 + kg * 4 + (j - 4));
-        av[j] = __builtin_bit_cast(__bf16, Vs[tok * G::vStride + blk * 16 + hl]);
-      }
-      o[blk] *= alpha;
-      o[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, phi, o[blk], 0, 0, 0);
-      o[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, plo, o[blk], 0, 0, 0);
-    }
-  }
-
-  // Partition of head hl over the whole wavefront.
-  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
-
-  // Merge the wavefronts' states through LDS and write one partial per head.
-  __syncthreads();
-  float *wm = reinterpret_cast<float *>(lds);
-  float *wl = wm + NW * 16;
-  float *wacc = wl + NW * 16;
-  if (ntiles > 0) {
-    if (lane < 16) {
-      wm[w * 16 + lane] = m_run;
-      wl[w * 16 + lane] = l_tot;
-    }
-#pragma unroll
-    for (int blk = 0; blk < DV / 16; ++blk)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        wacc[(w * 16 + hl) * DV + blk * 16 + kg * 4 + i] = o[blk][i];
-  }
-  if (sp.direct) stage_carry_in(sp, (size_t)b * Hq + (size_t)g * hpk, hpk, s_in);
-  __syncthreads();
-
-  if (ntiles > 0 || sp.direct) {
-    for (int e = threadIdx.x; e < hpk * DV; e += NW * 64) {
-      const int h = e / DV;
-      const int d = e % DV;
-      float M = -INFINITY, acc = 0.0f, L = 0.0f;
-      if (ntiles > 0) {
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, wm[ww * 16 + h]);
-        const float ref = exp_ref(M);
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) {
-          const float f = fast_exp2(wm[ww * 16 + h] - ref);
-          acc += f * wacc[(ww * 16 + h) * DV + d];
-          L += f * wl[ww * 16 + h];
-        }
-      }
-      const size_t row = (size_t)b * Hq + (size_t)g * hpk + h;
-      if (sp.direct) {  // the only chunk: fold carry_in, write the results
-        const float l_in = s_in[hpk + h];
-        fold_state(M, L, acc, s_in[h], l_in,
-                   l_in > 0.0f ? sp.in_acc[row * DV + d] : 0.0f);
-        write_final(sp, row, DV, d, M, L, acc);
-        continue;
-      }
-      const size_t col = row * a.total_cols + a.col_base + c;
-      float *pa = a.part_acc + col * DV + d;
-      float *pm = a.part_m + col;
-      float *pl = a.part_l + col;
-      if (STEP && sp.fuse) {  // read back by this launch's last work-group
-        coherent_store(pa, acc);
-        if (d == 0) {
-          coherent_store(pm, M * kLn2);
-          coherent_store(pl, L);
-        }
-      } else {
-        *pa = acc;
-        if (d == 0) {
-          *pm = M * kLn2;
-          *pl = L;
-        }
-      }
-    }
-  }
-
-  if (STEP && sp.fuse) {
-    const int nc = (n + a.chunk_tokens - 1) / a.chunk_tokens;
-    // an empty sequence has no partials: its first work-group folds alone
-    const bool last = nc == 0 || arrive_last(sp.counters + (size_t)b * Hkv + g,
-                                             nc, &s_flag);
-    if (last) {
-      __syncthreads();  // the LDS merge area is reused below
-      fold_group(a, sp, b, g, nc, reinterpret_cast<float *>(lds));
-    }
-  }
-}
-
-template <int DK, int DV, int NW, bool STEP>
-hipError_t launch_one(const PartitionArgs &a, const StepParams &sp,
-                      hipStream_t s) {
-  const int nwork = a.sched ? a.sched_len : a.total_items;
-  if (a.sel) {  // index-gathered: attend only, no bias
-    if (STEP || a.has_bias) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((partition_bf16_kernel<DK, DV, NW, false, false, true>),
-                       dim3(nwork), dim3(NW * 64), 0, s, a, sp);
-  } else if (a.has_bias) {
-    hipLaunchKernelGGL((partition_bf16_kernel<DK, DV, NW, STEP, true, false>),
-                       dim3(nwork), dim3(NW * 64), 0, s, a, sp);
-  } else {
-    hipLaunchKernelGGL((partition_bf16_kernel<DK, DV, NW, STEP, false, false>),
-                       dim3(nwork), dim3(NW * 64), 0, s, a, sp);
-  }
-  return hipGetLastError();
-}
-
-template <int DK, int DV, bool STEP>
-hipError_t launch_shape(const PartitionArgs &a, const StepParams &sp,
-                        hipStream_t s) {
-  return launch_one<DK, DV, partition_waves(DK, DV), STEP>(a, sp, s);
-}
-
-template <bool STEP>
-hipError_t dispatch(const PartitionArgs &a, const StepParams &sp,
-                    hipStream_t s) {
-  if (a.dk == 64 && a.dv == 64) return launch_shape<64, 64, STEP>(a, sp, s);
-  if (a.dk == 128 && a.dv == 128) return launch_shape<128, 128, STEP>(a, sp, s);
-  if (a.dk == 192 && a.dv == 128) return launch_shape<192, 128, STEP>(a, sp, s);
-  if (a.dk == 256 && a.dv == 256) return launch_shape<256, 256, STEP>(a, sp, s);
-  return hipErrorInvalidValue;
-}
-
-}  // namespace
 
 bool partition_bf16_supported(int dk, int dv, int hpk) {
   if (hpk < 1 || hpk > 16) return false;
@@ -448,12 +11,12 @@ bool partition_bf16_supported(int dk, int dv, int hpk) {
 
 hipError_t launch_partition_bf16(const PartitionArgs &a, const StepParams &ep,
                                  hipStream_t s) {
-  return dispatch<false>(a, ep, s);
+  return dispatch<false, false>(a, ep, s);
 }
 
 hipError_t launch_step_bf16(const PartitionArgs &a, const StepParams &sp,
                             hipStream_t s) {
-  return dispatch<true>(a, sp, s);
+  return dispatch<true, false>(a, sp, s);
 }
 
 }  // namespace gqa

@@ -24,6 +24,8 @@ __device__ __forceinline__ int select_branch(PartitionArgs &a, int &item) {
       const ExtraBranch &x = a.extra[e];
       a.k = x.k;
       a.v = x.v;
+      a.k_scale = x.k_scale;
+      a.v_scale = x.v_scale;
       a.lens = x.lens;
       a.bias = x.bias;
       a.bias_stride = x.bias_stride;

@@ -35,7 +35,7 @@ import torch
 
 BASE_SEED = 20261203
 
-DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
+DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -49,7 +49,8 @@ class DecodeWorkload:
     dk: int
     dv: int
     max_len: int
-    dtype: str = "bf16"            # storage dtype of q, K and V: "f32" | "bf16"
+    dtype: str = "bf16"            # storage of K and V: "f32" | "bf16" | "fp8"
+                                   # (fp8: E4M3 codes + scales, q in bf16)
     dist: str = "normal"           # "normal" | "uniform" | "spike"
     ragged: bool = False           # lens ~ U{1..max_len} instead of all max_len
     scale: float = 0.0             # 0 means 1/sqrt(dk)
@@ -72,6 +73,12 @@ class DecodeWorkload:
 
     @property
     def esz(self) -> int:
+        """Bytes per stored K/V element."""
+        return {"f32": 4, "bf16": 2, "fp8": 1}[self.dtype]
+
+    @property
+    def q_esz(self) -> int:
+        """Bytes per query element (bf16 queries go with fp8 caches)."""
         return 4 if self.dtype == "f32" else 2
 
     def resolved_scale(self) -> float:
@@ -117,6 +124,60 @@ GATHER_BF16 = DecodeWorkload(
     dtype="bf16", dist="normal", seed_index=6)
 GATHER_WIDTH = 2048
 GATHER_POOL = 64
+
+# fp8 KV storage (a "next" shape): the batched shape with K and V held as
+# one-byte E4M3 codes plus one fp32 scale per (sequence, KV head) each.
+BATCHED_FP8 = DecodeWorkload(
+    "batched_fp8_b16_hq32_hkv8_d128_t4096", batch=16, num_q_heads=32,
+    num_kv_heads=8, dk=128, dv=128, max_len=4096, dtype="fp8",
+    dist="normal", seed_index=7)
+
+E4M3_NAN = 0x7F
+
+
+def make_e4m3_codes(g: torch.Generator, shape, exp_lo: int = 4,
+                    exp_hi: int = 9) -> torch.Tensor:
+    """Random E4M3 bit patterns (uint8): uniform sign bit, exponent field
+    uniform over [exp_lo, exp_hi], uniform 3-bit mantissa.  Bit patterns
+    only (a log-uniform spread of magnitudes); exp_hi < 15 keeps the NaN
+    pattern out."""
+    sign = torch.randint(0, 2, shape, generator=g, dtype=torch.int32)
+    e = torch.randint(exp_lo, exp_hi + 1, shape, generator=g, dtype=torch.int32)
+    m = torch.randint(0, 8, shape, generator=g, dtype=torch.int32)
+    return ((sign << 7) | (e << 3) | m).to(torch.uint8)
+
+
+def make_fp8_inputs(w: DecodeWorkload, pad_code: int = E4M3_NAN,
+                    lens_override: Optional[list] = None) -> dict:
+    """Draw an fp8-cache workload on the CPU: q [B, Hq, dk] bf16 (normal),
+    lens [B] (as ``make_inputs``), K/V codes [B, max_len, Hkv, d] uint8
+    (``make_e4m3_codes`` over the live slots, ``pad_code`` — the NaN code by
+    default — past them) and fp32 scales k_scale [B, Hkv] ~ U(0.05, 0.5),
+    v_scale [B, Hkv] ~ U(0.1, 1.0).  Draw order: q, lens, K, V, scales."""
+    assert w.dtype == "fp8"
+    g = torch.Generator().manual_seed(w.seed)
+    B, Hq, Hkv, dk, dv, T = (w.batch, w.num_q_heads, w.num_kv_heads, w.dk,
+                             w.dv, w.max_len)
+    res = {"q": _normal(g, (B, Hq, dk)).to(torch.bfloat16)}
+    if lens_override is not None:
+        lens = torch.tensor(lens_override, dtype=torch.int32)
+        assert lens.numel() == B
+    elif w.ragged:
+        lens = torch.randint(1, T + 1, (B,), generator=g,
+                             dtype=torch.int64).to(torch.int32)
+    else:
+        lens = torch.full((B,), T, dtype=torch.int32)
+    res["lens"] = lens
+    k = torch.full((B, T, Hkv, dk), pad_code, dtype=torch.uint8)
+    v = torch.full((B, T, Hkv, dv), pad_code, dtype=torch.uint8)
+    for b in range(B):
+        n = int(min(max(int(lens[b]), 0), T))
+        k[b, :n] = make_e4m3_codes(g, (n, Hkv, dk))
+        v[b, :n] = make_e4m3_codes(g, (n, Hkv, dv))
+    res["k"], res["v"] = k, v
+    res["k_scale"] = _uniform(g, (B, Hkv), 0.05, 0.5)
+    res["v_scale"] = _uniform(g, (B, Hkv), 0.1, 1.0)
+    return res
 
 
 def make_index_rows(w: DecodeWorkload, lens, width: int, pool: int,
@@ -177,6 +238,7 @@ def make_inputs(w: DecodeWorkload, pad_value: float = float("nan"),
     ``wlens`` ``[B]``.  For the "spike" distribution it also returns
     ``spike_pos`` (the planted slot) and ``q_hat`` (fp32 unit queries).
     """
+    assert w.dtype != "fp8", "fp8 caches: make_fp8_inputs"
     g = torch.Generator().manual_seed(w.seed)
     B, Hq, Hkv, dk, dv, T = (w.batch, w.num_q_heads, w.num_kv_heads, w.dk,
                              w.dv, w.max_len)
@@ -244,10 +306,12 @@ def algorithmic_bytes(w: DecodeWorkload, lens) -> int:
     """HBM bytes one attend pass must move at minimum.
 
     K and V of every live token once per KV group, q once, the fp32 output
-    once.  Split-K partials are not counted (they are overhead).
+    once, and for fp8 caches the two fp32 scales of each (sequence, KV
+    head).  Split-K partials are not counted (they are overhead).
     """
     n_tot = sum(int(min(max(int(x), 0), w.max_len)) for x in lens)
     kv = n_tot * w.num_kv_heads * (w.dk + w.dv) * w.esz
-    q = w.batch * w.num_q_heads * w.dk * w.esz
+    q = w.batch * w.num_q_heads * w.dk * w.q_esz
     out = w.batch * w.num_q_heads * w.dv * 4
-    return kv + q + out
+    scales = w.batch * w.num_kv_heads * 2 * 4 if w.dtype == "fp8" else 0
+    return kv + q + out + scales

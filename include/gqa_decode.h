@@ -25,11 +25,12 @@
  *    before the checks pass.  GQA_ERR_DEVICE reports a failed launch.
  *  - All sizes are element counts unless named *_bytes.
  *  - q, cache->k, cache->v and the workspace must be 16-byte aligned.
- *  - Shapes with a kernel: bf16 caches with (dk, dv) in {(64, 64), (128, 128),
- *    (192, 128), (256, 256)} and 1..16 query heads per KV head (matrix-core
- *    path); fp32 caches with dk, dv multiples of 4 up to 256, 1..16 query
- *    heads per KV head and a 64-token tile that fits 64 KiB of LDS (vector
- *    ALU path).
+ *  - Shapes with a kernel: bf16 and fp8 caches with (dk, dv) in {(64, 64),
+ *    (128, 128), (192, 128), (256, 256)} and 1..16 query heads per KV head
+ *    (matrix-core path); fp32 caches with dk, dv multiples of 4 up to 256,
+ *    1..16 query heads per KV head and a 64-token tile that fits 64 KiB of
+ *    LDS (vector ALU path).
+ *  - fp8 caches (GQA_DTYPE_FP8_E4M3): queries and new K/V rows are bf16.
  *  - Errors: GQA_ERR_INVALID_ARGUMENT (a required pointer is NULL, a size is
  *    non-positive, a scale is not finite), GQA_ERR_SHAPE_MISMATCH (the query
  *    heads are not a multiple of the KV heads — usearch head_count "must
@@ -49,7 +50,7 @@
 extern "C" {
 #endif
 
-#define GQA_ABI_VERSION 2
+#define GQA_ABI_VERSION 3
 
 /* Only the entry points below are exported from the shared library. */
 #define GQA_API __attribute__((visibility("default")))
@@ -63,8 +64,26 @@ typedef enum gqa_status {
   GQA_ERR_DEVICE = 5
 } gqa_status;
 
-/* Storage type of q, K and V.  Outputs and carries are always fp32. */
-typedef enum gqa_dtype { GQA_DTYPE_F32 = 0, GQA_DTYPE_BF16 = 1 } gqa_dtype;
+/*
+ * Storage type of K and V (and of q and new rows, except for fp8 caches,
+ * whose q and new rows are bf16).  Outputs and carries are always fp32.
+ *
+ * GQA_DTYPE_FP8_E4M3: one byte per element, an OCP 8-bit floating-point
+ * E4M3 ("E4M3FN") code: sign, 4 exponent bits (bias 7), 3 mantissa bits,
+ * subnormals at exponent 0, NaN at S.1111.111, no infinities, largest
+ * finite value 448.  Code c of KV head g of sequence b stands for
+ * decode(c) * k_scale[b * num_kv_heads + g] (V: v_scale).  The pages leave
+ * the compressed storage format open (usearch "linear-algebra", section
+ * Attention: value rows are read in the index's own quantization; qualiaDB
+ * KvDictionary: a compressed-cache read path); this is the library's choice,
+ * and attention over such a cache is exact attention over the decoded
+ * values.
+ */
+typedef enum gqa_dtype {
+  GQA_DTYPE_F32 = 0,
+  GQA_DTYPE_BF16 = 1,
+  GQA_DTYPE_FP8_E4M3 = 2
+} gqa_dtype;
 
 /*
  * A batch of KV caches (needle-core struct KvCache: keys and values stored
@@ -74,6 +93,9 @@ typedef enum gqa_dtype { GQA_DTYPE_F32 = 0, GQA_DTYPE_BF16 = 1 } gqa_dtype;
  *   v: [batch][max_len][num_kv_heads][dv]   contiguous, `dtype` elements
  * The per-sequence fill level lives in a separate device int32 array `lens`.
  * Slots at or past lens[b] are never read by attend.
+ * k_scale, v_scale: fp32 [batch][num_kv_heads] device arrays (4-byte
+ * aligned, finite and positive) for fp8 caches, required there and ignored
+ * (may be NULL) for the other dtypes.
  */
 typedef struct gqa_cache {
   void *k;
@@ -84,6 +106,8 @@ typedef struct gqa_cache {
   int32_t dk;
   int32_t dv;
   int32_t dtype; /* gqa_dtype */
+  const float *k_scale;
+  const float *v_scale;
 } gqa_cache;
 
 /*
@@ -143,6 +167,10 @@ GQA_API const char *gqa_status_string(int32_t status);
  *     The page warns and returns without writing; here the drop is counted.
  * k_new [batch][num_kv_heads][dk], v_new [batch][num_kv_heads][dv], in the
  * cache dtype.  lens_out may alias lens_in.  dropped is a device int32.
+ * fp8 caches: k_new / v_new are bf16 (16-byte aligned) and are quantised on
+ * the way in: each value x of KV head g becomes the E4M3 code nearest to
+ * the fp32 quotient x / scale[b][g] (ties to the even mantissa; magnitudes
+ * above 448 saturate; NaN gives an unspecified code).
  */
 GQA_API gqa_status gqa_kv_append(const gqa_cache *cache, const void *k_new,
                          const void *v_new, const int32_t *lens_in,
@@ -158,7 +186,8 @@ GQA_API gqa_status gqa_kv_append(const gqa_cache *cache, const void *k_new,
  *   sink  NULL (no sinks) or a cache of S slots; ring: a cache of W slots;
  *   main_cache  NULL (evicted keys leave attention) or a cache of M slots.
  *   All three share batch, num_kv_heads, dk, dv and dtype; K/V rows of
- *   num_kv_heads * d elements must be a multiple of 4 bytes.
+ *   num_kv_heads * d elements must be a multiple of 4 bytes.  fp8 caches
+ *   are not supported here (GQA_ERR_UNSUPPORTED).
  *   count_in [batch]: tokens seen so far by each sequence.  With t =
  *   count_in[b]: t < S puts the token in sink slot t; otherwise it takes ring
  *   slot (t - S) % W, and if the ring was full (t - S >= W) the token it held
@@ -193,7 +222,7 @@ GQA_API size_t gqa_attend_workspace_bytes(const gqa_cache *cache, int32_t num_q_
 
 /*
  * attend_decode — one query token per sequence attends over its cache.
- *   q     [batch][num_q_heads][dk], cache dtype.
+ *   q     [batch][num_q_heads][dk], cache dtype (bf16 for fp8 caches).
  *   lens  [batch] device int32; keys attended are [0, clamp(lens[b], 0,
  *         max_len)).
  *   scale logit scale; 0 means 1/sqrt(dk) (usearch score_scale: a zero value
@@ -264,7 +293,9 @@ GQA_API gqa_status gqa_attend_combine(int32_t num_q_heads, const gqa_cache *cach
  *   lens_out must NOT alias lens_in (every work-group reads lens_in during the
  *   call); alternate two length arrays between steps.
  *   q, scale, bias, carry_in, carry_out, out: as in gqa_attend_decode (the
- *   bias row covers the new token's position too).
+ *   bias row covers the new token's position too).  fp8 caches: k_new and
+ *   v_new are bf16, quantised as in gqa_kv_append, and the step attends the
+ *   new token's decoded codes.
  *   workspace: at least gqa_decode_step_workspace_bytes() bytes, ZERO-FILLED
  *   before its first use.  Its tail holds per-(sequence, KV group) arrival
  *   counters that every completed call leaves at zero again; calls that
@@ -287,7 +318,8 @@ GQA_API gqa_status gqa_decode_step(const void *q, int32_t num_q_heads,
 /*
  * One cache of a multi-branch attend: its own K/V (and max_len), lengths and
  * optional bias (as in gqa_attend_decode).  Every branch of a call has the
- * same batch, num_kv_heads, dk, dv and dtype.
+ * same batch, num_kv_heads, dk, dv and dtype (fp8 branches each carry their
+ * own scales).
  */
 typedef struct gqa_branch {
   gqa_cache cache;

@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.gqa_abi_version() == 2
+    assert lib.gqa_abi_version() == 3
     names = [lib.gqa_status_string(i).decode() for i in range(7)]
     assert names == ["GQA_OK", "GQA_ERR_INVALID_ARGUMENT",
                      "GQA_ERR_SHAPE_MISMATCH", "GQA_ERR_UNSUPPORTED",
@@ -45,8 +45,9 @@ def test_version_and_status_strings(lib):
                      "GQA_ERR_UNKNOWN"]
 
 
-def _cache(B=16, T=4096, H=8, dk=128, dv=128, dtype=1, k=0x10000, v=0x20000):
-    return bd._Cache(k, v, B, T, H, dk, dv, dtype)
+def _cache(B=16, T=4096, H=8, dk=128, dv=128, dtype=1, k=0x10000, v=0x20000,
+           ks=None, vs=None):
+    return bd._Cache(k, v, B, T, H, dk, dv, dtype, ks, vs)
 
 
 def _plan(lib, c, hq, chunk=0):
@@ -302,3 +303,45 @@ def test_gathered_checks(lib):
     assert call(odd) == UNSUPPORTED
     assert call(huge) in (UNSUPPORTED, SHAPE)   # 8 q heads over 1 KV head ok
     assert call(c, n=nbytes - 1) == WORKSPACE
+
+
+def test_fp8_checks(lib):
+    """fp8 caches: the bf16 family's plan and shapes; scales required and
+    4-byte aligned; no kernel for other head widths; not accepted by
+    stream_append; unknown dtypes rejected."""
+    f8 = dict(dtype=bd.FP8_E4M3, ks=0xB0000, vs=0xB1000)
+    c8 = _cache(**f8)
+    _, p8 = _plan(lib, c8, 32)
+    st, pb = _plan(lib, _cache(), 32)
+    assert st == 0 and p8.chunk_tokens == pb.chunk_tokens and \
+        p8.num_chunks == pb.num_chunks and \
+        p8.workspace_bytes == pb.workspace_bytes, "same plan as bf16"
+    q, lens, ws, out = (ctypes.c_void_p(x) for x in
+                        (0x30000, 0x40000, 0x50000, 0x60000))
+
+    def attend(c, nbytes=p8.workspace_bytes):
+        return lib.gqa_attend_decode(q, 32, ctypes.byref(c), lens, 0.0, None,
+                                     0, None, None, out, ws, nbytes, None)
+
+    assert attend(c8, p8.workspace_bytes - 1) == WORKSPACE  # checks pass
+    for bad in (_cache(dtype=bd.FP8_E4M3, ks=None, vs=0xB1000),
+                _cache(dtype=bd.FP8_E4M3, ks=0xB0000, vs=None),
+                _cache(dtype=bd.FP8_E4M3, ks=0xB0002, vs=0xB1000)):
+        assert attend(bad) == INVALID
+    assert attend(_cache(dtype=3)) == INVALID
+    assert _plan(lib, _cache(dk=96, dv=96, **f8), 32)[0] == UNSUPPORTED
+    assert _plan(lib, _cache(dk=128, dv=64, **f8), 32)[0] == UNSUPPORTED
+    # kv_append: bf16 rows of an fp8 cache are read in 16-byte pieces
+    pp = ctypes.c_void_p(0x30000)
+    assert lib.gqa_kv_append(ctypes.byref(c8), ctypes.c_void_p(0x30008), pp,
+                             pp, pp, None, None) == INVALID
+    assert lib.gqa_kv_append(ctypes.byref(_cache(dtype=bd.FP8_E4M3)), pp, pp,
+                             pp, pp, None, None) == INVALID   # no scales
+    ring = _cache(B=4, T=128, H=2, **f8)
+    p = [ctypes.c_void_p(0x50000 + 0x1000 * i) for i in range(8)]
+    assert lib.gqa_stream_append(None, ctypes.byref(ring), None, p[0], p[1],
+                                 p[2], p[3], None, p[5], None, None,
+                                 None) == UNSUPPORTED
+    # a branch of another dtype
+    arr = (bd._Branch * 2)(_branch(c8), _branch(_cache()))
+    assert lib.gqa_attend_branches_workspace_bytes(arr, 2, 32) == 0
