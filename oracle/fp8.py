@@ -15,8 +15,9 @@ the design notes:
   largest finite magnitude is 448 (S.1111.110);
 * one fp32 scale per (sequence, KV head) for K and another for V: a stored
   code c stands for decode(c) * scale;
-* quantisation (the quantising append): the fp32 quotient x / scale,
-  correctly rounded, then the nearest E4M3 value, ties to the even mantissa,
+* quantisation (the quantising append): x times the fp32 reciprocal of the
+  scale (1 / scale correctly rounded to fp32, then the product correctly
+  rounded to fp32), then the nearest E4M3 value, ties to the even mantissa,
   magnitudes above 448 saturating to 448, the sign kept (also on zero);
 * attention over fp8 caches is exact attention over the decoded values.
 
@@ -79,10 +80,11 @@ def encode(x) -> np.ndarray:
 
 
 def quantize(x, scale) -> np.ndarray:
-    """Codes of x with a broadcast fp32 scale: the fp32 quotient x / scale,
-    then ``encode``."""
-    quo = np.asarray(x, dtype=np.float32) / np.asarray(scale, dtype=np.float32)
-    return encode(quo.astype(np.float32))
+    """Codes of x with a broadcast fp32 scale: x times the fp32 reciprocal of
+    the scale, rounded to fp32, then ``encode``."""
+    inv = (np.float32(1.0) / np.asarray(scale, dtype=np.float32)).astype(np.float32)
+    prod = np.asarray(x, dtype=np.float32) * inv
+    return encode(prod.astype(np.float32))
 
 
 def dequantize_cache(codes, scale) -> np.ndarray:

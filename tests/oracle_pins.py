@@ -647,9 +647,12 @@ def pin_fp8_encode(orc8):
 
 
 def pin_fp8_quantize(orc8):
-    """quantize(x, s) encodes x / s: with s a power of two every code
-    round-trips from its scaled value; 3 / 0.75 = 4 and 17 / 3 rounds to 5.5
-    (its nearest code)."""
+    """quantize(x, s) encodes x times the fp32 reciprocal of s: with s a power
+    of two every code round-trips from its scaled value; 3 * fl(1 / 0.75)
+    rounds to 4 and 17 * fl(1 / 3) to 5.5 (its nearest code).  Two inputs
+    whose exact quotient is an E4M3 midpoint (1.0625, 1.1875) but whose
+    product with the rounded reciprocal lands one fp32 step off it decide
+    the reading: both give code 0x39 (the quotient would give 0x38, 0x3A)."""
     finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)],
                       dtype=np.uint8)
     for s in (0.125, 1.0, 32.0):
@@ -658,6 +661,10 @@ def pin_fp8_quantize(orc8):
             f"scale {s}"
     assert orc8.quantize(np.float32(3.0), np.float32(0.75)) == 0x48
     assert orc8.quantize(np.float32(17.0), np.float32(3.0)) == 0x4B
+    assert orc8.quantize(np.float32(0.20383667945861816),
+                         np.float32(0.19184628129005432)) == 0x39
+    assert orc8.quantize(np.float32(0.5486176013946533),
+                         np.float32(0.4619937837123871)) == 0x39
 
 
 def _fp8_codes(rng, shape):

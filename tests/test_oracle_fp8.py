@@ -80,6 +80,11 @@ MUTANTS = {
                          lambda x, s: _real_encode(
                              np.asarray(x, np.float32) *
                              np.asarray(s, np.float32))),
+    "quotient_not_reciprocal": ("quantize",
+                                lambda x, s: _real_encode(
+                                    (np.asarray(x, np.float32) /
+                                     np.asarray(s, np.float32)).astype(
+                                         np.float32))),
     "scales_swapped": ("attend_fp8",
                        lambda q, kc, vc, ks, vs, *a, **kw:
                        _real_attend(q, kc, vc, vs, ks, *a, **kw)),
