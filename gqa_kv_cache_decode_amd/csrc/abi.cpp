@@ -96,13 +96,11 @@ bool uses_mfma(const gqa_cache *c) {
   return c->dtype != GQA_DTYPE_F32 || gqa::partition_f32_uses_mfma(c->dk, c->dv);
 }
 
-// Wavefronts per partition work-group (bf16 / fp8 kernel): four where a
-// wavefront's K/V tile is at most 32 x 256 bf16 values (dk + dv <= 256), two
-// for the wider heads, whose LDS tiles and registers would otherwise leave a
-// compute unit a single work-group.
+// Wavefronts per partition work-group of the bf16 / fp8 kernel (the rule
+// and its measurements are in launch.h).
 int partition_waves(const gqa_cache *c) {
   if (c->dtype == GQA_DTYPE_F32) return gqa::kPartitionWaves;
-  return gqa::partition_waves(c->dk, c->dv);
+  return gqa::partition_waves(c->dk, c->dv, c->dtype == GQA_DTYPE_FP8_E4M3);
 }
 
 // Chunk length: the largest power of two up to kMaxChunk that still gives

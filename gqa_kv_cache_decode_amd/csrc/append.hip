@@ -77,9 +77,9 @@ __global__ __launch_bounds__(kThreads) void append_kernel(AppendArgs a) {
   }
 }
 
-// kv_append into fp8 caches: the new bf16 rows are quantised (fp32 quotient
-// by the sequence's scale of that KV head, nearest E4M3 code, ties to even,
-// saturating at 448) into slot n, sixteen codes per thread and piece.
+// kv_append into fp8 caches: the new bf16 rows are quantised (times the fp32
+// reciprocal of the sequence's scale of that KV head, nearest E4M3 code, ties
+// to even, saturating at 448) into slot n, sixteen codes per thread and piece.
 __global__ __launch_bounds__(kThreads) void append_e4m3_kernel(AppendArgs a) {
   const int b = blockIdx.x;
   const int n = a.lens_in[b];
@@ -98,9 +98,11 @@ __global__ __launch_bounds__(kThreads) void append_e4m3_kernel(AppendArgs a) {
     const uint16_t *vn = static_cast<const uint16_t *>(a.v_new) +
                          (size_t)b * a.row_bytes_v;
     for (int e = threadIdx.x; e < a.row_bytes_k / 16; e += kThreads)
-      kd[e] = e4m3_quantize16(kn + e * 16, a.k_scale[sb + e * 16 / dk]);
+      kd[e] = e4m3_quantize16(kn + e * 16,
+                              e4m3_inv_scale(a.k_scale[sb + e * 16 / dk]));
     for (int e = threadIdx.x; e < a.row_bytes_v / 16; e += kThreads)
-      vd[e] = e4m3_quantize16(vn + e * 16, a.v_scale[sb + e * 16 / dv]);
+      vd[e] = e4m3_quantize16(vn + e * 16,
+                              e4m3_inv_scale(a.v_scale[sb + e * 16 / dv]));
   }
   __syncthreads();  // lens_in is read by every thread before lens_out is set
   if (threadIdx.x == 0) {

@@ -53,6 +53,54 @@ __device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
+// Maximum / sum over the four 16-lane rows of a wavefront (lanes i, i ^ 16,
+// i ^ 32, i ^ 48).  gfx950's row-swap permutes are VALU operations: the
+// 32-lane swap of x with itself yields the lower half of x in one result and
+// the upper half in the other (each repeated twice), the 16-lane swap the
+// even and the odd rows likewise, so two steps cover the four rows without a
+// round trip through LDS.
+__device__ __forceinline__ float rows_max(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x),
+                                                  __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x),
+                                                  __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float rows_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x),
+                                                  __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x),
+                                                  __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// LDS transpose load (ds_read_b64_tr_b16) from a generic pointer into LDS.
+// Each of the 16 lanes of a row fetches four consecutive 16-bit values at its
+// own address; lane j of the row then receives value j % 4 of the fetches of
+// lanes j / 4, j / 4 + 4, j / 4 + 8 and j / 4 + 12 (in that order).
+__device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4 *)(const_cast<uint16_t *>(p)));
+}
+
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+
+// LDS transpose load of bytes (ds_read_b64_tr_b8).  Each of the 16 lanes of a
+// row fetches eight consecutive bytes at its own address; lane j of the row
+// then receives byte j % 8 of the fetches of lanes j / 8, j / 8 + 2, ...,
+// j / 8 + 14 (in that order, lowest byte first).
+__device__ __forceinline__ i32x2 lds_read_tr8(const unsigned char *p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+      (lds_i32x2 *)(const_cast<unsigned char *>(p)));
+}
+
 // Butterfly reductions across the 64 lanes of a wavefront.
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll

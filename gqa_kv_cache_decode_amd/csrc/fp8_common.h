@@ -4,9 +4,9 @@
 // A cache of codes carries one fp32 scale per (sequence, KV head) for K and
 // one for V; code c stands for decode(c) * scale.  Every E4M3 value has at
 // most four significant bits and an exponent within bf16's range, so it is
-// exact in bf16: the kernels decode codes to bf16 and run the bf16 loop
-// unchanged, folding the K scale into the logit scale and the V scale into
-// the weighted value sum.
+// exact in bf16: the kernels stage codes in LDS and decode each MFMA operand
+// to bf16 as they read it, folding the K scale into the logit scale and the
+// V scale into the weighted value sum.
 #pragma once
 
 #include "device_common.h"
@@ -31,14 +31,11 @@ __device__ __forceinline__ uint2 e4m3x4_to_bf16(uint32_t w) {
   return r;
 }
 
-// Sixteen codes as sixteen bf16 values, in order: p0 holds elements 0..7,
-// p1 elements 8..15.
-__device__ __forceinline__ void e4m3x16_to_bf16(u32x4 c, u32x4 &p0,
-                                                u32x4 &p1) {
-  const uint2 a = e4m3x4_to_bf16(c.x), b = e4m3x4_to_bf16(c.y);
-  const uint2 d = e4m3x4_to_bf16(c.z), e = e4m3x4_to_bf16(c.w);
-  p0 = u32x4{a.x, a.y, b.x, b.y};
-  p1 = u32x4{d.x, d.y, e.x, e.y};
+// Eight codes (w0 holds codes 0..3, w1 codes 4..7, lowest byte first) as an
+// MFMA operand of eight bf16 values, in order.
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  const uint2 a = e4m3x4_to_bf16(w0), b = e4m3x4_to_bf16(w1);
+  return __builtin_bit_cast(bf16x8, u32x4{a.x, a.y, b.x, b.y});
 }
 
 // The code of x: nearest E4M3 value, ties to the even mantissa, magnitudes
@@ -58,14 +55,20 @@ __device__ __forceinline__ uint32_t e4m3_pack4(float x0, float x1, float x2,
   return (uint32_t)w;
 }
 
-// Codes of eight bf16 values (one 16-byte piece) divided by `scale`: the
-// quotient is the correctly rounded fp32 division.
-__device__ __forceinline__ uint2 e4m3_quantize8(u32x4 x, float scale) {
+// The factor a value is multiplied by before encoding: the correctly
+// rounded fp32 reciprocal of its scale.
+__device__ __forceinline__ float e4m3_inv_scale(float scale) {
+  return 1.0f / scale;
+}
+
+// Codes of eight bf16 values (one 16-byte piece) times `inv_scale`, each
+// product rounded to fp32.
+__device__ __forceinline__ uint2 e4m3_quantize8(u32x4 x, float inv_scale) {
   float f[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    f[2 * i] = __uint_as_float(x[i] << 16) / scale;
-    f[2 * i + 1] = __uint_as_float(x[i] & 0xFFFF0000u) / scale;
+    f[2 * i] = __uint_as_float(x[i] << 16) * inv_scale;
+    f[2 * i + 1] = __uint_as_float(x[i] & 0xFFFF0000u) * inv_scale;
   }
   uint2 r;
   r.x = e4m3_pack4(f[0], f[1], f[2], f[3]);
@@ -73,26 +76,28 @@ __device__ __forceinline__ uint2 e4m3_quantize8(u32x4 x, float scale) {
   return r;
 }
 
-// Codes of sixteen bf16 values at `src` (two 16-byte pieces).
+// Codes of sixteen bf16 values at `src` (two 16-byte pieces), times
+// `inv_scale`.
 __device__ __forceinline__ u32x4 e4m3_quantize16(const uint16_t *src,
-                                                 float scale) {
-  const uint2 a = e4m3_quantize8(stream_load16(src), scale);
-  const uint2 b = e4m3_quantize8(stream_load16(src + 8), scale);
+                                                 float inv_scale) {
+  const uint2 a = e4m3_quantize8(stream_load16(src), inv_scale);
+  const uint2 b = e4m3_quantize8(stream_load16(src + 8), inv_scale);
   return u32x4{a.x, a.y, b.x, b.y};
 }
 
 // Stores one KV group's rows of the new token (bf16 [d] each) into the cache
-// slot as codes, 16 codes per 16-byte piece, spread over the work-group's
+// slot as codes (kinv, vinv: e4m3_inv_scale of the group's scales), 16 codes
+// per 16-byte piece, spread over the work-group's
 // threads.  As for bf16 rows, nothing in the same launch reads the slot, so
 // the stores are not waited for.
 __device__ __forceinline__ void store_group_row_e4m3(
-    const uint16_t *kn, u32x4 *kd, int kpieces, float kscale,
-    const uint16_t *vn, u32x4 *vd, int vpieces, float vscale) {
+    const uint16_t *kn, u32x4 *kd, int kpieces, float kinv,
+    const uint16_t *vn, u32x4 *vd, int vpieces, float vinv) {
   for (int e = threadIdx.x; e < kpieces + vpieces; e += blockDim.x) {
     if (e < kpieces)
-      kd[e] = e4m3_quantize16(kn + e * 16, kscale);
+      kd[e] = e4m3_quantize16(kn + e * 16, kinv);
     else
-      vd[e - kpieces] = e4m3_quantize16(vn + (e - kpieces) * 16, vscale);
+      vd[e - kpieces] = e4m3_quantize16(vn + (e - kpieces) * 16, vinv);
   }
 }
 

@@ -10,11 +10,16 @@ namespace gqa {
 // Wavefronts per work-group of the fp32 matrix-core partition kernel.
 constexpr int kPartitionWaves = 2;
 
-// Work-group width of the bf16 partition kernel, measured on MI355X over the
-// workload shapes: four wavefronts where a 32-token K/V tile is small
-// (dk + dv <= 256), two for wider heads (their LDS tiles and registers would
-// leave one four-wavefront work-group per compute unit).
-constexpr int partition_waves(int dk, int dv) { return dk + dv <= 256 ? 4 : 2; }
+// Work-group width of the bf16 / fp8 partition kernel, measured on MI355X
+// over the workload shapes.  bf16: four wavefronts where a 32-token K/V tile
+// is small (dk + dv <= 256), two for wider heads (their LDS tiles and
+// registers would leave one four-wavefront work-group per compute unit).
+// fp8 (codes staged in LDS, half the bytes): eight for the narrowest heads
+// (dk + dv <= 128), whose 4 KB tiles need more wavefronts in flight, four
+// otherwise.
+constexpr int partition_waves(int dk, int dv, bool fp8 = false) {
+  return fp8 ? (dk + dv <= 128 ? 8 : 4) : (dk + dv <= 256 ? 4 : 2);
+}
 
 // A further cache attended by the same launch (multi-branch attention: the
 // branches' partials share one partial row per query row and one combine).

@@ -37,11 +37,12 @@
 // the append never stalls the stream.  The group's partials are folded by the
 // last work-group to finish when `fuse` is set.
 //
-// With fp8 storage (FP8) a 16-byte load brings sixteen codes, which are
-// decoded to bf16 on their way into LDS (exact: every E4M3 value is a bf16
-// value), so the loop above runs unchanged on half the bytes.  The group's K
-// scale multiplies the logit scale and its V scale the weighted value sum;
-// a decode step quantises the new token's rows with the same scales.
+// With fp8 storage (FP8) a 16-byte load brings sixteen codes, which go to
+// LDS as they are (half the LDS bytes); each MFMA operand is decoded to bf16
+// as it is read (exact: every E4M3 value is a bf16 value), the V operand
+// with one byte-transpose load per block.  The group's K scale multiplies
+// the logit scale and its V scale the weighted value sum; a decode step
+// quantises the new token's rows with the same scales.
 #pragma once
 
 #include "device_common.h"
@@ -65,9 +66,13 @@ struct Mfma16Geom {
   static constexpr int vLoads = kTileTokens * vPieces / 64;
   static_assert(kTileTokens * kPieces % 64 == 0, "K tile split");
   static_assert(kTileTokens * vPieces % 64 == 0, "V tile split");
-  static constexpr int kStride = DK + 8;  // LDS row stride in bf16 (+16 B pad)
+  // LDS rows: bf16 values for bf16 storage (stride in elements, +16 B pad);
+  // the codes themselves for fp8 storage (+16 B pad), decoded when read.
+  static constexpr int kStride = DK + 8;
   static constexpr int vStride = DV + 8;
-  static constexpr int waveLdsElems = kTileTokens * (kStride + vStride);
+  static constexpr int kRowBytes = FP8 ? DK + 16 : kStride * 2;
+  static constexpr int vRowBytes = FP8 ? DV + 16 : vStride * 2;
+  static constexpr int waveLdsBytes = kTileTokens * (kRowBytes + vRowBytes);
 };
 
 template <int DK, int DV, int NW, bool STEP, bool BIAS, bool GATHER, bool FP8>
@@ -77,7 +82,7 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
   constexpr int ES = G::kEsize;
   constexpr int PP = G::kPerPiece;
   constexpr int kMergeFloats = NW * 16 * (DV + 2);
-  constexpr int kTileBytes = NW * G::waveLdsElems * 2;
+  constexpr int kTileBytes = NW * G::waveLdsBytes;
   constexpr int kLdsBytes =
       kTileBytes > kMergeFloats * 4 ? kTileBytes : kMergeFloats * 4;
   __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
@@ -139,8 +144,18 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
       qf[s] = *reinterpret_cast<const bf16x8 *>(qrow + s * 32 + kg * 8);
   }
 
-  uint16_t *Ks = reinterpret_cast<uint16_t *>(lds) + w * G::waveLdsElems;
-  uint16_t *Vs = Ks + kTileTokens * G::kStride;
+  unsigned char *Ks8 = lds + w * G::waveLdsBytes;  // this wavefront's tiles
+  unsigned char *Vs8 = Ks8 + kTileTokens * G::kRowBytes;
+  uint16_t *Ks = reinterpret_cast<uint16_t *>(Ks8);  // bf16 storage
+  uint16_t *Vs = reinterpret_cast<uint16_t *>(Vs8);
+  // this lane's fetch address for the transpose loads of V (see below): bf16
+  // lane u = lane % 16 of group kg fetches V[kg*4 + u/4][4(u%4) ..+4]; fp8
+  // lane u fetches codes V[token(kg, u/2)][8(u%2) ..+8]
+  const uint16_t *vsrc = Vs + (kg * 4 + (lane & 15) / 4) * G::vStride + 4 * (lane & 3);
+  const int vk8 = (lane & 15) >> 1;
+  const unsigned char *vsrc8 =
+      Vs8 + (vk8 < 4 ? kg * 4 + vk8 : 16 + kg * 4 + (vk8 - 4)) * G::vRowBytes +
+      8 * (lane & 1);
 
   const size_t kTok = (size_t)Hkv * DK * ES;  // bytes between tokens
   const size_t vTok = (size_t)Hkv * DV * ES;
@@ -152,6 +167,9 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
   const float kscale = FP8 ? a.k_scale[(size_t)b * Hkv + g] : 1.0f;
   const float vscale = FP8 ? a.v_scale[(size_t)b * Hkv + g] : 1.0f;
   const float scale_log2 = a.scale_log2 * kscale;
+  // fp8 decode step: the new rows are multiplied by these before encoding
+  const float kinv = FP8 && STEP ? e4m3_inv_scale(kscale) : 1.0f;
+  const float vinv = FP8 && STEP ? e4m3_inv_scale(vscale) : 1.0f;
 
   // STEP: the work-group whose chunk holds the new slot stores the token's
   // rows of this group into the cache.  The stores are not waited for: later
@@ -165,9 +183,9 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
     vnew = static_cast<const uint16_t *>(sp.v_new) + ((size_t)b * Hkv + g) * DV;
     if (FP8)
       store_group_row_e4m3(knew, reinterpret_cast<u32x4 *>(Kg + (size_t)sl.n_old * kTok),
-                           DK / 16, kscale, vnew,
+                           DK / 16, kinv, vnew,
                            reinterpret_cast<u32x4 *>(Vg + (size_t)sl.n_old * vTok),
-                           DV / 16, vscale);
+                           DV / 16, vinv);
     else
       store_group_row(reinterpret_cast<const u32x4 *>(knew),
                       reinterpret_cast<u32x4 *>(Kg + (size_t)sl.n_old * kTok), DK / 8,
@@ -223,7 +241,7 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
         const int t = min(tile * kTileTokens + idx / G::kPieces, last);
         const int pc = (idx % G::kPieces) * PP;  // first element of the piece
         if (FP8)
-          kr[i] = t == rel ? e4m3_quantize16(knew + pc, kscale)
+          kr[i] = t == rel ? e4m3_quantize16(knew + pc, kinv)
                            : stream_load16(kb + (size_t)t * kTok + pc);
         else
           kr[i] = stream_load16(t == rel ? knew + pc
@@ -236,7 +254,7 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
         const int t = min(tile * kTileTokens + idx / G::vPieces, last);
         const int pc = (idx % G::vPieces) * PP;
         if (FP8)
-          vr[i] = t == rel ? e4m3_quantize16(vnew + pc, vscale)
+          vr[i] = t == rel ? e4m3_quantize16(vnew + pc, vinv)
                            : stream_load16(vb + (size_t)t * vTok + pc);
         else
           vr[i] = stream_load16(t == rel ? vnew + pc
@@ -288,22 +306,14 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
 #pragma unroll
     for (int i = 0; i < G::kLoads; ++i) {
       const int idx = i * 64 + lane;
-      u32x4 *dst = reinterpret_cast<u32x4 *>(Ks + (idx / G::kPieces) * G::kStride +
-                                             (idx % G::kPieces) * PP);
-      if (FP8)
-        e4m3x16_to_bf16(kr[i], dst[0], dst[1]);
-      else
-        dst[0] = kr[i];
+      *reinterpret_cast<u32x4 *>(Ks8 + (idx / G::kPieces) * G::kRowBytes +
+                                 (idx % G::kPieces) * 16) = kr[i];
     }
 #pragma unroll
     for (int i = 0; i < G::vLoads; ++i) {
       const int idx = i * 64 + lane;
-      u32x4 *dst = reinterpret_cast<u32x4 *>(Vs + (idx / G::vPieces) * G::vStride +
-                                             (idx % G::vPieces) * PP);
-      if (FP8)
-        e4m3x16_to_bf16(vr[i], dst[0], dst[1]);
-      else
-        dst[0] = vr[i];
+      *reinterpret_cast<u32x4 *>(Vs8 + (idx / G::vPieces) * G::vRowBytes +
+                                 (idx % G::vPieces) * 16) = vr[i];
     }
     const f32x4 bcur[2] = {br[0], br[1]};
     if (tile + NW < ntiles) issue(tile + NW);  // next tile in flight meanwhile
@@ -316,8 +326,15 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
       sacc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < DK / 32; ++s) {
-        const bf16x8 av = *reinterpret_cast<const bf16x8 *>(
-            Ks + (rb * 16 + hl) * G::kStride + s * 32 + kg * 8);
+        bf16x8 av;
+        if constexpr (FP8) {  // eight codes of token rb*16 + hl, decoded
+          const uint2 c = *reinterpret_cast<const uint2 *>(
+              Ks8 + (rb * 16 + hl) * G::kRowBytes + s * 32 + kg * 8);
+          av = e4m3x8_to_bf16x8(c.x, c.y);
+        } else {
+          av = *reinterpret_cast<const bf16x8 *>(
+              Ks + (rb * 16 + hl) * G::kStride + s * 32 + kg * 8);
+        }
         sacc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qf[s], sacc[rb],
                                                            0, 0, 0);
       }
@@ -337,8 +354,7 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
         mt = fmaxf(mt, v);
       }
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    mt = rows_max(mt);
     const float m_new = fmaxf(m_run, mt);
     const float ref = exp_ref(m_new);  // -inf only while every key is removed
     const float alpha = fast_exp2(m_run - ref);
@@ -356,16 +372,23 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
     }
     l_run = l_run * alpha + psum;
 
-    // acc^T += V^T P^T; the A operand gathers V[token(kg, j)][blk*16 + hl]
+    // acc^T += V^T P^T; the A operand holds V[token(kg, j)][blk*16 + hl]
     // with token(kg, j) = j < 4 ? kg*4 + j : 16 + kg*4 + (j - 4), the token
-    // order of this lane's P values.
+    // order of this lane's P values.  Two transpose loads bring it: lane
+    // u = lane % 16 of group kg fetches V[kg*4 + u/4][blk*16 + 4(u%4) ..+4]
+    // (and the same 16 tokens further), so that lane hl receives column
+    // blk*16 + hl of tokens kg*4 + 0..3.
 #pragma unroll
     for (int blk = 0; blk < DV / 16; ++blk) {
       bf16x8 av;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int tok = (j < 4) ? (kg * 4 + j) : (16 + kg * 4 + (j - 4));
-        av[j] = __builtin_bit_cast(__bf16, Vs[tok * G::vStride + blk * 16 + hl]);
+      if constexpr (FP8) {  // one byte-transpose load: all eight tokens
+        const i32x2 c = lds_read_tr8(vsrc8 + blk * 16);
+        av = e4m3x8_to_bf16x8(c.x, c.y);
+      } else {
+        const i16x4 lo = lds_read_tr16(vsrc + blk * 16);
+        const i16x4 hi = lds_read_tr16(vsrc + 16 * G::vStride + blk * 16);
+        av = __builtin_bit_cast(
+            bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
       o[blk] *= alpha;
       o[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, phi, o[blk], 0, 0, 0);
@@ -379,8 +402,7 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
   }
 
   // Partition of head hl over the whole wavefront.
-  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
+  const float l_tot = rows_sum(l_run);
 
   // Merge the wavefronts' states through LDS and write one partial per head.
   __syncthreads();
@@ -478,7 +500,7 @@ hipError_t launch_one(const PartitionArgs &a, const StepParams &sp,
 template <int DK, int DV, bool STEP, bool FP8>
 hipError_t launch_shape(const PartitionArgs &a, const StepParams &sp,
                         hipStream_t s) {
-  return launch_one<DK, DV, partition_waves(DK, DV), STEP, FP8>(a, sp, s);
+  return launch_one<DK, DV, partition_waves(DK, DV, FP8), STEP, FP8>(a, sp, s);
 }
 
 // Launches the kernel of the plan's head widths; fp8 storage must match

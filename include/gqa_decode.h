@@ -169,8 +169,9 @@ GQA_API const char *gqa_status_string(int32_t status);
  * cache dtype.  lens_out may alias lens_in.  dropped is a device int32.
  * fp8 caches: k_new / v_new are bf16 (16-byte aligned) and are quantised on
  * the way in: each value x of KV head g becomes the E4M3 code nearest to
- * the fp32 quotient x / scale[b][g] (ties to the even mantissa; magnitudes
- * above 448 saturate; NaN gives an unspecified code).
+ * x * r rounded to fp32, where r is 1 / scale[b][g] rounded to fp32 (ties to
+ * the even mantissa; magnitudes above 448 saturate; NaN gives an unspecified
+ * code).
  */
 GQA_API gqa_status gqa_kv_append(const gqa_cache *cache, const void *k_new,
                          const void *v_new, const int32_t *lens_in,

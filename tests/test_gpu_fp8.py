@@ -121,7 +121,7 @@ def test_e4m3_decode_every_code():
 def _append_rows(B, Hkv, d, scales, seed):
     """bf16 rows exercising the quantiser: normal values at the scale's
     range, a tenth far past 448 * scale, a tenth tiny, exact midpoints
-    between neighbouring codes (exact quotients where the scale is a power
+    between neighbouring codes (exact products where the scale is a power
     of two), +-0."""
     gen = torch.Generator().manual_seed(seed)
     s = scales[:, :, None].float()
@@ -171,6 +171,43 @@ def test_kv_append_quantises_bit_exact(dk, dv):
     assert bad.size == 0, f"K codes differ at {bad[:5].tolist()}: " \
         f"{gk[tuple(bad[0])]:#04x} vs {k2[tuple(bad[0])]:#04x}"
     assert np.array_equal(gv, v2), "V codes"
+
+
+# bf16 values x and scales s for which x * fl(1 / s) and x / s round to
+# different E4M3 codes: the append must follow the reciprocal reading.
+DECIDING = [(5.09375, 0.7546296715736389), (0.95703125, 0.8059210777282715),
+            (7.0, 0.8235293626785278), (11.9375, 0.9549999237060547),
+            (0.00775146484375, 0.4177631735801697),
+            (0.73046875, 0.6151316165924072)]
+
+
+def test_kv_append_reciprocal_reading():
+    """Values whose code depends on quantising with the rounded reciprocal
+    of the scale rather than the quotient: bit for bit as the oracle."""
+    g = _gqa()
+    B, T, Hkv, d = len(DECIDING), 2, 1, 64
+    xs = np.array([x for x, _ in DECIDING], dtype=np.float32)
+    ss = np.array([s for _, s in DECIDING], dtype=np.float32)
+    quo = of8.encode((xs / ss).astype(np.float32))
+    prod = of8.encode((xs * (np.float32(1) / ss).astype(np.float32)).astype(
+        np.float32))
+    assert np.all(quo != prod), "each case decides between the readings"
+    kn = torch.from_numpy(xs)[:, None, None].expand(B, Hkv, d).to(
+        torch.bfloat16).contiguous()
+    assert np.array_equal(kn[:, 0, 0].float().numpy(), xs), "bf16-exact"
+    sc = torch.from_numpy(ss)[:, None].contiguous()
+    k = torch.zeros(B, T, Hkv, d, dtype=torch.uint8)
+    kd = g.Fp8Cache(k.cuda(), sc.cuda())
+    vd = g.Fp8Cache(k.clone().cuda(), sc.cuda())
+    lens = torch.zeros(B, dtype=torch.int32).cuda()
+    say("[fp8] kv_append reciprocal reading")
+    g.kv_append(kd, vd, kn.cuda(), kn.cuda(), lens, torch.empty_like(lens))
+    torch.cuda.synchronize()
+    want, _, _, _ = of8.kv_append_fp8(k.numpy(), k.numpy(), kn.float().numpy(),
+                                      kn.float().numpy(), sc.numpy(),
+                                      sc.numpy(), np.zeros(B, np.int32))
+    assert np.array_equal(kd.codes.cpu().numpy(), want)
+    assert np.all(kd.codes.cpu().numpy()[:, 0, 0, 0] == prod)
 
 
 CASES = {
