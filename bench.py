@@ -432,12 +432,7 @@ def main():
         log(f"[bench] pure-read stream ceiling: {ceiling:.1f} GB/s")
 
     traffic = measured_traffic(profile_name(args), w.dtype)
-    mfma16 = w.dtype in ("bf16", "fp8")
-    waves = (4 if w.dk + w.dv <= 256 else 2) if mfma16 else 2
-    tmpl = (f"{w.dk}, {w.dv}, {waves}, false, "
-            f"{'true' if args.bias else 'false'}, {'true' if gather else 'false'}")
-    kernel = (f"partition_bf16_kernel<{tmpl}, {'true' if fp8 else 'false'}>"
-              if mfma16 else f"partition_f32_mfma_kernel<{tmpl}>")
+    kernel = kernel_name(w, args.bias, gather)
     if gather:
         kernel = f"attend_gathered call: select_kernel + {kernel} + combine"
     roofline = {"bound": "hbm", "achieved": round(achieved, 1),
@@ -481,6 +476,22 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def kernel_name(w, bias, gather):
+    """The dominant partition kernel's name as the profiler prints it
+    (template arguments: head widths, wavefronts, decode step, bias,
+    gathered, and fp8 for the bf16 / fp8 family)."""
+    tf = lambda b: "true" if b else "false"
+    flags = f"false, {tf(bias)}, {tf(gather)}"
+    if w.dtype == "f32":
+        return f"partition_f32_mfma_kernel<{w.dk}, {w.dv}, 2, {flags}>"
+    if w.dtype == "fp8":
+        waves = 8 if w.dk + w.dv <= 128 else 4
+    else:
+        waves = 4 if w.dk + w.dv <= 256 else 2
+    return (f"partition_bf16_kernel<{w.dk}, {w.dv}, {waves}, {flags}, "
+            f"{tf(w.dtype == 'fp8')}>")
 
 
 _BENCH_LIB = None

@@ -194,8 +194,12 @@ def test_branches_layout_and_checks(lib):
     win = _cache(B=1, T=128, H=4, k=0x30000, v=0x38000)
     arr = (bd._Branch * 2)(_branch(main), _branch(win, lens=0x48000))
     nbytes = lib.gqa_attend_branches_workspace_bytes(arr, 2, 32)
-    # main: 64 chunks of 4096; window: one chunk; rows = 32
-    ml = 32 * (64 + 1) * 4
+    # each branch chunked by its own plan; one partial row of 32 query rows
+    # over both branches' chunks
+    _, pm = _plan(lib, main, 32)
+    _, pw = _plan(lib, win, 32)
+    assert pm.num_chunks > 1 and pw.num_chunks == 1
+    ml = 32 * (pm.num_chunks + pw.num_chunks) * 4
     al = lambda x: (x + 255) // 256 * 256
     assert nbytes == 2 * al(ml) + al(ml * 128)
     q, out, ws = (ctypes.c_void_p(x) for x in (0x50000, 0x60000, 0x70000))
