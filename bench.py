@@ -489,7 +489,7 @@ def kernel_name(w, bias, gather):
     if w.dtype == "fp8":
         waves = 8 if w.dk + w.dv <= 128 else 4
     else:
-        waves = 4 if w.dk + w.dv <= 256 else 2
+        waves = 2
     return (f"partition_bf16_kernel<{w.dk}, {w.dv}, {waves}, {flags}, "
             f"{tf(w.dtype == 'fp8')}>")
 

@@ -11,14 +11,14 @@ namespace gqa {
 constexpr int kPartitionWaves = 2;
 
 // Work-group width of the bf16 / fp8 partition kernel, measured on MI355X
-// over the workload shapes.  bf16: four wavefronts where a 32-token K/V tile
-// is small (dk + dv <= 256), two for wider heads (their LDS tiles and
-// registers would leave one four-wavefront work-group per compute unit).
-// fp8 (codes staged in LDS, half the bytes): eight for the narrowest heads
-// (dk + dv <= 128), whose 4 KB tiles need more wavefronts in flight, four
-// otherwise.
+// over the workload shapes.  With one work-group per CU, each wavefront keeps
+// one tile of loads in flight, and the HBM read stream of this access pattern
+// ran fastest at about 32 KB in flight per CU (a load-only probe of the
+// batched shape: 38 us at 32 KB, 42 us at 64 KB for the same bytes): bf16
+// takes two wavefronts (16 KB tiles at d = 128), fp8 four (8 KB tiles), or
+// eight for the narrowest fp8 heads (dk + dv <= 128, 4 KB tiles).
 constexpr int partition_waves(int dk, int dv, bool fp8 = false) {
-  return fp8 ? (dk + dv <= 128 ? 8 : 4) : (dk + dv <= 256 ? 4 : 2);
+  return fp8 ? (dk + dv <= 128 ? 8 : 4) : 2;
 }
 
 // A further cache attended by the same launch (multi-branch attention: the
