@@ -32,10 +32,11 @@
 // In STEP mode the same launch is a whole decode step (needle-core
 // self_attn_incremental: push_kv, then attend over the cache including the new
 // token).  The work-group whose chunk holds the new slot stores the token's
-// rows into the cache without waiting for the stores, and the one tile that
-// holds the slot reads those rows from k_new/v_new instead of the cache, so
-// the append never stalls the stream.  The group's partials are folded by the
-// last work-group to finish when `fuse` is set.
+// rows into the cache without waiting for the stores; its tile loop reads only
+// the cache tokens before the slot, and its first wavefront folds the new
+// token in from k_new/v_new afterwards, so the append never stalls the stream
+// and the tile loop carries no special case.  The group's partials are folded
+// by the last work-group to finish when `fuse` is set.
 //
 // With fp8 storage (FP8) a 16-byte load brings sixteen codes, which go to
 // LDS as they are (half the LDS bytes); each MFMA operand is decoded to bf16
@@ -120,7 +121,11 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
   // sequence when final results are written in this launch: it still writes
   // the group's outputs.
   if (t0 >= n && !(c == 0 && (sp.direct || (STEP && sp.fuse)))) return;
-  const int t1 = min(t0 + a.chunk_tokens, n);
+  // Decode step: the work-group whose chunk holds the new slot (always the
+  // chunk's last live token) reads only the cache tokens before it in its
+  // tile loop and folds the new token in from k_new / v_new afterwards.
+  const bool has_new = stepping && sl.fresh && sl.n_old / a.chunk_tokens == c;
+  const int t1 = has_new ? sl.n_old : min(t0 + a.chunk_tokens, n);  // tiles: [t0, t1)
   const int ntiles = t1 > t0 ? (t1 - t0 + kTileTokens - 1) / kTileTokens : 0;
 
   const int lane = threadIdx.x & 63;
@@ -173,12 +178,9 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
 
   // STEP: the work-group whose chunk holds the new slot stores the token's
   // rows of this group into the cache.  The stores are not waited for: later
-  // calls read the slot, while this call reads the rows from k_new/v_new (the
-  // slot is the last live token of the chunk, relative position `rel`).
+  // calls read the slot, while this call takes the rows from k_new/v_new.
   const uint16_t *knew = nullptr, *vnew = nullptr;
-  int rel = -1;
-  if (stepping && sl.fresh && sl.n_old / a.chunk_tokens == c) {
-    rel = sl.n_old - t0;
+  if (has_new) {
     knew = static_cast<const uint16_t *>(sp.k_new) + ((size_t)b * Hkv + g) * DK;
     vnew = static_cast<const uint16_t *>(sp.v_new) + ((size_t)b * Hkv + g) * DV;
     if (FP8)
@@ -192,7 +194,6 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
                       reinterpret_cast<const u32x4 *>(vnew),
                       reinterpret_cast<u32x4 *>(Vg + (size_t)sl.n_old * vTok), DV / 8);
   }
-  const int rel_tile = rel >= 0 ? rel / kTileTokens : -1;
 
   // K/V are read exactly once per call, so the loads are nontemporal: they
   // stream through without displacing cached lines.  Tokens of a tile past
@@ -229,39 +230,6 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
         br[rb] = load4f(bview, (uint32_t)((tile * kTileTokens + rb * 16 + kg * 4) * 4));
-    }
-    if (STEP && tile == rel_tile) {
-      // the tile holding the new slot: that token (and the clamped tokens
-      // after it) come from k_new/v_new, the others from the cache
-      // (fp8: the new rows are quantised here exactly as they are stored)
-      const unsigned char *kb = Kg + (size_t)t0 * kTok, *vb = Vg + (size_t)t0 * vTok;
-#pragma unroll
-      for (int i = 0; i < G::kLoads; ++i) {
-        const int idx = i * 64 + lane;
-        const int t = min(tile * kTileTokens + idx / G::kPieces, last);
-        const int pc = (idx % G::kPieces) * PP;  // first element of the piece
-        if (FP8)
-          kr[i] = t == rel ? e4m3_quantize16(knew + pc, kinv)
-                           : stream_load16(kb + (size_t)t * kTok + pc);
-        else
-          kr[i] = stream_load16(t == rel ? knew + pc
-                                         : reinterpret_cast<const uint16_t *>(kb) +
-                                               (size_t)t * (kTok / 2) + pc);
-      }
-#pragma unroll
-      for (int i = 0; i < G::vLoads; ++i) {
-        const int idx = i * 64 + lane;
-        const int t = min(tile * kTileTokens + idx / G::vPieces, last);
-        const int pc = (idx % G::vPieces) * PP;
-        if (FP8)
-          vr[i] = t == rel ? e4m3_quantize16(vnew + pc, vinv)
-                           : stream_load16(vb + (size_t)t * vTok + pc);
-        else
-          vr[i] = stream_load16(t == rel ? vnew + pc
-                                         : reinterpret_cast<const uint16_t *>(vb) +
-                                               (size_t)t * (vTok / 2) + pc);
-      }
-      return;
     }
     if (GATHER) {
 #pragma unroll
@@ -396,6 +364,49 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
     }
   }
 
+  // The new token of a decode step, folded into wavefront 0's state: its
+  // logit from q and k_new (for fp8 caches, the decoded codes it is stored
+  // as), then the usual online update with its value row.
+  if (STEP && has_new && w == 0) {
+    float dot = 0.0f;
+#pragma unroll
+    for (int s = 0; s < DK / 32; ++s) {
+      const u32x4 raw = stream_load16(knew + s * 32 + kg * 8);
+      bf16x8 kv;
+      if constexpr (FP8) {
+        const uint2 code = e4m3_quantize8(raw, kinv);
+        kv = e4m3x8_to_bf16x8(code.x, code.y);
+      } else {
+        kv = __builtin_bit_cast(bf16x8, raw);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) dot += (float)qf[s][j] * (float)kv[j];
+    }
+    float sn = rows_sum(dot) * scale_log2;
+    if (BIAS && a.bias) sn += a.bias[(size_t)b * a.bias_stride + sl.n_old] * kLog2e;
+    const float m_new = fmaxf(m_run, sn);
+    const float ref = exp_ref(m_new);
+    const float alpha = fast_exp2(m_run - ref);
+    const float p = fast_exp2(sn - ref);
+    m_run = m_new;
+    l_run = l_run * alpha + (kg == 0 ? p : 0.0f);  // once per head column
+#pragma unroll
+    for (int blk = 0; blk < DV / 16; ++blk) {
+      // value rows blk*16 + kg*4 + i of this lane's acc^T entries
+      const uint2 raw = *reinterpret_cast<const uint2 *>(vnew + blk * 16 + kg * 4);
+      uint2 vb = raw;
+      if constexpr (FP8) {
+        vb = e4m3x4_to_bf16(e4m3_pack4(
+            __uint_as_float(raw.x << 16) * vinv, __uint_as_float(raw.x & 0xFFFF0000u) * vinv,
+            __uint_as_float(raw.y << 16) * vinv, __uint_as_float(raw.y & 0xFFFF0000u) * vinv));
+      }
+      const float vv[4] = {__uint_as_float(vb.x << 16), __uint_as_float(vb.x & 0xFFFF0000u),
+                           __uint_as_float(vb.y << 16), __uint_as_float(vb.y & 0xFFFF0000u)};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[blk][i] = o[blk][i] * alpha + p * vv[i];
+    }
+  }
+
   if (FP8) {
 #pragma unroll
     for (int blk = 0; blk < DV / 16; ++blk) o[blk] *= vscale;
@@ -409,7 +420,8 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
   float *wm = reinterpret_cast<float *>(lds);
   float *wl = wm + NW * 16;
   float *wacc = wl + NW * 16;
-  if (ntiles > 0) {
+  const bool live = ntiles > 0 || has_new;  // the work-group saw keys
+  if (live) {
     if (lane < 16) {
       wm[w * 16 + lane] = m_run;
       wl[w * 16 + lane] = l_tot;
@@ -423,12 +435,12 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
   if (sp.direct) stage_carry_in(sp, (size_t)b * Hq + (size_t)g * hpk, hpk, s_in);
   __syncthreads();
 
-  if (ntiles > 0 || sp.direct) {
+  if (live || sp.direct) {
     for (int e = threadIdx.x; e < hpk * DV; e += NW * 64) {
       const int h = e / DV;
       const int d = e % DV;
       float M = -INFINITY, acc = 0.0f, L = 0.0f;
-      if (ntiles > 0) {
+      if (live) {
 #pragma unroll
         for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, wm[ww * 16 + h]);
         const float ref = exp_ref(M);
