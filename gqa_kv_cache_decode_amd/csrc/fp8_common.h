@@ -18,16 +18,15 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 constexpr float kE4m3Max = 448.0f;
 
 // Four codes (the bytes of w, lowest first) as four bf16 values in two
-// words.  The hardware conversion decodes E4M3 exactly to fp32; the bf16 is
-// the upper half of that fp32 (its lower half is zero).
+// words: gfx950's packed E4M3 -> bf16 conversion, two codes per instruction,
+// with a unit scale (the conversion multiplies by the scale; 1 leaves every
+// decoded value as it is, and each is exact in bf16).
 __device__ __forceinline__ uint2 e4m3x4_to_bf16(uint32_t w) {
-  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);  // bytes 0, 1
-  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);   // bytes 2, 3
   uint2 r;
-  r.x = __builtin_amdgcn_perm(__float_as_uint(a.y), __float_as_uint(a.x),
-                              0x07060302u);
-  r.y = __builtin_amdgcn_perm(__float_as_uint(b.y), __float_as_uint(b.x),
-                              0x07060302u);
+  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(
+                                         w, 1.0f, false));  // bytes 0, 1
+  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(
+                                         w, 1.0f, true));   // bytes 2, 3
   return r;
 }
 
