@@ -22,6 +22,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 import types
@@ -541,10 +542,18 @@ def read_ceiling(torch, nbytes=4 << 30, reps=5):
     return best
 
 
+def code_text(src):
+    """C++ source with its comments removed and whitespace collapsed: what
+    the compiler sees, so that editing a comment keeps counter readings."""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
 def partition_source_hash(dtype):
     h = hashlib.sha256()
     for name in PARTITION_SOURCES[dtype]:
-        h.update((CSRC / name).read_bytes())
+        h.update(code_text((CSRC / name).read_text()).encode())
     return h.hexdigest()[:16]
 
 

@@ -25,9 +25,10 @@
 // product keeps ~16 bits of each weight (two MFMAs instead of one; the matrix
 // cores are far from busy on this HBM-bound loop).
 //
-// Heads are padded to 16 (the MFMA N width); padded heads see q = 0 and are
-// never written.  Tokens of a tile past the chunk end are loaded as zeros and
-// masked to -inf logits, so padding slots of the cache are never read.
+// Heads are padded to 16 (the MFMA N width); padded columns repeat the
+// group's last head and are never written.  Token offsets of a tile past the
+// chunk's last live token are clamped to that token and their logits masked
+// to -inf, so slots at or past the length are never read.
 //
 // In STEP mode the same launch is a whole decode step (needle-core
 // self_attn_incremental: push_kv, then attend over the cache including the new
@@ -130,7 +131,7 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
 
   const int lane = threadIdx.x & 63;
   // the wavefront's index, known to the compiler as uniform across its lanes
-  // (the tile loop and the branch to the new token's tile are then scalar)
+  // (the tile loop is then scalar)
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hl = lane & 15;  // head column of this lane
   const int kg = lane >> 4;  // lane group: k-slice of MFMA operands

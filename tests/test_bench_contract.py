@@ -82,3 +82,10 @@ def test_dominant_kernel_name(profile):
     bias = profile.endswith("_bias")
     w = bench.workload_by_name(profile[:-len("_bias")] if bias else profile)
     assert bench.kernel_name(w, bias, False) == rec["kernel"]
+
+
+def test_source_hash_ignores_comments_only():
+    a = "int f() { return 1; } // one\n/* a block\n   comment */\n"
+    b = "int f()  {\n  return 1;\n}"
+    assert bench.code_text(a) == bench.code_text(b)
+    assert bench.code_text("int f() { return 2; }") != bench.code_text(b)
