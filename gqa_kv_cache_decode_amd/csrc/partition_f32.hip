@@ -4,8 +4,8 @@
 // structure as the bf16 kernel, on the exact-fp32 MFMA 16x16x4.  A wavefront
 // takes 16-token tiles (the bytes of a 32-token bf16 tile), stages K and V once
 // per KV group in its own LDS slice, forms S^T[token][head] = K . q^T for all
-// heads of the group at once, folds the tile into each head's running maximum,
-// partition and weighted value sum (usearch attend), and accumulates
+// heads of the group at once, updates every head's maximum logit, sum of
+// exponentials and value accumulator with the tile (usearch attend), and accumulates
 // acc^T[dv][head] += V^T . P^T with P straight from the S^T registers.
 //
 // Vector-ALU family (any other head widths that are multiples of 4, up to

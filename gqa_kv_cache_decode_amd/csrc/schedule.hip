@@ -150,8 +150,8 @@ hipError_t launch_schedule(const ScheduleArgs &a, hipStream_t s) {
 
 // ---------------------------------------------------------------------------
 // Index-row selection for index-gathered decode (metrale DSA topk_to_mask:
-// duplicates collapse so a repeated token is attended once; INVALID and
-// out-of-range entries are dropped).  One work-group per sequence marks the
+// a slot named several times counts once; INVALID and out-of-range entries
+// are dropped).  One work-group per sequence marks the
 // named slots in an LDS bitmap of the sequence's live length, then writes
 // the set slots in ascending order (a prefix count over the bitmap words),
 // which also leaves the gathered rows in address order.

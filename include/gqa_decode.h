@@ -74,10 +74,10 @@ typedef enum gqa_status {
  * finite value 448.  Code c of KV head g of sequence b stands for
  * decode(c) * k_scale[b * num_kv_heads + g] (V: v_scale).  The pages leave
  * the compressed storage format open (usearch "linear-algebra", section
- * Attention: value rows are read in the index's own quantization; qualiaDB
- * KvDictionary: a compressed-cache read path); this is the library's choice,
- * and attention over such a cache is exact attention over the decoded
- * values.
+ * Attention: a value row comes back in whatever quantised form the index
+ * keeps it; qualiaDB KvDictionary: a compressed-cache read path); this is the
+ * library's choice, and attention over such a cache is exact attention over
+ * the decoded values.
  */
 typedef enum gqa_dtype {
   GQA_DTYPE_F32 = 0,
@@ -226,10 +226,9 @@ GQA_API size_t gqa_attend_workspace_bytes(const gqa_cache *cache, int32_t num_q_
  *   q     [batch][num_q_heads][dk], cache dtype (bf16 for fp8 caches).
  *   lens  [batch] device int32; keys attended are [0, clamp(lens[b], 0,
  *         max_len)).
- *   scale logit scale; 0 means 1/sqrt(dk) (usearch score_scale: a zero value
- *         asks for the derived scale, by convention one over the square root
- *         of the head width).
- *         Must be finite.
+ *   scale logit scale; 0 means 1/sqrt(dk) (usearch score_scale: zero is
+ *         replaced by the derived scale, by convention 1/sqrt of the key
+ *         width).  Must be finite.
  *   bias  NULL, or additive logit terms (needle-core self_attn_incremental,
  *         attn_bias: one term per cached position, added to the scaled dot
  *         product of every head): fp32, bias[b * bias_stride + t] for key t of

@@ -11,17 +11,17 @@ against it, their sum and the weighted value sum.  The passages followed:
 
 * needle-core ``attn.rs``, ``self_attn_incremental``: query head ``hi`` reads
   KV head ``hi / kv_repeat`` (contiguous grouping); every cached position is
-  scored as ``dot(q_head, k_head) * scale`` with ``scale = head_dim^-0.5``;
+  given the logit ``scale * <q_h, k_h>``, the scale being ``head_dim^-0.5``;
   the scores are softmaxed and the value rows are summed with those weights.
   Decode needs no causal mask: the query attends to exactly the cached rows.
-* usearch "linear-algebra", section Attention: each scored key updates the
-  head's running maximum, partition and weighted sum of values; the outputs are
+* usearch "linear-algebra", section Attention: every scored key updates three
+  per-head quantities (largest logit so far, sum of exponentials, weighted
+  value sum); the outputs are
   normalised by the partition; a carry per query row lets one branch continue
   another over the same queries.  Struct ``DenseSoftmaxState``:
   ``maximum_score`` holds the maximum logit so far (m), ``partition`` the sum
-  of exponentials relative to it (l).  A ``score_scale`` of zero asks for the
-  derived scale, whose conventional value is one over the square root of the
-  head width.
+  of exponentials relative to it (l).  A zero ``score_scale`` is replaced by
+  the derived one, 1/sqrt of the key width by convention.
 * cortiq-engine ``NystromState``, example ``o1_recovery.rs`` ``trial()``: the
   exact reference takes the maximum logit first and then the exponentials
   ``exp(l - mx)`` in double precision.

@@ -4,10 +4,10 @@ TEST INFRASTRUCTURE ONLY (like the rest of ``oracle``): plain numpy, fp64
 arithmetic except where the format fixes a narrower step.
 
 The pages fix no 8-bit format.  usearch "linear-algebra" (section Attention)
-reads every value row in the index's own quantization, and qualiaDB
-``KvDictionary`` (its decode of code words) serves a compressed-cache read
-path; neither names a scheme, so this module takes one reading, listed in
-the design notes:
+hands back each value row in whatever quantised form the index keeps it,
+and qualiaDB ``KvDictionary`` (its decode of code words) serves a
+compressed-cache read path; neither names a scheme, so this module takes one
+reading, listed in the design notes:
 
 * element format: OCP 8-bit floating point E4M3 (E4M3FN): a sign bit, a
   4-bit exponent with bias 7 and a 3-bit mantissa; exponent field 0 holds the

@@ -13,8 +13,8 @@ Passages followed:
 * cortiq-engine ``NystromState`` (struct doc, ``new``, ``step_group``): per
   KV group an exact window ring of width w (128 validated) and a buffer of
   permanent exact sink keys (4 by default), shared by the group's query
-  heads; a decode step inserts the group's (k, v) once and evicts the oldest
-  window key.  The page's far field (landmarks) is an approximation and is
+  heads; each decode step adds the group's new key/value row a single time
+  and drops the oldest window key.  The page's far field (landmarks) is an approximation and is
   not modelled: here the evicted key moves, exactly, into a main cache.
 
 Readings (listed in the design notes): the first ``S`` tokens of a sequence
