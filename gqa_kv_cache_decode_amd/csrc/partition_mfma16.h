@@ -77,16 +77,22 @@ struct Mfma16Geom {
   static constexpr int waveLdsBytes = kTileTokens * (kRowBytes + vRowBytes);
 };
 
+// The work-group's main LDS area: the wavefronts' tile slices, reused for the
+// merge of their states (NW * 16 rows of dv + 2 floats).
+template <int DK, int DV, int NW, bool FP8>
+constexpr int partition_lds_bytes() {
+  constexpr int tiles = NW * Mfma16Geom<DK, DV, FP8>::waveLdsBytes;
+  constexpr int merge = NW * 16 * (DV + 2) * 4;
+  return tiles > merge ? tiles : merge;
+}
+
 template <int DK, int DV, int NW, bool STEP, bool BIAS, bool GATHER, bool FP8>
 __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
     PartitionArgs args, StepParams sp) {
   using G = Mfma16Geom<DK, DV, FP8>;
   constexpr int ES = G::kEsize;
   constexpr int PP = G::kPerPiece;
-  constexpr int kMergeFloats = NW * 16 * (DV + 2);
-  constexpr int kTileBytes = NW * G::waveLdsBytes;
-  constexpr int kLdsBytes =
-      kTileBytes > kMergeFloats * 4 ? kTileBytes : kMergeFloats * 4;
+  constexpr int kLdsBytes = partition_lds_bytes<DK, DV, NW, FP8>();
   __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
   __shared__ int s_flag;
   __shared__ float s_in[32];  // carry_in m, l of the group's rows (direct)
@@ -492,20 +498,37 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
   }
 }
 
+// A scheduled launch runs its work-groups in several rounds.  There the read
+// stream ran fastest with at most two work-groups resident per CU (ragged
+// workload: 749 -> 738 us per launch against up to four by LDS; 771 us with
+// one), so such a launch reserves unused dynamic LDS that keeps a third out
+// of a CU's 160 KB.  The reservation is sized against the main LDS area
+// alone, a lower bound of the static LDS, so three never fit; two always do
+// (the total stays within 55 KB).
+constexpr int kCuLdsBytes = 160 * 1024;
+
+template <int DK, int DV, int NW, bool FP8>
+int residency_lds_bytes(const PartitionArgs &a) {
+  constexpr int kThird = kCuLdsBytes / 3 + 1;
+  constexpr int kMain = partition_lds_bytes<DK, DV, NW, FP8>();
+  return a.sched && kMain < kThird ? kThird - kMain : 0;
+}
+
 template <int DK, int DV, int NW, bool STEP, bool FP8>
 hipError_t launch_one(const PartitionArgs &a, const StepParams &sp,
                       hipStream_t s) {
   const int nwork = a.sched ? a.sched_len : a.total_items;
-  if (a.sel) {  // index-gathered: attend only, no bias
+  const int dyn = residency_lds_bytes<DK, DV, NW, FP8>(a);
+  if (a.sel) {  // index-gathered: attend only, no bias, never scheduled
     if (STEP || a.has_bias) return hipErrorInvalidValue;
     hipLaunchKernelGGL((partition_bf16_kernel<DK, DV, NW, false, false, true, FP8>),
                        dim3(nwork), dim3(NW * 64), 0, s, a, sp);
   } else if (a.has_bias) {
     hipLaunchKernelGGL((partition_bf16_kernel<DK, DV, NW, STEP, true, false, FP8>),
-                       dim3(nwork), dim3(NW * 64), 0, s, a, sp);
+                       dim3(nwork), dim3(NW * 64), dyn, s, a, sp);
   } else {
     hipLaunchKernelGGL((partition_bf16_kernel<DK, DV, NW, STEP, false, false, FP8>),
-                       dim3(nwork), dim3(NW * 64), 0, s, a, sp);
+                       dim3(nwork), dim3(NW * 64), dyn, s, a, sp);
   }
   return hipGetLastError();
 }
