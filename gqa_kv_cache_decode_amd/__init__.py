@@ -1,10 +1,11 @@
 """Exact grouped-query decode attention over a KV cache, HIP on MI355X (gfx950).
 
 The compute lives in ``libgqa_decode.so`` (hand-written HIP kernels behind a
-C ABI, declared in ``include/gqa_decode.h``).  ``kv_append``,
-``attend_decode`` and ``softmax_state_merge`` here are thin ctypes bindings:
-they marshal torch tensors and the current HIP stream into the C calls.  The
-library is loaded on first use and a missing build raises at once.
+C ABI, declared in ``include/gqa_decode.h``).  The functions here are thin
+ctypes bindings of the C entry points of the same names (without the
+``gqa_`` prefix): they marshal torch tensors and the current HIP stream into
+the C calls.  The library is loaded on first use and a missing build raises
+at once.
 """
 
 __all__ = ["kv_append", "attend_decode", "softmax_state_merge",
