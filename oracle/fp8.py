@@ -34,6 +34,7 @@ from typing import Optional
 import numpy as np
 
 from .attention import Carry, attend, kv_append
+from .streaming import stream_append
 
 E4M3_MAX = 448.0
 
@@ -118,3 +119,17 @@ def kv_append_fp8(k_cache, v_cache, k_new, v_new, k_scale, v_scale, lens):
     vs = np.asarray(v_scale, dtype=np.float32)[:, :, None]
     return kv_append(k_cache, v_cache, quantize(k_new, ks),
                      quantize(v_new, vs), lens)
+
+
+def stream_append_fp8(sink_k, sink_v, ring_k, ring_v, main_k, main_v,
+                      k_new, v_new, k_scale, v_scale, count):
+    """The sink / ring / main layout of ``oracle.streaming.stream_append``
+    (cortiq-engine ``NystromState``) over fp8 code caches whose three parts
+    share one K and one V scale per (sequence, KV head), [B, Hkv]: the new
+    rows (values exact in fp32, e.g. bf16) are quantised with those scales,
+    then placed as any cache row; a ring row a full ring evicts moves to main
+    as its codes, so it keeps its value.  Returns as ``stream_append``."""
+    ks = np.asarray(k_scale, dtype=np.float32)[:, :, None]
+    vs = np.asarray(v_scale, dtype=np.float32)[:, :, None]
+    return stream_append(sink_k, sink_v, ring_k, ring_v, main_k, main_v,
+                         quantize(k_new, ks), quantize(v_new, vs), count)

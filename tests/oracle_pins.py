@@ -741,5 +741,62 @@ def pin_fp8_append(orc8):
         np.array_equal(v2[keep], v[keep]), "other slots untouched"
 
 
+def pin_fp8_stream(orc8):
+    """The streaming layout over fp8 caches whose parts share the scales:
+    rows whose values are codes times power-of-two scales (per sequence and
+    KV head, different for K and V) land in sink / ring / main exactly as
+    those codes over a run of steps (the evicted ring rows move to main as
+    codes); a full main cache drops the token; attending the three decoded
+    parts equals attending the decoded history."""
+    import oracle.attention as att
+    import oracle.streaming as st
+    rng = np.random.default_rng(44)
+    B, Hq, Hkv, d, S, W, M = 2, 4, 2, 8, 2, 3, 4
+    ks = np.array([[0.25, 2.0], [8.0, 0.5]], dtype=np.float32)
+    vs = np.array([[0.5, 4.0], [1.0, 0.125]], dtype=np.float32)
+    z = lambda n: np.zeros((B, n, Hkv, d), dtype=np.uint8)
+    sk, sv, rk, rv, mk, mv = z(S), z(S), z(W), z(W), z(M), z(M)
+    count = np.array([0, 0])
+    hist = [[], []]
+    for step in range(S + W + M + 2):
+        kc = _fp8_codes(rng, (B, Hkv, d))
+        vc = _fp8_codes(rng, (B, Hkv, d))
+        kn = (orc8.decode(kc) * ks[:, :, None]).astype(np.float32)
+        vn = (orc8.decode(vc) * vs[:, :, None]).astype(np.float32)
+        before = count.copy()
+        sk, sv, rk, rv, mk, mv, count, dropped = orc8.stream_append_fp8(
+            sk, sv, rk, rv, mk, mv, kn, vn, ks, vs, count)
+        full = before - S - W >= M
+        assert dropped == int(full.sum()), "drops"
+        for b in range(B):
+            if full[b]:
+                assert count[b] == before[b], "full main: no change"
+            else:
+                assert count[b] == before[b] + 1, "count advances"
+                hist[b].append((kc[b], vc[b]))
+        for b in range(B):
+            t = int(count[b])
+            ns, nw, nm = st.stream_lengths(t, S, W, M)
+            for p in range(ns):
+                assert np.array_equal(sk[b, p], hist[b][p][0]), "sink codes"
+            for p in range(max(S, t - W), t):
+                assert np.array_equal(rk[b, (p - S) % W], hist[b][p][0]) and \
+                    np.array_equal(rv[b, (p - S) % W], hist[b][p][1]), "ring"
+            for j in range(nm):
+                assert np.array_equal(mk[b, j], hist[b][S + j][0]) and \
+                    np.array_equal(mv[b, j], hist[b][S + j][1]), "main codes"
+            q = rng.uniform(-1, 1, (1, Hq, d))
+            dq = lambda c: orc8.dequantize_cache(c, ks[b:b + 1])
+            dv = lambda c: orc8.dequantize_cache(c, vs[b:b + 1])
+            parts = [(dq(sk[b:b + 1]), dv(sv[b:b + 1]), [ns]),
+                     (dq(rk[b:b + 1]), dv(rv[b:b + 1]), [nw]),
+                     (dq(mk[b:b + 1]), dv(mv[b:b + 1]), [nm])]
+            got, _ = st.attend_branches(q, parts, 0.5)
+            hk = np.stack([h[0] for h in hist[b]])[None]
+            hv = np.stack([h[1] for h in hist[b]])[None]
+            want, _ = att.attend(q, dq(hk), dv(hv), [t], 0.5)
+            _close(got, want, 1e-14, f"fp8 stream t={t}")
+
+
 FP8_PINS = [pin_fp8_format, pin_fp8_encode, pin_fp8_quantize,
-            pin_fp8_attend, pin_fp8_append]
+            pin_fp8_attend, pin_fp8_append, pin_fp8_stream]

@@ -21,6 +21,7 @@ _real_quantize = f8.quantize
 _real_dequant = f8.dequantize_cache
 _real_attend = f8.attend_fp8
 _real_append = f8.kv_append_fp8
+_real_stream = f8.stream_append_fp8
 
 
 def _decode_bias8(code):
@@ -97,6 +98,13 @@ MUTANTS = {
     "append_k_with_v_scale": ("kv_append_fp8",
                               lambda k, v, kn, vn, ks, vs, lens:
                               _real_append(k, v, kn, vn, vs, vs, lens)),
+    "stream_k_with_v_scale": ("stream_append_fp8",
+                              lambda *a: _real_stream(*a[:8], a[9], a[9],
+                                                      a[10])),
+    "stream_scales_of_next_sequence": (
+        "stream_append_fp8",
+        lambda *a: _real_stream(*a[:8], np.roll(a[8], 1, axis=0),
+                                np.roll(a[9], 1, axis=0), a[10])),
 }
 
 
