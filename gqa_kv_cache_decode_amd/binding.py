@@ -477,7 +477,9 @@ def stream_append(ring_k, ring_v, k_new, v_new, count_in, count_out=None,
                   sink=None, main=None, dropped=None, lens=None):
     """One token per sequence into the sink / ring / main layout.
 
-    ``sink`` and ``main`` are optional (k, v) cache pairs.  Returns
+    ``sink`` and ``main`` are optional (k, v) cache pairs.  fp8 parts are
+    :class:`Fp8Cache` pairs sharing the ring's scale tensors (k_new / v_new
+    then bf16, quantised into the new slot).  Returns
     (count_out, lens_sink, lens_ring, lens_main): device int32 [batch]
     tensors (lens_sink / lens_main None without that part), the lengths
     :func:`attend_branches` takes; ``lens`` may give those three tensors to

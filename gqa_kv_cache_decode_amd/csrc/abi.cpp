@@ -667,7 +667,7 @@ gqa_status gqa_stream_append(const gqa_cache *sink, const gqa_cache *ring,
   gqa_status st = check_cache_dims(ring);
   if (st != GQA_OK) return st;
   if ((st = check_cache_data(ring)) != GQA_OK) return st;
-  if (ring->dtype == GQA_DTYPE_FP8_E4M3) return GQA_ERR_UNSUPPORTED;
+  const bool fp8 = ring->dtype == GQA_DTYPE_FP8_E4M3;
   for (const gqa_cache *c : {sink, main_cache}) {
     if (!c) continue;
     if ((st = check_cache_dims(c)) != GQA_OK) return st;
@@ -675,14 +675,23 @@ gqa_status gqa_stream_append(const gqa_cache *sink, const gqa_cache *ring,
     if (c->batch != ring->batch || c->num_kv_heads != ring->num_kv_heads ||
         c->dk != ring->dk || c->dv != ring->dv || c->dtype != ring->dtype)
       return GQA_ERR_SHAPE_MISMATCH;
+    // fp8: an evicted row moves to main as its codes, so the parts must
+    // share the scales
+    if (fp8 && (c->k_scale != ring->k_scale || c->v_scale != ring->v_scale))
+      return GQA_ERR_INVALID_ARGUMENT;
+  }
+  if (fp8) {  // four codes of one KV head per word, from 16-byte bf16 rows
+    if (ring->dk % 16 || ring->dv % 16) return GQA_ERR_UNSUPPORTED;
+    if (!aligned16(k_new) || !aligned16(v_new)) return GQA_ERR_INVALID_ARGUMENT;
   }
   if (!k_new || !v_new || !count_in || !count_out || !lens_ring ||
       (sink && !lens_sink) || (main_cache && !lens_main))
     return GQA_ERR_INVALID_ARGUMENT;
   const int64_t rk = (int64_t)ring->num_kv_heads * ring->dk * esize(ring->dtype);
   const int64_t rv = (int64_t)ring->num_kv_heads * ring->dv * esize(ring->dtype);
-  if (rk % 4 || rv % 4 || rk > std::numeric_limits<int32_t>::max() ||
-      rv > std::numeric_limits<int32_t>::max())
+  // (bf16 rows of an fp8 cache are read twice as wide as the code rows)
+  if (rk % 4 || rv % 4 || 2 * rk > std::numeric_limits<int32_t>::max() ||
+      2 * rv > std::numeric_limits<int32_t>::max())
     return GQA_ERR_UNSUPPORTED;
   const uintptr_t bits = reinterpret_cast<uintptr_t>(k_new) |
                          reinterpret_cast<uintptr_t>(v_new);
@@ -708,6 +717,10 @@ gqa_status gqa_stream_append(const gqa_cache *sink, const gqa_cache *ring,
   a.main_len = main_cache ? main_cache->max_len : 0;
   a.row_bytes_k = (int)rk;
   a.row_bytes_v = (int)rv;
+  a.fp8 = fp8 ? 1 : 0;
+  a.num_kv_heads = ring->num_kv_heads;
+  a.k_scale = fp8 ? ring->k_scale : nullptr;
+  a.v_scale = fp8 ? ring->v_scale : nullptr;
   return device_status(gqa::launch_stream_append(a, stream));
 }
 

@@ -123,7 +123,23 @@ __global__ __launch_bounds__(kThreads) void append_e4m3_kernel(AppendArgs a) {
 //          cache the old token simply leaves), then the new token takes r.
 // count_out = t + 1 unless dropped; lens_* = the live keys of each part.
 // One work-group per sequence; each thread copies its own 4-byte words, so
-// the old ring word is read before the same thread overwrites it.
+// the old ring word is read before the same thread overwrites it.  With fp8
+// caches a word holds four codes of one KV head, quantised from the four
+// bf16 values of the new row with that head's scale of the sequence.
+__device__ __forceinline__ uint32_t stream_word(const StreamAppendArgs &a,
+                                                const void *row, int i,
+                                                const float *scale, int b,
+                                                int d) {
+  if (!a.fp8) return static_cast<const uint32_t *>(row)[i];
+  const uint2 x = static_cast<const uint2 *>(row)[i];  // bf16 values 4i..4i+3
+  const float inv =
+      e4m3_inv_scale(scale[(size_t)b * a.num_kv_heads + 4 * i / d]);
+  return e4m3_pack4(__uint_as_float(x.x << 16) * inv,
+                    __uint_as_float(x.x & 0xFFFF0000u) * inv,
+                    __uint_as_float(x.y << 16) * inv,
+                    __uint_as_float(x.y & 0xFFFF0000u) * inv);
+}
+
 __global__ __launch_bounds__(kThreads) void stream_append_kernel(
     StreamAppendArgs a) {
   const int b = blockIdx.x;
@@ -150,15 +166,21 @@ __global__ __launch_bounds__(kThreads) void stream_append_kernel(
     vd = static_cast<uint32_t *>(a.ring_v) + ((size_t)b * W + r) * (a.row_bytes_v / 4);
   }
   if (ok) {
-    const uint32_t *kn = static_cast<const uint32_t *>(a.k_new) + (size_t)b * (a.row_bytes_k / 4);
-    const uint32_t *vn = static_cast<const uint32_t *>(a.v_new) + (size_t)b * (a.row_bytes_v / 4);
+    // the new rows: as stored (4-byte words), or bf16 for fp8 caches
+    const int in_esize = a.fp8 ? 2 : 1;  // input bytes per stored byte
+    const void *kn = static_cast<const unsigned char *>(a.k_new) +
+                     (size_t)b * a.row_bytes_k * in_esize;
+    const void *vn = static_cast<const unsigned char *>(a.v_new) +
+                     (size_t)b * a.row_bytes_v * in_esize;
+    const int dk = a.fp8 ? a.row_bytes_k / a.num_kv_heads : 0;
+    const int dv = a.fp8 ? a.row_bytes_v / a.num_kv_heads : 0;
     for (int i = threadIdx.x; i < a.row_bytes_k / 4; i += kThreads) {
       if (ek) ek[i] = kd[i];
-      kd[i] = kn[i];
+      kd[i] = stream_word(a, kn, i, a.k_scale, b, dk);
     }
     for (int i = threadIdx.x; i < a.row_bytes_v / 4; i += kThreads) {
       if (ev) ev[i] = vd[i];
-      vd[i] = vn[i];
+      vd[i] = stream_word(a, vn, i, a.v_scale, b, dv);
     }
   }
   __syncthreads();  // count_in is read by every thread before count_out is set

@@ -154,6 +154,11 @@ struct StreamAppendArgs {
   int32_t *dropped;
   int batch, sink, window, main_len;
   int row_bytes_k, row_bytes_v;  // bytes of one token's K/V row (multiple of 4)
+  // fp8 caches: the three parts share the scales; k_new / v_new are bf16
+  // rows [Hkv][d] quantised into the new slot (row_bytes_* are the code rows'
+  // bytes, Hkv * d), and an evicted row moves to main as its codes
+  int fp8, num_kv_heads;
+  const float *k_scale, *v_scale;  // [B][Hkv] each
 };
 
 // Index-row selection (DSA topk_to_mask): per sequence, the distinct cache

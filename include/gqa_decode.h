@@ -187,8 +187,12 @@ GQA_API gqa_status gqa_kv_append(const gqa_cache *cache, const void *k_new,
  *   sink  NULL (no sinks) or a cache of S slots; ring: a cache of W slots;
  *   main_cache  NULL (evicted keys leave attention) or a cache of M slots.
  *   All three share batch, num_kv_heads, dk, dv and dtype; K/V rows of
- *   num_kv_heads * d elements must be a multiple of 4 bytes.  fp8 caches
- *   are not supported here (GQA_ERR_UNSUPPORTED).
+ *   num_kv_heads * d elements must be a multiple of 4 bytes.  fp8 caches:
+ *   the three parts must share the scale arrays (the same k_scale and
+ *   v_scale pointers, else GQA_ERR_INVALID_ARGUMENT), since an evicted row
+ *   moves to main as its codes; k_new / v_new are then bf16 rows, 16-byte
+ *   aligned, quantised into the new slot as gqa_kv_append does; dk and dv
+ *   must be multiples of 16 (GQA_ERR_UNSUPPORTED otherwise).
  *   count_in [batch]: tokens seen so far by each sequence.  With t =
  *   count_in[b]: t < S puts the token in sink slot t; otherwise it takes ring
  *   slot (t - S) % W, and if the ring was full (t - S >= W) the token it held

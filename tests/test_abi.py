@@ -311,8 +311,9 @@ def test_gathered_checks(lib):
 
 def test_fp8_checks(lib):
     """fp8 caches: the bf16 family's plan and shapes; scales required and
-    4-byte aligned; no kernel for other head widths; not accepted by
-    stream_append; unknown dtypes rejected."""
+    4-byte aligned; no kernel for other head widths; stream_append needs
+    the parts to share the scales, aligned bf16 rows and widths of 16;
+    unknown dtypes rejected."""
     f8 = dict(dtype=bd.FP8_E4M3, ks=0xB0000, vs=0xB1000)
     c8 = _cache(**f8)
     _, p8 = _plan(lib, c8, 32)
@@ -341,11 +342,22 @@ def test_fp8_checks(lib):
                              pp, pp, None, None) == INVALID
     assert lib.gqa_kv_append(ctypes.byref(_cache(dtype=bd.FP8_E4M3)), pp, pp,
                              pp, pp, None, None) == INVALID   # no scales
+    # stream_append over fp8 parts: the parts share the scales, the bf16 rows
+    # are 16-byte aligned, the widths are multiples of 16
     ring = _cache(B=4, T=128, H=2, **f8)
     p = [ctypes.c_void_p(0x50000 + 0x1000 * i) for i in range(8)]
-    assert lib.gqa_stream_append(None, ctypes.byref(ring), None, p[0], p[1],
-                                 p[2], p[3], None, p[5], None, None,
-                                 None) == UNSUPPORTED
+    sa = lib.gqa_stream_append
+    other = _cache(B=4, T=64, H=2, k=0x60000, v=0x70000, dtype=bd.FP8_E4M3,
+                   ks=0xC0000, vs=f8["vs"])
+    assert sa(None, ctypes.byref(ring), ctypes.byref(other), p[0], p[1], p[2],
+              p[3], None, p[5], p[6], None, None) == INVALID
+    assert sa(ctypes.byref(other), ctypes.byref(ring), None, p[0], p[1], p[2],
+              p[3], p[4], p[5], None, None, None) == INVALID
+    assert sa(None, ctypes.byref(ring), None, ctypes.c_void_p(0x50008), p[1],
+              p[2], p[3], None, p[5], None, None, None) == INVALID
+    narrow = _cache(B=4, T=128, H=2, dk=72, dv=72, **f8)
+    assert sa(None, ctypes.byref(narrow), None, p[0], p[1], p[2], p[3], None,
+              p[5], None, None, None) == UNSUPPORTED
     # a branch of another dtype
     arr = (bd._Branch * 2)(_branch(c8), _branch(_cache()))
     assert lib.gqa_attend_branches_workspace_bytes(arr, 2, 32) == 0

@@ -232,3 +232,125 @@ def test_decode_step_branches(dt, dk, dv, Hq, Hkv):
     check_out(out.cpu().numpy(), want, vmax, dt, "decode_step_branches")
     check_carry(cout.m.cpu().numpy(), cout.l.cpu().numpy(), cw.m, cw.l, dt,
                 "decode_step_branches carry")
+
+
+@pytest.mark.parametrize("S,W,M", [(4, 16, 40), (0, 8, 20), (4, 8, 0)])
+def test_stream_steps_fp8(S, W, M):
+    """stream_append over fp8 caches whose three parts share the scales: the
+    new bf16 rows quantised into sink / ring slots and the evicted ring rows
+    moved to main as codes, bit for bit against the oracle over a run of
+    steps (an invalid count, a full main cache); attend_branches over the
+    three parts equals the oracle's attention over the decoded history."""
+    import oracle.fp8 as of8
+    g = _gqa()
+    B, Hq, Hkv, d = 3, 8, 2, 128
+    gen = torch.Generator().manual_seed(62)
+    ks = (torch.rand(B, Hkv, generator=gen) * 0.45 + 0.05).float()
+    vs = (torch.rand(B, Hkv, generator=gen) * 0.9 + 0.1).float()
+    ksd, vsd = ks.cuda(), vs.cuda()
+    z = lambda n: torch.zeros(B, n, Hkv, d, dtype=torch.uint8)
+    host = {"sk": z(S) if S else None, "sv": z(S) if S else None,
+            "rk": z(W), "rv": z(W),
+            "mk": z(M) if M else None, "mv": z(M) if M else None}
+    dev = {k: (None if t is None else t.cuda()) for k, t in host.items()}
+    part = lambda kk, vv: (g.Fp8Cache(dev[kk], ksd), g.Fp8Cache(dev[vv], vsd))
+    count = torch.tensor([0, 3, -1], dtype=torch.int32)
+    count_d = count.cuda()
+    # sequence 1 starts with 3 tokens already placed by the oracle
+    hist = [[] for _ in range(B)]
+    for i in range(3):
+        kn = (torch.randn(B, Hkv, d, generator=gen) * 4 * ks[:, :, None]).to(
+            torch.bfloat16)
+        vn = (torch.randn(B, Hkv, d, generator=gen) * 4 * vs[:, :, None]).to(
+            torch.bfloat16)
+        res = of8.stream_append_fp8(
+            *(None if host[k] is None else host[k].numpy()
+              for k in ("sk", "sv", "rk", "rv", "mk", "mv")),
+            kn.float().numpy(), vn.float().numpy(), ks.numpy(), vs.numpy(),
+            np.array([-1, i, -1]))
+        for k, arr in zip(("sk", "sv", "rk", "rv", "mk", "mv"), res[:6]):
+            if arr is not None:
+                host[k] = torch.from_numpy(arr)
+        hist[1].append((of8.quantize(kn[1].float().numpy(),
+                                     ks[1].numpy()[:, None]),
+                        of8.quantize(vn[1].float().numpy(),
+                                     vs[1].numpy()[:, None])))
+    dev = {k: (None if t is None else t.cuda()) for k, t in host.items()}
+    dropped = torch.zeros(1, dtype=torch.int32, device="cuda")
+    drop_ref = 0
+    steps = S + W + M + 4
+    say(f"[stream fp8] S={S} W={W} M={M}: {steps} steps")
+    for step in range(steps):
+        kn = (torch.randn(B, Hkv, d, generator=gen) * 4 * ks[:, :, None]).to(
+            torch.bfloat16)
+        vn = (torch.randn(B, Hkv, d, generator=gen) * 4 * vs[:, :, None]).to(
+            torch.bfloat16)
+        before = count.clone()
+        rk, rv = part("rk", "rv")
+        cnt_out, ls, lr, lm = g.stream_append(
+            rk, rv, kn.cuda(), vn.cuda(), count_d,
+            sink=part("sk", "sv") if S else None,
+            main=part("mk", "mv") if M else None, dropped=dropped)
+        torch.cuda.synchronize()
+        res = of8.stream_append_fp8(
+            *(None if host[k] is None else host[k].numpy()
+              for k in ("sk", "sv", "rk", "rv", "mk", "mv")),
+            kn.float().numpy(), vn.float().numpy(), ks.numpy(), vs.numpy(),
+            before.numpy())
+        for k, arr in zip(("sk", "sv", "rk", "rv", "mk", "mv"), res[:6]):
+            if arr is None:
+                continue
+            host[k] = torch.from_numpy(arr)
+            assert torch.equal(dev[k].cpu(), host[k]), \
+                f"S={S} W={W} M={M} step {step}: {k} codes differ"
+        count = torch.from_numpy(res[6])
+        drop_ref += res[7]
+        assert cnt_out.cpu().tolist() == count.tolist(), "count"
+        assert int(dropped.item()) == drop_ref, "dropped"
+        for b in range(2):
+            if int(count[b]) > int(before[b]):
+                hist[b].append((of8.quantize(kn[b].float().numpy(),
+                                             ks[b].numpy()[:, None]),
+                                of8.quantize(vn[b].float().numpy(),
+                                             vs[b].numpy()[:, None])))
+        count_d = cnt_out
+        if step % 6 == 5 or step == steps - 1:
+            q = torch.randn(B, Hq, d, generator=gen).to(torch.bfloat16)
+            branches = []
+            if S:
+                branches.append((*part("sk", "sv"), ls))
+            branches.append((*part("rk", "rv"), lr))
+            if M:
+                branches.append((*part("mk", "mv"), lm))
+            out = g.attend_branches(q.cuda(), branches, 0.0)
+            torch.cuda.synchronize()
+            for b in range(2):
+                t = int(count[b])
+                nm = ost.stream_lengths(t, S, W, M)[2]
+                keep = list(range(min(t, S))) + \
+                    list(range(max(S, t - W), t)) + list(range(S, S + nm))
+                kc = np.stack([hist[b][p][0] for p in keep])[None]
+                vc = np.stack([hist[b][p][1] for p in keep])[None]
+                want, _ = of8.attend_fp8(
+                    np64(q[b:b + 1]), kc, vc, ks[b:b + 1].double().numpy(),
+                    vs[b:b + 1].double().numpy(), [len(keep)], 0.0)
+                vmax = float(np.abs(of8.dequantize_cache(
+                    vc, vs[b:b + 1].double().numpy())).max())
+                check_out(out[b:b + 1].cpu().numpy(), want, vmax, "fp8",
+                          f"fp8 S={S} W={W} M={M} step {step} b={b} t={t}")
+            assert torch.all(out[2] == 0), "invalid sequence attends nothing"
+
+
+def test_stream_fp8_needs_shared_scales():
+    g = _gqa()
+    B, Hkv, d = 2, 2, 128
+    codes = lambda n: torch.zeros(B, n, Hkv, d, dtype=torch.uint8,
+                                  device="cuda")
+    s1 = torch.ones(B, Hkv, device="cuda")
+    s2 = torch.ones(B, Hkv, device="cuda")
+    ring = (g.Fp8Cache(codes(8), s1), g.Fp8Cache(codes(8), s1))
+    main = (g.Fp8Cache(codes(8), s2), g.Fp8Cache(codes(8), s2))
+    kn = torch.zeros(B, Hkv, d, dtype=torch.bfloat16, device="cuda")
+    count = torch.zeros(B, dtype=torch.int32, device="cuda")
+    with pytest.raises(g.GqaError, match="INVALID_ARGUMENT"):
+        g.stream_append(*ring, kn, kn, count, main=main)
