@@ -9,8 +9,9 @@
  *   out  = sum_j exp(s_j - m) V[b,j,g,:] / sum_j exp(s_j - m),  m = max_j s_j
  *
  * (needle-core attn.rs, self_attn_incremental: push_kv then attend over the
- * cache; query head hi reads KV head hi / kv_repeat; scores are
- * dot(q_head, k_head) * head_dim^-0.5, softmaxed, and the value rows summed.)
+ * cache; query head hi reads KV head hi / kv_repeat; each score is the q.k
+ * dot product times head_dim^-0.5, and the softmax weights sum the value
+ * rows.)
  * The result can also be handed out as a mergeable online-softmax carry
  * (m, l, acc) so that two branches over the same queries — for example a long
  * main cache and a recent window — fold into one (usearch
@@ -33,8 +34,8 @@
  *  - fp8 caches (GQA_DTYPE_FP8_E4M3): queries and new K/V rows are bf16.
  *  - Errors: GQA_ERR_INVALID_ARGUMENT (a required pointer is NULL, a size is
  *    non-positive, a scale is not finite), GQA_ERR_SHAPE_MISMATCH (the query
- *    heads are not a multiple of the KV heads — usearch head_count "must
- *    divide the rows" — or the sizes of two arguments disagree),
+ *    heads are not a multiple of the KV heads — usearch requires the head
+ *    count to split the rows evenly — or the sizes of two arguments disagree),
  *    GQA_ERR_UNSUPPORTED (no kernel for this dtype / head widths / group
  *    size), GQA_ERR_WORKSPACE_TOO_SMALL, GQA_ERR_DEVICE.
  */
