@@ -1,7 +1,7 @@
 // Log-sum-exp combine of split-K partials, and the carry merge.
 //
 // Both fold online-softmax states (usearch DenseAttendConfig.carry: a state per
-// query row lets one call continue another over the same queries, rescaling
+// query row lets one call resume another on the same query rows, rescaling
 // the partial softmaxes; DenseSoftmaxState: m is the maximum logit so far and
 // l the sum of exponentials relative to m).  For states (m_i, l_i, acc_i)
 // with M = max_i m_i:  l = sum_i e^(m_i - M) l_i,  acc = sum_i e^(m_i - M) acc_i.

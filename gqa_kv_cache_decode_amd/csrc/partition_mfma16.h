@@ -13,7 +13,7 @@
 //
 // Per 32-token tile a wavefront computes
 //   S^T[token][head] = K_tile[token][:] . q[head][:]         (MFMA, A = K)
-// then folds the tile into each head's running maximum m, partition l and
+// then folds the tile into the per-head state: maximum logit m, partition l and
 // weighted value sum acc (usearch attend: each scored key updates these three
 // per-head quantities), in base-2 units:
 //   m' = max(m, max_j s_j), alpha = 2^(m - m'), p_j = 2^(s_j - m'),

@@ -150,7 +150,7 @@ __device__ __forceinline__ void fold_state(float &m, float &L, float &acc,
 }
 
 // Writes column d of query row `row` from its final state: out = acc / L
-// (usearch: output rows already divided by the partition) and carry_out;
+// (usearch: the output rows come normalised by the partition) and carry_out;
 // an empty state gives out 0 and carry (-inf, 0, 0).
 __device__ __forceinline__ void write_final(const StepParams &sp, size_t row,
                                             int dv, int d, float m, float L,

@@ -242,11 +242,11 @@ GQA_API size_t gqa_attend_workspace_bytes(const gqa_cache *cache, int32_t num_q_
  *         removed is empty (out 0, carry (-inf, 0, 0), or carry_in).  Terms
  *         must not be NaN or +inf.  Ignored (with bias_stride) when NULL.
  *   carry_in   NULL, or a carry over the same query rows folded into this
- *              branch (usearch carry: one call continues another over the
- *              same queries, e.g. a recent-window branch).
+ *              branch (usearch carry: one call resumes another on the same
+ *              query rows, e.g. a recent-window branch).
  *   carry_out  NULL, or receives the merged carry; may alias carry_in.
- *   out   NULL, or [batch][num_q_heads][dv] fp32: the merged value mix already
- *         divided by the partition; rows with no keys at all get 0.
+ *   out   NULL, or [batch][num_q_heads][dv] fp32: the merged value mix
+ *         normalised by the partition; rows with no keys at all get 0.
  *   At least one of out / carry_out must be given.
  *   workspace  device buffer of at least gqa_attend_workspace_bytes().
  * Enqueues the split-K partition kernel (preceded by the schedule kernel for
@@ -345,7 +345,7 @@ GQA_API size_t gqa_attend_branches_workspace_bytes(const gqa_branch *branches,
  * live keys (branch i: keys [0, clamp(lens_i[b], 0, max_len_i)) of its own
  * cache), folded with carry_in, in one partition launch and one combine.
  * The branches' partial softmax states merge exactly as carries do (usearch
- * carry: one branch continues another over the same queries), so the result
+ * carry: one branch resumes another on the same query rows), so the result
  * is one pass over the concatenated keys: e.g. permanent sink keys, a recent
  * window and a main cache (cortiq-engine NystromState: exact window ring and
  * sink buffer, kept once per KV group).

@@ -17,8 +17,8 @@ against it, their sum and the weighted value sum.  The passages followed:
 * usearch "linear-algebra", section Attention: every scored key updates three
   per-head quantities (largest logit so far, sum of exponentials, weighted
   value sum); the outputs are
-  normalised by the partition; a carry per query row lets one branch continue
-  another over the same queries.  Struct ``DenseSoftmaxState``:
+  normalised by the partition; a carry per query row lets one branch resume
+  where another left off on the same query rows.  Struct ``DenseSoftmaxState``:
   ``maximum_score`` holds the maximum logit so far (m), ``partition`` the sum
   of exponentials relative to it (l).  A zero ``score_scale`` is replaced by
   the derived one, 1/sqrt of the key width by convention.

@@ -7,7 +7,8 @@ plain numpy, fp64 arithmetic, bit copies for cache data.
 Passages followed:
 
 * usearch "linear-algebra", section Attention: a carry per query row lets one
-  branch continue another over the same queries.  Attending several caches
+  branch resume where another left off on the same query rows.  Attending
+  several caches
   is therefore the carry of each branch folded in turn; it equals one pass
   over the concatenated keys.
 * cortiq-engine ``NystromState`` (struct doc, ``new``, ``step_group``): per
