@@ -155,3 +155,140 @@ def test_sweep(c):
     check_out(out.cpu().numpy(), want, max(vmax, 1e-30), w.dtype, _id(c))
     check_carry(cout.m.cpu().numpy(), cout.l.cpu().numpy(), cw.m, cw.l,
                 w.dtype, _id(c) + " carry")
+
+
+MFMA_WIDTHS = {"bf16": WIDTHS["bf16"], "fp8": WIDTHS["fp8"],
+               "f32": [(64, 64), (128, 128), (192, 128)]}
+
+
+def _multi_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        dt = str(rng.choice(["bf16", "bf16", "fp8", "f32"]))
+        dk, dv = MFMA_WIDTHS[dt][rng.integers(len(MFMA_WIDTHS[dt]))]
+        hkv = int(rng.choice([1, 2, 4]))
+        hpk = int(rng.choice([1, 2, 3, 4, 8, 16]))
+        B = int(rng.integers(1, 5))
+        cases.append(dict(i=i, dt=dt, dk=dk, dv=dv, hkv=hkv, hq=hkv * hpk,
+                          B=B, rng=int(rng.integers(1 << 30))))
+    return cases
+
+
+def _draw(c, T, lens, idx):
+    w = wl.DecodeWorkload(f"sweep{idx}", batch=c["B"], num_q_heads=c["hq"],
+                          num_kv_heads=c["hkv"], dk=c["dk"], dv=c["dv"],
+                          max_len=T, dtype=c["dt"], seed_index=idx)
+    return w, (wl.make_fp8_inputs(w, lens_override=lens) if c["dt"] == "fp8"
+               else wl.make_inputs(w, lens_override=lens))
+
+
+def _dev_cache(g, x, fp8):
+    if fp8:
+        return (g.Fp8Cache(x["k"].cuda(), x["k_scale"].cuda()),
+                g.Fp8Cache(x["v"].cuda(), x["v_scale"].cuda()))
+    return x["k"].cuda(), x["v"].cuda()
+
+
+def _values(x, fp8):
+    """The cache as the oracle attends it: fp64 values (fp8 decoded)."""
+    if fp8:
+        return (of8.dequantize_cache(x["k"].numpy(),
+                                     x["k_scale"].double().numpy()),
+                of8.dequantize_cache(x["v"].numpy(),
+                                     x["v_scale"].double().numpy()))
+    return np64(x["k"]), np64(x["v"])
+
+
+def _live_vmax(v, lens):
+    m = 0.0
+    for b in range(v.shape[0]):
+        n = int(min(max(int(lens[b]), 0), v.shape[1]))
+        if n:
+            m = max(m, float(np.abs(v[b, :n]).max()))
+    return m
+
+
+@pytest.mark.parametrize("c", _multi_cases(40, 2028),
+                         ids=lambda c: f"{c['i']}-{c['dt']}-d{c['dk']}x{c['dv']}"
+                                       f"-h{c['hq']}/{c['hkv']}-b{c['B']}")
+def test_sweep_branches(c):
+    """attend_branches over 1..4 caches of random lengths (one with a bias
+    now and then) and a carry_in, against the oracle's fold of the branches."""
+    import gqa_kv_cache_decode_amd as g
+    import oracle.streaming as ost
+    rng = np.random.default_rng(c["rng"])
+    fp8 = c["dt"] == "fp8"
+    nbr = int(rng.integers(1, 5))
+    dev_br, np_br, vmax = [], [], 0.0
+    for j in range(nbr):
+        T = int(rng.choice([1, 40, 130, 700, 2500]))
+        lens = [int(rng.integers(-1, T + 3)) for _ in range(c["B"])]
+        w, x = _draw(c, T, lens, 500 + 10 * c["i"] + j)
+        k, v = _dev_cache(g, x, fp8)
+        kv, vv = _values(x, fp8)
+        bias = None
+        if rng.random() < 0.3:
+            bias = torch.randn(c["B"], (T + 3) // 4 * 4,
+                               generator=torch.Generator().manual_seed(j))
+        dev_br.append((k, v, x["lens"].cuda(),
+                       None if bias is None else bias.cuda()))
+        np_br.append((kv, vv, x["lens"].numpy(),
+                      None if bias is None else bias[:, :T].double().numpy()))
+        vmax = max(vmax, _live_vmax(vv, x["lens"].numpy()))
+        q = x["q"]          # every draw gives a q of the same shape; keep the last
+    say(f"[sweep branches] {c['dt']} {nbr} branches "
+        f"T={[b[0].shape[1] if not fp8 else b[0].codes.shape[1] for b in dev_br]}")
+    rows = c["B"] * c["hq"]
+    cin = cin_np = None
+    if rng.random() < 0.5:
+        gen = torch.Generator().manual_seed(c["i"])
+        m = torch.randn(rows, generator=gen)
+        l = torch.rand(rows, generator=gen) + 0.5
+        l[::4] = 0.0
+        acc = torch.randn(rows, c["dv"], generator=gen)
+        cin = g.Carry(m.cuda(), l.cuda(), acc.cuda())
+        cin_np = oracle.Carry(m.double().numpy(), l.double().numpy(),
+                              acc.double().numpy())
+        vmax = max(vmax, float(np.max(np.abs(oracle.finalize(cin_np)))))
+    cout = g.empty_carry(rows, c["dv"])
+    out = g.attend_branches(q.cuda(), dev_br, 0.0, carry_in=cin,
+                            carry_out=cout)
+    torch.cuda.synchronize()
+    want, cw = ost.attend_branches(np64(q), np_br, 0.0, carry_in=cin_np)
+    what = f"branches {c['i']}"
+    check_out(out.cpu().numpy(), want, max(vmax, 1e-30), c["dt"], what)
+    check_carry(cout.m.cpu().numpy(), cout.l.cpu().numpy(), cw.m, cw.l,
+                c["dt"], what + " carry")
+
+
+@pytest.mark.parametrize("c", _multi_cases(40, 2029),
+                         ids=lambda c: f"{c['i']}-{c['dt']}-d{c['dk']}x{c['dv']}"
+                                       f"-h{c['hq']}/{c['hkv']}-b{c['B']}")
+def test_sweep_gathered(c):
+    """attend_gathered with random index rows (duplicates, INVALID and
+    out-of-range entries, empty rows) against the oracle's selection."""
+    import gqa_kv_cache_decode_amd as g
+    import oracle.streaming as ost
+    rng = np.random.default_rng(c["rng"])
+    fp8 = c["dt"] == "fp8"
+    T = int(rng.choice([1, 50, 300, 3000]))
+    lens = [int(rng.integers(-1, T + 3)) for _ in range(c["B"])]
+    w, x = _draw(c, T, lens, 700 + c["i"])
+    width = int(rng.choice([1, 7, 64, 500, 2100]))
+    idx = rng.integers(-3, T + 5, (c["B"], width)).astype(np.int32)
+    if width > 4:
+        idx[:, 1] = idx[:, 0]                   # a duplicate in every row
+    if c["B"] > 1 and rng.random() < 0.3:
+        idx[1] = -1                             # a row selecting nothing
+    k, v = _dev_cache(g, x, fp8)
+    say(f"[sweep gathered] {c['dt']} T={T} width={width}")
+    out = g.attend_gathered(x["q"].cuda(), k, v, x["lens"].cuda(),
+                            torch.from_numpy(idx).cuda(), 0.0)
+    torch.cuda.synchronize()
+    kv, vv = _values(x, fp8)
+    want, _ = ost.attend_gathered(np64(x["q"]), kv, vv, x["lens"].numpy(),
+                                  idx, 0.0)
+    check_out(out.cpu().numpy(), want,
+              max(_live_vmax(vv, x["lens"].numpy()), 1e-30), c["dt"],
+              f"gathered {c['i']}")
