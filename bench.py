@@ -494,7 +494,7 @@ def kernel_name(w, bias, gather):
     tf = lambda b: "true" if b else "false"
     flags = f"false, {tf(bias)}, {tf(gather)}"
     if w.dtype == "f32":
-        return f"partition_f32_mfma_kernel<{w.dk}, {w.dv}, 2, {flags}>"
+        return f"partition_f32_mfma_kernel<{w.dk}, {w.dv}, 4, {flags}>"
     if w.dtype == "fp8":
         waves = 8 if w.dk + w.dv <= 128 else 4
     else:
