@@ -7,7 +7,7 @@ closed forms (equal keys give the plain mean; a dominant key returns its own
 value row), a library routine (torch's fp64 ``scaled_dot_product_attention`` on
 repeat-copied heads), exact 50-digit evaluation of the softmax definition
 without a max shift, the carry algebra (any split merged equals one pass), the
-page's own recovery-trial reference, and special cases.
+a planted key's exact weight, and special cases.
 """
 
 from __future__ import annotations
@@ -103,56 +103,60 @@ def pin_dominant_key(orc):
             _close(c.l[b * Hq + h], 1.0, 1e-14, "partition of dominant key")
 
 
-def pin_recovery_trial(orc):
-    """The recovery trial of the cortiq-engine page: the exact answer's
-    channel 0 is the planted key's softmax weight; the page's reference
-    computes it from f32 logits and f64 exponentials.  An exact method gives
-    got[0] / want0 = 1."""
-    spec = json.loads((GOLDEN / "recovery_trial.json").read_text())
-    fixed, ours = spec["what_the_page_fixes"], spec["our_choices"]
-    d, dv, w, m = fixed["d"], fixed["dv"], ours["w"], ours["m"]
-    tol = ours["ratio_tolerance"]
-    for case in ours["cases"]:
-        amp, depth = case["amp"], case["depth"]
+def pin_planted_key(orc):
+    """A planted key along the query returns its value row (cortiq-engine,
+    NystromState page, example o1_recovery: a key pushed along the unit
+    query with channel 0 of the values zero everywhere else).
+
+    With V[j][0] = 0 for j != p and V[p][0] = 1, channel 0 of the exact
+    output is the planted key's softmax weight
+        w_p = 1 / sum_j exp(s_j - s_p),   s_j = <q, k_j> / sqrt(d),
+    evaluated here at 50 digits from the stored float64 values (every
+    float64 converts to a Decimal exactly), independently of the oracle.
+    The other channels are the same weights applied to the background value
+    rows.  Raising the amplitude must raise w_p towards 1 (recovery)."""
+    spec = json.loads((GOLDEN / "planted_key.json").read_text())
+    d, dv, n = spec["d"], spec["dv"], spec["n"]
+    for case in spec["cases"]:
         rng = np.random.default_rng(case["seed"])
-        unif = lambda n: rng.uniform(-1.0, 1.0, n).astype(np.float32)
-        t = 8 * m + w + depth
-
-        def unit():
-            u = unif(d)
-            return u / np.float32(np.sqrt(np.sum(u * u, dtype=np.float32)))
-
-        q_hat = unit()
-        rd = np.float32(np.sqrt(np.float32(d)))
-        q = q_hat * rd
-        ks = unif(t * d).reshape(t, d) * np.float32(1.732)
-        vs = unif(t * dv).reshape(t, dv)
-        vs[:, 0] = 0.0
-        p = t - depth
-        ks[p] += np.float32(amp) * q_hat
-        vs[p, 0] = 1.0
-        k_new = unif(d) * np.float32(1.732)
-        v_new = unif(dv)
-        v_new[0] = 0.0
-        # the page's exact reference: f32 logits, their max, f64 exp sums
-        keys = np.vstack([ks, k_new[None]])
-        vals = np.vstack([vs, v_new[None]])
-        logits = [np.float32(np.sum(q * keys[j], dtype=np.float32)) / rd
-                  for j in range(t + 1)]
-        mx = max(logits)
-        den = num0 = 0.0
-        for j, lg in enumerate(logits):
-            e = math.exp(float(np.float32(lg - mx)))
-            den += e
-            num0 += e * float(vals[j, 0])
-        want0 = num0 / den
-        assert abs(want0) >= 1e-4, "trial case too weak to measure"
-        out, _ = orc.attend(q[None, None].astype(np.float64),
-                            keys[None, :, None].astype(np.float64),
-                            vals[None, :, None].astype(np.float64),
-                            [t + 1], scale=1.0 / math.sqrt(d))
-        ratio = out[0, 0, 0] / want0
-        assert abs(ratio - 1.0) <= tol, f"recovery ratio {ratio} ({case})"
+        u = rng.uniform(-1.0, 1.0, d)
+        q_hat = u / np.linalg.norm(u)
+        q = math.sqrt(d) * q_hat
+        keys = spec["key_spread"] * rng.uniform(-1.0, 1.0, (n, d))
+        vals = rng.uniform(-1.0, 1.0, (n, dv))
+        vals[:, 0] = 0.0
+        p = n - case["depth"]
+        weights = []
+        for amp in case["amps"]:
+            k = keys.copy()
+            v = vals.copy()
+            k[p] += amp * q_hat
+            v[p, 0] = 1.0
+            out, c = orc.attend(q[None, None], k[None, :, None],
+                                v[None, :, None], [n], scale=0.0)
+            with localcontext() as ctx:
+                ctx.prec = 50
+                rs = Decimal(d).sqrt()
+                s = [sum(Decimal(float(q[i])) * Decimal(float(k[j, i]))
+                         for i in range(d)) / rs for j in range(n)]
+                e = [(sj - s[p]).exp() for sj in s]
+                den = sum(e)
+                want = [float(sum(e[j] * Decimal(float(v[j, ch]))
+                                  for j in range(n)) / den)
+                        for ch in range(dv)]
+                w_p = float(1 / den)
+            assert abs(want[0] - w_p) <= 1e-15
+            _close(out[0, 0, 0], w_p, 1e-13 * max(w_p, 1e-300),
+                   f"planted weight amp={amp} depth={case['depth']}")
+            _close(out[0, 0], np.array(want), 1e-13,
+                   f"planted output amp={amp}")
+            # m is the largest logit: the planted one once it leads
+            if w_p > 0.5:
+                _close(c.m[0], float(s[p]), 1e-12, "m at the planted key")
+            weights.append(w_p)
+        assert all(a < b for a, b in zip(weights, weights[1:])), \
+            f"weight must grow with the amplitude: {weights}"
+        assert weights[-1] > 0.99, "a large amplitude recovers the key"
 
 
 # --- library routine ------------------------------------------------------
@@ -342,7 +346,7 @@ def pin_kv_append(orc):
             "full cache untouched"
 
 
-ALL_PINS = [pin_equal_keys, pin_dominant_key, pin_recovery_trial,
+ALL_PINS = [pin_equal_keys, pin_dominant_key, pin_planted_key,
             pin_gqa_is_repeated_mha, pin_brute_force, pin_split_merge,
             pin_special_cases, pin_kv_append]
 
