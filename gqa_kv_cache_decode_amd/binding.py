@@ -82,6 +82,7 @@ _SIGNATURES = {
                                    _CARRY_P, _CARRY_P, _P, _P,
                                    ctypes.c_size_t, _P]),
     "gqa_abi_version": (_I32, []),
+    "gqa_profile_next_launch": (_I32, [_P, _P]),
     "gqa_status_string": (ctypes.c_char_p, [_I32]),
     "gqa_kv_append": (_I32, [_CACHE_P, _P, _P, _P, _P, _P, _P]),
     "gqa_attend_plan": (_I32, [_CACHE_P, _I32, _I32, _PLAN_P]),
@@ -582,3 +583,11 @@ def attend_gathered(q, k_cache, v_cache, lens, idx, scale: float = 0.0,
         "attend_gathered")
     return out
 
+
+def profile_next_launch(start: int, stop: int) -> None:
+    """gqa_profile_next_launch: the next partition kernel this thread
+    enqueues is bracketed by the two hipEvent_t handles (raw ints; 0, 0
+    cancels)."""
+    _check(library().gqa_profile_next_launch(_P(start or None),
+                                             _P(stop or None)),
+           "profile_next_launch")

@@ -204,23 +204,46 @@ void set_storage(PartitionArgs *a, const gqa_cache *c) {
   a->v_scale = fp8 ? c->v_scale : nullptr;
 }
 
+// The calling host thread's pending profiling request
+// (gqa_profile_next_launch): events to record around its next partition
+// launch.
+thread_local hipEvent_t t_prof_start = nullptr;
+thread_local hipEvent_t t_prof_stop = nullptr;
+
+// Enqueues one partition (or decode-step) kernel, bracketed by the pending
+// profiling events if there are any (the request is consumed here).
+template <class Launch>
+hipError_t profiled(hipStream_t s, Launch launch) {
+  hipEvent_t e0 = t_prof_start, e1 = t_prof_stop;
+  if (!e0) return launch();
+  t_prof_start = t_prof_stop = nullptr;
+  hipError_t e = hipEventRecord(e0, s);
+  if (e != hipSuccess) return e;
+  if ((e = launch()) != hipSuccess) return e;
+  return hipEventRecord(e1, s);
+}
+
 // The partition (or whole decode step) kernel family of the cache's dtype.
 hipError_t launch_partition(const gqa_cache *c, const PartitionArgs &a,
                             const gqa::StepParams &ep, hipStream_t s) {
-  switch (c->dtype) {
-    case GQA_DTYPE_BF16: return gqa::launch_partition_bf16(a, ep, s);
-    case GQA_DTYPE_FP8_E4M3: return gqa::launch_partition_fp8(a, ep, s);
-    default: return gqa::launch_partition_f32(a, ep, s);
-  }
+  return profiled(s, [&] {
+    switch (c->dtype) {
+      case GQA_DTYPE_BF16: return gqa::launch_partition_bf16(a, ep, s);
+      case GQA_DTYPE_FP8_E4M3: return gqa::launch_partition_fp8(a, ep, s);
+      default: return gqa::launch_partition_f32(a, ep, s);
+    }
+  });
 }
 
 hipError_t launch_step(const gqa_cache *c, const PartitionArgs &a,
                        const gqa::StepParams &sp, hipStream_t s) {
-  switch (c->dtype) {
-    case GQA_DTYPE_BF16: return gqa::launch_step_bf16(a, sp, s);
-    case GQA_DTYPE_FP8_E4M3: return gqa::launch_step_fp8(a, sp, s);
-    default: return gqa::launch_step_f32(a, sp, s);
-  }
+  return profiled(s, [&] {
+    switch (c->dtype) {
+      case GQA_DTYPE_BF16: return gqa::launch_step_bf16(a, sp, s);
+      case GQA_DTYPE_FP8_E4M3: return gqa::launch_step_fp8(a, sp, s);
+      default: return gqa::launch_step_f32(a, sp, s);
+    }
+  });
 }
 
 // The partial layout and work items of a one-cache launch.
@@ -237,14 +260,17 @@ void single_branch(PartitionArgs *a) {
 // Enqueues the schedule kernel of a scheduled plan and points the partition
 // launch at its table (a no-op for an unscheduled plan).
 gqa_status schedule_checked(const gqa_cache *c, const gqa_plan &plan,
-                            const int32_t *lens, bool step, void *ws,
-                            PartitionArgs *a, hipStream_t s) {
+                            const int32_t *lens, bool step, int32_t *lens_out,
+                            int32_t *dropped, void *ws, PartitionArgs *a,
+                            hipStream_t s) {
   a->sched = nullptr;
   a->sched_len = 0;
   if (plan.sched_entries == 0) return GQA_OK;
   gqa::ScheduleArgs sa;
   sa.lens = lens;
   sa.step = step ? 1 : 0;
+  sa.lens_out = lens_out;
+  sa.dropped = dropped;
   sa.batch = c->batch;
   sa.max_len = c->max_len;
   sa.num_kv_heads = c->num_kv_heads;
@@ -306,7 +332,8 @@ gqa_status partition_checked(const void *q, int32_t hq, const gqa_cache *c,
   a.part_m = reinterpret_cast<float *>(base);
   a.part_l = reinterpret_cast<float *>(base + plan->off_l);
   a.part_acc = reinterpret_cast<float *>(base + plan->off_acc);
-  gqa_status st = schedule_checked(c, *plan, lens, false, ws, &a, s);
+  gqa_status st =
+      schedule_checked(c, *plan, lens, false, nullptr, nullptr, ws, &a, s);
   if (st != GQA_OK) return st;
   return device_status(launch_partition(c, a, ep, s));
 }
@@ -607,6 +634,13 @@ gqa_status plan_gathered(const gqa_cache *c, int32_t hq, int32_t width,
 extern "C" {
 
 int32_t gqa_abi_version(void) { return GQA_ABI_VERSION; }
+
+gqa_status gqa_profile_next_launch(hipEvent_t start, hipEvent_t stop) {
+  if ((start == nullptr) != (stop == nullptr)) return GQA_ERR_INVALID_ARGUMENT;
+  t_prof_start = start;
+  t_prof_stop = stop;
+  return GQA_OK;
+}
 
 const char *gqa_status_string(int32_t status) {
   switch (status) {
@@ -1001,8 +1035,8 @@ gqa_status gqa_decode_step(const void *q, int32_t num_q_heads,
   a.part_l = reinterpret_cast<float *>(base + plan.off_l);
   a.part_acc = reinterpret_cast<float *>(base + plan.off_acc);
 
-  if ((st = schedule_checked(cache, plan, lens_in, true, workspace, &a,
-                             stream)) != GQA_OK)
+  if ((st = schedule_checked(cache, plan, lens_in, true, lens_out, dropped,
+                             workspace, &a, stream)) != GQA_OK)
     return st;
   gqa::StepParams sp = final_epilogue(cache, plan, carry_in, carry_out, out);
   sp.k_new = k_new;

@@ -2,7 +2,9 @@
 //  - a pure 16-byte-vector nontemporal read stream, the practical HBM read
 //    ceiling the decode kernels are compared with;
 //  - a plain copy of known size, whose hardware-counter readings calibrate the
-//    fetch/write byte counters.
+//    fetch/write byte counters;
+//  - a bounded spin kernel, and timing events for the decode library's
+//    per-launch profiling request.
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -62,6 +64,29 @@ __attribute__((visibility("default"))) int gqa_bench_spin(int microseconds,
   return hipGetLastError() == hipSuccess ? 0 : 5;
 }
 
+
+// Creates `n` timing events into `ev` (handles as 64-bit words).
+__attribute__((visibility("default"))) int gqa_bench_events_create(
+    int n, hipEvent_t *ev) {
+  if (n <= 0 || !ev) return 1;
+  for (int i = 0; i < n; ++i)
+    if (hipEventCreate(&ev[i]) != hipSuccess) return 5;
+  return 0;
+}
+
+__attribute__((visibility("default"))) int gqa_bench_events_destroy(
+    int n, hipEvent_t *ev) {
+  for (int i = 0; i < n; ++i)
+    if (ev[i] && hipEventDestroy(ev[i]) != hipSuccess) return 5;
+  return 0;
+}
+
+// Milliseconds between two recorded events (waits for the second).
+__attribute__((visibility("default"))) int gqa_bench_events_elapsed(
+    hipEvent_t a, hipEvent_t b, float *ms) {
+  if (hipEventSynchronize(b) != hipSuccess) return 5;
+  return hipEventElapsedTime(ms, a, b) == hipSuccess ? 0 : 5;
+}
 
 // Reads `bytes` (a multiple of 16) from `src`; `sink` needs `blocks` words.
 __attribute__((visibility("default"))) int gqa_bench_read_stream(

@@ -81,6 +81,10 @@ struct PartitionArgs {
 struct ScheduleArgs {
   const int32_t *lens;  // [B]
   int step;             // lengths are decode-step inputs (the new token counts)
+  // decode step: the per-sequence bookkeeping, done here for every sequence
+  // (a sequence with nothing to attend has no work item to do it)
+  int32_t *lens_out;    // [B]
+  int32_t *dropped;     // [1] or NULL
   int batch, max_len, num_kv_heads, chunk_tokens, num_chunks;
   int32_t *table;       // [table_len]
   int table_len;

@@ -74,7 +74,8 @@ __global__ __launch_bounds__(NW * 64) void partition_f32_mfma_kernel(
   const bool stepping = STEP && branch == a.append_branch;
   const SeqLen sl = seq_len(a, sp, b, stepping);
   const int n = sl.n;
-  if (stepping && g == 0 && c == 0 && threadIdx.x == 0) step_bookkeeping(sp, b, sl);
+  if (stepping && !a.sched && g == 0 && c == 0 && threadIdx.x == 0)
+    step_bookkeeping(sp, b, sl);  // (a scheduled launch's schedule kernel does it)
   const int t0 = c * a.chunk_tokens;
   if (t0 >= n && !(c == 0 && (sp.direct || (STEP && sp.fuse)))) return;
   const int t1 = min(t0 + a.chunk_tokens, n);

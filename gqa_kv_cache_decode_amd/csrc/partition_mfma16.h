@@ -122,7 +122,8 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
   const bool stepping = STEP && branch == a.append_branch;
   const SeqLen sl = seq_len(a, sp, b, stepping);
   const int n = sl.n;
-  if (stepping && g == 0 && c == 0 && threadIdx.x == 0) step_bookkeeping(sp, b, sl);
+  if (stepping && !a.sched && g == 0 && c == 0 && threadIdx.x == 0)
+    step_bookkeeping(sp, b, sl);  // (a scheduled launch's schedule kernel does it)
   const int t0 = c * a.chunk_tokens;
   // A work-group with nothing live exits, except the first of an empty
   // sequence when final results are written in this launch: it still writes

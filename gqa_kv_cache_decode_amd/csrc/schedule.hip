@@ -21,7 +21,9 @@
 //     end of its list (those blocks exit at once).
 //
 // Items are (b * num_kv_heads + g) * num_chunks + c, the partition kernel's
-// own numbering.  Sequences with no live token contribute nothing: with a
+// own numbering.  For a decode step this kernel also writes every sequence's
+// new length and counts the drops (the partition kernels leave that to it
+// when a schedule is present).  Sequences with no live token contribute nothing: with a
 // schedule the partition writes partials only, and the combine kernel covers
 // empty rows.
 #include "device_common.h"
@@ -54,8 +56,12 @@ __global__ __launch_bounds__(kScheduleThreads) void schedule_kernel(
     int n;
     if (a.step) {  // decode step: the new token is attended when appended
       const int n_old = a.lens[b];
-      n = (n_old >= 0 && n_old < a.max_len) ? n_old + 1
-                                            : clamp_len(n_old, a.max_len);
+      const bool fresh = n_old >= 0 && n_old < a.max_len;
+      n = fresh ? n_old + 1 : clamp_len(n_old, a.max_len);
+      // needle-core push_kv: the length grows by one, or a full cache (or a
+      // negative length) is left as it is and the drop counted
+      a.lens_out[b] = fresh ? n_old + 1 : n_old;
+      if (!fresh && a.dropped) atomicAdd(a.dropped, 1);
     } else {
       n = clamp_len(a.lens[b], a.max_len);
     }

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define GQA_ABI_VERSION 3
+#define GQA_ABI_VERSION 4
 
 /* Only the entry points below are exported from the shared library. */
 #define GQA_API __attribute__((visibility("default")))
@@ -157,6 +157,23 @@ GQA_API int32_t gqa_abi_version(void);
 
 /* Static, NUL-terminated name of a status code. */
 GQA_API const char *gqa_status_string(int32_t status);
+
+/*
+ * Profiling aid (not a step of the method): the next call made on the
+ * calling host thread that enqueues a partition kernel — the kernel that
+ * streams the cache, launched by gqa_attend_decode, gqa_attend_partition,
+ * gqa_decode_step, gqa_attend_branches, gqa_decode_step_branches and
+ * gqa_attend_gathered — records `start` on its stream immediately before
+ * that kernel and `stop` immediately after it, so that
+ * hipEventElapsedTime(start, stop) is that one kernel's time on the device,
+ * without the calls' other kernels (schedule, selection, combine).
+ *   start, stop  events owned by the caller, created with timing enabled;
+ *                both NULL cancels a pending request.
+ * The request is consumed by that one launch; a call whose argument checks
+ * fail enqueues nothing and leaves it pending.  GQA_ERR_INVALID_ARGUMENT if
+ * exactly one of the two is NULL.  No HIP call is made here.
+ */
+GQA_API gqa_status gqa_profile_next_launch(hipEvent_t start, hipEvent_t stop);
 
 /*
  * kv_append — needle-core KvCache::push_kv, batched.

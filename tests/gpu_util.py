@@ -69,13 +69,23 @@ def oracle_rows(x: dict, w: wl.DecodeWorkload, rows_bg, carry_in=None,
     return res
 
 
+def rel_l2(got: np.ndarray, want: np.ndarray) -> float:
+    """Relative L2 error ||got - want|| / ||want|| over all the rows given
+    (the cortiq-engine recovery example's background-error diagnostic); 0
+    when both are zero."""
+    num = float(np.linalg.norm(np.asarray(got, np.float64) - want))
+    den = float(np.linalg.norm(want))
+    return num / den if den > 0 else num
+
+
 def check_out(got: np.ndarray, want: np.ndarray, vmax: float, dtype: str,
               what: str) -> float:
     assert np.all(np.isfinite(got)), f"{what}: non-finite GPU output"
     err = float(np.max(np.abs(got - want))) if got.size else 0.0
     bound = TOL[dtype] * max(vmax, 1e-30)
     say(f"  {what}: max|err| = {err:.3e}  (bound {bound:.3e}, "
-        f"{err / max(vmax, 1e-30):.2e} * max|V|)")
+        f"{err / max(vmax, 1e-30):.2e} * max|V|), rel L2 "
+        f"{rel_l2(got, want):.2e}")
     assert err <= bound, f"{what}: max|err| {err:.3e} > {bound:.3e}"
     return err
 

@@ -30,14 +30,14 @@ def _declared():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     for n in names:
         assert hasattr(lib, n), f"missing export {n}"
     assert set(names) == set(bd._SIGNATURES), "binding covers the header"
 
 
 def test_version_and_status_strings(lib):
-    assert lib.gqa_abi_version() == 3
+    assert lib.gqa_abi_version() == 4
     names = [lib.gqa_status_string(i).decode() for i in range(7)]
     assert names == ["GQA_OK", "GQA_ERR_INVALID_ARGUMENT",
                      "GQA_ERR_SHAPE_MISMATCH", "GQA_ERR_UNSUPPORTED",
@@ -361,3 +361,13 @@ def test_fp8_checks(lib):
     # a branch of another dtype
     arr = (bd._Branch * 2)(_branch(c8), _branch(_cache()))
     assert lib.gqa_attend_branches_workspace_bytes(arr, 2, 32) == 0
+
+
+def test_profile_request_validation(lib):
+    """One event without the other is rejected; setting and cancelling a
+    request makes no HIP call."""
+    P = ctypes.c_void_p
+    assert lib.gqa_profile_next_launch(P(0x1000), None) == INVALID
+    assert lib.gqa_profile_next_launch(None, P(0x1000)) == INVALID
+    assert lib.gqa_profile_next_launch(P(0x1000), P(0x2000)) == OK
+    assert lib.gqa_profile_next_launch(None, None) == OK

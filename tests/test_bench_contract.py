@@ -1,8 +1,9 @@
 """bench.py's host-side contract, without a GPU: more than one GPU is refused
-with a message, the byte counts behind `value` and `roofline.achieved` are
-the algorithmic ones, the recorded HBM traffic is only reported for the
-kernel sources it was measured on, and the kernel it names as dominant is
-the one the committed counter readings were taken on."""
+with a message, the default run covers the five workloads with the ragged
+batch as the headline, the byte counts behind `value` and
+`roofline.achieved` are the algorithmic ones, the recorded HBM traffic is
+only reported for the kernel sources (and the kernel) it was measured on,
+and the host phase's oracle units are the decode step's exact inputs."""
 
 import json
 import re
@@ -80,8 +81,75 @@ def test_dominant_kernel_name(profile):
     counter readings of that workload were taken on."""
     rec = json.loads((ROOT / "profiles" / f"traffic_{profile}.json").read_text())
     bias = profile.endswith("_bias")
-    w = bench.workload_by_name(profile[:-len("_bias")] if bias else profile)
-    assert bench.kernel_name(w, bias, False) == rec["kernel"]
+    name = profile[:-len("_bias")] if bias else profile
+    case = bench.CASES[name].__new__(bench.CASES[name])
+    case.w, case.bias = bench.workload_by_name(name), bias
+    assert case.kernel() == rec["kernel"]
+
+
+def test_default_run_is_the_five_workloads():
+    args = bench.parse_args([])
+    assert args.workload == "all"
+    assert bench.DEFAULT_SET == ["tiny", "batched", "ragged", "long", "spike"]
+    assert bench.HEADLINE == "ragged"
+    names = [bench.workload_by_name(n).name for n in bench.DEFAULT_SET]
+    assert names == [w.name for w in wl.WORKLOADS]
+
+
+def _post_append(x, kn, vn):
+    """The cache the decode step attends: the new token at slot lens - 1."""
+    k, v = x["k"].clone(), x["v"].clone()
+    for b, n in enumerate(x["lens"].tolist()):
+        k[b, n - 1] = kn[b]
+        v[b, n - 1] = vn[b]
+    return k, v
+
+
+@pytest.mark.parametrize("name", ["tiny", "batched"])
+def test_host_oracle_units_are_the_step(name, monkeypatch):
+    """The forked oracle workers evaluate every (sequence, KV group) unit of
+    the step's inputs (the cache with the new token at its slot), and the
+    output check scores a perfect answer as zero error."""
+    import numpy as np
+    import oracle
+    args = bench.parse_args(["--workload", name])
+    case = bench.CASES[name](name, args)
+    if name == "batched":   # keep the test small: two sequences
+        w = case.w.replace(batch=2, max_len=300)
+        monkeypatch.setattr(bench, "workload_by_name", lambda n: w)
+        case = bench.CASES[name](name, args)
+    res = bench.run_oracle(case, 2, 0.5)
+    assert len(res["outs"]) == len(case.units)
+    k, v = _post_append(case.x, case.k_new, case.v_new)
+    f64 = lambda t: t.float().numpy().astype(np.float64)
+    ref, _ = oracle.attend(f64(case.x["q"]), f64(k), f64(v),
+                           case.x["lens"].numpy(), case.w.scale)
+    for (b, g), (o, vmax) in res["outs"].items():
+        h = case.w.hpk
+        assert np.array_equal(o, ref[b, g * h:(g + 1) * h])
+    chk = bench.check_outputs(case, ref.astype(np.float32), res["outs"])
+    assert chk["units_checked"] == len(case.units)
+    assert chk["within_tolerance"] and chk["rel_l2"] < 1e-6
+    bad = ref.astype(np.float32).copy()
+    bad[0, 0, 0] += 1.0
+    assert not bench.check_outputs(case, bad, res["outs"])["within_tolerance"]
+
+
+def test_step_byte_accounting():
+    """A step moves the attended K/V once per KV group (the cached part from
+    the cache, the new token's rows read and written once each), q, the
+    lengths and the fp32 output."""
+    args = bench.parse_args(["--workload", "batched"])
+    case = bench.SingleCase.__new__(bench.SingleCase)
+    case.w, case.bias = wl.BATCHED_BF16, False
+    import numpy as np
+    case.lens = np.full(16, 4096)
+    w = case.w
+    kv = 16 * 4095 * 8 * 256 * 2
+    new = 16 * 8 * 256 * (2 + 2)
+    q = 16 * 32 * 128 * 2
+    out = 16 * 32 * 128 * 4
+    assert case.step_bytes() == kv + new + q + 2 * 16 * 4 + out
 
 
 def test_source_hash_ignores_comments_only():

@@ -1,8 +1,8 @@
-"""The five workloads at full size, in the launch configuration the benchmark
-times (the library's own split-K plan), against the oracle: every row where
-the oracle is quick, sampled (sequence, KV group) units elsewhere, plus
-properties that hold at any size on every row (finite outputs, each output a
-convex combination of value rows, 1 <= l <= n for the carry)."""
+"""The five workloads at full size, with the library's own split-K plan,
+against the oracle on every (sequence, KV group) unit, plus properties that
+hold at any size on every row (finite outputs, each output a convex
+combination of value rows, 1 <= l <= n for the carry).  The ragged
+workload's scheduled launch also has its block -> item table checked."""
 
 import numpy as np
 import pytest
@@ -11,6 +11,7 @@ import torch
 import oracle
 from gpu_util import (check_carry, check_out, live_vmax, np64, oracle_rows,
                       say, to_dev)
+from test_gpu_schedule import _check_table
 from gqa_kv_cache_decode_amd import workloads as wl
 
 pytestmark = pytest.mark.gpu
@@ -85,20 +86,28 @@ def test_full_batched_bf16():
 
 
 def test_full_ragged_bf16():
+    """Every (sequence, KV group) unit of the ragged batch, through the
+    partition / combine pair with the library's scheduled plan, whose
+    device-built block -> item table is checked too."""
+    g = _gqa()
     w = wl.RAGGED_BF16
     say("[full] ragged: drawing 8 GiB of K/V")
     x = wl.make_inputs(w)
     d = to_dev(x)
-    got, c = _run(w, d)
-    del d
+    plan = g.attend_plan(d["k"], d["v"], w.num_q_heads)
+    ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device="cuda")
+    g.attend_partition(d["q"], d["k"], d["v"], d["lens"], plan, ws, w.scale)
+    c = g.empty_carry(w.batch * w.num_q_heads, w.dv)
+    out = g.attend_combine(w.num_q_heads, d["k"], d["v"], d["lens"], plan, ws,
+                           carry_out=c)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    _check_table(ws, plan, x["lens"], w)
+    del d, ws
     torch.cuda.empty_cache()
-    lens = x["lens"].numpy()
-    rng = np.random.default_rng(3)
-    bs = sorted(set(rng.choice(w.batch, 10, replace=False).tolist() +
-                    [int(lens.argmax()), int(lens.argmin())]))
-    units = [(b, int(rng.integers(w.num_kv_heads))) for b in bs]
-    say(f"[full] ragged: oracle on units {units}")
-    _check_units(w, x, got, c, units, "ragged bf16, sampled units")
+    units = [(b, g_) for b in range(w.batch) for g_ in range(w.num_kv_heads)]
+    say(f"[full] ragged: oracle on all {len(units)} units")
+    _check_units(w, x, got, c, units, "ragged bf16, every unit")
     _properties(w, x, got, c, "ragged bf16")
 
 
@@ -134,9 +143,8 @@ def test_full_wide_spike():
     say("[full] spike: drawing inputs")
     x = wl.make_inputs(w)
     got, c = _run(w, to_dev(x))
-    rng = np.random.default_rng(5)
-    units = [(b, int(rng.integers(w.num_kv_heads))) for b in range(w.batch)]
-    ref = _check_units(w, x, got, c, units, "spike bf16, sampled units")
+    units = [(b, g) for b in range(w.batch) for g in range(w.num_kv_heads)]
+    ref = _check_units(w, x, got, c, units, "spike bf16, every unit")
     _properties(w, x, got, c, "spike bf16")
     ratios = []
     for (b, h), (o, _, _, _) in ref.items():

@@ -4,7 +4,7 @@ attends the whole cache, the new token included) by the step launch itself,
 then split-K partials and the combine (the library's own plan).  Checked
 against the oracle (needle-core push_kv then attend): the cache written bit
 for bit, the lengths, and the output and carry on every (sequence, KV group)
-unit where the oracle is quick, on sampled units elsewhere.  The long-context
+unit.  The long-context
 step is decode_step_branches over the main cache and the window, the new
 token entering the window, against one oracle pass over the concatenated
 keys."""
@@ -111,9 +111,27 @@ def test_full_step_batched_bf16(with_bias):
                 "bf16", "batched step + bias carry")
 
 
+def test_full_step_ragged():
+    """bench.py's headline step: the ragged batch (64 sequences of 1..32768
+    keys, NaN padding past each length), scheduled, the new token at slot
+    lens - 1; the whole cache bit for bit and every unit."""
+    w = wl.RAGGED_BF16
+    say("[full step] ragged: drawing 8 GiB of K/V")
+    x = wl.make_inputs(w)
+    kn, vn = _new_rows(w, w.seed + 1000, torch.bfloat16)
+    d, got, cout, slots = _step(w, x, kn, vn)
+    assert slots == (x["lens"] - 1).tolist()
+    x["k"], x["v"] = _appended(x, kn, vn, slots)
+    _check_cache(d["k"], d["v"], x["k"], x["v"], "ragged step")
+    del d
+    torch.cuda.empty_cache()
+    units = [(b, g) for b in range(w.batch) for g in range(w.num_kv_heads)]
+    _check_rows(w, x, got, cout, units, "ragged step, every unit")
+
+
 def test_full_step_wide_spike():
     """The spike shape (dk 192, 16 heads per KV group, 64K keys, every cache
-    full but the new slot): one sampled KV group per sequence."""
+    full but the new slot): every unit."""
     w = wl.WIDE_SPIKE_BF16
     say("[full step] spike: drawing inputs")
     x = wl.make_inputs(w)
@@ -129,9 +147,8 @@ def test_full_step_wide_spike():
                        x["k"][:, :slots[0]].view(torch.int16)), "K untouched"
     del d
     x["k"], x["v"] = _appended(x, kn, vn, slots)
-    rng = np.random.default_rng(7)
-    units = [(b, int(rng.integers(w.num_kv_heads))) for b in range(w.batch)]
-    _check_rows(w, x, got, cout, units, "spike step, sampled units")
+    units = [(b, g) for b in range(w.batch) for g in range(w.num_kv_heads)]
+    _check_rows(w, x, got, cout, units, "spike step, every unit")
 
 
 def test_full_step_fp8():

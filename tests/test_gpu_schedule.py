@@ -97,6 +97,7 @@ def test_scheduled_decode_step():
     lens = _lens(w.batch, w.max_len, 32)
     lens[5] = w.max_len - 1   # the append fills the cache
     lens[6] = 4095            # the new token opens the second chunk
+    lens[7] = -2              # negative: nothing appended, drop counted
     x = wl.make_inputs(w, lens_override=lens.clamp(0, w.max_len).tolist(),
                        pad_value=0.0)
     d = to_dev(x)
@@ -111,16 +112,20 @@ def test_scheduled_decode_step():
     lo = torch.empty_like(li)
     ws = g.step_workspace(d["k"], d["v"], w.num_q_heads)
     cout = g.empty_carry(w.batch * w.num_q_heads, w.dv)
+    lo.fill_(12345)           # every entry must be written by the step
+    dropped = torch.zeros(1, dtype=torch.int32, device="cuda")
     out = g.decode_step(d["q"], d["k"], d["v"], kn.cuda(), vn.cuda(), li, lo,
-                        w.scale, carry_out=cout, workspace=ws)
+                        w.scale, carry_out=cout, workspace=ws,
+                        dropped=dropped)
     torch.cuda.synchronize()
     bits = lambda t: t.view(torch.int16)
-    k_ref, v_ref, l_ref, _ = oracle.kv_append(
+    k_ref, v_ref, l_ref, n_drop = oracle.kv_append(
         bits(x["k"]).numpy(), bits(x["v"]).numpy(), bits(kn).numpy(),
         bits(vn).numpy(), lens.numpy())
     assert np.array_equal(bits(d["k"].cpu()).numpy(), k_ref), "K after append"
     assert np.array_equal(bits(d["v"].cpu()).numpy(), v_ref), "V after append"
     assert lo.cpu().numpy().tolist() == l_ref.tolist(), "lens"
+    assert int(dropped.item()) == n_drop == 3, "drops: full, past, negative"
     _check_table(ws, plan, torch.from_numpy(l_ref.astype(np.int32)), w)
     xa = {"q": x["q"], "k": torch.from_numpy(k_ref).view(w.torch_dtype),
           "v": torch.from_numpy(v_ref).view(w.torch_dtype),
