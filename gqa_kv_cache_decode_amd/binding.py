@@ -20,6 +20,8 @@ LIB_PATH = Path(__file__).resolve().with_name("libgqa_decode.so")
 
 DTYPE_CODES = {torch.float32: 0, torch.bfloat16: 1}
 FP8_E4M3 = 2                       # gqa_dtype of an Fp8Cache
+CHUNK_BALANCED = -1                # GQA_CHUNK_BALANCED: attend_plan asks for
+                                   # a balanced plan
 FP8_STORAGE = (torch.uint8, torch.float8_e4m3fn)
 
 
@@ -51,7 +53,8 @@ class Plan(ctypes.Structure):
     _fields_ = [("chunk_tokens", ctypes.c_int32), ("num_chunks", ctypes.c_int32),
                 ("off_l", ctypes.c_size_t), ("off_acc", ctypes.c_size_t),
                 ("off_sched", ctypes.c_size_t), ("sched_entries", ctypes.c_int32),
-                ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace_bytes", ctypes.c_size_t),
+                ("balanced_groups", ctypes.c_int32), ("off_own", ctypes.c_size_t)]
 
 
 _lib = None

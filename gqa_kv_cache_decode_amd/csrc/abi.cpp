@@ -3,6 +3,7 @@
 // synchronises, and no HIP call happens before the checks pass.
 #include "gqa_decode.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <limits>
@@ -41,6 +42,12 @@ constexpr int64_t kScheduleMinItems = 1024;
 constexpr int32_t kScheduledMaxChunk = 2048;
 constexpr int64_t kScheduleMaxSeqs = 8192;
 constexpr int64_t kScheduleMaxChunks = 4096;
+// Such a launch over a bf16 / fp8 cache with the library's own chunking is
+// balanced instead: kBalancedGroups work-groups (two per CU of the MI355X's
+// 256), all resident at once, each streaming an equal contiguous range of
+// the units' 32-token tiles, so no ragged last round is left.
+constexpr int kNumCUs = 256;
+constexpr int kBalancedGroups = 2 * kNumCUs;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -133,11 +140,47 @@ int32_t auto_chunk(const gqa_cache *c) {
   return chunk;
 }
 
+// The layout of a balanced plan (false when the shape does not allow one):
+// 2 * kBalancedGroups piece slots of hpk rows (part_m / part_l / part_acc),
+// one whole-unit state per query row (own_m / own_l / own_acc, for calls
+// that write no final results), and the balance kernel's tile prefix
+// (batch + 1 int32 at off_sched).
+bool balanced_plan(const gqa_cache *c, int32_t hq, gqa_plan *p) {
+  const int64_t tiles = ((int64_t)c->max_len + gqa::kBalanceTile - 1) /
+                        gqa::kBalanceTile;
+  // tile indices are int32; a whole unit is addressed with 32-bit offsets
+  const int64_t span = (int64_t)c->max_len * c->num_kv_heads *
+                       (c->dk > c->dv ? c->dk : c->dv) * esize(c->dtype);
+  const int64_t units = (int64_t)c->batch * c->num_kv_heads;
+  if (units * tiles > std::numeric_limits<int32_t>::max() ||
+      units * 2 * kBalancedGroups > std::numeric_limits<int32_t>::max() ||
+      span >= ((int64_t)1 << 31))
+    return false;
+  const size_t hpk = hq / c->num_kv_heads;
+  const size_t rows = (size_t)c->batch * hq;
+  const size_t ml = 2 * (size_t)kBalancedGroups * hpk * sizeof(float);
+  p->chunk_tokens = gqa::kBalanceTile;
+  p->num_chunks = 2 * kBalancedGroups;
+  p->off_l = align_up(ml);
+  p->off_acc = p->off_l + align_up(ml);
+  p->off_own = p->off_acc + align_up(ml * c->dv);
+  const size_t own_ml = align_up(rows * sizeof(float));
+  p->off_sched = p->off_own + 2 * own_ml + align_up(rows * c->dv * sizeof(float));
+  p->sched_entries = c->batch + 1;
+  p->workspace_bytes = p->off_sched + align_up((size_t)p->sched_entries * sizeof(int32_t));
+  p->balanced_groups = kBalancedGroups;
+  return true;
+}
+
 gqa_status make_plan(const gqa_cache *c, int32_t hq, int32_t chunk_tokens,
                      gqa_plan *p) {
   gqa_status st = check_cache_dims(c);
   if (st != GQA_OK) return st;
   if ((st = check_heads(c, hq)) != GQA_OK) return st;
+  if (chunk_tokens == GQA_CHUNK_BALANCED) {  // requested explicitly
+    if (c->dtype == GQA_DTYPE_F32) return GQA_ERR_UNSUPPORTED;
+    return balanced_plan(c, hq, p) ? GQA_OK : GQA_ERR_UNSUPPORTED;
+  }
   if (chunk_tokens < 0 || chunk_tokens % kChunkQuantum != 0)
     return GQA_ERR_INVALID_ARGUMENT;
   const int32_t chunk = chunk_tokens ? chunk_tokens : auto_chunk(c);
@@ -162,9 +205,15 @@ gqa_status make_plan(const gqa_cache *c, int32_t hq, int32_t chunk_tokens,
   // mean, so 8 * (ceil(groups / 8) + num_kv_heads * nchunk) entries suffice.
   p->off_sched = 0;
   p->sched_entries = 0;
+  p->balanced_groups = 0;
+  p->off_own = 0;
+  const bool multi_round = nchunk > 1 && groups >= kScheduleMinItems &&
+                           uses_mfma(c) && c->batch <= kScheduleMaxSeqs;
+  if (multi_round && chunk_tokens == 0 && c->dtype != GQA_DTYPE_F32 &&
+      balanced_plan(c, hq, p))
+    return GQA_OK;
   const int64_t entries = 8 * ((groups + 7) / 8 + c->num_kv_heads * nchunk);
-  if (nchunk > 1 && groups >= kScheduleMinItems && uses_mfma(c) &&
-      c->batch <= kScheduleMaxSeqs && nchunk <= kScheduleMaxChunks &&
+  if (multi_round && nchunk <= kScheduleMaxChunks &&
       entries <= std::numeric_limits<int32_t>::max()) {
     p->off_sched = p->workspace_bytes;
     p->sched_entries = (int32_t)entries;
@@ -178,12 +227,17 @@ gqa_status check_plan(const gqa_cache *c, int32_t hq, const gqa_plan *plan,
                       size_t ws_bytes, const void *ws) {
   if (!plan) return GQA_ERR_INVALID_ARGUMENT;
   gqa_plan want;
-  gqa_status st = make_plan(c, hq, plan->chunk_tokens, &want);
+  gqa_status st = make_plan(
+      c, hq, plan->balanced_groups ? GQA_CHUNK_BALANCED : plan->chunk_tokens,
+      &want);
   if (st != GQA_OK) return st;
-  if (plan->chunk_tokens == 0 || want.num_chunks != plan->num_chunks ||
+  if (plan->chunk_tokens == 0 || want.chunk_tokens != plan->chunk_tokens ||
+      want.num_chunks != plan->num_chunks ||
       want.off_l != plan->off_l || want.off_acc != plan->off_acc ||
       want.off_sched != plan->off_sched ||
       want.sched_entries != plan->sched_entries ||
+      want.balanced_groups != plan->balanced_groups ||
+      want.off_own != plan->off_own ||
       want.workspace_bytes != plan->workspace_bytes)
     return GQA_ERR_SHAPE_MISMATCH;
   if (!ws) return GQA_ERR_INVALID_ARGUMENT;
@@ -265,6 +319,9 @@ gqa_status schedule_checked(const gqa_cache *c, const gqa_plan &plan,
                             hipStream_t s) {
   a->sched = nullptr;
   a->sched_len = 0;
+  a->pre = nullptr;
+  a->balanced = 0;
+  a->own_m = a->own_l = a->own_acc = nullptr;
   if (plan.sched_entries == 0) return GQA_OK;
   gqa::ScheduleArgs sa;
   sa.lens = lens;
@@ -278,6 +335,20 @@ gqa_status schedule_checked(const gqa_cache *c, const gqa_plan &plan,
   sa.num_chunks = plan.num_chunks;
   sa.table = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + plan.off_sched);
   sa.table_len = plan.sched_entries;
+  if (plan.balanced_groups) {  // the tile prefix, then one range per group
+    gqa_status st = device_status(gqa::launch_balance(sa, s));
+    if (st != GQA_OK) return st;
+    char *base = static_cast<char *>(ws);
+    const size_t rows = (size_t)c->batch * a->num_kv_heads * a->hpk;
+    a->pre = sa.table;
+    a->balanced = plan.balanced_groups;
+    a->own_m = reinterpret_cast<float *>(base + plan.off_own);
+    a->own_l = reinterpret_cast<float *>(base + plan.off_own +
+                                         align_up(rows * sizeof(float)));
+    a->own_acc = reinterpret_cast<float *>(base + plan.off_own +
+                                           2 * align_up(rows * sizeof(float)));
+    return GQA_OK;
+  }
   gqa_status st = device_status(gqa::launch_schedule(sa, s));
   if (st != GQA_OK) return st;
   a->sched = sa.table;
@@ -298,8 +369,14 @@ gqa::StepParams final_epilogue(const gqa_cache *c, const gqa_plan &plan,
   ep.out_l = cout ? cout->l : nullptr;
   ep.out_acc = cout ? cout->acc : nullptr;
   ep.out = out;
-  ep.direct = plan.num_chunks == 1 && uses_mfma(c) ? 1 : 0;
+  // a single chunk, or a balanced plan's units seen whole by one work-group
+  ep.direct = (plan.num_chunks == 1 && uses_mfma(c)) || plan.balanced_groups ? 1 : 0;
   return ep;
+}
+
+// Whether the partition launch leaves no fold to a combine launch.
+bool finished_in_partition(const gqa_plan &plan, const gqa::StepParams &ep) {
+  return ep.direct && !plan.balanced_groups;
 }
 
 gqa_status partition_checked(const void *q, int32_t hq, const gqa_cache *c,
@@ -341,8 +418,23 @@ gqa_status partition_checked(const void *q, int32_t hq, const gqa_cache *c,
 gqa_status combine_checked(int32_t hq, const gqa_cache *c, const int32_t *lens,
                            const gqa_plan *plan, const void *ws,
                            const gqa_carry *cin, const gqa_carry *cout,
-                           float *out, hipStream_t s) {
+                           float *out, hipStream_t s, bool owned_final = false) {
   CombineArgs a;
+  a.balanced = plan->balanced_groups;
+  a.hpk = hq / c->num_kv_heads;
+  a.owned_final = owned_final ? 1 : 0;
+  a.pre = nullptr;
+  a.own_m = a.own_l = a.own_acc = nullptr;
+  if (a.balanced) {
+    const char *b = static_cast<const char *>(ws);
+    const size_t rows = (size_t)c->batch * hq;
+    a.pre = reinterpret_cast<const int32_t *>(b + plan->off_sched);
+    a.own_m = reinterpret_cast<const float *>(b + plan->off_own);
+    a.own_l = reinterpret_cast<const float *>(b + plan->off_own +
+                                              align_up(rows * sizeof(float)));
+    a.own_acc = reinterpret_cast<const float *>(
+        b + plan->off_own + 2 * align_up(rows * sizeof(float)));
+  }
   a.batch = c->batch;
   a.num_q_heads = hq;
   a.dv = c->dv;
@@ -436,8 +528,8 @@ gqa_status plan_branches(const gqa_branch *br, int32_t n, int32_t hq,
       return GQA_ERR_SHAPE_MISMATCH;
     if ((st = check_heads(c, hq)) != GQA_OK) return st;
     if (!uses_mfma(c)) return GQA_ERR_UNSUPPORTED;
-    gqa_plan one;
-    if ((st = make_plan(c, hq, 0, &one)) != GQA_OK) return st;
+    gqa_plan one;  // (the library's chunking, never a balanced plan)
+    if ((st = make_plan(c, hq, auto_chunk(c), &one)) != GQA_OK) return st;
     p->chunk[i] = one.chunk_tokens;
     p->num_chunks[i] = one.num_chunks;
     p->col_base[i] = (int32_t)cols;
@@ -617,10 +709,10 @@ gqa_status plan_gathered(const gqa_cache *c, int32_t hq, int32_t width,
   g->sel_cap = width < c->max_len ? width : c->max_len;
   g->vcache = *c;
   g->vcache.max_len = g->sel_cap;
-  if ((st = make_plan(&g->vcache, hq, 0, &g->plan)) != GQA_OK) return st;
-  if (g->plan.chunk_tokens > gqa::kGatherChunk &&
-      (st = make_plan(&g->vcache, hq, gqa::kGatherChunk, &g->plan)) != GQA_OK)
-    return st;
+  // the library's chunking (never a balanced plan), chunks of at most
+  // kGatherChunk slots
+  const int32_t chunk = std::min(auto_chunk(&g->vcache), gqa::kGatherChunk);
+  if ((st = make_plan(&g->vcache, hq, chunk, &g->plan)) != GQA_OK) return st;
   g->off_sel = g->plan.workspace_bytes;
   g->off_count =
       g->off_sel + align_up((size_t)c->batch * g->sel_cap * sizeof(int32_t));
@@ -824,9 +916,9 @@ gqa_status gqa_attend_decode(const void *q, int32_t num_q_heads,
       final_epilogue(cache, plan, carry_in, carry_out, out);
   st = partition_checked(q, num_q_heads, cache, lens, scale, bias, bias_stride,
                          &plan, workspace, ep, stream);
-  if (st != GQA_OK || ep.direct) return st;
+  if (st != GQA_OK || finished_in_partition(plan, ep)) return st;
   return combine_checked(num_q_heads, cache, lens, &plan, workspace, carry_in,
-                         carry_out, out, stream);
+                         carry_out, out, stream, ep.direct != 0);
 }
 
 gqa_status gqa_softmax_state_merge(const gqa_carry *a, const gqa_carry *b,
@@ -1047,9 +1139,9 @@ gqa_status gqa_decode_step(const void *q, int32_t num_q_heads,
   sp.counters = reinterpret_cast<int *>(base + plan.workspace_bytes);
   sp.fuse = !sp.direct && step_fuses(cache, num_q_heads, plan) ? 1 : 0;
   st = device_status(launch_step(cache, a, sp, stream));
-  if (st != GQA_OK || sp.fuse || sp.direct) return st;
+  if (st != GQA_OK || sp.fuse || finished_in_partition(plan, sp)) return st;
   return combine_checked(num_q_heads, cache, lens_out, &plan, workspace,
-                         carry_in, carry_out, out, stream);
+                         carry_in, carry_out, out, stream, sp.direct != 0);
 }
 
 }  // extern "C"

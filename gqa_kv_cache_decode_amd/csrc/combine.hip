@@ -97,6 +97,63 @@ __global__ __launch_bounds__(THREADS) void combine_kernel(CombineArgs a) {
   }
 }
 
+// Balanced plans: one work-group per query row, one thread per value column.
+// The row's unit (sequence b, KV group g) covers tiles [u0, u1) of the
+// concatenation; ranges r0 = range(u0) .. r1 = range(u1 - 1) saw it.  One
+// range: the unit's state is final already (owned_final) or in own_*; more:
+// the first range left its piece in slot 2 * r0 + 1, each later one in slot
+// 2 * r.  The pieces and carry_in fold by log-sum-exp merge.
+__global__ __launch_bounds__(256) void combine_balanced_kernel(CombineArgs a) {
+  const int row = blockIdx.x;
+  const int d = threadIdx.x;
+  const int Hq = a.num_q_heads, hpk = a.hpk, Hkv = Hq / hpk;
+  const int b = row / Hq, h = row % Hq, g = h / hpk, hh = h % hpk;
+  const int P = a.balanced, total = a.pre[a.batch];
+  const int pb = a.pre[b];
+  const int nt = (a.pre[b + 1] - pb) / Hkv;
+  int r0 = 0, r1 = -1;  // no pieces
+  bool own = false;
+  if (nt > 0) {
+    const int u0 = pb + g * nt;
+    r0 = range_of_tile(u0, P, total);
+    r1 = range_of_tile(u0 + nt - 1, P, total);
+    if (r0 == r1) {
+      if (a.owned_final) return;
+      own = true;
+    }
+  }
+  if (d >= a.dv) return;
+  float m = -INFINITY, L = 0.0f, acc = 0.0f;  // base-2 running state
+  auto fold = [&](float mi, float li, float ai) {
+    // a piece whose keys were all removed by the bias has m = -inf, l = 0
+    const float mn = fmaxf(m, mi), ref = exp_ref(mn);
+    const float fo = fast_exp2(m - ref), fi = fast_exp2(mi - ref);
+    acc = acc * fo + ai * fi;
+    L = L * fo + li * fi;
+    m = mn;
+  };
+  if (own) {
+    fold(a.own_m[row] * kLog2e, a.own_l[row], a.own_acc[(size_t)row * a.dv + d]);
+  } else {
+    for (int r = r0; r <= r1; ++r) {
+      const size_t pr = (2 * (size_t)r + (r == r0 ? 1 : 0)) * hpk + hh;
+      fold(a.part_m[pr] * kLog2e, a.part_l[pr], a.part_acc[pr * a.dv + d]);
+    }
+  }
+  const float in_l = a.in_l ? a.in_l[row] : 0.0f;
+  if (in_l > 0.0f)
+    fold(a.in_m[row] * kLog2e, in_l, a.in_acc[(size_t)row * a.dv + d]);
+  const bool live = L > 0.0f;
+  if (a.out) a.out[(size_t)row * a.dv + d] = live ? acc / L : 0.0f;
+  if (a.out_acc) {
+    a.out_acc[(size_t)row * a.dv + d] = live ? acc : 0.0f;
+    if (d == 0) {
+      a.out_m[row] = live ? m * kLn2 : -INFINITY;
+      a.out_l[row] = live ? L : 0.0f;
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const size_t row = blockIdx.x;
   const float la = a.a_l[row], lb = a.b_l[row];
@@ -126,6 +183,12 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s) {
   const int rows = a.batch * a.num_q_heads;
+  if (a.balanced) {
+    if (a.dv > 256 || a.num_branches != 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(combine_balanced_kernel, dim3(rows),
+                       dim3((a.dv + 63) / 64 * 64), 0, s, a);
+    return hipGetLastError();
+  }
   if (a.total_cols >= 32)
     hipLaunchKernelGGL(combine_kernel<1024>, dim3(rows), dim3(1024), 0, s, a);
   else

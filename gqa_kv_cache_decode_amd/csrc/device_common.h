@@ -114,6 +114,12 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+__device__ __forceinline__ int wave_sum_int(int x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
 // Makes this wavefront's own LDS writes visible to its other lanes and keeps
 // the compiler from moving LDS accesses across the point.  Only valid for LDS
 // regions private to one wavefront.
@@ -136,6 +142,19 @@ __device__ __forceinline__ int clamp_len(int n, int max_len) {
 __device__ __forceinline__ int xcd_local_item(int i, int n) {
   const int per = n >> 3;
   return (i < (per << 3)) ? (i & 7) * per + (i >> 3) : i;
+}
+
+// Balanced launches: block i (on XCD i % 8) takes range (i % 8) * (P / 8) +
+// i / 8 of the P equal ranges (P a multiple of 8), so each XCD streams one
+// contiguous eighth of the work.  Range r covers tiles
+// [floor(r * total / P), floor((r + 1) * total / P)).
+__device__ __forceinline__ int balanced_range(int i, int P) {
+  return (i & 7) * (P >> 3) + (i >> 3);
+}
+
+// The range holding tile x: the largest r with floor(r * total / P) <= x.
+__device__ __forceinline__ int range_of_tile(int x, int P, int total) {
+  return (int)(((int64_t)(x + 1) * P - 1) / total);
 }
 
 }  // namespace gqa

@@ -75,9 +75,20 @@ struct PartitionArgs {
   // fixed map; sched_len entries, one per block.
   const int32_t *sched;
   int sched_len;
+  // Balanced launch (balanced > 0 work-groups, partition_balanced_kernel):
+  // pre[b] is the first 32-token tile of sequence b's units, pre[batch] the
+  // total (balance kernel).  part_* then hold 2 * balanced piece slots of
+  // hpk rows; a unit one work-group saw whole writes its final results when
+  // the epilogue is direct, else its state (natural-log m) into own_*
+  // [rows] / [rows][dv].
+  const int32_t *pre = nullptr;
+  int balanced = 0;
+  float *own_m = nullptr, *own_l = nullptr, *own_acc = nullptr;
 };
 
-// Inputs of the schedule kernel (one work-group).
+// Inputs of the schedule kernel and of the balance kernel (one work-group
+// each; the balance kernel writes its tile prefix `pre` [batch + 1] into
+// `table`).
 struct ScheduleArgs {
   const int32_t *lens;  // [B]
   int step;             // lengths are decode-step inputs (the new token counts)
@@ -121,6 +132,13 @@ struct CombineArgs {
   int num_branches;
   CombineBranch br[1 + kMaxExtraBranches];
   const float *part_m, *part_l, *part_acc;
+  // Balanced plan (balanced > 0 work-groups): the pieces of units cut by a
+  // range end are folded per query row; a unit one work-group saw whole is
+  // skipped when `owned_final` (its results are written) or folded from
+  // own_* otherwise.  pre: the balance kernel's tile prefix.
+  int balanced = 0, hpk = 0, owned_final = 0;
+  const int32_t *pre = nullptr;
+  const float *own_m = nullptr, *own_l = nullptr, *own_acc = nullptr;
   const float *in_m, *in_l, *in_acc;   // carry_in, all NULL if absent
   float *out_m, *out_l, *out_acc;      // carry_out, all NULL if absent
   float *out;                          // [rows][dv] or NULL
@@ -210,6 +228,9 @@ hipError_t launch_step_f32(const PartitionArgs &a, const StepParams &sp,
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
 size_t schedule_lds_bytes(int batch, int num_chunks);
 hipError_t launch_schedule(const ScheduleArgs &a, hipStream_t s);
+// The tile prefix of a balanced plan (and a decode step's bookkeeping).
+hipError_t launch_balance(const ScheduleArgs &a, hipStream_t s);
+constexpr int kBalanceTile = 32;  // tokens per tile of a balanced plan
 hipError_t launch_merge(const MergeArgs &a, hipStream_t s);
 hipError_t launch_append(const AppendArgs &a, hipStream_t s);
 hipError_t launch_stream_append(const StreamAppendArgs &a, hipStream_t s);

@@ -86,54 +86,25 @@ constexpr int partition_lds_bytes() {
   return tiles > merge ? tiles : merge;
 }
 
+// One segment of one (sequence b, KV group g): cache tokens [t0, t1) streamed
+// tile by tile by the work-group's wavefronts (wavefront w takes tiles w,
+// w + NW, ...), plus, when `has_new`, the decode step's new token (stored
+// into slot n_old and folded in from k_new / v_new).  Every wavefront's state
+// (base-2 m, partition, acc^T) is left in the LDS merge area for the
+// epilogue (`merged_state`), after a work-group barrier; with `stage_in` the
+// group's carry_in m / l are staged in s_in before that barrier.  Returns
+// whether the segment saw any key.
 template <int DK, int DV, int NW, bool STEP, bool BIAS, bool GATHER, bool FP8>
-__global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
-    PartitionArgs args, StepParams sp) {
+__device__ __forceinline__ bool stream_segment(const PartitionArgs &a,
+                                               const StepParams &sp, int b,
+                                               int g, int t0, int t1,
+                                               bool has_new, int n_old,
+                                               bool stage_in,
+                                               unsigned char *lds,
+                                               int *s_slot, float *s_in) {
   using G = Mfma16Geom<DK, DV, FP8>;
   constexpr int ES = G::kEsize;
-  constexpr int PP = G::kPerPiece;
-  constexpr int kLdsBytes = partition_lds_bytes<DK, DV, NW, FP8>();
-  __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
-  __shared__ int s_flag;
-  __shared__ float s_in[32];  // carry_in m, l of the group's rows (direct)
-  __shared__ int s_slot[GATHER ? kGatherChunk : 1];  // gathered cache slots
-
-  PartitionArgs a = args;
-  int item, branch = 0;
-  if (a.sched) {  // scheduled launch: the table entry, or nothing to do
-    item = a.sched[blockIdx.x];
-    if (item < 0) return;
-  } else {
-    // the block's branch (multi-branch launch: each branch owns a block
-    // range starting at a multiple of 8), then its item within the branch
-    item = blockIdx.x;
-    branch = select_branch(a, item);
-    const int nitems = a.batch * a.num_kv_heads * a.num_chunks;
-    if (item >= nitems) return;  // padding up to the next branch
-    item = xcd_local_item(item, nitems);
-  }
-  const int Hkv = a.num_kv_heads, hpk = a.hpk, nchunk = a.num_chunks;
-  const int c = item % nchunk;
-  const int bg = item / nchunk;
-  const int g = bg % Hkv;
-  const int b = bg / Hkv;
-
-  // decode step: this branch takes the new token (the others attend as is)
-  const bool stepping = STEP && branch == a.append_branch;
-  const SeqLen sl = seq_len(a, sp, b, stepping);
-  const int n = sl.n;
-  if (stepping && !a.sched && g == 0 && c == 0 && threadIdx.x == 0)
-    step_bookkeeping(sp, b, sl);  // (a scheduled launch's schedule kernel does it)
-  const int t0 = c * a.chunk_tokens;
-  // A work-group with nothing live exits, except the first of an empty
-  // sequence when final results are written in this launch: it still writes
-  // the group's outputs.
-  if (t0 >= n && !(c == 0 && (sp.direct || (STEP && sp.fuse)))) return;
-  // Decode step: the work-group whose chunk holds the new slot (always the
-  // chunk's last live token) reads only the cache tokens before it in its
-  // tile loop and folds the new token in from k_new / v_new afterwards.
-  const bool has_new = stepping && sl.fresh && sl.n_old / a.chunk_tokens == c;
-  const int t1 = has_new ? sl.n_old : min(t0 + a.chunk_tokens, n);  // tiles: [t0, t1)
+  const int Hkv = a.num_kv_heads, hpk = a.hpk;
   const int ntiles = t1 > t0 ? (t1 - t0 + kTileTokens - 1) / kTileTokens : 0;
 
   const int lane = threadIdx.x & 63;
@@ -184,28 +155,28 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
   const float kinv = FP8 && STEP ? e4m3_inv_scale(kscale) : 1.0f;
   const float vinv = FP8 && STEP ? e4m3_inv_scale(vscale) : 1.0f;
 
-  // STEP: the work-group whose chunk holds the new slot stores the token's
+  // STEP: the work-group whose segment holds the new slot stores the token's
   // rows of this group into the cache.  The stores are not waited for: later
   // calls read the slot, while this call takes the rows from k_new/v_new.
   const uint16_t *knew = nullptr, *vnew = nullptr;
-  if (has_new) {
+  if (STEP && has_new) {
     knew = static_cast<const uint16_t *>(sp.k_new) + ((size_t)b * Hkv + g) * DK;
     vnew = static_cast<const uint16_t *>(sp.v_new) + ((size_t)b * Hkv + g) * DV;
     if (FP8)
-      store_group_row_e4m3(knew, reinterpret_cast<u32x4 *>(Kg + (size_t)sl.n_old * kTok),
+      store_group_row_e4m3(knew, reinterpret_cast<u32x4 *>(Kg + (size_t)n_old * kTok),
                            DK / 16, kinv, vnew,
-                           reinterpret_cast<u32x4 *>(Vg + (size_t)sl.n_old * vTok),
+                           reinterpret_cast<u32x4 *>(Vg + (size_t)n_old * vTok),
                            DV / 16, vinv);
     else
       store_group_row(reinterpret_cast<const u32x4 *>(knew),
-                      reinterpret_cast<u32x4 *>(Kg + (size_t)sl.n_old * kTok), DK / 8,
+                      reinterpret_cast<u32x4 *>(Kg + (size_t)n_old * kTok), DK / 8,
                       reinterpret_cast<const u32x4 *>(vnew),
-                      reinterpret_cast<u32x4 *>(Vg + (size_t)sl.n_old * vTok), DV / 8);
+                      reinterpret_cast<u32x4 *>(Vg + (size_t)n_old * vTok), DV / 8);
   }
 
   // K/V are read exactly once per call, so the loads are nontemporal: they
   // stream through without displacing cached lines.  Tokens of a tile past
-  // the chunk's last live token load that last token again (a finite row
+  // the segment's last live token load that last token again (a finite row
   // whose logit is masked, so its weight is exactly 0): no branches, and no
   // slot at or past the length is ever read.
   const int last = max(t1 - t0 - 1, 0);  // last live token, relative to t0
@@ -224,8 +195,8 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
       s_slot[e] = a.sel[(size_t)b * a.max_len + t0 + e];
     __syncthreads();
   }
-  // The additive bias of the chunk's live tokens (needle-core attn_bias: one
-  // term per position, shared by the heads); loads past the view return 0.
+  // The additive bias of the segment's live tokens (needle-core attn_bias:
+  // one term per position, shared by the heads); loads past the view return 0.
   const __amdgpu_buffer_rsrc_t bview =
       BIAS && a.bias ? buffer_view(a.bias + (size_t)b * a.bias_stride + t0,
                          (uint32_t)((t1 - t0) * 4))
@@ -391,7 +362,7 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
       for (int j = 0; j < 8; ++j) dot += (float)qf[s][j] * (float)kv[j];
     }
     float sn = rows_sum(dot) * scale_log2;
-    if (BIAS && a.bias) sn += a.bias[(size_t)b * a.bias_stride + sl.n_old] * kLog2e;
+    if (BIAS && a.bias) sn += a.bias[(size_t)b * a.bias_stride + n_old] * kLog2e;
     const float m_new = fmaxf(m_run, sn);
     const float ref = exp_ref(m_new);
     const float alpha = fast_exp2(m_run - ref);
@@ -423,12 +394,12 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
   // Partition of head hl over the whole wavefront.
   const float l_tot = rows_sum(l_run);
 
-  // Merge the wavefronts' states through LDS and write one partial per head.
+  // Each wavefront's state into the merge area (the tile slices are free).
   __syncthreads();
   float *wm = reinterpret_cast<float *>(lds);
   float *wl = wm + NW * 16;
   float *wacc = wl + NW * 16;
-  const bool live = ntiles > 0 || has_new;  // the work-group saw keys
+  const bool live = ntiles > 0 || has_new;  // the segment saw keys
   if (live) {
     if (lane < 16) {
       wm[w * 16 + lane] = m_run;
@@ -440,34 +411,116 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
       for (int i = 0; i < 4; ++i)
         wacc[(w * 16 + hl) * DV + blk * 16 + kg * 4 + i] = o[blk][i];
   }
-  if (sp.direct) stage_carry_in(sp, (size_t)b * Hq + (size_t)g * hpk, hpk, s_in);
+  if (stage_in) stage_carry_in(sp, (size_t)b * Hq + (size_t)g * hpk, hpk, s_in);
   __syncthreads();
+  return live;
+}
 
-  if (live || sp.direct) {
+// The work-group's merged state of head h, column d, from the wavefronts'
+// states `stream_segment` left in the LDS merge area (m in base-2 units;
+// -inf / 0 / 0 when the segment saw no key).
+template <int DV, int NW>
+__device__ __forceinline__ void merged_state(const unsigned char *lds, bool live,
+                                             int h, int d, float &M, float &L,
+                                             float &acc) {
+  const float *wm = reinterpret_cast<const float *>(lds);
+  const float *wl = wm + NW * 16;
+  const float *wacc = wl + NW * 16;
+  M = -INFINITY;
+  acc = 0.0f;
+  L = 0.0f;
+  if (!live) return;
+#pragma unroll
+  for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, wm[ww * 16 + h]);
+  const float ref = exp_ref(M);
+#pragma unroll
+  for (int ww = 0; ww < NW; ++ww) {
+    const float f = fast_exp2(wm[ww * 16 + h] - ref);
+    acc += f * wacc[(ww * 16 + h) * DV + d];
+    L += f * wl[ww * 16 + h];
+  }
+}
+
+// Final results of a group whose keys one work-group saw in full: carry_in
+// (staged in s_in) folded in, then out and carry_out.
+template <int DV, int NW>
+__device__ __forceinline__ void write_group_direct(const StepParams &sp,
+                                                   size_t row0, int hpk,
+                                                   bool live,
+                                                   const unsigned char *lds,
+                                                   const float *s_in) {
+  for (int e = threadIdx.x; e < hpk * DV; e += NW * 64) {
+    const int h = e / DV, d = e % DV;
+    float M, L, acc;
+    merged_state<DV, NW>(lds, live, h, d, M, L, acc);
+    const size_t row = row0 + h;
+    const float l_in = s_in[hpk + h];
+    fold_state(M, L, acc, s_in[h], l_in,
+               l_in > 0.0f ? sp.in_acc[row * DV + d] : 0.0f);
+    write_final(sp, row, DV, d, M, L, acc);
+  }
+}
+
+template <int DK, int DV, int NW, bool STEP, bool BIAS, bool GATHER, bool FP8>
+__global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
+    PartitionArgs args, StepParams sp) {
+  constexpr int kLdsBytes = partition_lds_bytes<DK, DV, NW, FP8>();
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
+  __shared__ int s_flag;
+  __shared__ float s_in[32];  // carry_in m, l of the group's rows (direct)
+  __shared__ int s_slot[GATHER ? kGatherChunk : 1];  // gathered cache slots
+
+  PartitionArgs a = args;
+  int item, branch = 0;
+  if (a.sched) {  // scheduled launch: the table entry, or nothing to do
+    item = a.sched[blockIdx.x];
+    if (item < 0) return;
+  } else {
+    // the block's branch (multi-branch launch: each branch owns a block
+    // range starting at a multiple of 8), then its item within the branch
+    item = blockIdx.x;
+    branch = select_branch(a, item);
+    const int nitems = a.batch * a.num_kv_heads * a.num_chunks;
+    if (item >= nitems) return;  // padding up to the next branch
+    item = xcd_local_item(item, nitems);
+  }
+  const int Hkv = a.num_kv_heads, hpk = a.hpk, nchunk = a.num_chunks;
+  const int c = item % nchunk;
+  const int bg = item / nchunk;
+  const int g = bg % Hkv;
+  const int b = bg / Hkv;
+
+  // decode step: this branch takes the new token (the others attend as is)
+  const bool stepping = STEP && branch == a.append_branch;
+  const SeqLen sl = seq_len(a, sp, b, stepping);
+  const int n = sl.n;
+  if (stepping && !a.sched && g == 0 && c == 0 && threadIdx.x == 0)
+    step_bookkeeping(sp, b, sl);  // (a scheduled launch's schedule kernel does it)
+  const int t0 = c * a.chunk_tokens;
+  // A work-group with nothing live exits, except the first of an empty
+  // sequence when final results are written in this launch: it still writes
+  // the group's outputs.
+  if (t0 >= n && !(c == 0 && (sp.direct || (STEP && sp.fuse)))) return;
+  // Decode step: the work-group whose chunk holds the new slot (always the
+  // chunk's last live token) reads only the cache tokens before it in its
+  // tile loop and folds the new token in from k_new / v_new afterwards.
+  const bool has_new = stepping && sl.fresh && sl.n_old / a.chunk_tokens == c;
+  const int t1 = has_new ? sl.n_old : min(t0 + a.chunk_tokens, n);  // tiles: [t0, t1)
+
+  const bool live = stream_segment<DK, DV, NW, STEP, BIAS, GATHER, FP8>(
+      a, sp, b, g, t0, t1, has_new, sl.n_old, sp.direct != 0, lds, s_slot, s_in);
+
+  const int Hq = Hkv * hpk;
+  const size_t row0 = (size_t)b * Hq + (size_t)g * hpk;
+  if (sp.direct) {  // the only chunk: fold carry_in, write the results
+    write_group_direct<DV, NW>(sp, row0, hpk, live, lds, s_in);
+  } else if (live) {  // one partial per (query row, chunk)
     for (int e = threadIdx.x; e < hpk * DV; e += NW * 64) {
       const int h = e / DV;
       const int d = e % DV;
-      float M = -INFINITY, acc = 0.0f, L = 0.0f;
-      if (live) {
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, wm[ww * 16 + h]);
-        const float ref = exp_ref(M);
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) {
-          const float f = fast_exp2(wm[ww * 16 + h] - ref);
-          acc += f * wacc[(ww * 16 + h) * DV + d];
-          L += f * wl[ww * 16 + h];
-        }
-      }
-      const size_t row = (size_t)b * Hq + (size_t)g * hpk + h;
-      if (sp.direct) {  // the only chunk: fold carry_in, write the results
-        const float l_in = s_in[hpk + h];
-        fold_state(M, L, acc, s_in[h], l_in,
-                   l_in > 0.0f ? sp.in_acc[row * DV + d] : 0.0f);
-        write_final(sp, row, DV, d, M, L, acc);
-        continue;
-      }
-      const size_t col = row * a.total_cols + a.col_base + c;
+      float M, L, acc;
+      merged_state<DV, NW>(lds, live, h, d, M, L, acc);
+      const size_t col = (row0 + h) * a.total_cols + a.col_base + c;
       float *pa = a.part_acc + col * DV + d;
       float *pm = a.part_m + col;
       float *pl = a.part_l + col;
@@ -499,6 +552,108 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
   }
 }
 
+// Balanced launch (a plan with many items over several rounds of
+// work-groups, where fixed chunks leave a ragged last round): the units'
+// 32-token tiles, concatenated in (sequence, KV group) order, are cut into
+// gridDim.x equal contiguous ranges, one per work-group, all resident at
+// once.  a.pre[b] (from the balance kernel) is the first tile of sequence b's
+// units; sequence b's KV group g covers tiles [pre[b] + g * nt_b,
+// pre[b] + (g + 1) * nt_b) with nt_b its tiles per group.  A work-group walks
+// the units its range overlaps: a unit wholly inside the range gets its final
+// results here (carry_in folded, out and carry_out written); a unit cut by
+// the range's ends leaves one piece per work-group that saw it, in piece
+// slot 2 * r (the range's first unit, begun before it) or 2 * r + 1 (its last
+// unit, continuing past it), which the balanced combine folds.  Range r of
+// block i is (i % 8) * (P / 8) + i / 8, so each XCD streams one contiguous
+// eighth of the work.
+template <int DK, int DV, int NW, bool STEP, bool BIAS, bool FP8>
+__global__ __launch_bounds__(NW * 64) void partition_balanced_kernel(
+    PartitionArgs a, StepParams sp) {
+  constexpr int kLdsBytes = partition_lds_bytes<DK, DV, NW, FP8>();
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
+  __shared__ float s_in[32];
+  __shared__ int s_count;
+
+  const int P = gridDim.x;
+  const int r = balanced_range(blockIdx.x, P);
+  const int B = a.batch, Hkv = a.num_kv_heads, hpk = a.hpk;
+  const int total = a.pre[B];
+  const int start = (int)((int64_t)r * total / P);
+  const int end = (int)((int64_t)(r + 1) * total / P);
+  if (start >= end) return;
+
+  // first sequence of the range: the last b with pre[b] <= start (the count
+  // of such entries, minus one; sequences without tiles repeat an entry)
+  if (threadIdx.x == 0) s_count = 0;
+  __syncthreads();
+  int cnt = 0;
+  for (int i = threadIdx.x; i <= B; i += NW * 64) cnt += a.pre[i] <= start;
+  cnt = wave_sum_int(cnt);
+  if ((threadIdx.x & 63) == 0) atomicAdd(&s_count, cnt);
+  __syncthreads();
+  int b = s_count - 1;
+  int pb = a.pre[b], pn = a.pre[b + 1];
+  int g = (start - pb) / ((pn - pb) / Hkv);
+  const int Hq = Hkv * hpk;
+
+  for (int cur = start; cur < end;) {
+    const int nt = (pn - pb) / Hkv;  // tiles per KV group of sequence b
+    const int u0 = pb + g * nt, u1 = u0 + nt;
+    const int s0 = max(u0, start), s1 = min(u1, end);
+    const SeqLen sl = seq_len(a, sp, b, STEP);
+    const int n = sl.n;
+    const int t0 = (s0 - u0) * kTileTokens;
+    const int tend = min((s1 - u0) * kTileTokens, n);
+    // decode step: the segment holding the unit's last tile holds the slot
+    const bool has_new = STEP && sl.fresh && s1 == u1;
+    const int t1 = has_new ? sl.n_old : tend;
+    const bool owned = u0 >= start && u1 <= end;
+    const bool direct = owned && sp.direct;
+    const bool live = stream_segment<DK, DV, NW, STEP, BIAS, false, FP8>(
+        a, sp, b, g, t0, t1, has_new, sl.n_old, direct, lds, nullptr, s_in);
+    const size_t row0 = (size_t)b * Hq + (size_t)g * hpk;
+    if (direct) {
+      write_group_direct<DV, NW>(sp, row0, hpk, live, lds, s_in);
+    } else if (owned) {  // partials-only call: the unit's whole state
+      for (int e = threadIdx.x; e < hpk * DV; e += NW * 64) {
+        const int h = e / DV, d = e % DV;
+        float M, L, acc;
+        merged_state<DV, NW>(lds, live, h, d, M, L, acc);
+        const size_t row = row0 + h;
+        a.own_acc[row * DV + d] = acc;
+        if (d == 0) {
+          a.own_m[row] = M * kLn2;
+          a.own_l[row] = L;
+        }
+      }
+    } else {
+      const size_t slot = 2 * (size_t)r + (u0 < start ? 0 : 1);
+      for (int e = threadIdx.x; e < hpk * DV; e += NW * 64) {
+        const int h = e / DV, d = e % DV;
+        float M, L, acc;
+        merged_state<DV, NW>(lds, live, h, d, M, L, acc);
+        const size_t pr = slot * hpk + h;  // piece row
+        a.part_acc[pr * DV + d] = acc;
+        if (d == 0) {
+          a.part_m[pr] = M * kLn2;
+          a.part_l[pr] = L;
+        }
+      }
+    }
+    cur = s1;
+    if (cur >= end) break;
+    __syncthreads();  // the merge area is reused by the next segment
+    if (++g == Hkv) {  // next sequence with tiles
+      g = 0;
+      do {
+        ++b;
+        pb = pn;
+        pn = a.pre[b + 1];
+      } while (pn == pb);
+    }
+  }
+}
+
 // A scheduled launch runs its work-groups in several rounds.  There the read
 // stream ran fastest with at most two work-groups resident per CU (ragged
 // workload: 749 -> 738 us per launch against up to four by LDS; 771 us with
@@ -515,9 +670,34 @@ int residency_lds_bytes(const PartitionArgs &a) {
   return a.sched && kMain < kThird ? kThird - kMain : 0;
 }
 
+// A balanced launch has exactly kBalancedPerCu work-groups per CU, all
+// resident at once: unused dynamic LDS keeps one more out of a CU, so the
+// ranges spread evenly over the CUs.
+constexpr int kBalancedPerCu = 2;
+
+template <int DK, int DV, int NW, bool FP8>
+constexpr int balanced_lds_bytes() {
+  constexpr int kShare = kCuLdsBytes / (kBalancedPerCu + 1) + 1;
+  constexpr int kMain = partition_lds_bytes<DK, DV, NW, FP8>();
+  return kMain < kShare ? kShare - kMain : 0;
+}
+
 template <int DK, int DV, int NW, bool STEP, bool FP8>
 hipError_t launch_one(const PartitionArgs &a, const StepParams &sp,
                       hipStream_t s) {
+  if (a.balanced) {  // one resident work-group per range, two per CU
+    if (a.sel || a.num_extra || a.sched || (sp.fuse && STEP) ||
+        a.balanced % 8)
+      return hipErrorInvalidValue;
+    const int dyn = balanced_lds_bytes<DK, DV, NW, FP8>();
+    if (a.has_bias)
+      hipLaunchKernelGGL((partition_balanced_kernel<DK, DV, NW, STEP, true, FP8>),
+                         dim3(a.balanced), dim3(NW * 64), dyn, s, a, sp);
+    else
+      hipLaunchKernelGGL((partition_balanced_kernel<DK, DV, NW, STEP, false, FP8>),
+                         dim3(a.balanced), dim3(NW * 64), dyn, s, a, sp);
+    return hipGetLastError();
+  }
   const int nwork = a.sched ? a.sched_len : a.total_items;
   const int dyn = residency_lds_bytes<DK, DV, NW, FP8>(a);
   if (a.sel) {  // index-gathered: attend only, no bias, never scheduled

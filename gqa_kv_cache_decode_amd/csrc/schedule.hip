@@ -139,6 +139,77 @@ size_t schedule_lds_bytes(int batch, int num_chunks) {
   return sizeof(int) * ((size_t)2 * batch + 8 * (size_t)per + num_chunks + 1);
 }
 
+// ---------------------------------------------------------------------------
+// Tile prefix of a balanced plan: pre[b] = num_kv_heads * (sum over b' < b of
+// the 32-token tiles of sequence b'), pre[batch] = the total, so that the
+// partition's work-groups can cut the concatenated tiles of all (sequence,
+// KV group) units into equal ranges.  A decode step's lengths count the new
+// token, and its per-sequence bookkeeping is done here as well.
+namespace {
+
+constexpr int kBalanceThreads = 1024;
+
+__global__ __launch_bounds__(kBalanceThreads) void balance_kernel(
+    ScheduleArgs a) {
+  __shared__ int wave_tot[kBalanceThreads / 64];
+  const int B = a.batch;
+  const int per = (B + kBalanceThreads - 1) / kBalanceThreads;
+  const int b0 = threadIdx.x * per, b1 = min(b0 + per, B);
+  int mine = 0;
+  for (int b = b0; b < b1; ++b) {
+    int n;
+    if (a.step) {
+      const int n_old = a.lens[b];
+      const bool fresh = n_old >= 0 && n_old < a.max_len;
+      n = fresh ? n_old + 1 : clamp_len(n_old, a.max_len);
+      // needle-core push_kv: the length grows by one, or a full cache (or a
+      // negative length) is left as it is and the drop counted
+      a.lens_out[b] = fresh ? n_old + 1 : n_old;
+      if (!fresh && a.dropped) atomicAdd(a.dropped, 1);
+    } else {
+      n = clamp_len(a.lens[b], a.max_len);
+    }
+    mine += (n + kBalanceTile - 1) / kBalanceTile;
+  }
+  // exclusive prefix of the threads' counts across the work-group
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int inc = mine;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(inc, off, 64);
+    if (lane >= off) inc += y;
+  }
+  if (lane == 63) wave_tot[wave] = inc;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += wave_tot[w];
+  int run = base + inc - mine;
+  for (int b = b0; b < b1; ++b) {
+    a.table[b] = run * a.num_kv_heads;
+    int n;
+    if (a.step) {
+      const int n_old = a.lens[b];
+      n = (n_old >= 0 && n_old < a.max_len) ? n_old + 1
+                                            : clamp_len(n_old, a.max_len);
+    } else {
+      n = clamp_len(a.lens[b], a.max_len);
+    }
+    run += (n + kBalanceTile - 1) / kBalanceTile;
+  }
+  if (threadIdx.x == kBalanceThreads - 1) {
+    int total = 0;
+    for (int w = 0; w < kBalanceThreads / 64; ++w) total += wave_tot[w];
+    a.table[B] = total * a.num_kv_heads;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_balance(const ScheduleArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL(balance_kernel, dim3(1), dim3(kBalanceThreads), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_schedule(const ScheduleArgs &a, hipStream_t s) {
   const size_t lds = schedule_lds_bytes(a.batch, a.num_chunks);
   if (lds > 65536) {

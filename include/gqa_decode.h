@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define GQA_ABI_VERSION 4
+#define GQA_ABI_VERSION 5
 
 /* Only the entry points below are exported from the shared library. */
 #define GQA_API __attribute__((visibility("default")))
@@ -139,6 +139,25 @@ typedef struct gqa_carry {
  * holds the work schedule the library computes on the device before each
  * partition launch: sched_entries int32 at off_sched (a block -> item table
  * that gives the GPU's eight XCDs equal shares of the live chunks).
+ *
+ * Balanced plans (balanced_groups > 0; the library's choice for a bf16 /
+ * fp8 cache whose chunked launch would run in several rounds of
+ * work-groups, or asked for with GQA_CHUNK_BALANCED; such an explicit plan
+ * suits batches of very unequal lengths, since chunks of fixed length then
+ * leave some work-groups far longer than others): the 32-token tiles of all
+ * (sequence, KV group) units,
+ * concatenated, are cut into balanced_groups equal contiguous ranges, one
+ * per work-group, all resident at once (no ragged last round).  Then
+ * chunk_tokens = 32, num_chunks = 2 * balanced_groups piece slots, and
+ *   part_m / part_l [num_chunks][hpk], part_acc [num_chunks][hpk][dv]:
+ *       the partial states of units cut by a range end (slot 2 r + 1: the
+ *       unit range r ends in; slot 2 r: the unit range r begins in);
+ *   own_m [rows] at off_own, own_l [rows] and own_acc [rows][dv] next (each
+ *       at a 256-byte aligned offset): the state of a unit one range holds
+ *       whole, written by gqa_attend_partition;
+ *   sched_entries = batch + 1 int32 at off_sched: the first tile of each
+ *       sequence's units, and the total.
+ *
  * The workspace needs no initialisation and is only scratch between the
  * partition and combine of one call.
  */
@@ -150,6 +169,8 @@ typedef struct gqa_plan {
   size_t off_sched;
   int32_t sched_entries;
   size_t workspace_bytes;
+  int32_t balanced_groups;
+  size_t off_own;
 } gqa_plan;
 
 /* Version of this ABI (GQA_ABI_VERSION). */
@@ -234,9 +255,14 @@ GQA_API gqa_status gqa_stream_append(const gqa_cache *sink,
 
 /*
  * Plan the split-K decomposition for `cache` and `num_q_heads` query heads.
- * chunk_tokens = 0 picks the library's choice; otherwise it must be a
- * positive multiple of 64.  Pure host computation (no HIP calls).
+ * chunk_tokens = 0 picks the library's choice (a balanced plan for a bf16 /
+ * fp8 cache whose chunked launch would run in several rounds of
+ * work-groups; chunks otherwise); GQA_CHUNK_BALANCED asks for a balanced
+ * plan (bf16 / fp8 caches; GQA_ERR_UNSUPPORTED for fp32 or when a whole
+ * unit's rows span 2 GiB or more); otherwise it must be a positive multiple
+ * of 64 (a chunked plan).  Pure host computation (no HIP calls).
  */
+#define GQA_CHUNK_BALANCED (-1)
 GQA_API gqa_status gqa_attend_plan(const gqa_cache *cache, int32_t num_q_heads,
                            int32_t chunk_tokens, gqa_plan *plan);
 

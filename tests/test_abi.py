@@ -37,7 +37,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.gqa_abi_version() == 4
+    assert lib.gqa_abi_version() == 5
     names = [lib.gqa_status_string(i).decode() for i in range(7)]
     assert names == ["GQA_OK", "GQA_ERR_INVALID_ARGUMENT",
                      "GQA_ERR_SHAPE_MISMATCH", "GQA_ERR_UNSUPPORTED",
@@ -371,3 +371,61 @@ def test_profile_request_validation(lib):
     assert lib.gqa_profile_next_launch(None, P(0x1000)) == INVALID
     assert lib.gqa_profile_next_launch(P(0x1000), P(0x2000)) == OK
     assert lib.gqa_profile_next_launch(None, None) == OK
+
+
+def test_balanced_plan_layout(lib):
+    """A bf16 / fp8 cache whose chunked launch would take several rounds of
+    work-groups gets a balanced plan from the library (never from an
+    explicit chunk length, never for fp32): 512 work-groups, 1024 piece
+    slots of hpk rows, a whole-unit state per query row, the tile prefix;
+    every area 256-byte aligned and disjoint."""
+    up = lambda x: (x + 255) // 256 * 256
+    for dtype, esz in ((1, 2), (2, 1)):
+        ks = 0x30000 if dtype == 2 else None
+        c = _cache(B=64, T=32768, H=8, dtype=dtype, ks=ks, vs=ks)
+        st, p = _plan(lib, c, 64)
+        assert st == OK and p.balanced_groups == 512
+        assert p.chunk_tokens == 32 and p.num_chunks == 1024
+        hpk, rows = 8, 64 * 64
+        ml = 1024 * hpk * 4
+        assert p.off_l == up(ml) and p.off_acc == 2 * up(ml)
+        assert p.off_own == p.off_acc + up(ml * 128)
+        assert p.off_sched == p.off_own + 2 * up(rows * 4) + up(rows * 128 * 4)
+        assert p.sched_entries == 65
+        assert p.workspace_bytes == p.off_sched + up(65 * 4)
+        assert lib.gqa_attend_workspace_bytes(ctypes.byref(c), 64) == \
+            p.workspace_bytes
+        # an explicit chunk length keeps the chunked (scheduled) plan
+        st, q = _plan(lib, c, 64, chunk=2048)
+        assert st == OK and q.balanced_groups == 0 and q.sched_entries > 0
+    st, p = _plan(lib, _cache(B=64, T=32768, H=8, dtype=0), 64)
+    assert st == OK and p.balanced_groups == 0 and p.sched_entries > 0
+    # asked for explicitly: the same layout on any bf16 / fp8 shape, never
+    # for fp32
+    st, p = _plan(lib, _cache(B=2, T=300, H=2), 4, chunk=-1)
+    assert st == OK and p.balanced_groups == 512 and p.sched_entries == 3
+    st, _ = _plan(lib, _cache(B=2, T=300, H=2, dtype=0), 4, chunk=-1)
+    assert st == UNSUPPORTED
+    st, _ = _plan(lib, _cache(B=2, T=300, H=2), 4, chunk=-2)
+    assert st == INVALID
+    # one round of work-groups: chunked, no schedule
+    st, p = _plan(lib, _cache(), 32)
+    assert st == OK and p.balanced_groups == 0 and p.sched_entries == 0
+
+
+def test_balanced_plan_tampering_is_rejected(lib):
+    """A balanced plan handed back with any field changed is refused before
+    anything is enqueued."""
+    c = _cache(B=64, T=32768, H=8)
+    st, p = _plan(lib, c, 64)
+    assert st == OK and p.balanced_groups
+    P = ctypes.c_void_p
+    for field, delta in (("balanced_groups", 8), ("off_own", 256),
+                         ("num_chunks", 2), ("chunk_tokens", 32)):
+        bad = bd.Plan.from_buffer_copy(p)
+        setattr(bad, field, getattr(bad, field) + delta)
+        st = lib.gqa_attend_partition(P(0x40000), 64, ctypes.byref(c),
+                                      P(0x50000), 0.0, None, 0,
+                                      ctypes.byref(bad), P(0x60000),
+                                      p.workspace_bytes, None)
+        assert st == SHAPE, field

@@ -290,7 +290,7 @@ STEP_CASES = {
     "d128_direct": wl.BATCHED_FP8.replace(batch=8, max_len=200),
     "d128_fused": wl.BATCHED_FP8.replace(batch=3, num_q_heads=8,
                                          num_kv_heads=2, max_len=300),
-    "d64_scheduled": wl.BATCHED_FP8.replace(batch=64, num_q_heads=8,
+    "d64_balanced": wl.BATCHED_FP8.replace(batch=64, num_q_heads=8,
                                             num_kv_heads=8, dk=64, dv=64,
                                             max_len=4100),
     "dk192_hpk16": wl.BATCHED_FP8.replace(batch=3, num_q_heads=64,

@@ -89,11 +89,13 @@ def test_scheduled_partition(name):
 
 
 def test_scheduled_decode_step():
-    """decode_step with an automatic plan large enough to be scheduled; the
-    schedule counts the new token of each appended sequence."""
+    """decode_step with an automatic plan large enough to be scheduled (an
+    fp32 cache: bf16 / fp8 ones get a balanced plan instead); the schedule
+    counts the new token of each appended sequence and does the lengths and
+    drops of every sequence."""
     g = _gqa()
-    w = wl.RAGGED_BF16.replace(batch=64, num_q_heads=16, num_kv_heads=8,
-                               dk=64, dv=64, max_len=4100)
+    w = wl.TINY_F32.replace(batch=64, num_q_heads=16, num_kv_heads=8,
+                            dk=64, dv=64, max_len=4100, scale=0.0)
     lens = _lens(w.batch, w.max_len, 32)
     lens[5] = w.max_len - 1   # the append fills the cache
     lens[6] = 4095            # the new token opens the second chunk
@@ -102,7 +104,8 @@ def test_scheduled_decode_step():
                        pad_value=0.0)
     d = to_dev(x)
     plan = g.attend_plan(d["k"], d["v"], w.num_q_heads)
-    assert plan.sched_entries > 0, "scheduled plan expected"
+    assert plan.sched_entries > 0 and plan.balanced_groups == 0, \
+        "scheduled plan expected"
     gen = torch.Generator().manual_seed(33)
     kn = torch.randn(w.batch, w.num_kv_heads, w.dk, generator=gen).to(
         w.torch_dtype)
