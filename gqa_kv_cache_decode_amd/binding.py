@@ -54,7 +54,7 @@ class Plan(ctypes.Structure):
                 ("off_l", ctypes.c_size_t), ("off_acc", ctypes.c_size_t),
                 ("off_sched", ctypes.c_size_t), ("sched_entries", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_size_t),
-                ("balanced_groups", ctypes.c_int32), ("off_own", ctypes.c_size_t)]
+                ("balanced_groups", ctypes.c_int32)]
 
 
 _lib = None

@@ -43,9 +43,10 @@ constexpr int32_t kScheduledMaxChunk = 2048;
 constexpr int64_t kScheduleMaxSeqs = 8192;
 constexpr int64_t kScheduleMaxChunks = 4096;
 // Such a launch over a bf16 / fp8 cache with the library's own chunking is
-// balanced instead: kBalancedGroups work-groups (two per CU of the MI355X's
-// 256), all resident at once, each streaming an equal contiguous range of
-// the units' 32-token tiles, so no ragged last round is left.
+// balanced instead: kBalancedGroups persistent work-groups (two per CU of
+// the MI355X's 256) take items from a work queue of runs that shrink
+// towards its end, so no ragged last round is left and faster work-groups
+// take more of the work.
 constexpr int kNumCUs = 256;
 constexpr int kBalancedGroups = 2 * kNumCUs;
 
@@ -140,34 +141,36 @@ int32_t auto_chunk(const gqa_cache *c) {
   return chunk;
 }
 
+// Runs the balance kernel may cut a sequence of at most `tiles` 32-token
+// tiles into (its three phases, launch.h): at most tiles * 0.0212 + 12.
+int64_t queue_runs_per_seq(int64_t tiles) { return tiles * 212 / 10000 + 12; }
+
 // The layout of a balanced plan (false when the shape does not allow one):
-// 2 * kBalancedGroups piece slots of hpk rows (part_m / part_l / part_acc),
-// one whole-unit state per query row (own_m / own_l / own_acc, for calls
-// that write no final results), and the balance kernel's tile prefix
-// (batch + 1 int32 at off_sched).
+// one piece slot of hpk rows per queue item (part_m / part_l / part_acc),
+// then the work queue (int32 words at off_sched).
 bool balanced_plan(const gqa_cache *c, int32_t hq, gqa_plan *p) {
   const int64_t tiles = ((int64_t)c->max_len + gqa::kBalanceTile - 1) /
                         gqa::kBalanceTile;
-  // tile indices are int32; a whole unit is addressed with 32-bit offsets
+  const int64_t runs = (int64_t)c->batch * queue_runs_per_seq(tiles);
+  const int64_t items = runs * c->num_kv_heads;
+  const int64_t words = gqa::queue_runs_offset(c->batch) + 3 * runs;
+  // a run's rows are addressed with 32-bit offsets from the sequence start
   const int64_t span = (int64_t)c->max_len * c->num_kv_heads *
                        (c->dk > c->dv ? c->dk : c->dv) * esize(c->dtype);
-  const int64_t units = (int64_t)c->batch * c->num_kv_heads;
-  if (units * tiles > std::numeric_limits<int32_t>::max() ||
-      units * 2 * kBalancedGroups > std::numeric_limits<int32_t>::max() ||
+  const int64_t hpk = hq / c->num_kv_heads;
+  if (items * hpk > std::numeric_limits<int32_t>::max() ||
+      words > std::numeric_limits<int32_t>::max() ||
+      (int64_t)c->batch * tiles > std::numeric_limits<int32_t>::max() ||
       span >= ((int64_t)1 << 31))
     return false;
-  const size_t hpk = hq / c->num_kv_heads;
-  const size_t rows = (size_t)c->batch * hq;
-  const size_t ml = 2 * (size_t)kBalancedGroups * hpk * sizeof(float);
+  const size_t ml = (size_t)items * hpk * sizeof(float);
   p->chunk_tokens = gqa::kBalanceTile;
-  p->num_chunks = 2 * kBalancedGroups;
+  p->num_chunks = (int32_t)items;
   p->off_l = align_up(ml);
   p->off_acc = p->off_l + align_up(ml);
-  p->off_own = p->off_acc + align_up(ml * c->dv);
-  const size_t own_ml = align_up(rows * sizeof(float));
-  p->off_sched = p->off_own + 2 * own_ml + align_up(rows * c->dv * sizeof(float));
-  p->sched_entries = c->batch + 1;
-  p->workspace_bytes = p->off_sched + align_up((size_t)p->sched_entries * sizeof(int32_t));
+  p->off_sched = p->off_acc + align_up(ml * c->dv);
+  p->sched_entries = (int32_t)words;
+  p->workspace_bytes = p->off_sched + align_up((size_t)words * sizeof(int32_t));
   p->balanced_groups = kBalancedGroups;
   return true;
 }
@@ -178,7 +181,7 @@ gqa_status make_plan(const gqa_cache *c, int32_t hq, int32_t chunk_tokens,
   if (st != GQA_OK) return st;
   if ((st = check_heads(c, hq)) != GQA_OK) return st;
   if (chunk_tokens == GQA_CHUNK_BALANCED) {  // requested explicitly
-    if (c->dtype == GQA_DTYPE_F32) return GQA_ERR_UNSUPPORTED;
+    if (c->dtype == GQA_DTYPE_F32 || !uses_mfma(c)) return GQA_ERR_UNSUPPORTED;
     return balanced_plan(c, hq, p) ? GQA_OK : GQA_ERR_UNSUPPORTED;
   }
   if (chunk_tokens < 0 || chunk_tokens % kChunkQuantum != 0)
@@ -206,7 +209,6 @@ gqa_status make_plan(const gqa_cache *c, int32_t hq, int32_t chunk_tokens,
   p->off_sched = 0;
   p->sched_entries = 0;
   p->balanced_groups = 0;
-  p->off_own = 0;
   const bool multi_round = nchunk > 1 && groups >= kScheduleMinItems &&
                            uses_mfma(c) && c->batch <= kScheduleMaxSeqs;
   if (multi_round && chunk_tokens == 0 && c->dtype != GQA_DTYPE_F32 &&
@@ -237,7 +239,6 @@ gqa_status check_plan(const gqa_cache *c, int32_t hq, const gqa_plan *plan,
       want.off_sched != plan->off_sched ||
       want.sched_entries != plan->sched_entries ||
       want.balanced_groups != plan->balanced_groups ||
-      want.off_own != plan->off_own ||
       want.workspace_bytes != plan->workspace_bytes)
     return GQA_ERR_SHAPE_MISMATCH;
   if (!ws) return GQA_ERR_INVALID_ARGUMENT;
@@ -319,9 +320,8 @@ gqa_status schedule_checked(const gqa_cache *c, const gqa_plan &plan,
                             hipStream_t s) {
   a->sched = nullptr;
   a->sched_len = 0;
-  a->pre = nullptr;
+  a->queue = nullptr;
   a->balanced = 0;
-  a->own_m = a->own_l = a->own_acc = nullptr;
   if (plan.sched_entries == 0) return GQA_OK;
   gqa::ScheduleArgs sa;
   sa.lens = lens;
@@ -335,18 +335,11 @@ gqa_status schedule_checked(const gqa_cache *c, const gqa_plan &plan,
   sa.num_chunks = plan.num_chunks;
   sa.table = reinterpret_cast<int32_t *>(static_cast<char *>(ws) + plan.off_sched);
   sa.table_len = plan.sched_entries;
-  if (plan.balanced_groups) {  // the tile prefix, then one range per group
+  if (plan.balanced_groups) {  // the work queue, then the persistent launch
     gqa_status st = device_status(gqa::launch_balance(sa, s));
     if (st != GQA_OK) return st;
-    char *base = static_cast<char *>(ws);
-    const size_t rows = (size_t)c->batch * a->num_kv_heads * a->hpk;
-    a->pre = sa.table;
+    a->queue = sa.table;
     a->balanced = plan.balanced_groups;
-    a->own_m = reinterpret_cast<float *>(base + plan.off_own);
-    a->own_l = reinterpret_cast<float *>(base + plan.off_own +
-                                         align_up(rows * sizeof(float)));
-    a->own_acc = reinterpret_cast<float *>(base + plan.off_own +
-                                           2 * align_up(rows * sizeof(float)));
     return GQA_OK;
   }
   gqa_status st = device_status(gqa::launch_schedule(sa, s));
@@ -369,14 +362,13 @@ gqa::StepParams final_epilogue(const gqa_cache *c, const gqa_plan &plan,
   ep.out_l = cout ? cout->l : nullptr;
   ep.out_acc = cout ? cout->acc : nullptr;
   ep.out = out;
-  // a single chunk, or a balanced plan's units seen whole by one work-group
-  ep.direct = (plan.num_chunks == 1 && uses_mfma(c)) || plan.balanced_groups ? 1 : 0;
+  ep.direct = plan.num_chunks == 1 && uses_mfma(c) ? 1 : 0;
   return ep;
 }
 
 // Whether the partition launch leaves no fold to a combine launch.
-bool finished_in_partition(const gqa_plan &plan, const gqa::StepParams &ep) {
-  return ep.direct && !plan.balanced_groups;
+bool finished_in_partition(const gqa_plan &, const gqa::StepParams &ep) {
+  return ep.direct != 0;
 }
 
 gqa_status partition_checked(const void *q, int32_t hq, const gqa_cache *c,
@@ -418,23 +410,13 @@ gqa_status partition_checked(const void *q, int32_t hq, const gqa_cache *c,
 gqa_status combine_checked(int32_t hq, const gqa_cache *c, const int32_t *lens,
                            const gqa_plan *plan, const void *ws,
                            const gqa_carry *cin, const gqa_carry *cout,
-                           float *out, hipStream_t s, bool owned_final = false) {
+                           float *out, hipStream_t s) {
   CombineArgs a;
   a.balanced = plan->balanced_groups;
   a.hpk = hq / c->num_kv_heads;
-  a.owned_final = owned_final ? 1 : 0;
-  a.pre = nullptr;
-  a.own_m = a.own_l = a.own_acc = nullptr;
-  if (a.balanced) {
-    const char *b = static_cast<const char *>(ws);
-    const size_t rows = (size_t)c->batch * hq;
-    a.pre = reinterpret_cast<const int32_t *>(b + plan->off_sched);
-    a.own_m = reinterpret_cast<const float *>(b + plan->off_own);
-    a.own_l = reinterpret_cast<const float *>(b + plan->off_own +
-                                              align_up(rows * sizeof(float)));
-    a.own_acc = reinterpret_cast<const float *>(
-        b + plan->off_own + 2 * align_up(rows * sizeof(float)));
-  }
+  a.queue = a.balanced ? reinterpret_cast<const int32_t *>(
+                             static_cast<const char *>(ws) + plan->off_sched)
+                       : nullptr;
   a.batch = c->batch;
   a.num_q_heads = hq;
   a.dv = c->dv;
@@ -723,6 +705,28 @@ gqa_status plan_gathered(const gqa_cache *c, int32_t hq, int32_t width,
 
 }  // namespace
 
+namespace gqa {
+
+gqa_status attend_decode_check(const void *q, int32_t hq, const gqa_cache *c,
+                               const int32_t *lens, float scale,
+                               const float *bias, int64_t bias_stride,
+                               const gqa_carry *carry_in,
+                               const gqa_carry *carry_out, const float *out,
+                               size_t *workspace_bytes) {
+  gqa_status st = check_attend_args(q, hq, c, lens, scale);
+  if (st != GQA_OK) return st;
+  if ((st = check_bias(c, bias, bias_stride)) != GQA_OK) return st;
+  if ((st = check_combine_args(hq, c, lens, carry_in, carry_out, out)) !=
+      GQA_OK)
+    return st;
+  gqa_plan plan;
+  if ((st = make_plan(c, hq, 0, &plan)) != GQA_OK) return st;
+  *workspace_bytes = plan.workspace_bytes;
+  return GQA_OK;
+}
+
+}  // namespace gqa
+
 extern "C" {
 
 int32_t gqa_abi_version(void) { return GQA_ABI_VERSION; }
@@ -901,12 +905,11 @@ gqa_status gqa_attend_decode(const void *q, int32_t num_q_heads,
                              const gqa_carry *carry_out, float *out,
                              void *workspace, size_t workspace_bytes,
                              hipStream_t stream) {
-  gqa_status st = check_attend_args(q, num_q_heads, cache, lens, scale);
+  size_t need = 0;
+  gqa_status st = gqa::attend_decode_check(q, num_q_heads, cache, lens, scale,
+                                           bias, bias_stride, carry_in,
+                                           carry_out, out, &need);
   if (st != GQA_OK) return st;
-  if ((st = check_bias(cache, bias, bias_stride)) != GQA_OK) return st;
-  if ((st = check_combine_args(num_q_heads, cache, lens, carry_in, carry_out,
-                               out)) != GQA_OK)
-    return st;
   gqa_plan plan;
   if ((st = make_plan(cache, num_q_heads, 0, &plan)) != GQA_OK) return st;
   if ((st = check_plan(cache, num_q_heads, &plan, workspace_bytes, workspace)) !=
@@ -918,7 +921,7 @@ gqa_status gqa_attend_decode(const void *q, int32_t num_q_heads,
                          &plan, workspace, ep, stream);
   if (st != GQA_OK || finished_in_partition(plan, ep)) return st;
   return combine_checked(num_q_heads, cache, lens, &plan, workspace, carry_in,
-                         carry_out, out, stream, ep.direct != 0);
+                         carry_out, out, stream);
 }
 
 gqa_status gqa_softmax_state_merge(const gqa_carry *a, const gqa_carry *b,
@@ -1141,7 +1144,7 @@ gqa_status gqa_decode_step(const void *q, int32_t num_q_heads,
   st = device_status(launch_step(cache, a, sp, stream));
   if (st != GQA_OK || sp.fuse || finished_in_partition(plan, sp)) return st;
   return combine_checked(num_q_heads, cache, lens_out, &plan, workspace,
-                         carry_in, carry_out, out, stream, sp.direct != 0);
+                         carry_in, carry_out, out, stream);
 }
 
 }  // extern "C"

@@ -98,31 +98,22 @@ __global__ __launch_bounds__(THREADS) void combine_kernel(CombineArgs a) {
 }
 
 // Balanced plans: one work-group per query row, one thread per value column.
-// The row's unit (sequence b, KV group g) covers tiles [u0, u1) of the
-// concatenation; ranges r0 = range(u0) .. r1 = range(u1 - 1) saw it.  One
-// range: the unit's state is final already (owned_final) or in own_*; more:
-// the first range left its piece in slot 2 * r0 + 1, each later one in slot
-// 2 * r.  The pieces and carry_in fold by log-sum-exp merge.
+// The row's sequence b has, in each phase k of the work queue, the runs
+// base[k] + pre_k[b] .. base[k] + pre_k[b + 1] - 1; queue item r *
+// num_kv_heads + g (g the row's KV group) left its piece in that slot.  The
+// pieces and carry_in fold by log-sum-exp merge.
 __global__ __launch_bounds__(256) void combine_balanced_kernel(CombineArgs a) {
   const int row = blockIdx.x;
   const int d = threadIdx.x;
   const int Hq = a.num_q_heads, hpk = a.hpk, Hkv = Hq / hpk;
   const int b = row / Hq, h = row % Hq, g = h / hpk, hh = h % hpk;
-  const int P = a.balanced, total = a.pre[a.batch];
-  const int pb = a.pre[b];
-  const int nt = (a.pre[b + 1] - pb) / Hkv;
-  int r0 = 0, r1 = -1;  // no pieces
-  bool own = false;
-  if (nt > 0) {
-    const int u0 = pb + g * nt;
-    r0 = range_of_tile(u0, P, total);
-    r1 = range_of_tile(u0 + nt - 1, P, total);
-    if (r0 == r1) {
-      if (a.owned_final) return;
-      own = true;
-    }
-  }
-  if (d >= a.dv) return;
+  const int B = a.batch;
+  const bool worker = d < a.dv;
+  // carry_in is read before the barrier below: carry_out may alias it
+  const float in_l = a.in_l ? a.in_l[row] : 0.0f;
+  const float in_m = in_l > 0.0f ? a.in_m[row] : -INFINITY;
+  const float in_acc =
+      in_l > 0.0f && worker ? a.in_acc[(size_t)row * a.dv + d] : 0.0f;
   float m = -INFINITY, L = 0.0f, acc = 0.0f;  // base-2 running state
   auto fold = [&](float mi, float li, float ai) {
     // a piece whose keys were all removed by the bias has m = -inf, l = 0
@@ -132,17 +123,21 @@ __global__ __launch_bounds__(256) void combine_balanced_kernel(CombineArgs a) {
     L = L * fo + li * fi;
     m = mn;
   };
-  if (own) {
-    fold(a.own_m[row] * kLog2e, a.own_l[row], a.own_acc[(size_t)row * a.dv + d]);
-  } else {
-    for (int r = r0; r <= r1; ++r) {
-      const size_t pr = (2 * (size_t)r + (r == r0 ? 1 : 0)) * hpk + hh;
-      fold(a.part_m[pr] * kLog2e, a.part_l[pr], a.part_acc[pr * a.dv + d]);
+  if (worker) {
+    for (int k = 0; k < kQueuePhases; ++k) {
+      const int *pre = a.queue + kQueuePre + k * (B + 1);
+      const int base = a.queue[kQueueBase + k];
+      const int r1 = base + pre[b + 1];
+#pragma unroll 4
+      for (int r = base + pre[b]; r < r1; ++r) {
+        const size_t pr = ((size_t)r * Hkv + g) * hpk + hh;
+        fold(a.part_m[pr] * kLog2e, a.part_l[pr], a.part_acc[pr * a.dv + d]);
+      }
     }
   }
-  const float in_l = a.in_l ? a.in_l[row] : 0.0f;
-  if (in_l > 0.0f)
-    fold(a.in_m[row] * kLog2e, in_l, a.in_acc[(size_t)row * a.dv + d]);
+  if (in_l > 0.0f) fold(in_m * kLog2e, in_l, in_acc);
+  __syncthreads();  // every thread has read carry_in
+  if (!worker) return;
   const bool live = L > 0.0f;
   if (a.out) a.out[(size_t)row * a.dv + d] = live ? acc / L : 0.0f;
   if (a.out_acc) {

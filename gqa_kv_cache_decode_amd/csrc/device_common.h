@@ -144,17 +144,4 @@ __device__ __forceinline__ int xcd_local_item(int i, int n) {
   return (i < (per << 3)) ? (i & 7) * per + (i >> 3) : i;
 }
 
-// Balanced launches: block i (on XCD i % 8) takes range (i % 8) * (P / 8) +
-// i / 8 of the P equal ranges (P a multiple of 8), so each XCD streams one
-// contiguous eighth of the work.  Range r covers tiles
-// [floor(r * total / P), floor((r + 1) * total / P)).
-__device__ __forceinline__ int balanced_range(int i, int P) {
-  return (i & 7) * (P >> 3) + (i >> 3);
-}
-
-// The range holding tile x: the largest r with floor(r * total / P) <= x.
-__device__ __forceinline__ int range_of_tile(int x, int P, int total) {
-  return (int)(((int64_t)(x + 1) * P - 1) / total);
-}
-
 }  // namespace gqa

@@ -5,7 +5,19 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "gqa_decode.h"
+
 namespace gqa {
+
+// Every argument check of gqa_attend_decode except those of the workspace
+// (pure host computation, no HIP call); on success *workspace_bytes is the
+// workspace its plan needs.
+gqa_status attend_decode_check(const void *q, int32_t hq, const gqa_cache *c,
+                               const int32_t *lens, float scale,
+                               const float *bias, int64_t bias_stride,
+                               const gqa_carry *carry_in,
+                               const gqa_carry *carry_out, const float *out,
+                               size_t *workspace_bytes);
 
 // Wavefronts per work-group of the fp32 matrix-core partition kernel.  The
 // fp32 caches that matter are short and latency-bound: with four, a 64-token
@@ -75,20 +87,36 @@ struct PartitionArgs {
   // fixed map; sched_len entries, one per block.
   const int32_t *sched;
   int sched_len;
-  // Balanced launch (balanced > 0 work-groups, partition_balanced_kernel):
-  // pre[b] is the first 32-token tile of sequence b's units, pre[batch] the
-  // total (balance kernel).  part_* then hold 2 * balanced piece slots of
-  // hpk rows; a unit one work-group saw whole writes its final results when
-  // the epilogue is direct, else its state (natural-log m) into own_*
-  // [rows] / [rows][dv].
-  const int32_t *pre = nullptr;
+  // Balanced launch (balanced > 0 persistent work-groups,
+  // partition_balanced_kernel): the work queue the balance kernel built (see
+  // the kQueue* layout below); part_* then hold one piece slot of hpk rows
+  // per queue item.
+  int32_t *queue = nullptr;
   int balanced = 0;
-  float *own_m = nullptr, *own_l = nullptr, *own_acc = nullptr;
 };
 
+// Work queue of a balanced plan (int32 words, built by the balance kernel):
+//   [kQueueCounter]   next item to take (0 before the partition launch)
+//   [kQueueItems]     items: runs * num_kv_heads
+//   [kQueueBase + k]  first run of phase k, k = 0..3 (the last: all runs)
+//   [kQueuePre + k * (batch + 1) + b]  sequence b's first run within phase k
+//   then 3 words per run: sequence, first tile, end tile (32-token tiles).
+// Phase k cuts each sequence's tiles into runs of kQueueRun<k> tiles: phase
+// 0 takes the whole runs of its first 3/4, phase 1 those of the next part
+// up to 23/25, phase 2 the rest (its last run may be short).
+constexpr int kQueueCounter = 0;
+constexpr int kQueueItems = 1;
+constexpr int kQueueBase = 2;
+constexpr int kQueuePre = 6;
+constexpr int kQueueRun0 = 128, kQueueRun1 = 32, kQueueRun2 = 8;
+constexpr int kQueuePhases = 3;
+
+__host__ __device__ constexpr int queue_runs_offset(int batch) {
+  return kQueuePre + kQueuePhases * (batch + 1);
+}
+
 // Inputs of the schedule kernel and of the balance kernel (one work-group
-// each; the balance kernel writes its tile prefix `pre` [batch + 1] into
-// `table`).
+// each; the balance kernel writes the work queue into `table`).
 struct ScheduleArgs {
   const int32_t *lens;  // [B]
   int step;             // lengths are decode-step inputs (the new token counts)
@@ -132,13 +160,10 @@ struct CombineArgs {
   int num_branches;
   CombineBranch br[1 + kMaxExtraBranches];
   const float *part_m, *part_l, *part_acc;
-  // Balanced plan (balanced > 0 work-groups): the pieces of units cut by a
-  // range end are folded per query row; a unit one work-group saw whole is
-  // skipped when `owned_final` (its results are written) or folded from
-  // own_* otherwise.  pre: the balance kernel's tile prefix.
-  int balanced = 0, hpk = 0, owned_final = 0;
-  const int32_t *pre = nullptr;
-  const float *own_m = nullptr, *own_l = nullptr, *own_acc = nullptr;
+  // Balanced plan (balanced > 0): each query row's pieces (one per queue
+  // item of its sequence and KV group) are folded; queue: the work queue.
+  int balanced = 0, hpk = 0;
+  const int32_t *queue = nullptr;
   const float *in_m, *in_l, *in_acc;   // carry_in, all NULL if absent
   float *out_m, *out_l, *out_acc;      // carry_out, all NULL if absent
   float *out;                          // [rows][dv] or NULL
@@ -228,7 +253,7 @@ hipError_t launch_step_f32(const PartitionArgs &a, const StepParams &sp,
 hipError_t launch_combine(const CombineArgs &a, hipStream_t s);
 size_t schedule_lds_bytes(int batch, int num_chunks);
 hipError_t launch_schedule(const ScheduleArgs &a, hipStream_t s);
-// The tile prefix of a balanced plan (and a decode step's bookkeeping).
+// The work queue of a balanced plan (and a decode step's bookkeeping).
 hipError_t launch_balance(const ScheduleArgs &a, hipStream_t s);
 constexpr int kBalanceTile = 32;  // tokens per tile of a balanced plan
 hipError_t launch_merge(const MergeArgs &a, hipStream_t s);

@@ -553,104 +553,61 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
 }
 
 // Balanced launch (a plan with many items over several rounds of
-// work-groups, where fixed chunks leave a ragged last round): the units'
-// 32-token tiles, concatenated in (sequence, KV group) order, are cut into
-// gridDim.x equal contiguous ranges, one per work-group, all resident at
-// once.  a.pre[b] (from the balance kernel) is the first tile of sequence b's
-// units; sequence b's KV group g covers tiles [pre[b] + g * nt_b,
-// pre[b] + (g + 1) * nt_b) with nt_b its tiles per group.  A work-group walks
-// the units its range overlaps: a unit wholly inside the range gets its final
-// results here (carry_in folded, out and carry_out written); a unit cut by
-// the range's ends leaves one piece per work-group that saw it, in piece
-// slot 2 * r (the range's first unit, begun before it) or 2 * r + 1 (its last
-// unit, continuing past it), which the balanced combine folds.  Range r of
-// block i is (i % 8) * (P / 8) + i / 8, so each XCD streams one contiguous
-// eighth of the work.
+// work-groups, where fixed chunks leave a ragged last round, and where the
+// work-groups' read rates differ by tens of percent from one CU or XCD to
+// another): a work queue.  The balance kernel cuts every sequence into runs
+// of 32-token tiles in three phases of shrinking run length (kQueueRun0/1/2
+// tiles) and lists them phase by phase, sequence by sequence; item i of the
+// queue is run i / num_kv_heads for KV group i % num_kv_heads, so the groups
+// of one run, which share its cache rows, are taken one after the other.
+// a.balanced persistent work-groups take items from one counter until the
+// queue is empty (the next index is fetched while the current item streams),
+// so faster work-groups simply take more items and the last ones are short.
+// Every item leaves its partial state in piece slot i; the balanced combine
+// folds each query row's pieces.  A decode step's new token is stored and
+// folded by the item whose run holds the sequence's last tile.
 template <int DK, int DV, int NW, bool STEP, bool BIAS, bool FP8>
 __global__ __launch_bounds__(NW * 64) void partition_balanced_kernel(
     PartitionArgs a, StepParams sp) {
   constexpr int kLdsBytes = partition_lds_bytes<DK, DV, NW, FP8>();
   __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
-  __shared__ float s_in[32];
-  __shared__ int s_count;
+  __shared__ int s_item;
 
-  const int P = gridDim.x;
-  const int r = balanced_range(blockIdx.x, P);
-  const int B = a.batch, Hkv = a.num_kv_heads, hpk = a.hpk;
-  const int total = a.pre[B];
-  const int start = (int)((int64_t)r * total / P);
-  const int end = (int)((int64_t)(r + 1) * total / P);
-  if (start >= end) return;
-
-  // first sequence of the range: the last b with pre[b] <= start (the count
-  // of such entries, minus one; sequences without tiles repeat an entry)
-  if (threadIdx.x == 0) s_count = 0;
+  const int Hkv = a.num_kv_heads, hpk = a.hpk;
+  int *queue = a.queue;
+  const int total = queue[kQueueItems];
+  const int *runs = queue + queue_runs_offset(a.batch);
+  if (threadIdx.x == 0) s_item = atomicAdd(queue + kQueueCounter, 1);
   __syncthreads();
-  int cnt = 0;
-  for (int i = threadIdx.x; i <= B; i += NW * 64) cnt += a.pre[i] <= start;
-  cnt = wave_sum_int(cnt);
-  if ((threadIdx.x & 63) == 0) atomicAdd(&s_count, cnt);
-  __syncthreads();
-  int b = s_count - 1;
-  int pb = a.pre[b], pn = a.pre[b + 1];
-  int g = (start - pb) / ((pn - pb) / Hkv);
-  const int Hq = Hkv * hpk;
-
-  for (int cur = start; cur < end;) {
-    const int nt = (pn - pb) / Hkv;  // tiles per KV group of sequence b
-    const int u0 = pb + g * nt, u1 = u0 + nt;
-    const int s0 = max(u0, start), s1 = min(u1, end);
+  int item = s_item;
+  while (item < total) {
+    const int run = item / Hkv, g = item - run * Hkv;
+    const int b = runs[3 * run], t0t = runs[3 * run + 1], t1t = runs[3 * run + 2];
+    int next = 0;
+    if (threadIdx.x == 0) next = atomicAdd(queue + kQueueCounter, 1);
     const SeqLen sl = seq_len(a, sp, b, STEP);
     const int n = sl.n;
-    const int t0 = (s0 - u0) * kTileTokens;
-    const int tend = min((s1 - u0) * kTileTokens, n);
-    // decode step: the segment holding the unit's last tile holds the slot
-    const bool has_new = STEP && sl.fresh && s1 == u1;
+    const int t0 = t0t * kTileTokens;
+    const int tend = min(t1t * kTileTokens, n);
+    // decode step: the run holding the sequence's last tile holds the slot
+    const bool has_new = STEP && sl.fresh && tend == n;
     const int t1 = has_new ? sl.n_old : tend;
-    const bool owned = u0 >= start && u1 <= end;
-    const bool direct = owned && sp.direct;
     const bool live = stream_segment<DK, DV, NW, STEP, BIAS, false, FP8>(
-        a, sp, b, g, t0, t1, has_new, sl.n_old, direct, lds, nullptr, s_in);
-    const size_t row0 = (size_t)b * Hq + (size_t)g * hpk;
-    if (direct) {
-      write_group_direct<DV, NW>(sp, row0, hpk, live, lds, s_in);
-    } else if (owned) {  // partials-only call: the unit's whole state
-      for (int e = threadIdx.x; e < hpk * DV; e += NW * 64) {
-        const int h = e / DV, d = e % DV;
-        float M, L, acc;
-        merged_state<DV, NW>(lds, live, h, d, M, L, acc);
-        const size_t row = row0 + h;
-        a.own_acc[row * DV + d] = acc;
-        if (d == 0) {
-          a.own_m[row] = M * kLn2;
-          a.own_l[row] = L;
-        }
-      }
-    } else {
-      const size_t slot = 2 * (size_t)r + (u0 < start ? 0 : 1);
-      for (int e = threadIdx.x; e < hpk * DV; e += NW * 64) {
-        const int h = e / DV, d = e % DV;
-        float M, L, acc;
-        merged_state<DV, NW>(lds, live, h, d, M, L, acc);
-        const size_t pr = slot * hpk + h;  // piece row
-        a.part_acc[pr * DV + d] = acc;
-        if (d == 0) {
-          a.part_m[pr] = M * kLn2;
-          a.part_l[pr] = L;
-        }
+        a, sp, b, g, t0, t1, has_new, sl.n_old, false, lds, nullptr, nullptr);
+    for (int e = threadIdx.x; e < hpk * DV; e += NW * 64) {
+      const int h = e / DV, d = e % DV;
+      float M, L, acc;
+      merged_state<DV, NW>(lds, live, h, d, M, L, acc);
+      const size_t pr = (size_t)item * hpk + h;  // piece row
+      a.part_acc[pr * DV + d] = acc;
+      if (d == 0) {
+        a.part_m[pr] = M * kLn2;
+        a.part_l[pr] = L;
       }
     }
-    cur = s1;
-    if (cur >= end) break;
-    __syncthreads();  // the merge area is reused by the next segment
-    if (++g == Hkv) {  // next sequence with tiles
-      g = 0;
-      do {
-        ++b;
-        pb = pn;
-        pn = a.pre[b + 1];
-      } while (pn == pb);
-    }
+    if (threadIdx.x == 0) s_item = next;
+    __syncthreads();  // the next index is visible; the merge area is free
+    item = s_item;
   }
 }
 

@@ -140,67 +140,118 @@ size_t schedule_lds_bytes(int batch, int num_chunks) {
 }
 
 // ---------------------------------------------------------------------------
-// Tile prefix of a balanced plan: pre[b] = num_kv_heads * (sum over b' < b of
-// the 32-token tiles of sequence b'), pre[batch] = the total, so that the
-// partition's work-groups can cut the concatenated tiles of all (sequence,
-// KV group) units into equal ranges.  A decode step's lengths count the new
-// token, and its per-sequence bookkeeping is done here as well.
+// Work queue of a balanced plan (layout in launch.h): every sequence's
+// 32-token tiles are cut into runs of three shrinking lengths, listed phase
+// by phase and, within a phase, sequence by sequence, so that the queue ends
+// with short items whatever the lengths.  A decode step's lengths count the
+// new token, and its per-sequence bookkeeping is done here as well.
 namespace {
 
 constexpr int kBalanceThreads = 1024;
 
-__global__ __launch_bounds__(kBalanceThreads) void balance_kernel(
-    ScheduleArgs a) {
-  __shared__ int wave_tot[kBalanceThreads / 64];
-  const int B = a.batch;
-  const int per = (B + kBalanceThreads - 1) / kBalanceThreads;
-  const int b0 = threadIdx.x * per, b1 = min(b0 + per, B);
-  int mine = 0;
-  for (int b = b0; b < b1; ++b) {
-    int n;
-    if (a.step) {
-      const int n_old = a.lens[b];
-      const bool fresh = n_old >= 0 && n_old < a.max_len;
-      n = fresh ? n_old + 1 : clamp_len(n_old, a.max_len);
+// Runs of each phase for a sequence of nt tiles.
+struct PhaseRuns {
+  int start[kQueuePhases + 1];  // tile where each phase starts; [3] = nt
+  int count[kQueuePhases];
+};
+
+__device__ __forceinline__ PhaseRuns phase_runs(int nt) {
+  PhaseRuns p;
+  const int64_t n = nt;
+  const int e0 = (int)(n * 3 / 4 / kQueueRun0 * kQueueRun0);
+  const int t1 = (int)(n * 23 / 25);
+  const int e1 = e0 + max(t1 - e0, 0) / kQueueRun1 * kQueueRun1;
+  p.start[0] = 0;
+  p.start[1] = e0;
+  p.start[2] = e1;
+  p.start[3] = nt;
+  p.count[0] = e0 / kQueueRun0;
+  p.count[1] = (e1 - e0) / kQueueRun1;
+  p.count[2] = (nt - e1 + kQueueRun2 - 1) / kQueueRun2;
+  return p;
+}
+
+__device__ __forceinline__ int seq_tiles(const ScheduleArgs &a, int b,
+                                         bool bookkeeping) {
+  int n;
+  if (a.step) {
+    const int n_old = a.lens[b];
+    const bool fresh = n_old >= 0 && n_old < a.max_len;
+    n = fresh ? n_old + 1 : clamp_len(n_old, a.max_len);
+    if (bookkeeping) {
       // needle-core push_kv: the length grows by one, or a full cache (or a
       // negative length) is left as it is and the drop counted
       a.lens_out[b] = fresh ? n_old + 1 : n_old;
       if (!fresh && a.dropped) atomicAdd(a.dropped, 1);
-    } else {
-      n = clamp_len(a.lens[b], a.max_len);
     }
-    mine += (n + kBalanceTile - 1) / kBalanceTile;
+  } else {
+    n = clamp_len(a.lens[b], a.max_len);
   }
-  // exclusive prefix of the threads' counts across the work-group
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int inc = mine;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(inc, off, 64);
-    if (lane >= off) inc += y;
-  }
-  if (lane == 63) wave_tot[wave] = inc;
-  __syncthreads();
-  int base = 0;
-  for (int w = 0; w < wave; ++w) base += wave_tot[w];
-  int run = base + inc - mine;
+  return (n + kBalanceTile - 1) / kBalanceTile;
+}
+
+__global__ __launch_bounds__(kBalanceThreads) void balance_kernel(
+    ScheduleArgs a) {
+  __shared__ int wave_tot[kQueuePhases][kBalanceThreads / 64];
+  __shared__ int base[kQueuePhases + 1];
+  const int B = a.batch;
+  int *q = a.table;
+  const int per = (B + kBalanceThreads - 1) / kBalanceThreads;
+  const int b0 = min((int)threadIdx.x * per, B), b1 = min(b0 + per, B);
+  int mine[kQueuePhases] = {0, 0, 0};
   for (int b = b0; b < b1; ++b) {
-    a.table[b] = run * a.num_kv_heads;
-    int n;
-    if (a.step) {
-      const int n_old = a.lens[b];
-      n = (n_old >= 0 && n_old < a.max_len) ? n_old + 1
-                                            : clamp_len(n_old, a.max_len);
-    } else {
-      n = clamp_len(a.lens[b], a.max_len);
+    const PhaseRuns p = phase_runs(seq_tiles(a, b, true));
+    for (int k = 0; k < kQueuePhases; ++k) mine[k] += p.count[k];
+  }
+  // exclusive prefix of each phase's counts across the work-group
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int inc[kQueuePhases];
+  for (int k = 0; k < kQueuePhases; ++k) {
+    inc[k] = mine[k];
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(inc[k], off, 64);
+      if (lane >= off) inc[k] += y;
     }
-    run += (n + kBalanceTile - 1) / kBalanceTile;
+    if (lane == 63) wave_tot[k][wave] = inc[k];
   }
-  if (threadIdx.x == kBalanceThreads - 1) {
-    int total = 0;
-    for (int w = 0; w < kBalanceThreads / 64; ++w) total += wave_tot[w];
-    a.table[B] = total * a.num_kv_heads;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int k = 0; k < kQueuePhases; ++k) {
+      base[k] = run;
+      for (int w = 0; w < kBalanceThreads / 64; ++w) run += wave_tot[k][w];
+    }
+    base[kQueuePhases] = run;
+    q[kQueueCounter] = 0;
+    q[kQueueItems] = run * a.num_kv_heads;
+    for (int k = 0; k <= kQueuePhases; ++k) q[kQueueBase + k] = base[k];
   }
+  __syncthreads();
+  int run_at[kQueuePhases];
+  for (int k = 0; k < kQueuePhases; ++k) {
+    int before = 0;
+    for (int w = 0; w < wave; ++w) before += wave_tot[k][w];
+    run_at[k] = before + inc[k] - mine[k];  // within phase k
+  }
+  int *runs = q + queue_runs_offset(B);
+  for (int b = b0; b < b1; ++b) {
+    const PhaseRuns p = phase_runs(seq_tiles(a, b, false));
+    for (int k = 0; k < kQueuePhases; ++k) {
+      q[kQueuePre + k * (B + 1) + b] = run_at[k];
+      const int len = k == 0 ? kQueueRun0 : k == 1 ? kQueueRun1 : kQueueRun2;
+      for (int j = 0; j < p.count[k]; ++j) {
+        int *r = runs + 3 * (base[k] + run_at[k] + j);
+        r[0] = b;
+        r[1] = p.start[k] + j * len;
+        r[2] = min(p.start[k] + (j + 1) * len, p.start[k + 1]);
+      }
+      run_at[k] += p.count[k];
+    }
+  }
+  if (threadIdx.x == kBalanceThreads - 1)
+    for (int k = 0; k < kQueuePhases; ++k)
+      q[kQueuePre + k * (B + 1) + B] = base[k + 1] - base[k];
 }
 
 }  // namespace

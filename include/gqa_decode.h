@@ -142,21 +142,20 @@ typedef struct gqa_carry {
  *
  * Balanced plans (balanced_groups > 0; the library's choice for a bf16 /
  * fp8 cache whose chunked launch would run in several rounds of
- * work-groups, or asked for with GQA_CHUNK_BALANCED; such an explicit plan
- * suits batches of very unequal lengths, since chunks of fixed length then
- * leave some work-groups far longer than others): the 32-token tiles of all
- * (sequence, KV group) units,
- * concatenated, are cut into balanced_groups equal contiguous ranges, one
- * per work-group, all resident at once (no ragged last round).  Then
- * chunk_tokens = 32, num_chunks = 2 * balanced_groups piece slots, and
+ * work-groups, or asked for with GQA_CHUNK_BALANCED, which suits batches of
+ * very unequal lengths, since chunks of one length then leave some
+ * work-groups far longer than others): a work queue.  Every sequence's
+ * 32-token tiles are cut into runs — of 128 tiles over its first 3/4, of 32
+ * tiles up to 23/25 of it, of 8 tiles over the rest — listed phase by phase,
+ * sequence by sequence; queue item i is run i / num_kv_heads for KV group
+ * i % num_kv_heads.  balanced_groups persistent work-groups take items from
+ * the queue until it is empty, so the work spreads by the work-groups'
+ * actual speed and ends with short items.  Then chunk_tokens = 32,
+ * num_chunks = the most items the shape can need (one piece slot each), and
  *   part_m / part_l [num_chunks][hpk], part_acc [num_chunks][hpk][dv]:
- *       the partial states of units cut by a range end (slot 2 r + 1: the
- *       unit range r ends in; slot 2 r: the unit range r begins in);
- *   own_m [rows] at off_own, own_l [rows] and own_acc [rows][dv] next (each
- *       at a 256-byte aligned offset): the state of a unit one range holds
- *       whole, written by gqa_attend_partition;
- *   sched_entries = batch + 1 int32 at off_sched: the first tile of each
- *       sequence's units, and the total.
+ *       item i's partial state (hpk rows), in slot i;
+ *   sched_entries int32 at off_sched: the queue (its counter, item count,
+ *       phase starts, per-sequence run offsets and the runs themselves).
  *
  * The workspace needs no initialisation and is only scratch between the
  * partition and combine of one call.
@@ -170,7 +169,6 @@ typedef struct gqa_plan {
   int32_t sched_entries;
   size_t workspace_bytes;
   int32_t balanced_groups;
-  size_t off_own;
 } gqa_plan;
 
 /* Version of this ABI (GQA_ABI_VERSION). */

@@ -376,23 +376,26 @@ def test_profile_request_validation(lib):
 def test_balanced_plan_layout(lib):
     """A bf16 / fp8 cache whose chunked launch would take several rounds of
     work-groups gets a balanced plan from the library (never from an
-    explicit chunk length, never for fp32): 512 work-groups, 1024 piece
-    slots of hpk rows, a whole-unit state per query row, the tile prefix;
-    every area 256-byte aligned and disjoint."""
+    explicit chunk length, never for fp32): 512 persistent work-groups, one
+    piece slot of hpk rows per queue item (at most tiles * 0.0212 + 12 runs
+    per sequence, times the KV heads), then the queue; every area 256-byte
+    aligned and disjoint."""
     up = lambda x: (x + 255) // 256 * 256
-    for dtype, esz in ((1, 2), (2, 1)):
+    for dtype in (1, 2):
         ks = 0x30000 if dtype == 2 else None
         c = _cache(B=64, T=32768, H=8, dtype=dtype, ks=ks, vs=ks)
         st, p = _plan(lib, c, 64)
         assert st == OK and p.balanced_groups == 512
-        assert p.chunk_tokens == 32 and p.num_chunks == 1024
-        hpk, rows = 8, 64 * 64
-        ml = 1024 * hpk * 4
+        runs = 64 * (1024 * 212 // 10000 + 12)
+        items = runs * 8
+        assert p.chunk_tokens == 32 and p.num_chunks == items
+        hpk = 8
+        ml = items * hpk * 4
         assert p.off_l == up(ml) and p.off_acc == 2 * up(ml)
-        assert p.off_own == p.off_acc + up(ml * 128)
-        assert p.off_sched == p.off_own + 2 * up(rows * 4) + up(rows * 128 * 4)
-        assert p.sched_entries == 65
-        assert p.workspace_bytes == p.off_sched + up(65 * 4)
+        assert p.off_sched == p.off_acc + up(ml * 128)
+        words = 6 + 3 * 65 + 3 * runs
+        assert p.sched_entries == words
+        assert p.workspace_bytes == p.off_sched + up(words * 4)
         assert lib.gqa_attend_workspace_bytes(ctypes.byref(c), 64) == \
             p.workspace_bytes
         # an explicit chunk length keeps the chunked (scheduled) plan
@@ -400,10 +403,10 @@ def test_balanced_plan_layout(lib):
         assert st == OK and q.balanced_groups == 0 and q.sched_entries > 0
     st, p = _plan(lib, _cache(B=64, T=32768, H=8, dtype=0), 64)
     assert st == OK and p.balanced_groups == 0 and p.sched_entries > 0
-    # asked for explicitly: the same layout on any bf16 / fp8 shape, never
-    # for fp32
+    # asked for explicitly: any bf16 / fp8 shape, never fp32
     st, p = _plan(lib, _cache(B=2, T=300, H=2), 4, chunk=-1)
-    assert st == OK and p.balanced_groups == 512 and p.sched_entries == 3
+    assert st == OK and p.balanced_groups == 512
+    assert p.sched_entries == 6 + 3 * 3 + 3 * 2 * (10 * 212 // 10000 + 12)
     st, _ = _plan(lib, _cache(B=2, T=300, H=2, dtype=0), 4, chunk=-1)
     assert st == UNSUPPORTED
     st, _ = _plan(lib, _cache(B=2, T=300, H=2), 4, chunk=-2)
@@ -420,7 +423,7 @@ def test_balanced_plan_tampering_is_rejected(lib):
     st, p = _plan(lib, c, 64)
     assert st == OK and p.balanced_groups
     P = ctypes.c_void_p
-    for field, delta in (("balanced_groups", 8), ("off_own", 256),
+    for field, delta in (("balanced_groups", 8), ("off_sched", 256),
                          ("num_chunks", 2), ("chunk_tokens", 32)):
         bad = bd.Plan.from_buffer_copy(p)
         setattr(bad, field, getattr(bad, field) + delta)

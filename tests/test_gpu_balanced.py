@@ -1,16 +1,14 @@
 """Balanced launches: a bf16 / fp8 cache whose chunked launch would take
-several rounds of work-groups gets the library's balanced plan (every
-(sequence, KV group) unit's 32-token tiles, concatenated, cut into 512 equal
-contiguous ranges, one per resident work-group).  Checked against the
-oracle through every entry point that takes such a plan: attend_decode
-(units seen whole written by the partition launch, the pieces of the others
-folded by the combine), the attend_partition / attend_combine pair (whole
-units through the per-row state area), and decode_step (the append in the
-same launch, the lengths and drops written by the balance kernel).  Shapes
-cover empty, negative, full and past-the-cache lengths, one unit spanning
-many ranges among tiny ones, fewer tiles than work-groups, every compiled
-head shape, the additive bias, carry_in and fp8 caches.  The balance
-kernel's tile prefix is checked exactly."""
+several rounds of work-groups gets the library's balanced plan (a work
+queue of runs of 32-token tiles, shrinking towards its end, taken by 512
+persistent work-groups).  Checked against the oracle through every entry
+point that takes such a plan: attend_decode, the attend_partition /
+attend_combine pair, and decode_step (the append in the same launch, the
+lengths and drops written by the balance kernel).  Shapes cover empty,
+negative, full and past-the-cache lengths, one long sequence among tiny
+ones, fewer items than work-groups, every compiled head shape, the additive
+bias, carry_in and fp8 caches.  The queue the balance kernel builds is
+checked word for word."""
 
 import math
 
@@ -33,16 +31,47 @@ def _gqa():
     return g
 
 
-def _check_prefix(ws, plan, lens, w):
-    """pre[b] = Hkv * sum_{b' < b} ceil(n_b' / 32), pre[B] the total."""
-    assert plan.balanced_groups > 0, "balanced plan expected"
+def _phase_runs(nt):
+    """The three phases of a sequence of nt tiles: runs of 128 tiles over
+    the whole runs of its first 3/4, of 32 up to 23/25, of 8 over the rest."""
+    e0 = nt * 3 // 4 // 128 * 128
+    e1 = e0 + max(nt * 23 // 25 - e0, 0) // 32 * 32
+    return [(0, e0, 128), (e0, e1, 32), (e1, nt, 8)]
+
+
+def _check_queue(ws, plan, lens, w, launched=True):
+    """The work queue, word for word: the runs phase by phase and sequence
+    by sequence, each sequence's first run per phase, the item count; after
+    the partition launch the counter has passed every item once and each of
+    the 512 work-groups' final fetch."""
+    assert plan.balanced_groups == 512, "balanced plan expected"
     t = ws[plan.off_sched:plan.off_sched + 4 * plan.sched_entries]
-    pre = t.cpu().view(torch.int32).numpy()
+    q = t.cpu().view(torch.int32).numpy().astype(np.int64)
+    B = w.batch
     n = np.clip(np.asarray(lens, dtype=np.int64), 0, w.max_len)
-    tiles = (n + TILE - 1) // TILE
-    want = np.concatenate([[0], np.cumsum(tiles)]) * w.num_kv_heads
-    assert pre.tolist() == want.tolist(), "tile prefix"
-    return int(want[-1])
+    nt = (n + TILE - 1) // TILE
+    runs, base, pre = [], [], []
+    for k in range(3):
+        base.append(len(runs))
+        pk = []
+        for b in range(B):
+            pk.append(len(runs) - base[k])
+            s, e, L = _phase_runs(int(nt[b]))[k]
+            runs += [(b, s + j * L, min(s + (j + 1) * L, e))
+                     for j in range(-(-(e - s) // L))]
+        pk.append(len(runs) - base[k])
+        pre.append(pk)
+    base.append(len(runs))
+    items = len(runs) * w.num_kv_heads
+    assert q[1] == items, "item count"
+    assert q[2:6].tolist() == base, "phase starts"
+    off = 6 + 3 * (B + 1)
+    assert q[6:off].reshape(3, B + 1).tolist() == pre, "runs per sequence"
+    got = q[off:off + 3 * len(runs)].reshape(-1, 3)
+    assert got.tolist() == [list(r) for r in runs], "runs"
+    if launched:
+        assert q[0] == items + 512, "every item taken once"
+    return items
 
 
 def _random_carry(rows, dv, seed):
@@ -162,8 +191,8 @@ def test_balanced_attend_decode(name):
     out = g.attend_decode(d["q"], d["k"], d["v"], d["lens"], w.scale,
                           carry_in=c, carry_out=c, workspace=ws)
     torch.cuda.synchronize()
-    total = _check_prefix(ws, plan, lens, w)
-    say(f"  tiles {total} over {plan.balanced_groups} ranges")
+    items = _check_queue(ws, plan, lens, w)
+    say(f"  {items} queue items over {plan.balanced_groups} work-groups")
     _oracle_check(x, w, out, c, f"balanced attend_decode {name}",
                   carry_in=cin)
 
@@ -192,7 +221,7 @@ def test_balanced_partition_combine(name):
     out = g.attend_combine(w.num_q_heads, d["k"], d["v"], d["lens"], plan, ws,
                            carry_in=_dev_carry(cin), carry_out=cout)
     torch.cuda.synchronize()
-    _check_prefix(ws, plan, lens, w)
+    _check_queue(ws, plan, lens, w)
     _oracle_check(x, w, out, cout, f"balanced partition/combine {name}",
                   carry_in=cin)
 
@@ -244,7 +273,7 @@ def test_balanced_decode_step(name, with_bias):
     assert np.array_equal(bits(d["v"].cpu()).numpy(), v_ref), "V after append"
     assert lo.cpu().numpy().tolist() == l_ref.tolist(), "lens"
     assert int(dropped.item()) == n_drop, "drops"
-    _check_prefix(ws, plan, l_ref, w)
+    _check_queue(ws, plan, l_ref, w)
     xa = {"q": x["q"], "k": torch.from_numpy(k_ref).view(w.torch_dtype),
           "v": torch.from_numpy(v_ref).view(w.torch_dtype),
           "lens": torch.from_numpy(l_ref.astype(np.int32))}
@@ -284,7 +313,7 @@ def test_balanced_decode_step_fp8():
     assert lo.cpu().tolist() == l2.tolist(), "lens"
     assert np.array_equal(kc.codes.cpu().numpy(), k2), "K codes"
     assert np.array_equal(vc.codes.cpu().numpy(), v2), "V codes"
-    _check_prefix(ws, plan, l2, w)
+    _check_queue(ws, plan, l2, w)
     ref, cref = of8.attend_fp8(np64(x["q"]), k2, v2,
                                x["k_scale"].double().numpy(),
                                x["v_scale"].double().numpy(), l2, w.scale)

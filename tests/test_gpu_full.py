@@ -2,7 +2,7 @@
 against the oracle on every (sequence, KV group) unit, plus properties that
 hold at any size on every row (finite outputs, each output a convex
 combination of value rows, 1 <= l <= n for the carry).  The ragged
-workload's balanced launch also has its tile prefix checked."""
+workload's balanced launch also has its work queue checked."""
 
 import numpy as np
 import pytest
@@ -11,7 +11,7 @@ import torch
 import oracle
 from gpu_util import (check_carry, check_out, live_vmax, np64, oracle_rows,
                       say, to_dev)
-from test_gpu_balanced import _check_prefix
+from test_gpu_balanced import _check_queue
 from gqa_kv_cache_decode_amd import workloads as wl
 
 pytestmark = pytest.mark.gpu
@@ -88,7 +88,7 @@ def test_full_batched_bf16():
 def test_full_ragged_bf16():
     """Every (sequence, KV group) unit of the ragged batch, through the
     partition / combine pair with the library's own (balanced) plan, whose
-    device-built tile prefix is checked too."""
+    device-built work queue is checked too."""
     g = _gqa()
     w = wl.RAGGED_BF16
     say("[full] ragged: drawing 8 GiB of K/V")
@@ -103,7 +103,7 @@ def test_full_ragged_bf16():
     torch.cuda.synchronize()
     got = out.cpu().numpy()
     assert plan.balanced_groups > 0, "balanced plan expected"
-    _check_prefix(ws, plan, x["lens"], w)
+    _check_queue(ws, plan, x["lens"], w)
     del d, ws
     torch.cuda.empty_cache()
     units = [(b, g_) for b in range(w.batch) for g_ in range(w.num_kv_heads)]
