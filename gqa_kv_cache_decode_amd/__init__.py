@@ -13,7 +13,8 @@ __all__ = ["kv_append", "attend_decode", "softmax_state_merge",
            "stream_append", "decode_step_branches", "attend_gathered",
            "attend_partition", "attend_combine", "attend_plan",
            "workspace_bytes", "Carry", "Fp8Cache", "empty_carry", "GqaError",
-           "library", "profile_next_launch", "CHUNK_BALANCED"]
+           "library", "profile_next_launch", "CHUNK_BALANCED",
+           "attend_decode_noalloc"]
 
 
 def __getattr__(name):

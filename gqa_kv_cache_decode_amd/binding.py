@@ -93,6 +93,9 @@ _SIGNATURES = {
     "gqa_attend_decode": (_I32, [_P, _I32, _CACHE_P, _P, ctypes.c_float,
                                  _P, ctypes.c_int64, _CARRY_P, _CARRY_P, _P,
                                  _P, ctypes.c_size_t, _P]),
+    "gqa_attend_decode_noalloc": (_I32, [_P, _I32, _CACHE_P, _P,
+                                         ctypes.c_float, _P, ctypes.c_int64,
+                                         _CARRY_P, _CARRY_P, _P, _P]),
     "gqa_attend_partition": (_I32, [_P, _I32, _CACHE_P, _P, ctypes.c_float,
                                     _P, ctypes.c_int64, _PLAN_P, _P,
                                     ctypes.c_size_t, _P]),
@@ -335,6 +338,25 @@ def attend_decode(q, k_cache, v_cache, lens, scale: float = 0.0,
         cout,
         _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(q)), "attend_decode")
+    return out
+
+
+def attend_decode_noalloc(q, k_cache, v_cache, lens, scale: float = 0.0,
+                          carry_in: Optional[Carry] = None,
+                          carry_out: Optional[Carry] = None, out=_AUTO,
+                          bias=None):
+    """attend_decode on the library's own device scratch array (no
+    workspace argument): for callers that cannot allocate.  ``out`` as in
+    attend_decode (pass an existing tensor to allocate nothing here)."""
+    c, hq = _attend_args(q, k_cache, v_cache, lens)
+    bp, bs = _bias(c, bias)
+    if out is _AUTO:
+        out = torch.empty(c.batch, hq, c.dv, dtype=torch.float32,
+                          device=q.device)
+    cin, cout = _carries(c, hq, carry_in, carry_out, out)
+    _check(library().gqa_attend_decode_noalloc(
+        _ptr(q), hq, ctypes.byref(c), _ptr(lens), float(scale), bp, bs, cin,
+        cout, _ptr(out), _stream(q)), "attend_decode_noalloc")
     return out
 
 

@@ -25,6 +25,7 @@ BENCH_LIB = PKG / "libgqa_bench.so"   # measurement helpers, not the decode ABI
 ARCH = "gfx950"
 
 SOURCES = ["abi.cpp", "append.hip", "partition_bf16.hip", "partition_fp8.hip",
+           "noalloc.hip",
            "partition_f32.hip",
            "combine.hip", "schedule.hip"]
 BENCH_SOURCES = ["bench_kernels.hip"]

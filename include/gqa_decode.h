@@ -303,6 +303,32 @@ GQA_API gqa_status gqa_attend_decode(const void *q, int32_t num_q_heads,
                              hipStream_t stream);
 
 /*
+ * attend_decode_noalloc — gqa_attend_decode without a workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  It
+ * allocates nothing: its scratch is a 32 MiB array of the library's own that
+ * every GPU the library runs on holds from the library's load until the
+ * process ends.  Arguments as in gqa_attend_decode; the same kernels run.
+ *   A call whose plan needs more than 32 MiB of workspace (more than
+ *   gqa_attend_workspace_bytes reports would fit) returns
+ *   GQA_ERR_WORKSPACE_TOO_SMALL; every argument check is made before any
+ *   HIP call.  The first call on a device resolves the array's address on
+ *   that device (the current device; `stream`, if not NULL, must belong to
+ *   it, else GQA_ERR_INVALID_ARGUMENT).
+ *   Every call on one GPU shares that GPU's array: calls that overlap on one
+ *   GPU (concurrent streams or host threads) race; calls in stream order do
+ *   not.
+ */
+GQA_API gqa_status gqa_attend_decode_noalloc(const void *q, int32_t num_q_heads,
+                                             const gqa_cache *cache,
+                                             const int32_t *lens, float scale,
+                                             const float *bias,
+                                             int64_t bias_stride,
+                                             const gqa_carry *carry_in,
+                                             const gqa_carry *carry_out,
+                                             float *out, hipStream_t stream);
+
+/*
  * First half of attend_decode with an explicit plan: writes the partial
  * carries of every live (query row, chunk) into the workspace (layout in
  * gqa_plan).  Arguments as in gqa_attend_decode.

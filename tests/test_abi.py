@@ -30,7 +30,7 @@ def _declared():
 
 def test_exports_every_declared_symbol(lib):
     names = _declared()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     for n in names:
         assert hasattr(lib, n), f"missing export {n}"
     assert set(names) == set(bd._SIGNATURES), "binding covers the header"
@@ -432,3 +432,27 @@ def test_balanced_plan_tampering_is_rejected(lib):
                                       ctypes.byref(bad), P(0x60000),
                                       p.workspace_bytes, None)
         assert st == SHAPE, field
+
+
+def test_noalloc_rejects_before_any_hip_call(lib):
+    """The allocation-free attend_decode checks its arguments, and that its
+    plan fits the library's 32 MiB scratch array, before any HIP call (so
+    these run on a machine without a GPU)."""
+    P = ctypes.c_void_p
+    big = _cache(B=64, T=1 << 20, H=8, dtype=0)   # fp32 chunked: > 32 MiB
+    assert lib.gqa_attend_workspace_bytes(ctypes.byref(big), 64) > 32 << 20
+    out = P(0x70000)
+    st = lib.gqa_attend_decode_noalloc(P(0x40000), 64, ctypes.byref(big),
+                                       P(0x50000), 0.0, None, 0, None, None,
+                                       out, None)
+    assert st == WORKSPACE
+    c = _cache()
+    assert lib.gqa_attend_decode_noalloc(None, 32, ctypes.byref(c),
+                                         P(0x50000), 0.0, None, 0, None, None,
+                                         out, None) == INVALID
+    assert lib.gqa_attend_decode_noalloc(P(0x40000), 30, ctypes.byref(c),
+                                         P(0x50000), 0.0, None, 0, None, None,
+                                         out, None) == SHAPE
+    assert lib.gqa_attend_decode_noalloc(P(0x40000), 32, ctypes.byref(c),
+                                         P(0x50000), float("nan"), None, 0,
+                                         None, None, out, None) == INVALID
