@@ -38,6 +38,11 @@ COMMON = [
 ]
 # Packed fp32 VALU ops stay off: the compiler must not form them by itself.
 DEVICE_ONLY = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# The partition kernels take work-queue items with a single-lane atomic whose
+# result is needed only after the current item: the wave-level atomic
+# rewrite would wait for it at once (it combines the lanes' results).
+PER_SOURCE = {s: ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]
+              for s in ("partition_bf16.hip", "partition_fp8.hip")}
 
 
 def hipcc() -> str:
@@ -52,6 +57,7 @@ def _compile(src: str) -> Path:
     cmd = [hipcc(), *COMMON]
     if src.endswith(".hip"):
         cmd += DEVICE_ONLY
+    cmd += PER_SOURCE.get(src, [])
     cmd += ["-c", str(CSRC / src), "-o", str(obj)]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
