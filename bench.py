@@ -129,20 +129,42 @@ def kv_bytes(w, lens_total, hkv=None):
     return lens_total * (hkv or w.num_kv_heads) * (w.dk + w.dv) * w.esz
 
 
-def kernel_name(w, bias, gather, step=True):
+def library_plan(w):
+    """The library's own plan for the workload's cache (a host-only call)."""
+    from gqa_kv_cache_decode_amd import binding as bd
+    dt = {"f32": 0, "bf16": 1, "fp8": 2}[w.dtype]
+    sc = 0x30000 if w.dtype == "fp8" else None
+    c = bd._Cache(0x10000, 0x20000, w.batch, w.max_len, w.num_kv_heads, w.dk,
+                  w.dv, dt, sc, sc)
+    p = bd.Plan()
+    st = bd.library().gqa_attend_plan(ctypes.byref(c), w.num_q_heads, 0,
+                                      ctypes.byref(p))
+    assert st == 0, "no plan for the workload"
+    return p
+
+
+def kernel_name(w, bias, gather, step=True, balanced=None):
     """The partition kernel's name as the profiler prints it (template
     arguments: head widths, wavefronts, decode step, bias, gathered, and fp8
-    for the bf16 / fp8 family)."""
+    for the bf16 / fp8 family; a balanced plan's kernel has no gathered
+    form).  `balanced`: whether the library's plan is balanced (asked from
+    the library when None)."""
     tf = lambda b: "true" if b else "false"
-    flags = f"{tf(step)}, {tf(bias)}, {tf(gather)}"
     if w.dtype == "f32":
+        flags = f"{tf(step)}, {tf(bias)}, {tf(gather)}"
         return f"partition_f32_mfma_kernel<{w.dk}, {w.dv}, 4, {flags}>"
     if w.dtype == "fp8":
         waves = 8 if w.dk + w.dv <= 128 else 4
     else:
         waves = 2
-    return (f"partition_bf16_kernel<{w.dk}, {w.dv}, {waves}, {flags}, "
-            f"{tf(w.dtype == 'fp8')}>")
+    if balanced is None:
+        balanced = not gather and library_plan(w).balanced_groups > 0
+    fp8 = tf(w.dtype == "fp8")
+    if balanced:
+        return (f"partition_balanced_kernel<{w.dk}, {w.dv}, {waves}, "
+                f"{tf(step)}, {tf(bias)}, {fp8}>")
+    return (f"partition_bf16_kernel<{w.dk}, {w.dv}, {waves}, {tf(step)}, "
+            f"{tf(bias)}, {tf(gather)}, {fp8}>")
 
 
 # ---------------------------------------------------------------------------
@@ -344,7 +366,8 @@ class LongCase(Case):
                 self.new_row_bytes() + self.fixed_bytes() + self.out_bytes())
 
     def kernel(self):
-        return kernel_name(self.w, False, False)
+        # the branches' launch is never balanced
+        return kernel_name(self.w, False, False, balanced=False)
 
     def gpu(self, copies):
         return LongGpu(self, copies)
@@ -375,7 +398,7 @@ class StreamCase(Case):
                 5 * w.batch * 4 + self.out_bytes())
 
     def kernel(self):
-        return kernel_name(self.w, False, False, step=False)
+        return kernel_name(self.w, False, False, step=False, balanced=False)
 
     def gpu(self, copies):
         return StreamGpu(self, copies)
@@ -392,7 +415,7 @@ class GatherCase(Case):
         self.bias = False
 
     def kernel(self):
-        return kernel_name(self.w, False, True, step=False)
+        return kernel_name(self.w, False, True, step=False, balanced=False)
 
     def gpu(self, copies):
         return GatherGpu(self, copies)

@@ -157,3 +157,16 @@ def test_source_hash_ignores_comments_only():
     b = "int f()  {\n  return 1;\n}"
     assert bench.code_text(a) == bench.code_text(b)
     assert bench.code_text("int f() { return 2; }") != bench.code_text(b)
+
+
+def test_kernel_names_follow_the_plan():
+    """The ragged batch runs the balanced (work-queue) kernel, the other
+    workloads the chunked one."""
+    names = {n: bench.workload_by_name(n) for n in bench.DEFAULT_SET}
+    assert bench.kernel_name(names["ragged"], False, False).startswith(
+        "partition_balanced_kernel<128, 128, 2, true, false, false>")
+    for n in ("batched", "spike"):
+        assert bench.kernel_name(names[n], False, False).startswith(
+            "partition_bf16_kernel<")
+    assert bench.kernel_name(names["tiny"], False, False).startswith(
+        "partition_f32_mfma_kernel<64, 64, 4, true")
