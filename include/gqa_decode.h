@@ -26,11 +26,14 @@
  *    before the checks pass.  GQA_ERR_DEVICE reports a failed launch.
  *  - All sizes are element counts unless named *_bytes.
  *  - q, cache->k, cache->v and the workspace must be 16-byte aligned.
- *  - Shapes with a kernel: bf16 and fp8 caches with (dk, dv) in {(64, 64),
- *    (128, 128), (192, 128), (256, 256)} and 1..16 query heads per KV head
- *    (matrix-core path); fp32 caches with dk, dv multiples of 4 up to 256,
- *    1..16 query heads per KV head and a 64-token tile that fits 64 KiB of
- *    LDS (vector ALU path).
+ *  - Shapes with a kernel: bf16, fp8 and fp32 caches with (dk, dv) in
+ *    {(64, 64), (128, 128), (192, 128), (256, 256)} and 1..16 query heads per
+ *    KV head run on the matrix cores (MFMA 16x16x32 bf16, or the exact-fp32
+ *    MFMA 16x16x4 for fp32 caches); fp32 caches with other head widths —
+ *    multiples of 4 up to 256, 1..16 query heads per KV head and a 64-token
+ *    tile that fits 64 KiB of LDS — run on the vector ALUs (every entry point
+ *    but gqa_attend_branches, gqa_decode_step_branches and
+ *    gqa_attend_gathered, which need a matrix-core shape).
  *  - fp8 caches (GQA_DTYPE_FP8_E4M3): queries and new K/V rows are bf16.
  *  - Errors: GQA_ERR_INVALID_ARGUMENT (a required pointer is NULL, a size is
  *    non-positive, a scale is not finite), GQA_ERR_SHAPE_MISMATCH (the query
