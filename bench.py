@@ -110,6 +110,11 @@ def parse_args(argv=None):
     p.add_argument("--bias", action="store_true",
                    help="attend with an additive logit bias (fp32 per "
                         "sequence and position, N(0, 1))")
+    p.add_argument("--set", action="append", default=[], metavar="FIELD=N",
+                   help="replace an integer field of the workload's shape "
+                        "(batch, num_q_heads, num_kv_heads, dk, dv, max_len; "
+                        "repeatable), for sweeps and counter runs of one "
+                        "workload; its traffic record then does not apply")
     p.add_argument("--profile-pass", action="store_true",
                    help="no timing: a few eager steps of one workload and "
                         f"three {COPY_BYTES >> 20} MiB calibration copies, "
@@ -123,6 +128,26 @@ def workload_by_name(name):
             "ragged": wl.RAGGED_BF16, "long": wl.LONG_WINDOW_BF16,
             "spike": wl.WIDE_SPIKE_BF16, "stream": wl.LONG_WINDOW_BF16,
             "gather": wl.GATHER_BF16, "fp8": wl.BATCHED_FP8}[name]
+
+
+SHAPE_FIELDS = ("batch", "num_q_heads", "num_kv_heads", "dk", "dv", "max_len")
+
+
+def shaped_workload(name, overrides):
+    """The named workload with `overrides` ("field=N" strings) applied; the
+    name records them."""
+    w = workload_by_name(name)
+    if not overrides:
+        return w
+    kv = {}
+    for item in overrides:
+        field, _, val = item.partition("=")
+        if field not in SHAPE_FIELDS or not val.lstrip("-").isdigit():
+            raise SystemExit(f"--set {item}: expected one of "
+                             f"{', '.join(SHAPE_FIELDS)} = an integer")
+        kv[field] = int(val)
+    tag = "_".join(f"{k}{v}" for k, v in kv.items())
+    return w.replace(name=f"{w.name}+{tag}", **kv)
 
 
 def kv_bytes(w, lens_total, hkv=None):
@@ -200,7 +225,7 @@ class Case:
     def __init__(self, name, args):
         from gqa_kv_cache_decode_amd import workloads as wl
         self.name = name
-        self.w = workload_by_name(name)
+        self.w = shaped_workload(name, args.set)
         self.args = args
         self.bias = bool(args.bias)
         w = self.w
@@ -917,8 +942,8 @@ def gpu_phase(torch, case, args, oracle_res):
         "kernel_bytes": dom_bytes,
         "kernel_gbs": round(kgbs, 1),
         "kernel_hbm_frac": round(kgbs / HBM_PEAK_GBS, 4),
-        "kernel_traffic": measured_traffic(profile_name(case.name, case.bias),
-                                           w.dtype, kernel),
+        "kernel_traffic": None if case.args.set else measured_traffic(
+            profile_name(case.name, case.bias), w.dtype, kernel),
         "parity": (check_outputs(case, out, oracle_res["outs"])
                    if oracle_res else None),
     }

@@ -170,3 +170,19 @@ def test_kernel_names_follow_the_plan():
             "partition_bf16_kernel<")
     assert bench.kernel_name(names["tiny"], False, False).startswith(
         "partition_f32_mfma_kernel<64, 64, 4, true")
+
+
+def test_shape_overrides():
+    """--set replaces integer shape fields, names the result after them, and
+    rejects anything else."""
+    args = bench.parse_args(["--workload", "tiny", "--set", "max_len=1024",
+                             "--set", "batch=2"])
+    w = bench.shaped_workload("tiny", args.set)
+    base = bench.workload_by_name("tiny")
+    assert (w.max_len, w.batch) == (1024, 2)
+    assert w.name == base.name + "+max_len1024_batch2"
+    assert w.replace(name=base.name, max_len=base.max_len, batch=base.batch) == base
+    assert bench.shaped_workload("tiny", []) is base
+    for bad in (["dtype=1"], ["dk=x"], ["scale=2"]):
+        with pytest.raises(SystemExit):
+            bench.shaped_workload("tiny", bad)
