@@ -615,7 +615,7 @@ def gather_bytes(case, gpu):
     from gqa_kv_cache_decode_amd import workloads as wl
     w = case.w
     # the distinct selected rows (mean over the index sets), q, the index
-    # rows read by the selection kernel, the output
+    # rows (read by the partition launch, which selects), the output
     return (kv_bytes(w, gpu.n_sel) + w.batch * w.num_q_heads * w.dk * w.q_esz +
             w.batch * wl.GATHER_WIDTH * 4 + case.out_bytes())
 
@@ -917,7 +917,7 @@ def gpu_phase(torch, case, args, oracle_res):
     kgbs = dom_bytes / (kavg * 1e-3) / 1e9
     kernel = case.kernel()
     if isinstance(case, GatherCase):
-        kernel = f"attend_gathered: select_kernel + {kernel} + combine_kernel"
+        kernel = f"attend_gathered: {kernel} + combine_kernel"
     res = {
         "workload": w.name, "kv_dtype": "fp8_e4m3" if w.dtype == "fp8"
         else w.dtype,

@@ -308,7 +308,9 @@ void single_branch(PartitionArgs *a) {
   a->total_items = a->batch * a->num_kv_heads * a->num_chunks;
   a->num_extra = 0;
   a->append_branch = 0;
-  a->sel = nullptr;
+  a->idx = nullptr;
+  a->width = 0;
+  a->sel_count = nullptr;
   a->cache_len = a->max_len;
 }
 
@@ -598,7 +600,9 @@ gqa_status branches_checked(const void *q, int32_t num_q_heads,
   a.total_items = (int)p.total_items;
   a.num_extra = num_branches - 1;
   a.append_branch = step ? step->append_branch : -1;
-  a.sel = nullptr;
+  a.idx = nullptr;
+  a.width = 0;
+  a.sel_count = nullptr;
   a.cache_len = c0->max_len;
   set_storage(&a, c0);
   for (int32_t i = 1; i < num_branches; ++i) {
@@ -667,15 +671,19 @@ gqa_status branches_checked(const void *q, int32_t num_q_heads,
 
 // Layout of an index-gathered attend: the split-K plan of the selection
 // (a cache of min(width, max_len) slots per sequence, chunks of at most
-// kGatherChunk), then the selected slots [batch][sel_cap] and their counts.
+// kGatherChunk), then the selection sizes [batch] the partition launch
+// writes for the combine.
 struct GatherPlan {
   gqa_cache vcache;
   gqa_plan plan;
   int32_t sel_cap;
-  size_t off_sel, off_count, workspace_bytes;
+  size_t off_count, workspace_bytes;
 };
 
-constexpr int32_t kGatherMaxLen = 1 << 20;  // LDS bitmap of the selection
+// Longest cache an index-gathered launch takes: each of its work-groups
+// rebuilds the sequence's selection over the live length, one LDS bitmap
+// window at a time.
+constexpr int32_t kGatherMaxLen = 1 << 20;
 
 gqa_status plan_gathered(const gqa_cache *c, int32_t hq, int32_t width,
                          GatherPlan *g) {
@@ -695,9 +703,7 @@ gqa_status plan_gathered(const gqa_cache *c, int32_t hq, int32_t width,
   // kGatherChunk slots
   const int32_t chunk = std::min(auto_chunk(&g->vcache), gqa::kGatherChunk);
   if ((st = make_plan(&g->vcache, hq, chunk, &g->plan)) != GQA_OK) return st;
-  g->off_sel = g->plan.workspace_bytes;
-  g->off_count =
-      g->off_sel + align_up((size_t)c->batch * g->sel_cap * sizeof(int32_t));
+  g->off_count = g->plan.workspace_bytes;
   g->workspace_bytes =
       g->off_count + align_up((size_t)c->batch * sizeof(int32_t));
   return GQA_OK;
@@ -1010,22 +1016,11 @@ gqa_status gqa_attend_gathered(const void *q, int32_t num_q_heads,
   if (!workspace || !aligned16(workspace)) return GQA_ERR_INVALID_ARGUMENT;
   if (workspace_bytes < g.workspace_bytes) return GQA_ERR_WORKSPACE_TOO_SMALL;
   char *base = static_cast<char *>(workspace);
-  int32_t *sel = reinterpret_cast<int32_t *>(base + g.off_sel);
   int32_t *count = reinterpret_cast<int32_t *>(base + g.off_count);
 
-  gqa::SelectArgs sa;
-  sa.idx = idx;
-  sa.width = width;
-  sa.lens = lens;
-  sa.batch = cache->batch;
-  sa.max_len = cache->max_len;
-  sa.sel = sel;
-  sa.sel_stride = g.sel_cap;
-  sa.count = count;
-  if ((st = device_status(gqa::launch_select(sa, stream))) != GQA_OK) return st;
-
-  // the selection attended as a cache of sel_cap slots whose token t is
-  // cache slot sel[b][t]
+  // the selection attended as a cache of at most sel_cap keys: the partition
+  // launch's work-groups select from the index rows themselves and write
+  // each sequence's selection size for the combine
   const gqa::StepParams ep =
       final_epilogue(&g.vcache, g.plan, carry_in, carry_out, out);
   const double sc =
@@ -1034,7 +1029,7 @@ gqa_status gqa_attend_gathered(const void *q, int32_t num_q_heads,
   a.q = q;
   a.k = cache->k;
   a.v = cache->v;
-  a.lens = count;
+  a.lens = lens;
   a.batch = cache->batch;
   a.max_len = g.sel_cap;
   a.num_kv_heads = cache->num_kv_heads;
@@ -1045,7 +1040,9 @@ gqa_status gqa_attend_gathered(const void *q, int32_t num_q_heads,
   a.num_chunks = g.plan.num_chunks;
   single_branch(&a);
   set_storage(&a, cache);
-  a.sel = sel;
+  a.idx = idx;
+  a.width = width;
+  a.sel_count = count;
   a.cache_len = cache->max_len;
   a.scale_log2 = (float)(sc * 1.4426950408889634);
   a.bias = nullptr;

@@ -102,41 +102,108 @@ __global__ __launch_bounds__(THREADS) void combine_kernel(CombineArgs a) {
 // base[k] + pre_k[b] .. base[k] + pre_k[b + 1] - 1; queue item r *
 // num_kv_heads + g (g the row's KV group) left its piece in that slot.  The
 // pieces and carry_in fold by log-sum-exp merge.
+//
+// The fold is shaped for latency: the three phases' bounds are read in one
+// round, then every piece's m and l (one piece per thread, into LDS) and
+// each column's first kCombineRegs values go out together; the weights
+// 2^(m_i - M) are formed from LDS by every thread, so no piece waits for the
+// one before it.  More pieces than a batch of LDS slots fold batch by batch
+// with the usual rescale.
+constexpr int kCombineRegs = 16;
+constexpr int kCombineBatch = 512;
+
+// Slot of piece i of a row whose phases hold n0, n01 - n0 and the rest of
+// its pieces, from runs r0 + i, r1 + i and r2 + i (r1, r2 offset by the
+// earlier phases' counts).
+__device__ __forceinline__ size_t piece_slot(int i, int n0, int n01, int r0,
+                                             int r1, int r2,
+                                             size_t run_stride, size_t col) {
+  const int r = i < n0 ? r0 + i : i < n01 ? r1 + i : r2 + i;
+  return (size_t)r * run_stride + col;
+}
+
 __global__ __launch_bounds__(256) void combine_balanced_kernel(CombineArgs a) {
+  __shared__ int s_r0[kQueuePhases], s_n[kQueuePhases];
+  __shared__ float s_m[kCombineBatch], s_l[kCombineBatch];
   const int row = blockIdx.x;
-  const int d = threadIdx.x;
+  const int d = threadIdx.x, nt = blockDim.x;
   const int Hq = a.num_q_heads, hpk = a.hpk, Hkv = Hq / hpk;
   const int b = row / Hq, h = row % Hq, g = h / hpk, hh = h % hpk;
   const int B = a.batch;
   const bool worker = d < a.dv;
-  // carry_in is read before the barrier below: carry_out may alias it
+  // carry_in is read before the barriers below: carry_out may alias it
   const float in_l = a.in_l ? a.in_l[row] : 0.0f;
   const float in_m = in_l > 0.0f ? a.in_m[row] : -INFINITY;
   const float in_acc =
       in_l > 0.0f && worker ? a.in_acc[(size_t)row * a.dv + d] : 0.0f;
+  if (d < kQueuePhases) {
+    const int *pre = a.queue + kQueuePre + d * (B + 1);
+    s_r0[d] = a.queue[kQueueBase + d] + pre[b];
+    s_n[d] = pre[b + 1] - pre[b];
+  }
+  __syncthreads();
+  const int n0 = s_n[0], n01 = n0 + s_n[1], n = n01 + s_n[2];
+  const int r0 = s_r0[0], r1 = s_r0[1] - n0, r2 = s_r0[2] - n01;
+  const size_t col = (size_t)g * hpk + hh;
+  const size_t run_stride = (size_t)Hkv * hpk;
+  auto slot = [=](int i) {
+    return piece_slot(i, n0, n01, r0, r1, r2, run_stride, col);
+  };
+  // The loads carry no branch of their own (a branch per load would make the
+  // compiler wait for each before the next): pieces past n repeat the last.
+  const int dd = worker ? d : 0;
+  float av[kCombineRegs];
+  if (n > 0) {
+#pragma unroll
+    for (int i = 0; i < kCombineRegs; ++i)
+      av[i] = a.part_acc[slot(min(i, n - 1)) * a.dv + dd];
+  }
+
   float m = -INFINITY, L = 0.0f, acc = 0.0f;  // base-2 running state
-  auto fold = [&](float mi, float li, float ai) {
-    // a piece whose keys were all removed by the bias has m = -inf, l = 0
+  for (int i0 = 0; i0 < n; i0 += kCombineBatch) {
+    const int nb = min(kCombineBatch, n - i0);
+    for (int i = d; i < nb; i += nt) {
+      const size_t pr = slot(i0 + i);
+      const float li = a.part_l[pr], mi = a.part_m[pr];
+      // a piece whose keys were all removed by the bias has l = 0
+      s_m[i] = li > 0.0f ? mi * kLog2e : -INFINITY;
+      s_l[i] = li;
+    }
+    __syncthreads();
+    float mb = -INFINITY;
+    for (int i = 0; i < nb; ++i) mb = fmaxf(mb, s_m[i]);
+    const float mn = fmaxf(m, mb), ref = exp_ref(mn);
+    const float fo = fast_exp2(m - ref);
+    acc *= fo;
+    L *= fo;
+    m = mn;
+    int i = 0;
+    if (i0 == 0) {
+#pragma unroll
+      for (int j = 0; j < kCombineRegs; ++j) {
+        const int jj = min(j, nb - 1);
+        const float w = j < nb ? fast_exp2(s_m[jj] - ref) : 0.0f;
+        L += w * s_l[jj];
+        acc += w * av[j];
+      }
+      i = kCombineRegs;
+    }
+#pragma unroll 8
+    for (; i < nb; ++i) {
+      const float w = fast_exp2(s_m[i] - ref);
+      L += w * s_l[i];
+      if (worker) acc += w * a.part_acc[slot(i0 + i) * a.dv + d];
+    }
+    __syncthreads();  // the batch's LDS slots are read before the next fill
+  }
+  if (in_l > 0.0f) {
+    const float mi = in_m * kLog2e;
     const float mn = fmaxf(m, mi), ref = exp_ref(mn);
     const float fo = fast_exp2(m - ref), fi = fast_exp2(mi - ref);
-    acc = acc * fo + ai * fi;
-    L = L * fo + li * fi;
+    acc = acc * fo + in_acc * fi;
+    L = L * fo + in_l * fi;
     m = mn;
-  };
-  if (worker) {
-    for (int k = 0; k < kQueuePhases; ++k) {
-      const int *pre = a.queue + kQueuePre + k * (B + 1);
-      const int base = a.queue[kQueueBase + k];
-      const int r1 = base + pre[b + 1];
-#pragma unroll 4
-      for (int r = base + pre[b]; r < r1; ++r) {
-        const size_t pr = ((size_t)r * Hkv + g) * hpk + hh;
-        fold(a.part_m[pr] * kLog2e, a.part_l[pr], a.part_acc[pr * a.dv + d]);
-      }
-    }
   }
-  if (in_l > 0.0f) fold(in_m * kLog2e, in_l, in_acc);
-  __syncthreads();  // every thread has read carry_in
   if (!worker) return;
   const bool live = L > 0.0f;
   if (a.out) a.out[(size_t)row * a.dv + d] = live ? acc / L : 0.0f;

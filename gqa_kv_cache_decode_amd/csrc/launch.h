@@ -74,11 +74,15 @@ struct PartitionArgs {
   const float *bias;    // [B][bias_stride] additive logit terms, or NULL
   long long bias_stride;
   int has_bias;         // any branch of the launch has a bias
-  // Index-gathered launch: token t < lens[b] of sequence b is cache slot
-  // sel[b * max_len + t] (max_len is then the selection's row width) of a
-  // cache holding cache_len slots per sequence.  NULL otherwise, with
-  // cache_len = max_len.
-  const int32_t *sel;
+  // Index-gathered launch: sequence b attends the distinct slots below
+  // clamp(lens[b], 0, cache_len) that its index row idx[b * width ..
+  // + width) names, in ascending order, as a cache of that many keys
+  // (max_len is then the selection's capacity, min(width, cache_len)); the
+  // launch writes each sequence's selection size to sel_count[b].  NULL
+  // otherwise, with cache_len = max_len.
+  const int32_t *idx;
+  int width;
+  int32_t *sel_count;
   int cache_len;
   float *part_m;        // [rows][num_chunks]  (natural-log units)
   float *part_l;        // [rows][num_chunks]
@@ -211,19 +215,6 @@ struct StreamAppendArgs {
   const float *k_scale, *v_scale;  // [B][Hkv] each
 };
 
-// Index-row selection (DSA topk_to_mask): per sequence, the distinct cache
-// slots s < clamp(lens[b], 0, max_len) named by idx[b][0..width), ascending,
-// into sel[b][0..count[b]) (row stride sel_stride).
-struct SelectArgs {
-  const int32_t *idx;
-  int width;
-  const int32_t *lens;
-  int batch, max_len;
-  int32_t *sel;
-  int sel_stride;
-  int32_t *count;
-};
-
 // Longest chunk of an index-gathered launch (its slots are staged in LDS).
 constexpr int kGatherChunk = 2048;
 
@@ -259,7 +250,5 @@ constexpr int kBalanceTile = 32;  // tokens per tile of a balanced plan
 hipError_t launch_merge(const MergeArgs &a, hipStream_t s);
 hipError_t launch_append(const AppendArgs &a, hipStream_t s);
 hipError_t launch_stream_append(const StreamAppendArgs &a, hipStream_t s);
-size_t select_lds_bytes(int max_len);
-hipError_t launch_select(const SelectArgs &a, hipStream_t s);
 
 }  // namespace gqa

@@ -15,6 +15,7 @@
 // query heads (needle-core attn.rs: each KV head serves its query heads by
 // broadcast).
 #include "device_common.h"
+#include "gather_common.h"
 #include "launch.h"
 #include "step_common.h"
 
@@ -50,6 +51,7 @@ __global__ __launch_bounds__(NW * 64) void partition_f32_mfma_kernel(
   __shared__ int s_flag;
   __shared__ float s_in[32];  // carry_in m, l of the group's rows (direct)
   __shared__ int s_slot[GATHER ? kGatherChunk : 1];  // gathered cache slots
+  __shared__ int s_wave[2 * NW];  // the in-launch selection's prefix sums
 
   PartitionArgs a = args;
   int item, branch = 0;
@@ -73,10 +75,21 @@ __global__ __launch_bounds__(NW * 64) void partition_f32_mfma_kernel(
   // decode step: this branch takes the new token (the others attend as is)
   const bool stepping = STEP && branch == a.append_branch;
   const SeqLen sl = seq_len(a, sp, b, stepping);
-  const int n = sl.n;
+  int n = sl.n;
   if (stepping && !a.sched && g == 0 && c == 0 && threadIdx.x == 0)
     step_bookkeeping(sp, b, sl);  // (a scheduled launch's schedule kernel does it)
   const int t0 = c * a.chunk_tokens;
+  if (GATHER) {
+    // the selection is attended as a cache of n keys, its t-th slot in
+    // ascending order being token t; this chunk's slots go to s_slot (the
+    // tile area is the selection's scratch until the tiles start)
+    n = gather_select<NW * 64>(a.idx + (size_t)b * a.width, a.width,
+                               clamp_len(a.lens[b], a.cache_len), t0,
+                               a.chunk_tokens, s_slot,
+                               reinterpret_cast<uint32_t *>(lds), kLdsFloats,
+                               s_wave);
+    if (g == 0 && c == 0 && threadIdx.x == 0) a.sel_count[b] = n;
+  }
   if (t0 >= n && !(c == 0 && (sp.direct || (STEP && sp.fuse)))) return;
   const int t1 = min(t0 + a.chunk_tokens, n);
   const int ntiles = t1 > t0 ? (t1 - t0 + kF32Tile - 1) / kF32Tile : 0;
@@ -131,17 +144,12 @@ __global__ __launch_bounds__(NW * 64) void partition_f32_mfma_kernel(
       Kg + (size_t)t0 * kTok, (uint32_t)(((size_t)last * kTok + DK) * 4));
   const __amdgpu_buffer_rsrc_t vview = buffer_view(
       Vg + (size_t)t0 * vTok, (uint32_t)(((size_t)last * vTok + DV) * 4));
-  // Index-gathered: the chunk's cache slots, staged in LDS; the views then
+  // Index-gathered: the chunk's cache slots are in s_slot; the views then
   // span the sequence's whole cache (slots are absolute)
   const __amdgpu_buffer_rsrc_t gkview = buffer_view(
       Kg, GATHER ? (uint32_t)(((size_t)(a.cache_len - 1) * kTok + DK) * 4) : 0u);
   const __amdgpu_buffer_rsrc_t gvview = buffer_view(
       Vg, GATHER ? (uint32_t)(((size_t)(a.cache_len - 1) * vTok + DV) * 4) : 0u);
-  if (GATHER) {
-    for (int e = threadIdx.x; e <= last && t1 > t0; e += NW * 64)
-      s_slot[e] = a.sel[(size_t)b * a.max_len + t0 + e];
-    __syncthreads();
-  }
   // additive bias of the chunk's live tokens (loads past the view return 0)
   const __amdgpu_buffer_rsrc_t bview =
       BIAS && a.bias ? buffer_view(a.bias + (size_t)b * a.bias_stride + t0,
@@ -349,8 +357,8 @@ template <int DK, int DV, bool STEP>
 hipError_t launch_mfma(const PartitionArgs &a, const StepParams &sp,
                        hipStream_t s) {
   const int nwork = a.sched ? a.sched_len : a.total_items;
-  if (a.sel) {  // index-gathered: attend only, no bias
-    if (STEP || a.has_bias) return hipErrorInvalidValue;
+  if (a.idx) {  // index-gathered: attend only, no bias, never scheduled
+    if (STEP || a.has_bias || a.sched) return hipErrorInvalidValue;
     hipLaunchKernelGGL(
         (partition_f32_mfma_kernel<DK, DV, kPartitionWaves, false, false, true>),
         dim3(nwork), dim3(kPartitionWaves * 64), 0, s, a, sp);
@@ -557,7 +565,7 @@ bool partition_f32_uses_mfma(int dk, int dv) { return mfma_shape(dk, dv); }
 hipError_t launch_partition_f32(const PartitionArgs &a, const StepParams &ep,
                                 hipStream_t s) {
   if (mfma_shape(a.dk, a.dv)) return dispatch_mfma<false>(a, ep, s);
-  if (ep.direct || ep.fuse || a.sched || a.sel) return hipErrorInvalidValue;
+  if (ep.direct || ep.fuse || a.sched || a.idx) return hipErrorInvalidValue;
   const int nwork = a.batch * a.num_kv_heads * a.num_chunks;
   const size_t lds = partition_f32_lds_bytes(a.dk, a.dv, a.hpk);
   if (lds > 65536) {

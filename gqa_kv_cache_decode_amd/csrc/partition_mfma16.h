@@ -49,6 +49,7 @@
 
 #include "device_common.h"
 #include "fp8_common.h"
+#include "gather_common.h"
 #include "launch.h"
 #include "step_common.h"
 
@@ -93,7 +94,8 @@ constexpr int partition_lds_bytes() {
 // (base-2 m, partition, acc^T) is left in the LDS merge area for the
 // epilogue (`merged_state`), after a work-group barrier; with `stage_in` the
 // group's carry_in m / l are staged in s_in before that barrier.  Returns
-// whether the segment saw any key.
+// whether the segment saw any key.  Index-gathered (GATHER): token t0 + e of
+// the segment is cache slot s_slot[e].
 template <int DK, int DV, int NW, bool STEP, bool BIAS, bool GATHER, bool FP8>
 __device__ __forceinline__ bool stream_segment(const PartitionArgs &a,
                                                const StepParams &sp, int b,
@@ -184,17 +186,13 @@ __device__ __forceinline__ bool stream_segment(const PartitionArgs &a,
       Kg + (size_t)t0 * kTok, (uint32_t)((size_t)last * kTok + DK * ES));
   const __amdgpu_buffer_rsrc_t vview = buffer_view(
       Vg + (size_t)t0 * vTok, (uint32_t)((size_t)last * vTok + DV * ES));
-  // Index-gathered: the chunk's cache slots, staged in LDS; the views then
-  // span the sequence's whole cache (slots are absolute)
+  // Index-gathered: the chunk's cache slots are in s_slot (staged by the
+  // caller); the views then span the sequence's whole cache (slots are
+  // absolute)
   const __amdgpu_buffer_rsrc_t gkview = buffer_view(
       Kg, GATHER ? (uint32_t)((size_t)(a.cache_len - 1) * kTok + DK * ES) : 0u);
   const __amdgpu_buffer_rsrc_t gvview = buffer_view(
       Vg, GATHER ? (uint32_t)((size_t)(a.cache_len - 1) * vTok + DV * ES) : 0u);
-  if (GATHER) {
-    for (int e = threadIdx.x; e <= last && t1 > t0; e += NW * 64)
-      s_slot[e] = a.sel[(size_t)b * a.max_len + t0 + e];
-    __syncthreads();
-  }
   // The additive bias of the segment's live tokens (needle-core attn_bias:
   // one term per position, shared by the heads); loads past the view return 0.
   const __amdgpu_buffer_rsrc_t bview =
@@ -469,6 +467,7 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
   __shared__ int s_flag;
   __shared__ float s_in[32];  // carry_in m, l of the group's rows (direct)
   __shared__ int s_slot[GATHER ? kGatherChunk : 1];  // gathered cache slots
+  __shared__ int s_wave[2 * NW];  // the in-launch selection's prefix sums
 
   PartitionArgs a = args;
   int item, branch = 0;
@@ -493,10 +492,21 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
   // decode step: this branch takes the new token (the others attend as is)
   const bool stepping = STEP && branch == a.append_branch;
   const SeqLen sl = seq_len(a, sp, b, stepping);
-  const int n = sl.n;
+  int n = sl.n;
   if (stepping && !a.sched && g == 0 && c == 0 && threadIdx.x == 0)
     step_bookkeeping(sp, b, sl);  // (a scheduled launch's schedule kernel does it)
   const int t0 = c * a.chunk_tokens;
+  if (GATHER) {
+    // the selection is attended as a cache of n keys, its t-th slot in
+    // ascending order being token t; this chunk's slots go to s_slot (the
+    // tile area is the selection's scratch until the tiles start)
+    n = gather_select<NW * 64>(a.idx + (size_t)b * a.width, a.width,
+                               clamp_len(a.lens[b], a.cache_len), t0,
+                               a.chunk_tokens, s_slot,
+                               reinterpret_cast<uint32_t *>(lds), kLdsBytes / 4,
+                               s_wave);
+    if (g == 0 && c == 0 && threadIdx.x == 0) a.sel_count[b] = n;
+  }
   // A work-group with nothing live exits, except the first of an empty
   // sequence when final results are written in this launch: it still writes
   // the group's outputs.
@@ -643,7 +653,7 @@ template <int DK, int DV, int NW, bool STEP, bool FP8>
 hipError_t launch_one(const PartitionArgs &a, const StepParams &sp,
                       hipStream_t s) {
   if (a.balanced) {  // one resident work-group per range, two per CU
-    if (a.sel || a.num_extra || a.sched || (sp.fuse && STEP) ||
+    if (a.idx || a.num_extra || a.sched || (sp.fuse && STEP) ||
         a.balanced % 8)
       return hipErrorInvalidValue;
     const int dyn = balanced_lds_bytes<DK, DV, NW, FP8>();
@@ -657,8 +667,8 @@ hipError_t launch_one(const PartitionArgs &a, const StepParams &sp,
   }
   const int nwork = a.sched ? a.sched_len : a.total_items;
   const int dyn = residency_lds_bytes<DK, DV, NW, FP8>(a);
-  if (a.sel) {  // index-gathered: attend only, no bias, never scheduled
-    if (STEP || a.has_bias) return hipErrorInvalidValue;
+  if (a.idx) {  // index-gathered: attend only, no bias, never scheduled
+    if (STEP || a.has_bias || a.sched) return hipErrorInvalidValue;
     hipLaunchKernelGGL((partition_bf16_kernel<DK, DV, NW, false, false, true, FP8>),
                        dim3(nwork), dim3(NW * 64), 0, s, a, sp);
   } else if (a.has_bias) {

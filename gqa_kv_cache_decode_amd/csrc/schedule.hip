@@ -275,83 +275,3 @@ hipError_t launch_schedule(const ScheduleArgs &a, hipStream_t s) {
 }
 
 }  // namespace gqa
-
-// ---------------------------------------------------------------------------
-// Index-row selection for index-gathered decode (metrale DSA topk_to_mask:
-// a slot named several times counts once; INVALID and out-of-range entries
-// are dropped).  One work-group per sequence marks the
-// named slots in an LDS bitmap of the sequence's live length, then writes
-// the set slots in ascending order (a prefix count over the bitmap words),
-// which also leaves the gathered rows in address order.
-namespace gqa {
-namespace {
-
-constexpr int kSelectThreads = 1024;
-
-__global__ __launch_bounds__(kSelectThreads) void select_kernel(SelectArgs a) {
-  extern __shared__ uint32_t bits[];
-  __shared__ int wave_sum[kSelectThreads / 64];
-  const int b = blockIdx.x;
-  const int n = clamp_len(a.lens[b], a.max_len);
-  const int nw = (n + 31) >> 5;
-  for (int w = threadIdx.x; w < nw; w += blockDim.x) bits[w] = 0u;
-  __syncthreads();
-  const int32_t *row = a.idx + (size_t)b * a.width;
-  for (int j = threadIdx.x; j < a.width; j += blockDim.x) {
-    const int i = row[j];
-    if (i >= 0 && i < n) atomicOr(&bits[i >> 5], 1u << (i & 31));
-  }
-  __syncthreads();
-  // each thread owns a contiguous run of words; exclusive prefix of the
-  // runs' bit counts across the work-group
-  const int per = (nw + kSelectThreads - 1) / kSelectThreads;
-  const int w0 = threadIdx.x * per, w1 = min(w0 + per, nw);
-  int cnt = 0;
-  for (int w = w0; w < w1; ++w) cnt += __popc(bits[w]);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int inc = cnt;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(inc, off, 64);
-    if (lane >= off) inc += y;
-  }
-  if (lane == 63) wave_sum[wave] = inc;
-  __syncthreads();
-  int base = 0, total = 0;
-  for (int w = 0; w < kSelectThreads / 64; ++w) {
-    if (w < wave) base += wave_sum[w];
-    total += wave_sum[w];
-  }
-  int pos = base + inc - cnt;
-  int32_t *sel = a.sel + (size_t)b * a.sel_stride;
-  for (int w = w0; w < w1; ++w) {
-    uint32_t m = bits[w];
-    while (m) {
-      const int bit = __ffs(m) - 1;
-      sel[pos++] = (w << 5) + bit;
-      m &= m - 1;
-    }
-  }
-  if (threadIdx.x == 0) a.count[b] = total;
-}
-
-}  // namespace
-
-size_t select_lds_bytes(int max_len) {
-  return sizeof(uint32_t) * (size_t)((max_len + 31) / 32);
-}
-
-hipError_t launch_select(const SelectArgs &a, hipStream_t s) {
-  const size_t lds = select_lds_bytes(a.max_len);
-  if (lds > 65536) {
-    const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(select_kernel),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL(select_kernel, dim3(a.batch), dim3(kSelectThreads), lds,
-                     s, a);
-  return hipGetLastError();
-}
-
-}  // namespace gqa

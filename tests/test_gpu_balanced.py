@@ -39,6 +39,12 @@ def _phase_runs(nt):
     return [(0, e0, 128), (e0, e1, 32), (e1, nt, 8)]
 
 
+def _seq_runs(nt, k):
+    """Runs (first, end tile) of phase k of a sequence of nt tiles."""
+    s, e, L = _phase_runs(nt)[k]
+    return [(s + j * L, min(s + (j + 1) * L, e)) for j in range(-(-(e - s) // L))]
+
+
 def _check_queue(ws, plan, lens, w, launched=True):
     """The work queue, word for word: the runs phase by phase and sequence
     by sequence, each sequence's first run per phase, the item count; after
@@ -56,9 +62,7 @@ def _check_queue(ws, plan, lens, w, launched=True):
         pk = []
         for b in range(B):
             pk.append(len(runs) - base[k])
-            s, e, L = _phase_runs(int(nt[b]))[k]
-            runs += [(b, s + j * L, min(s + (j + 1) * L, e))
-                     for j in range(-(-(e - s) // L))]
+            runs += [(b, t0, t1) for t0, t1 in _seq_runs(int(nt[b]), k)]
         pk.append(len(runs) - base[k])
         pre.append(pk)
     base.append(len(runs))
@@ -323,3 +327,30 @@ def test_balanced_decode_step_fp8():
     check_out(out.cpu().numpy(), ref, vmax, "fp8", "balanced fp8 step")
     check_carry(cout.m.cpu().numpy(), cout.l.cpu().numpy(), cref.m, cref.l,
                 "fp8", "balanced fp8 step carry")
+
+
+def test_balanced_many_pieces():
+    """Rows with hundreds of pieces: one 800K-token sequence (533 runs, more
+    than the combine folds per batch) beside a 140K-token one (97 runs), so
+    the combine's register, loop and multi-batch paths all fold pieces."""
+    g = _gqa()
+    w = wl.RAGGED_BF16.replace(batch=2, num_q_heads=2, num_kv_heads=1, dk=64,
+                               dv=64, max_len=800000, dist="normal")
+    lens = torch.tensor([800000, 140000], dtype=torch.int32)
+    runs = [sum(len(_seq_runs(-(-n // TILE), k)) for k in range(3))
+            for n in lens.tolist()]
+    assert runs[0] > 512 and 32 < runs[1] < 512, runs
+    x = wl.make_inputs(w, lens_override=lens.tolist())
+    say(f"[balanced] many pieces: runs per row {runs}")
+    d = to_dev(x)
+    plan = g.attend_plan(d["k"], d["v"], w.num_q_heads, g.CHUNK_BALANCED)
+    assert plan.balanced_groups == 512
+    ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device="cuda")
+    g.attend_partition(d["q"], d["k"], d["v"], d["lens"], plan, ws, w.scale)
+    cin = _random_carry(w.batch * w.num_q_heads, w.dv, 49)
+    cout = g.empty_carry(w.batch * w.num_q_heads, w.dv)
+    out = g.attend_combine(w.num_q_heads, d["k"], d["v"], d["lens"], plan, ws,
+                           carry_in=_dev_carry(cin), carry_out=cout)
+    torch.cuda.synchronize()
+    _check_queue(ws, plan, lens, w)
+    _oracle_check(x, w, out, cout, "balanced many pieces", carry_in=cin)

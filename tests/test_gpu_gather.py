@@ -2,8 +2,9 @@
 consecutive-token pools and single tokens, with duplicates, INVALID (-1)
 padding, slots past the live length and rows that select nothing; every
 compiled head width of both families; a selection that fits one chunk
-(written directly) and one split over many chunks; a carry_in with
-carry_out aliasing it."""
+(written directly) and one split over many chunks; live lengths longer than
+one window of the launch's selection bitmap; a carry_in with carry_out
+aliasing it."""
 
 import numpy as np
 import pytest
@@ -64,6 +65,15 @@ CASES = {
     "f32_d64": (wl.TINY_F32.replace(batch=3, max_len=1000), 400, 16),
     "f32_d128": (wl.TINY_F32.replace(batch=3, num_q_heads=8, num_kv_heads=4,
                                      dk=128, dv=128, max_len=900), 300, 8),
+    # live lengths past one LDS window of the in-launch selection (49152
+    # slots for bf16 64-wide heads, 92832 for fp32 64-wide heads): ranks
+    # carried across several windows
+    "bf16_d64_windows": (wl.BATCHED_BF16.replace(batch=3, num_q_heads=2,
+                                                 num_kv_heads=1, dk=64, dv=64,
+                                                 max_len=400000), 3000, 64),
+    "f32_d64_windows": (wl.TINY_F32.replace(batch=2, num_q_heads=2,
+                                            num_kv_heads=1, max_len=600000),
+                        2000, 16),
 }
 
 
