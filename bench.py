@@ -916,8 +916,6 @@ def gpu_phase(torch, case, args, oracle_res):
     gbs = step_bytes / (med * 1e-3) / 1e9
     kgbs = dom_bytes / (kavg * 1e-3) / 1e9
     kernel = case.kernel()
-    if isinstance(case, GatherCase):
-        kernel = f"attend_gathered: {kernel} + combine_kernel"
     res = {
         "workload": w.name, "kv_dtype": "fp8_e4m3" if w.dtype == "fp8"
         else w.dtype,

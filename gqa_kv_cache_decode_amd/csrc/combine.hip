@@ -110,7 +110,7 @@ __global__ __launch_bounds__(THREADS) void combine_kernel(CombineArgs a) {
 // one before it.  More pieces than a batch of LDS slots fold batch by batch
 // with the usual rescale.
 constexpr int kCombineRegs = 16;
-constexpr int kCombineBatch = 512;
+constexpr int kCombineBatch = 256;
 
 // Slot of piece i of a row whose phases hold n0, n01 - n0 and the rest of
 // its pieces, from runs r0 + i, r1 + i and r2 + i (r1, r2 offset by the
