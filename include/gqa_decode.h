@@ -358,7 +358,10 @@ GQA_API gqa_status gqa_attend_combine(int32_t num_q_heads, const gqa_cache *cach
 /*
  * decode_step — kv_append then attend_decode, as one decode step (needle-core
  * self_attn_incremental: push_kv, then attend over the cache including the new
- * token), in one kernel launch for the matrix-core shapes.
+ * token), in one partition launch for the matrix-core shapes (preceded, for a
+ * plan with a work schedule or queue, by the kernel that builds it, and
+ * followed by the combine unless the plan is small enough to fold in the
+ * launch).
  *   For every sequence b with n = lens_in[b]: if 0 <= n < max_len the token's
  *   K/V rows (k_new [batch][num_kv_heads][dk], v_new [...][dv]) are written to
  *   slot n and the query attends over [0, n + 1); otherwise nothing is written,
