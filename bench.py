@@ -74,7 +74,7 @@ WARM_REPLAYS = 5            # untimed replays of the step graph before timing
 DEFAULT_SET = ["tiny", "batched", "ragged", "long", "spike"]
 HEADLINE = "ragged"         # the largest workload that fits one GPU
 ONE_THREAD_SET = ["tiny", "batched"]   # also timed on one host core
-MAX_HOST_WORKERS = 16       # the host cores a one-GPU machine gives a job
+MAX_HOST_WORKERS = 16       # host processes at most (one GPU's share of a node)
 # max |out - out_oracle| <= TOL * max|V| over the attended values
 TOL = {"f32": 1e-5, "bf16": 4e-3, "fp8": 4e-3}
 
@@ -1011,23 +1011,23 @@ def main(argv=None):
         profile_pass(torch, cases[names[0]], args)
         return
 
-    configs = {}
+    per_workload = {}
     for n in names:
-        configs[n] = gpu_phase(torch, cases[n], args, oracle_res.get(n))
+        per_workload[n] = gpu_phase(torch, cases[n], args, oracle_res.get(n))
         cases[n].x = None   # host copies are no longer needed
 
     ceiling = None
     if not args.no_ceiling:
         ceiling = read_ceiling(torch)
         log(f"[bench] pure-read stream ceiling: {ceiling:.1f} GB/s")
-        for r in configs.values():
+        for r in per_workload.values():
             r["step_frac_of_read_ceiling"] = round(r["gbs_per_step"] / ceiling,
                                                    4)
             r["kernel_frac_of_read_ceiling"] = round(r["kernel_gbs"] / ceiling,
                                                      4)
 
-    head_name = HEADLINE if HEADLINE in configs else names[0]
-    head = configs[head_name]
+    head_name = HEADLINE if HEADLINE in per_workload else names[0]
+    head = per_workload[head_name]
     hw = cases[head_name].w
     cpu = None
     if oracle_res:
@@ -1082,7 +1082,7 @@ def main(argv=None):
                      "algorithmic_bytes_per_launch": head["kernel_bytes"],
                      "avg_launch_us": head["kernel_avg_us"]},
         "cpu_baseline": cpu,
-        "configs": configs,
+        "configs": per_workload,
     }
     print(json.dumps(line), flush=True)
 
