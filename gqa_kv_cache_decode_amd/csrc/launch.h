@@ -97,6 +97,9 @@ struct PartitionArgs {
   // per queue item.
   int32_t *queue = nullptr;
   int balanced = 0;
+  // fp32 launches of a few work-groups: 8 blocks per item, block 8i doing
+  // item i (all on one XCD); set by the fp32 launcher
+  int one_xcd = 0;
 };
 
 // Work queue of a balanced plan (int32 words, built by the balance kernel):

@@ -58,6 +58,12 @@ __global__ __launch_bounds__(NW * 64) void partition_f32_mfma_kernel(
   if (a.sched) {  // scheduled launch: the table entry, or nothing to do
     item = a.sched[blockIdx.x];
     if (item < 0) return;
+  } else if (a.one_xcd) {
+    // a small single-cache launch on one XCD: block i runs on XCD i % 8, so
+    // only every eighth block works and the kernel's code is fetched into
+    // one XCD's L2 instead of eight
+    if (blockIdx.x % 8 != 0) return;
+    item = blockIdx.x / 8;
   } else {
     // the block's branch (multi-branch launch: each branch owns a block
     // range starting at a multiple of 8), then its item within the branch
@@ -353,10 +359,16 @@ __global__ __launch_bounds__(NW * 64) void partition_f32_mfma_kernel(
   }
 }
 
+// Launches of at most this many work-groups run on one XCD (one_xcd).
+constexpr int kOneXcdItems = 32;
+
 template <int DK, int DV, bool STEP>
-hipError_t launch_mfma(const PartitionArgs &a, const StepParams &sp,
+hipError_t launch_mfma(const PartitionArgs &args, const StepParams &sp,
                        hipStream_t s) {
-  const int nwork = a.sched ? a.sched_len : a.total_items;
+  PartitionArgs a = args;
+  a.one_xcd = !a.sched && a.num_extra == 0 && a.total_items <= kOneXcdItems;
+  const int nwork = a.sched ? a.sched_len : a.one_xcd ? 8 * a.total_items
+                                                      : a.total_items;
   if (a.idx) {  // index-gathered: attend only, no bias, never scheduled
     if (STEP || a.has_bias || a.sched) return hipErrorInvalidValue;
     hipLaunchKernelGGL(
