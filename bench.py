@@ -188,6 +188,16 @@ def kernel_name(w, bias, gather, step=True, balanced=None):
     if balanced:
         return (f"partition_balanced_kernel<{w.dk}, {w.dv}, {waves}, "
                 f"{tf(step)}, {tf(bias)}, {fp8}>")
+    if (w.dtype == "fp8" and not gather and w.dk + w.dv <= 128 and
+            w.num_kv_heads % waves == 0):
+        # the group-split launch (64-wide fp8 heads): a plain chunked plan
+        # whose items, in sets of `waves` KV groups, are one round of one
+        # work-group per CU
+        p = library_plan(w)
+        if (p.sched_entries == 0 and p.num_chunks > 1 and
+                256 <= w.batch * w.num_kv_heads * p.num_chunks // waves < 512):
+            return (f"partition_split_kernel<{w.dk}, {w.dv}, {waves}, "
+                    f"{tf(step)}, {tf(bias)}, {fp8}>")
     return (f"partition_bf16_kernel<{w.dk}, {w.dv}, {waves}, {tf(step)}, "
             f"{tf(bias)}, {tf(gather)}, {fp8}>")
 

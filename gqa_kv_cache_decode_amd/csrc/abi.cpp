@@ -111,12 +111,53 @@ int partition_waves(const gqa_cache *c) {
   return gqa::partition_waves(c->dk, c->dv, c->dtype == GQA_DTYPE_FP8_E4M3);
 }
 
-// Chunk length: the largest power of two up to kMaxChunk that still gives
-// every CU a work-group (short caches go down to kChunkQuantum tokens, so a
-// small branch spreads over more work-groups), with at most kMaxTokensPerWave
-// tokens per wavefront, and no longer than the cache needs.  A batch with
-// enough (sequence, KV group) units and short caches gets a single chunk: its
-// partition launch then writes the final results itself.
+// KV groups per work-group of a plain chunked launch (group split, launch.h):
+// 1 except for fp8 caches whose KV heads divide into sets of partition_waves.
+int64_t group_split(const gqa_cache *c) {
+  return uses_mfma(c) ? gqa::group_split(c->dk, c->dv,
+                                         c->dtype == GQA_DTYPE_FP8_E4M3,
+                                         c->num_kv_heads)
+                      : 1;
+}
+
+// Whether a plan of nchunk chunks over this cache launches the group split:
+// split-K, and its work-groups one round of one per CU (launch.h).
+bool split_plan(const gqa_cache *c, int64_t nchunk) {
+  const int64_t split = group_split(c);
+  const int64_t wgs = (int64_t)c->batch * c->num_kv_heads / split * nchunk;
+  return split > 1 && nchunk > 1 && wgs >= gqa::kSplitMinGroups &&
+         wgs < gqa::kSplitMaxGroups;
+}
+
+// Chunk length for `sets` work-groups per chunk index and `wave_share`
+// wavefronts per (KV group, chunk): the largest power of two up to kMaxChunk
+// that still gives at least `min_groups` work-groups, one per CU (short caches
+// go down to kChunkQuantum tokens, so a small branch spreads over more
+// work-groups), with at most kMaxTokensPerWave tokens per wavefront, and no
+// longer than the cache needs.
+int32_t chunk_length(const gqa_cache *c, int64_t sets, int64_t wave_share,
+                     int64_t min_groups) {
+  int32_t chunk = kMaxChunk;
+  while (chunk > kChunkQuantum &&
+         (chunk / wave_share > kMaxTokensPerWave ||
+          sets * ((c->max_len + chunk - 1) / chunk) < min_groups))
+    chunk /= 2;
+  while (chunk > kChunkQuantum && chunk / 2 >= c->max_len) chunk /= 2;
+  // A launch big enough to be scheduled runs in several rounds; there the
+  // last round's chunks set the tail, and shorter ones measured faster.
+  const int64_t nchunk = (c->max_len + chunk - 1) / chunk;
+  if (uses_mfma(c) && chunk > kScheduledMaxChunk && nchunk > 1 &&
+      sets * nchunk >= kScheduleMinItems)
+    chunk = kScheduledMaxChunk;
+  return chunk;
+}
+
+// The library's chunk length.  A batch with enough (sequence, KV group) units
+// and short caches gets a single chunk: its partition launch then writes the
+// final results itself.  A split-K plan over a cache that allows the group
+// split (launch.h) is sized for it (a work-group holds `split` KV groups, a
+// wavefront a whole chunk of its group) when that launch is one round of one
+// work-group per CU.
 int32_t auto_chunk(const gqa_cache *c) {
   const int64_t units = (int64_t)c->batch * c->num_kv_heads;
   const int64_t waves = uses_mfma(c) ? partition_waves(c) : 1;
@@ -126,18 +167,14 @@ int32_t auto_chunk(const gqa_cache *c) {
   const int64_t tile = c->dtype == GQA_DTYPE_F32 ? 16 : 32;
   if (uses_mfma(c) && c->max_len <= 2 * waves * tile)
     return (c->max_len + kChunkQuantum - 1) / kChunkQuantum * kChunkQuantum;
-  int32_t chunk = kMaxChunk;
-  while (chunk > kChunkQuantum &&
-         (chunk / waves > kMaxTokensPerWave ||
-          units * ((c->max_len + chunk - 1) / chunk) < kMinGroups))
-    chunk /= 2;
-  while (chunk > kChunkQuantum && chunk / 2 >= c->max_len) chunk /= 2;
-  // A launch big enough to be scheduled runs in several rounds; there the
-  // last round's chunks set the tail, and shorter ones measured faster.
-  const int64_t nchunk = (c->max_len + chunk - 1) / chunk;
-  if (uses_mfma(c) && chunk > kScheduledMaxChunk && nchunk > 1 &&
-      units * nchunk >= kScheduleMinItems)
-    chunk = kScheduledMaxChunk;
+  const int32_t chunk = chunk_length(c, units, waves, kMinGroups);
+  const int64_t split = group_split(c);
+  if (split > 1 && (c->max_len + chunk - 1) / chunk > 1) {
+    const int32_t sc = chunk_length(c, units / split,
+                                    waves > split ? waves / split : 1,
+                                    gqa::kSplitMinGroups);
+    if (split_plan(c, (c->max_len + sc - 1) / sc)) return sc;
+  }
   return chunk;
 }
 
@@ -209,8 +246,10 @@ gqa_status make_plan(const gqa_cache *c, int32_t hq, int32_t chunk_tokens,
   p->off_sched = 0;
   p->sched_entries = 0;
   p->balanced_groups = 0;
+  // (a group-split launch is one round of work-groups: never scheduled)
   const bool multi_round = nchunk > 1 && groups >= kScheduleMinItems &&
-                           uses_mfma(c) && c->batch <= kScheduleMaxSeqs;
+                           uses_mfma(c) && c->batch <= kScheduleMaxSeqs &&
+                           !split_plan(c, nchunk);
   if (multi_round && chunk_tokens == 0 && c->dtype != GQA_DTYPE_F32 &&
       balanced_plan(c, hq, p))
     return GQA_OK;

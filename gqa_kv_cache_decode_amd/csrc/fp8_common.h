@@ -86,13 +86,14 @@ __device__ __forceinline__ u32x4 e4m3_quantize16(const uint16_t *src,
 
 // Stores one KV group's rows of the new token (bf16 [d] each) into the cache
 // slot as codes (kinv, vinv: e4m3_inv_scale of the group's scales), 16 codes
-// per 16-byte piece, spread over the work-group's
-// threads.  As for bf16 rows, nothing in the same launch reads the slot, so
-// the stores are not waited for.
+// per 16-byte piece, spread over the threads first, first + stride, ...  As
+// for bf16 rows, nothing in the same launch reads the slot, so the stores are
+// not waited for.
 __device__ __forceinline__ void store_group_row_e4m3(
     const uint16_t *kn, u32x4 *kd, int kpieces, float kinv,
-    const uint16_t *vn, u32x4 *vd, int vpieces, float vinv) {
-  for (int e = threadIdx.x; e < kpieces + vpieces; e += blockDim.x) {
+    const uint16_t *vn, u32x4 *vd, int vpieces, float vinv, int first,
+    int stride) {
+  for (int e = first; e < kpieces + vpieces; e += stride) {
     if (e < kpieces)
       kd[e] = e4m3_quantize16(kn + e * 16, kinv);
     else

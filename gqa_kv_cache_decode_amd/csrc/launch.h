@@ -36,6 +36,29 @@ constexpr int partition_waves(int dk, int dv, bool fp8 = false) {
   return fp8 ? (dk + dv <= 128 ? 8 : 4) : 2;
 }
 
+// Group split: a plain chunked launch over an fp8 cache with 64-wide heads
+// gives each wavefront of a work-group its own KV group over the whole chunk,
+// the work-group holding split_waves consecutive groups of one sequence
+// (partition_mfma16.h, partition_split_kernel).  Returns the groups per
+// work-group, or 1 where it does not apply.  Measured on the batched fp8 shape
+// (B 16, 8 KV heads, 4096 tokens), same box: 64-wide heads 22.2-22.6 ->
+// 21.7-22.0 us per step (kernel 21.5 -> 20.2-20.8 us); 128-wide heads slower,
+// 32.1-32.8 -> 33.3-34.3 us (the kernel the same, 29.8 us, and eight partials
+// per query row to combine instead of two), and slower still with eight
+// wavefronts per work-group (34.3) or two work-groups per CU (35.3-35.6), so
+// the other widths keep the shared-group launch.  It is taken where its
+// work-groups are one round of one per CU, at least kSplitMinGroups and fewer
+// than kSplitMaxGroups (more take a scheduled or balanced plan): the planner
+// sizes chunks for it, a wavefront streaming a whole chunk of its group.
+constexpr int split_waves(int dk, int dv) { return partition_waves(dk, dv, true); }
+constexpr int group_split(int dk, int dv, bool fp8, int num_kv_heads) {
+  return fp8 && dk + dv <= 128 && num_kv_heads % split_waves(dk, dv) == 0
+             ? split_waves(dk, dv)
+             : 1;
+}
+constexpr int kSplitMinGroups = 256;
+constexpr int kSplitMaxGroups = 512;
+
 // A further cache attended by the same launch (multi-branch attention: the
 // branches' partials share one partial row per query row and one combine).
 // Every branch has the launch's batch, heads and head widths.

@@ -139,7 +139,8 @@ __global__ __launch_bounds__(NW * 64) void partition_f32_mfma_kernel(
     store_group_row(reinterpret_cast<const u32x4 *>(knew),
                     reinterpret_cast<u32x4 *>(Kg + (size_t)sl.n_old * kTok), DK / 4,
                     reinterpret_cast<const u32x4 *>(vnew),
-                    reinterpret_cast<u32x4 *>(Vg + (size_t)sl.n_old * vTok), DV / 4);
+                    reinterpret_cast<u32x4 *>(Vg + (size_t)sl.n_old * vTok), DV / 4,
+                    threadIdx.x, blockDim.x);
   }
   const int rel_tile = rel >= 0 ? rel / kF32Tile : -1;
 

@@ -95,8 +95,11 @@ constexpr int partition_lds_bytes() {
 // epilogue (`merged_state`), after a work-group barrier; with `stage_in` the
 // group's carry_in m / l are staged in s_in before that barrier.  Returns
 // whether the segment saw any key.  Index-gathered (GATHER): token t0 + e of
-// the segment is cache slot s_slot[e].
-template <int DK, int DV, int NW, bool STEP, bool BIAS, bool GATHER, bool FP8>
+// the segment is cache slot s_slot[e].  Group split (SPLIT): wavefront w
+// takes KV group g + w and every tile of the segment, so its state is that
+// group's alone (no stage_in).
+template <int DK, int DV, int NW, bool STEP, bool BIAS, bool GATHER, bool FP8,
+          bool SPLIT = false>
 __device__ __forceinline__ bool stream_segment(const PartitionArgs &a,
                                                const StepParams &sp, int b,
                                                int g, int t0, int t1,
@@ -116,6 +119,7 @@ __device__ __forceinline__ bool stream_segment(const PartitionArgs &a,
   const int hl = lane & 15;  // head column of this lane
   const int kg = lane >> 4;  // lane group: k-slice of MFMA operands
   const int Hq = Hkv * hpk;
+  const int gw = SPLIT ? g + w : g;  // this wavefront's KV group
 
   // q as the B operand of S^T = K q^T: lane holds head hl, dims s*32+kg*8..+8.
   // Padding columns (hl >= hpk) repeat the group's last head; they are never
@@ -124,7 +128,7 @@ __device__ __forceinline__ bool stream_segment(const PartitionArgs &a,
   bf16x8 qf[DK / 32];
   {
     const uint16_t *qrow = static_cast<const uint16_t *>(a.q) +
-                           ((size_t)b * Hq + (size_t)g * hpk + min(hl, hpk - 1)) * DK;
+                           ((size_t)b * Hq + (size_t)gw * hpk + min(hl, hpk - 1)) * DK;
 #pragma unroll
     for (int s = 0; s < DK / 32; ++s)
       qf[s] = *reinterpret_cast<const bf16x8 *>(qrow + s * 32 + kg * 8);
@@ -146,34 +150,38 @@ __device__ __forceinline__ bool stream_segment(const PartitionArgs &a,
   const size_t kTok = (size_t)Hkv * DK * ES;  // bytes between tokens
   const size_t vTok = (size_t)Hkv * DV * ES;
   unsigned char *Kg = static_cast<unsigned char *>(const_cast<void *>(a.k)) +
-                      ((size_t)b * a.cache_len * Hkv + g) * DK * ES;
+                      ((size_t)b * a.cache_len * Hkv + gw) * DK * ES;
   unsigned char *Vg = static_cast<unsigned char *>(const_cast<void *>(a.v)) +
-                      ((size_t)b * a.cache_len * Hkv + g) * DV * ES;
+                      ((size_t)b * a.cache_len * Hkv + gw) * DV * ES;
   // fp8: the group's scales (K into the logit scale, V into acc at the end)
-  const float kscale = FP8 ? a.k_scale[(size_t)b * Hkv + g] : 1.0f;
-  const float vscale = FP8 ? a.v_scale[(size_t)b * Hkv + g] : 1.0f;
+  const float kscale = FP8 ? a.k_scale[(size_t)b * Hkv + gw] : 1.0f;
+  const float vscale = FP8 ? a.v_scale[(size_t)b * Hkv + gw] : 1.0f;
   const float scale_log2 = a.scale_log2 * kscale;
   // fp8 decode step: the new rows are multiplied by these before encoding
   const float kinv = FP8 && STEP ? e4m3_inv_scale(kscale) : 1.0f;
   const float vinv = FP8 && STEP ? e4m3_inv_scale(vscale) : 1.0f;
 
   // STEP: the work-group whose segment holds the new slot stores the token's
-  // rows of this group into the cache.  The stores are not waited for: later
-  // calls read the slot, while this call takes the rows from k_new/v_new.
+  // rows of this group (of each wavefront's group when split) into the cache.
+  // The stores are not waited for: later calls read the slot, while this call
+  // takes the rows from k_new/v_new.
   const uint16_t *knew = nullptr, *vnew = nullptr;
   if (STEP && has_new) {
-    knew = static_cast<const uint16_t *>(sp.k_new) + ((size_t)b * Hkv + g) * DK;
-    vnew = static_cast<const uint16_t *>(sp.v_new) + ((size_t)b * Hkv + g) * DV;
+    knew = static_cast<const uint16_t *>(sp.k_new) + ((size_t)b * Hkv + gw) * DK;
+    vnew = static_cast<const uint16_t *>(sp.v_new) + ((size_t)b * Hkv + gw) * DV;
+    const int first = SPLIT ? lane : (int)threadIdx.x;
+    const int stride = SPLIT ? 64 : NW * 64;
     if (FP8)
       store_group_row_e4m3(knew, reinterpret_cast<u32x4 *>(Kg + (size_t)n_old * kTok),
                            DK / 16, kinv, vnew,
                            reinterpret_cast<u32x4 *>(Vg + (size_t)n_old * vTok),
-                           DV / 16, vinv);
+                           DV / 16, vinv, first, stride);
     else
       store_group_row(reinterpret_cast<const u32x4 *>(knew),
                       reinterpret_cast<u32x4 *>(Kg + (size_t)n_old * kTok), DK / 8,
                       reinterpret_cast<const u32x4 *>(vnew),
-                      reinterpret_cast<u32x4 *>(Vg + (size_t)n_old * vTok), DV / 8);
+                      reinterpret_cast<u32x4 *>(Vg + (size_t)n_old * vTok), DV / 8,
+                      first, stride);
   }
 
   // K/V are read exactly once per call, so the loads are nontemporal: they
@@ -243,9 +251,12 @@ __device__ __forceinline__ bool stream_segment(const PartitionArgs &a,
 #pragma unroll
   for (int blk = 0; blk < DV / 16; ++blk) o[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  int tile = w;
+  // wavefront w takes tiles w, w + NW, ... of the group, or all of them when
+  // the wavefronts hold different groups
+  constexpr int kStep = SPLIT ? 1 : NW;
+  int tile = SPLIT ? 0 : w;
   if (tile < ntiles) issue(tile);
-  for (; tile < ntiles; tile += NW) {
+  for (; tile < ntiles; tile += kStep) {
     const int tb = t0 + tile * kTileTokens;
     wave_lds_sync();  // previous tile's LDS reads are done
 #pragma unroll
@@ -261,7 +272,7 @@ __device__ __forceinline__ bool stream_segment(const PartitionArgs &a,
                                  (idx % G::vPieces) * 16) = vr[i];
     }
     const f32x4 bcur[2] = {br[0], br[1]};
-    if (tile + NW < ntiles) issue(tile + NW);  // next tile in flight meanwhile
+    if (tile + kStep < ntiles) issue(tile + kStep);  // next tile in flight meanwhile
     wave_lds_sync();
 
     // S^T for tokens rb*16 + kg*4 + i (i < 4), head hl
@@ -341,10 +352,11 @@ __device__ __forceinline__ bool stream_segment(const PartitionArgs &a,
     }
   }
 
-  // The new token of a decode step, folded into wavefront 0's state: its
-  // logit from q and k_new (for fp8 caches, the decoded codes it is stored
-  // as), then the usual online update with its value row.
-  if (STEP && has_new && w == 0) {
+  // The new token of a decode step, folded into wavefront 0's state (every
+  // wavefront's, for its own group, when split): its logit from q and k_new
+  // (for fp8 caches, the decoded codes it is stored as), then the usual online
+  // update with its value row.
+  if (STEP && has_new && (SPLIT || w == 0)) {
     float dot = 0.0f;
 #pragma unroll
     for (int s = 0; s < DK / 32; ++s) {
@@ -562,6 +574,64 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
   }
 }
 
+// Group-split chunked launch (fp8 caches with 64-wide heads, plain chunked
+// plans: no schedule, queue, further branch or gathered index, and a combine
+// launch after it; launch.h group_split).
+// Work-group (b, q, c) holds the NW consecutive KV groups q NW .. q NW + NW - 1
+// of sequence b over chunk c, and wavefront w streams group q NW + w over the
+// whole chunk.  The KV heads of one token lie side by side in the cache, so
+// the work-group's loads of a tile cover NW groups' rows of the same tokens at
+// the same time, where NW work-groups would read them at different times
+// (for E4M3 rows of 128 bytes at a 1 KiB token stride, the batched shape, a
+// load-only probe read the cache in 22.0 us this way against 24.9 us).  Each
+// wavefront's state is its group's partial for the chunk; nothing is merged.
+template <int DK, int DV, int NW, bool STEP, bool BIAS, bool FP8>
+__global__ __launch_bounds__(NW * 64) void partition_split_kernel(
+    PartitionArgs a, StepParams sp) {
+  constexpr int kLdsBytes = partition_lds_bytes<DK, DV, NW, FP8>();
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsBytes];
+
+  const int Hkv = a.num_kv_heads, hpk = a.hpk, nchunk = a.num_chunks;
+  const int nq = Hkv / NW;  // work-groups per (sequence, chunk)
+  const int nitems = a.batch * nq * nchunk;  // the grid (launch_one)
+  if ((int)blockIdx.x >= nitems) return;
+  const int item = xcd_local_item(blockIdx.x, nitems);
+  const int c = item % nchunk;
+  const int bq = item / nchunk;
+  const int g = (bq % nq) * NW;  // the work-group's first KV group
+  const int b = bq / nq;
+
+  const SeqLen sl = seq_len(a, sp, b, STEP);
+  const int n = sl.n;
+  if (STEP && g == 0 && c == 0 && threadIdx.x == 0) step_bookkeeping(sp, b, sl);
+  const int t0 = c * a.chunk_tokens;
+  if (t0 >= n) return;  // the combine takes only live chunks
+  // decode step: the chunk holding the new slot (the last live token) reads
+  // the cache tokens before it and folds the new token in afterwards
+  const bool has_new = STEP && sl.fresh && sl.n_old / a.chunk_tokens == c;
+  const int t1 = has_new ? sl.n_old : min(t0 + a.chunk_tokens, n);
+  stream_segment<DK, DV, NW, STEP, BIAS, false, FP8, true>(
+      a, sp, b, g, t0, t1, has_new, sl.n_old, false, lds, nullptr, nullptr);
+
+  // every wavefront's state, as stream_segment left it in the merge area, is
+  // one partial: wavefront wv's head h is query row (g + wv) hpk + h
+  const float *wm = reinterpret_cast<const float *>(lds);
+  const float *wl = wm + NW * 16;
+  const float *wacc = wl + NW * 16;
+  const size_t row0 = (size_t)b * Hkv * hpk + (size_t)g * hpk;
+  for (int e = threadIdx.x; e < NW * hpk * DV; e += NW * 64) {
+    const int wh = e / DV;  // wv * hpk + h
+    const int d = e - wh * DV;
+    const int wv = wh / hpk, h = wh - wv * hpk;
+    const size_t col = (row0 + wh) * a.total_cols + a.col_base + c;
+    a.part_acc[col * DV + d] = wacc[(wv * 16 + h) * DV + d];
+    if (d == 0) {
+      a.part_m[col] = wm[wv * 16 + h] * kLn2;
+      a.part_l[col] = wl[wv * 16 + h];
+    }
+  }
+}
+
 // Balanced launch (a plan with many items over several rounds of
 // work-groups, where fixed chunks leave a ragged last round, and where the
 // work-groups' read rates differ by tens of percent from one CU or XCD to
@@ -664,6 +734,22 @@ hipError_t launch_one(const PartitionArgs &a, const StepParams &sp,
       hipLaunchKernelGGL((partition_balanced_kernel<DK, DV, NW, STEP, false, FP8>),
                          dim3(a.balanced), dim3(NW * 64), dyn, s, a, sp);
     return hipGetLastError();
+  }
+  if constexpr (FP8 && DK + DV <= 128) {
+    constexpr int SW = split_waves(DK, DV);
+    const int nwork = a.total_items / SW;
+    if (group_split(DK, DV, FP8, a.num_kv_heads) == SW &&
+        a.total_items == a.batch * a.num_kv_heads * a.num_chunks &&
+        nwork >= kSplitMinGroups && nwork < kSplitMaxGroups && !a.sched &&
+        a.num_extra == 0 && !a.idx && !sp.direct && !(STEP && sp.fuse)) {
+      if (a.has_bias)
+        hipLaunchKernelGGL((partition_split_kernel<DK, DV, SW, STEP, true, FP8>),
+                           dim3(nwork), dim3(SW * 64), 0, s, a, sp);
+      else
+        hipLaunchKernelGGL((partition_split_kernel<DK, DV, SW, STEP, false, FP8>),
+                           dim3(nwork), dim3(SW * 64), 0, s, a, sp);
+      return hipGetLastError();
+    }
   }
   const int nwork = a.sched ? a.sched_len : a.total_items;
   const int dyn = residency_lds_bytes<DK, DV, NW, FP8>(a);

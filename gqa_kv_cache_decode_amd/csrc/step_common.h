@@ -76,12 +76,13 @@ __device__ __forceinline__ void step_bookkeeping(const StepParams &sp, int b,
 }
 
 // Stores one KV group's rows of the new token (16-byte pieces) into the cache
-// slot.  Nothing in the same launch reads the slot, so the stores are not
+// slot, spread over the threads first, first + stride, ...  Nothing in the same launch reads the slot, so the stores are not
 // waited for; the launch's end makes them visible to later calls.
 __device__ __forceinline__ void store_group_row(const u32x4 *kn, u32x4 *kd,
                                                 int kpieces, const u32x4 *vn,
-                                                u32x4 *vd, int vpieces) {
-  for (int e = threadIdx.x; e < kpieces + vpieces; e += blockDim.x) {
+                                                u32x4 *vd, int vpieces,
+                                                int first, int stride) {
+  for (int e = first; e < kpieces + vpieces; e += stride) {
     if (e < kpieces)
       kd[e] = kn[e];
     else

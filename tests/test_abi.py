@@ -363,6 +363,37 @@ def test_fp8_checks(lib):
     assert lib.gqa_attend_branches_workspace_bytes(arr, 2, 32) == 0
 
 
+def test_fp8_group_split_plan(lib):
+    """fp8 chunking for the group split (64-wide heads: a work-group holds
+    eight KV groups, a wavefront a whole chunk of its group): the chunk gives
+    the split launch one round of one work-group per CU (256 to 511), with no
+    schedule; other shapes keep the bf16 rule."""
+    f8 = dict(dtype=bd.FP8_E4M3, ks=0xB0000, vs=0xB1000)
+    d64 = dict(dk=64, dv=64)
+    cases = [
+        # (cache fields, hq, chunk, chunks): the batched fp8 shape with
+        # 64-wide heads: eight wavefronts, eight groups per work-group
+        (dict(B=16, T=4096, H=8, **d64), 32, 256, 16),
+        # a test size that takes the split
+        (dict(B=16, T=1100, H=8, **d64), 32, 64, 18),
+    ]
+    for kw, hq, chunk, n in cases:
+        st, p = _plan(lib, _cache(**kw, **f8), hq)
+        assert st == 0 and (p.chunk_tokens, p.num_chunks) == (chunk, n), kw
+        assert p.sched_entries == 0 and p.balanced_groups == 0, kw
+        assert 256 <= kw["B"] * kw["H"] * n // 8 < 512, kw
+    # wider heads, too few work-groups, or KV heads that do not divide into
+    # sets of eight: the bf16 rule
+    for kw, hq in [(dict(B=16, T=4096, H=8), 32), (dict(B=8, T=2000, H=8), 32),
+                   (dict(B=4, T=1500, H=8, **d64), 32),
+                   (dict(B=16, T=4096, H=4, **d64), 16),
+                   (dict(B=8, T=600, H=8, **d64), 32)]:
+        _, p = _plan(lib, _cache(**kw, **f8), hq)
+        _, pb = _plan(lib, _cache(**kw), hq)
+        assert (p.chunk_tokens, p.num_chunks) == (pb.chunk_tokens,
+                                                  pb.num_chunks), kw
+
+
 def test_profile_request_validation(lib):
     """One event without the other is rejected; setting and cancelling a
     request makes no HIP call."""

@@ -161,7 +161,7 @@ def test_source_hash_ignores_comments_only():
 
 def test_kernel_names_follow_the_plan():
     """The ragged batch runs the balanced (work-queue) kernel, the other
-    workloads the chunked one."""
+    bf16 workloads the chunked one."""
     names = {n: bench.workload_by_name(n) for n in bench.DEFAULT_SET}
     assert bench.kernel_name(names["ragged"], False, False).startswith(
         "partition_balanced_kernel<128, 128, 2, true, false, false>")
@@ -170,6 +170,13 @@ def test_kernel_names_follow_the_plan():
             "partition_bf16_kernel<")
     assert bench.kernel_name(names["tiny"], False, False).startswith(
         "partition_f32_mfma_kernel<64, 64, 4, true")
+    # the fp8 batched step: the shared-group launch at 128-wide heads, the
+    # group split (eight KV groups per work-group) at 64-wide ones
+    fp8 = bench.workload_by_name("fp8")
+    assert bench.kernel_name(fp8, False, False) == (
+        "partition_bf16_kernel<128, 128, 4, true, false, false, true>")
+    assert bench.kernel_name(fp8.replace(dk=64, dv=64), False, False) == (
+        "partition_split_kernel<64, 64, 8, true, false, true>")
 
 
 def test_shape_overrides():

@@ -218,8 +218,10 @@ CASES = {
                     None),
     "d128_explicit": (wl.BATCHED_FP8.replace(batch=4, max_len=1000), "ragged",
                       128),
+    # (two KV heads: the group split does not apply, so 1024 items are a
+    # scheduled launch)
     "d128_scheduled": (wl.BATCHED_FP8.replace(batch=64, num_q_heads=16,
-                                              num_kv_heads=4, max_len=1000),
+                                              num_kv_heads=2, max_len=1000),
                        "ragged", 128),
     "dk192_hpk16": (wl.BATCHED_FP8.replace(batch=3, num_q_heads=64,
                                            num_kv_heads=4, dk=192, dv=128,
@@ -229,7 +231,23 @@ CASES = {
     "d256_mha": (wl.BATCHED_FP8.replace(batch=3, num_q_heads=2,
                                         num_kv_heads=2, dk=256, dv=256,
                                         max_len=600), "ragged", None),
+    # group split (64-wide heads): eight KV groups per work-group, a
+    # wavefront per group over the whole chunk
+    "d64_groupsplit": (wl.BATCHED_FP8.replace(batch=16, dk=64, dv=64,
+                                              max_len=1100), "ragged", None),
+    "d64_groupsplit_4k": (wl.BATCHED_FP8.replace(batch=16, dk=64, dv=64),
+                          "ragged", None),
 }
+
+
+def _assert_group_split(g, w, kc, vc):
+    """The library's plan for w is one the group-split launch takes: a plain
+    chunked plan whose items, in sets of eight, are one round of one
+    work-group per CU."""
+    plan = g.attend_plan(kc, vc, w.num_q_heads, 0)
+    assert w.dk + w.dv <= 128 and w.num_kv_heads % 8 == 0
+    assert plan.sched_entries == 0 and plan.balanced_groups == 0
+    assert 256 <= w.batch * w.num_kv_heads * plan.num_chunks // 8 < 512
 
 
 def _lens(w, seed, cap=None):
@@ -260,6 +278,8 @@ def test_attend_fp8(name, extra):
         bias_np = bias.double().numpy()
         bias = bias.cuda()
     cout = g.empty_carry(rows, w.dv)
+    if "groupsplit" in name:
+        _assert_group_split(g, w, kc, vc)
     say(f"[fp8] attend {name} {extra}")
     if chunk is None:
         out = g.attend_decode(q, kc, vc, ld, w.scale, carry_in=cin,
@@ -299,6 +319,9 @@ STEP_CASES = {
     "d256_mha": wl.BATCHED_FP8.replace(batch=3, num_q_heads=2,
                                        num_kv_heads=2, dk=256, dv=256,
                                        max_len=600),
+    "d64_groupsplit": wl.BATCHED_FP8.replace(batch=16, dk=64, dv=64,
+                                             max_len=1100),
+    "d64_groupsplit_4k": wl.BATCHED_FP8.replace(batch=16, dk=64, dv=64),
 }
 
 
@@ -323,12 +346,14 @@ def test_decode_step_fp8(name):
     lo = torch.empty_like(li)
     dropped = torch.zeros(1, dtype=torch.int32, device="cuda")
     bias = bias_np = None
-    if name == "d128_split":
+    if name in ("d128_split", "d64_groupsplit"):
         bias = torch.randn(w.batch, w.max_len, generator=gen)
         bias_np = bias.double().numpy()
         bias = bias.cuda()
     ws = g.step_workspace(kc, vc, w.num_q_heads)
     cout = g.empty_carry(w.batch * w.num_q_heads, w.dv)
+    if "groupsplit" in name:
+        _assert_group_split(g, w, kc, vc)
     say(f"[fp8] decode_step {name}")
     out = g.decode_step(x["q"].cuda(), kc, vc, kn.cuda(), vn.cuda(), li, lo,
                         w.scale, carry_out=cout, workspace=ws,
