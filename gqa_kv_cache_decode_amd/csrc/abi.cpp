@@ -344,7 +344,11 @@ hipError_t launch_step(const gqa_cache *c, const PartitionArgs &a,
 void single_branch(PartitionArgs *a) {
   a->total_cols = a->num_chunks;
   a->col_base = 0;
-  a->total_items = a->batch * a->num_kv_heads * a->num_chunks;
+  // (make_plan keeps a chunked plan's items within int32; a balanced plan's
+  // num_chunks counts piece slots, and its launch takes items from the queue
+  // instead)
+  const int64_t items = (int64_t)a->batch * a->num_kv_heads * a->num_chunks;
+  a->total_items = items <= std::numeric_limits<int32_t>::max() ? (int)items : 0;
   a->num_extra = 0;
   a->append_branch = 0;
   a->idx = nullptr;
