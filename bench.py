@@ -64,11 +64,11 @@ CSRC = ROOT / "gqa_kv_cache_decode_amd" / "csrc"
 # Sources of the dominant (partition) kernel: recorded counter readings are
 # only reported while these are unchanged.
 _MFMA16 = ["partition_mfma16.h", "fp8_common.h", "device_common.h", "launch.h",
-           "step_common.h"]
+           "step_common.h", "gather_common.h"]
 PARTITION_SOURCES = {"bf16": ["partition_bf16.hip"] + _MFMA16,
                      "fp8": ["partition_fp8.hip"] + _MFMA16,
                      "f32": ["partition_f32.hip", "device_common.h", "launch.h",
-                             "step_common.h"]}
+                             "step_common.h", "gather_common.h"]}
 COPY_BYTES = 256 << 20      # calibration copy for the byte counters
 WARM_REPLAYS = 5            # untimed replays of the step graph before timing
 DEFAULT_SET = ["tiny", "batched", "ragged", "long", "spike"]

@@ -65,8 +65,8 @@ CASES = {
     "f32_d64": (wl.TINY_F32.replace(batch=3, max_len=1000), 400, 16),
     "f32_d128": (wl.TINY_F32.replace(batch=3, num_q_heads=8, num_kv_heads=4,
                                      dk=128, dv=128, max_len=900), 300, 8),
-    # live lengths past one LDS window of the in-launch selection (49152
-    # slots for bf16 64-wide heads, 92832 for fp32 64-wide heads): ranks
+    # live lengths past one LDS window of the in-launch selection (65536
+    # slots for bf16 64-wide heads, 131072 for fp32 64-wide heads): ranks
     # carried across several windows
     "bf16_d64_windows": (wl.BATCHED_BF16.replace(batch=3, num_q_heads=2,
                                                  num_kv_heads=1, dk=64, dv=64,
