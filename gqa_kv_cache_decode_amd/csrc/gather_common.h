@@ -77,9 +77,10 @@ constexpr int kSelectWordsPerThread = 16;
 // dense run of slots (a pool of consecutive tokens) costs no more than a
 // sparse one and an empty word costs almost nothing.
 template <int NT>
-__device__ int gather_select(const int32_t *row, int width, int n, int lo,
-                             int cap, int *s_slot, uint32_t *lds,
-                             int lds_words, int *s_wave) {
+__device__ __forceinline__ int gather_select(const int32_t *row, int width,
+                                             int n, int lo, int cap,
+                                             int *s_slot, uint32_t *lds,
+                                             int lds_words, int *s_wave) {
   constexpr int kPer = kSelectWordsPerThread;
   const int hi = lo + cap;
   // bitmap words per window: the bitmap and its first ranks fit the scratch,
@@ -89,15 +90,22 @@ __device__ int gather_select(const int32_t *row, int width, int n, int lo,
   int *wpos = reinterpret_cast<int *>(lds + win);
   int *range = reinterpret_cast<int *>(lds + lds_words - 2);  // [wa, wb]
   const int j = threadIdx.x & 31;  // the bit a lane places
+  // the first batch of index entries is loaded before anything waits for
+  // n (the caller's length load is then in flight with it) and again at each
+  // later window, while the bitmap clears
+  int v[kSelectBatch];
+#pragma unroll
+  for (int k = 0; k < kSelectBatch; ++k)
+    v[k] = row[min(k * NT + (int)threadIdx.x, width - 1)];
   int base = 0;  // rank of the window's first selected slot
   for (int s0 = 0; s0 < n; s0 += win * 32) {
     const int s1 = min(s0 + win * 32, n);
     const int nw = (s1 - s0 + 31) >> 5;
-    // the first batch of index entries is loaded while the bitmap clears
-    int v[kSelectBatch];
+    if (s0 > 0) {
 #pragma unroll
-    for (int k = 0; k < kSelectBatch; ++k)
-      v[k] = row[min(k * NT + (int)threadIdx.x, width - 1)];
+      for (int k = 0; k < kSelectBatch; ++k)
+        v[k] = row[min(k * NT + (int)threadIdx.x, width - 1)];
+    }
     for (int w = threadIdx.x; w < nw; w += NT) bits[w] = 0u;
     if (threadIdx.x == 0) {
       range[0] = nw;

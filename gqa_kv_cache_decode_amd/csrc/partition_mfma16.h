@@ -483,14 +483,15 @@ __global__ __launch_bounds__(NW * 64) void partition_bf16_kernel(
 
   PartitionArgs a = args;
   int item, branch = 0;
-  if (a.sched) {  // scheduled launch: the table entry, or nothing to do
+  if (!GATHER && a.sched) {  // scheduled launch: the table entry, or nothing to do
     item = a.sched[blockIdx.x];
     if (item < 0) return;
   } else {
     // the block's branch (multi-branch launch: each branch owns a block
     // range starting at a multiple of 8), then its item within the branch
+    // (a gathered launch has one branch and no schedule)
     item = blockIdx.x;
-    branch = select_branch(a, item);
+    if (!GATHER) branch = select_branch(a, item);
     const int nitems = a.batch * a.num_kv_heads * a.num_chunks;
     if (item >= nitems) return;  // padding up to the next branch
     item = xcd_local_item(item, nitems);
@@ -753,8 +754,8 @@ hipError_t launch_one(const PartitionArgs &a, const StepParams &sp,
   }
   const int nwork = a.sched ? a.sched_len : a.total_items;
   const int dyn = residency_lds_bytes<DK, DV, NW, FP8>(a);
-  if (a.idx) {  // index-gathered: attend only, no bias, never scheduled
-    if (STEP || a.has_bias || a.sched) return hipErrorInvalidValue;
+  if (a.idx) {  // index-gathered: attend only, one branch, no bias or schedule
+    if (STEP || a.has_bias || a.sched || a.num_extra) return hipErrorInvalidValue;
     hipLaunchKernelGGL((partition_bf16_kernel<DK, DV, NW, false, false, true, FP8>),
                        dim3(nwork), dim3(NW * 64), 0, s, a, sp);
   } else if (a.has_bias) {
