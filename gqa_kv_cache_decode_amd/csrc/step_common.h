@@ -16,6 +16,8 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 // Points `a` at the branch that owns block `item` of a multi-branch launch
 // (branches hold ascending block ranges) and makes `item` local to it.
 __device__ __forceinline__ int select_branch(PartitionArgs &a, int &item) {
+  // (a one-cache launch reads none of the further branches' fields)
+  if (a.num_extra == 0) return 0;
   int base = 0, branch = 0;
 #pragma unroll
   for (int e = 0; e < kMaxExtraBranches; ++e) {
