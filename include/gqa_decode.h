@@ -188,7 +188,7 @@ GQA_API const char *gqa_status_string(int32_t status);
  * gqa_attend_gathered — records `start` on its stream immediately before
  * that kernel and `stop` immediately after it, so that
  * hipEventElapsedTime(start, stop) is that one kernel's time on the device,
- * without the calls' other kernels (schedule, selection, combine).
+ * without the calls' other kernels (schedule or balance, combine).
  *   start, stop  events owned by the caller, created with timing enabled;
  *                both NULL cancels a pending request.
  * The request is consumed by that one launch; a call whose argument checks
